@@ -1,0 +1,249 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic. Both the float64 oracle and the HIP path are fed from it,
+and it imports neither of them (numpy only, so it also runs where torch is
+absent).
+
+Values that the GPU reads as bfloat16 are drawn as float32 N(0,1) and rounded to
+bfloat16 with round-to-nearest-even. They are returned twice: as the raw uint16
+bit patterns (what the device tensor holds) and, on request, as float32 arrays
+holding exactly the same values (bf16 -> fp32 is exact), which the oracle widens
+to float64.
+
+Draw order inside one workload is fixed: lengths, then Q, then K, then V (or the
+shared cache), then the page permutation, then sparse indices, then sinks.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+# One seed per workload of the benchmark set.
+SEED_TINY_DENSE = 1001
+SEED_VARLEN_PREFILL = 1002
+SEED_PAGED_DECODE = 1003
+SEED_MLA_DECODE = 1004
+SEED_SPARSE_MLA = 1005
+
+_CHUNK = 1 << 24  # elements drawn per call when filling large tensors
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even) and return the
+    16-bit patterns as uint16. Inputs here are finite normals, so NaN/Inf
+    handling is not needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> 16) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bfloat16 bit patterns to float32 (exact)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """N(0,1) float32 draws rounded to bfloat16, returned as uint16 bits.
+    Large tensors are drawn in fixed-size chunks in C order, so the stream of
+    draws does not depend on memory limits."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, _CHUNK):
+        e = min(n, s + _CHUNK)
+        out[s:e] = bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def _paged_table(rng: np.random.Generator, lens: np.ndarray, page: int):
+    """Block table for sequences of the given lengths: one pool holding exactly
+    the pages needed, handed out as consecutive chunks of a random permutation.
+    Entries past a sequence's last page are -1."""
+    nblk = (lens + page - 1) // page
+    pool = int(nblk.sum())
+    perm = rng.permutation(pool).astype(np.int32)
+    width = max(1, int(nblk.max()))
+    table = np.full((len(lens), width), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return table, pool
+
+
+@dataclasses.dataclass
+class Dense:
+    """Packed variable-length problem: q (Tq,Hq,D), k (Tk,Hkv,D), v (Tk,Hkv,Dv).
+    For bfloat16 workloads the arrays hold uint16 bits; for float32 workloads
+    they hold float32 values."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cu_seqlens_q: np.ndarray
+    cu_seqlens_k: np.ndarray
+    dtype: str  # "bf16" or "f32"
+    scale: float
+    causal: bool
+    window: tuple
+    sinks: np.ndarray | None = None
+
+    @property
+    def batch(self):
+        return len(self.cu_seqlens_q) - 1
+
+    def f32(self, name):
+        a = getattr(self, name)
+        return bits_to_f32(a) if self.dtype == "bf16" else a
+
+
+def tiny_dense(seed: int = SEED_TINY_DENSE, s: int = 128, h: int = 4, d: int = 64) -> Dense:
+    """B=1, Sq=Sk=s, Hq=Hkv=h, head dim d, float32 N(0,1), non-causal,
+    scale 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((s, h, d), dtype=np.float32)
+    k = rng.standard_normal((s, h, d), dtype=np.float32)
+    v = rng.standard_normal((s, h, d), dtype=np.float32)
+    cu = np.array([0, s], dtype=np.int32)
+    return Dense(q, k, v, cu, cu.copy(), "f32", 1.0 / np.sqrt(d), False, (-1, -1))
+
+
+def varlen(seed: int, lens_q, lens_k=None, hq: int = 32, hkv: int = 8, d: int = 128,
+           dv: int | None = None, dtype: str = "bf16", causal: bool = True,
+           window=(-1, -1), scale: float | None = None, with_sinks: bool = False) -> Dense:
+    """Packed varlen problem with explicit per-sequence lengths."""
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = lens_q if lens_k is None else np.asarray(lens_k, dtype=np.int64)
+    return _varlen_draw(rng, lens_q, lens_k, hq, hkv, d, dv or d, dtype, causal,
+                        window, scale, with_sinks)
+
+
+def _varlen_draw(rng, lens_q, lens_k, hq, hkv, d, dv, dtype, causal, window, scale,
+                 with_sinks):
+    tq, tk = int(lens_q.sum()), int(lens_k.sum())
+    if dtype == "bf16":
+        q = _normal_bf16(rng, (tq, hq, d))
+        k = _normal_bf16(rng, (tk, hkv, d))
+        v = _normal_bf16(rng, (tk, hkv, dv))
+    else:
+        q = rng.standard_normal((tq, hq, d), dtype=np.float32)
+        k = rng.standard_normal((tk, hkv, d), dtype=np.float32)
+        v = rng.standard_normal((tk, hkv, dv), dtype=np.float32)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
+    return Dense(q, k, v, cu_q, cu_k, dtype, scale if scale is not None else 1.0 / np.sqrt(d),
+                 causal, tuple(window), sinks)
+
+
+def varlen_prefill(seed: int = SEED_VARLEN_PREFILL, nseq: int = 8, lo: int = 512,
+                   hi: int = 4096, hq: int = 32, hkv: int = 8, d: int = 128) -> Dense:
+    """Causal GQA prefill: nseq lengths uniform in [lo, hi] packed with
+    cu_seqlens, bf16 N(0,1), scale 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, endpoint=True, size=nseq)
+    return _varlen_draw(rng, lens, lens, hq, hkv, d, d, "bf16", True, (-1, -1), None, False)
+
+
+@dataclasses.dataclass
+class Paged:
+    """Decode against a paged cache. q (B,Sq,Hq,D) bits; k_cache (P,page,Hkv,D)
+    bits; v_cache (P,page,Hkv,Dv) bits, or None when K and V share one cache
+    (the value of key j is then its first dv entries)."""
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray | None
+    block_table: np.ndarray
+    cache_seqlens: np.ndarray
+    page_size: int
+    dv: int
+    scale: float
+    causal: bool
+    sinks: np.ndarray | None = None
+
+    @property
+    def batch(self):
+        return self.q.shape[0]
+
+
+def paged(seed: int, lens, sq: int = 1, hq: int = 32, hkv: int = 8, d: int = 128,
+          dv: int | None = None, page: int = 64, shared_kv: bool = False,
+          causal: bool = False, scale: float | None = None, with_sinks: bool = False) -> Paged:
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    return _paged_draw(rng, lens, sq, hq, hkv, d, dv or d, page, shared_kv, causal,
+                       scale, with_sinks)
+
+
+def _paged_draw(rng, lens, sq, hq, hkv, d, dv, page, shared_kv, causal, scale, with_sinks):
+    b = len(lens)
+    nblk = (lens + page - 1) // page
+    pool = max(1, int(nblk.sum()))
+    q = _normal_bf16(rng, (b, sq, hq, d))
+    k_cache = _normal_bf16(rng, (pool, page, hkv, d))
+    v_cache = None if shared_kv else _normal_bf16(rng, (pool, page, hkv, dv))
+    table, _ = _paged_table(rng, lens, page)
+    sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
+    return Paged(q, k_cache, v_cache, table, lens.astype(np.int32), page, dv,
+                 scale if scale is not None else 1.0 / np.sqrt(d), causal, sinks)
+
+
+def paged_decode(seed: int = SEED_PAGED_DECODE, batch: int = 64, lo: int = 1024,
+                 hi: int = 32768, page: int = 64, hq: int = 32, hkv: int = 8,
+                 d: int = 128) -> Paged:
+    """GQA decode: one query token per sequence, cache lengths uniform in
+    [lo, hi], bf16 N(0,1) K and V caches, non-causal, scale 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, endpoint=True, size=batch)
+    return _paged_draw(rng, lens, 1, hq, hkv, d, d, page, False, False, None, False)
+
+
+def mla_decode(seed: int = SEED_MLA_DECODE, batch: int = 64, sq: int = 2, hq: int = 128,
+               d: int = 576, dv: int = 512, page: int = 64, lo: int = 2048,
+               hi: int = 16384) -> Paged:
+    """MLA-absorbed decode: one latent+rope row of width d per cached token,
+    one KV head, value = first dv entries of the row, scale 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, endpoint=True, size=batch)
+    return _paged_draw(rng, lens, sq, hq, 1, d, dv, page, True, False, None, False)
+
+
+@dataclasses.dataclass
+class Sparse:
+    """Top-k sparse MLA: q (B,Sq,Hq,D) bits, kv (B,Sk,1,D) bits, indices
+    (B,Sq,1,topk) int32 with -1 marking unused slots, sinks (Hq) float32 or None."""
+    q: np.ndarray
+    kv: np.ndarray
+    indices: np.ndarray
+    sinks: np.ndarray | None
+    dv: int
+    scale: float
+    sparse_mode: int
+
+    @property
+    def batch(self):
+        return self.q.shape[0]
+
+
+def sparse_mla(seed: int = SEED_SPARSE_MLA, batch: int = 4, sq: int = 4096, sk: int = 32768,
+               hq: int = 64, d: int = 576, dv: int = 512, topk: int = 2048,
+               sparse_mode: int = 3, with_sinks: bool = True,
+               scale: float | None = None) -> Sparse:
+    """Per query token t, topk distinct key indices drawn without replacement
+    from its bottom-right causal prefix [0, sk - sq + t] (all of them, in random
+    order, when the prefix is shorter than topk), padded with -1. One sink logit
+    per query head, float32 N(0,1)."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (batch, sq, hq, d))
+    kv = _normal_bf16(rng, (batch, sk, 1, d))
+    idx = np.full((batch, sq, 1, topk), -1, dtype=np.int32)
+    delta = sk - sq
+    for b in range(batch):
+        for t in range(sq):
+            p = max(0, min(sk, delta + t + 1))
+            n = min(topk, p)
+            if n:
+                idx[b, t, 0, :n] = rng.choice(p, n, replace=False)
+    sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
+    return Sparse(q, kv, idx, sinks, dv, scale if scale is not None else 1.0 / np.sqrt(d),
+                  sparse_mode)

@@ -1,0 +1,468 @@
+"""Pins for the float64 oracle, checked against what the pages and mathematics
+fix: hand-derived closed forms (tests/golden), invariants, special cases that
+reduce to a library routine, and brute force on tiny inputs. A final test
+plants typical mistakes in the oracle and checks that the pins catch each one.
+CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from attention_attn_fwd_02_amd import inputs
+from oracle import attention as orc
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- closed forms
+def check_golden():
+    with open(GOLDEN) as f:
+        cases = json.load(f)
+    for c in cases:
+        if c["kind"] == "rows":
+            o, lse = orc.attend_rows(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                                     c["scale"], None, c.get("sink"))
+        elif c["kind"] == "dense":
+            o, lse = orc.attention_dense(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                                         c["scale"], c["causal"], tuple(c["window"]))
+        elif c["kind"] == "combine":
+            op = np.array(c["o_partial"])[:, :, :]          # (2 splits, 1 row, 2)
+            lp = np.array(c["lse_partial"])                  # (2, 1)
+            o, lse = orc.combine(op, lp, [0, 2], 1, 1, 1, 2)
+            np.testing.assert_allclose(o.ravel(), c["o"], rtol=0, atol=1e-14, err_msg=c["name"])
+            np.testing.assert_allclose(lse.ravel(), [c["lse"]], rtol=0, atol=1e-14)
+            o, lse = orc.combine(op, lp, [0, 2], 1, 1, 1, 2, sinks=[c["sink"]])
+            np.testing.assert_allclose(o.ravel(), c["o_sink"], rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lse.ravel(), [c["lse"]], rtol=0, atol=1e-14)
+            continue
+        elif c["kind"] == "sparse":
+            sk = c["sk"]
+            q = np.zeros((1, c["sq"], 1, 2))
+            kv = np.zeros((1, sk, 1, 2))
+            kv[0, :, 0, 0] = np.arange(sk)        # value (first entry) = key index
+            idx = np.array(c["indices"], dtype=np.int32).reshape(1, 1, 1, -1)
+            o, lse = orc.mla_sparse(q, kv, idx, 1.0, c["mode"], None, dv=1)
+            np.testing.assert_allclose(o.ravel(), [c["o"]], rtol=0, atol=1e-14, err_msg=c["name"])
+            np.testing.assert_allclose(lse.ravel(), [c["lse"]], rtol=0, atol=1e-14)
+            continue
+        np.testing.assert_allclose(o, np.array(c["o"]), rtol=0, atol=1e-13, err_msg=c["name"])
+        np.testing.assert_allclose(lse, np.array(c["lse"]), rtol=0, atol=1e-13, err_msg=c["name"])
+
+
+def test_golden_closed_forms():
+    check_golden()
+
+
+# ------------------------------------------------------------------ invariants
+def check_rows_sum_to_one():
+    """With V = identity the output row is the probability row itself."""
+    rng = _rng(1)
+    n = 9
+    q, k = rng.standard_normal((5, 4)), rng.standard_normal((n, 4))
+    vis = orc.visible_band(5, n, True, 2, -1)
+    o, _ = orc.attend_rows(q, k, np.eye(n), 0.7, vis)
+    np.testing.assert_allclose(o.sum(axis=1), 1.0, atol=1e-12)
+    assert (o >= 0).all() and (o[~vis] == 0).all()
+
+
+def test_rows_sum_to_one():
+    check_rows_sum_to_one()
+
+
+def check_lse_identity():
+    rng = _rng(2)
+    q, k, v = rng.standard_normal((6, 5)), rng.standard_normal((11, 5)), rng.standard_normal((11, 3))
+    vis = orc.visible_band(6, 11, True)
+    _, lse = orc.attend_rows(q, k, v, 0.4, vis)
+    for i in range(6):
+        s = [0.4 * math.fsum(q[i] * k[j]) for j in range(11) if vis[i, j]]
+        mx = max(s)
+        ref = math.log(math.fsum(math.exp(x - mx) for x in s)) + mx
+        assert abs(lse[i] - ref) <= 1e-12
+        assert mx - 1e-12 <= lse[i] <= mx + math.log(len(s)) + 1e-12
+
+
+def test_lse_identity():
+    check_lse_identity()
+
+
+def check_identical_keys():
+    """All keys equal: O is the mean of the values, LSE = S + log|J|."""
+    rng = _rng(3)
+    q = rng.standard_normal((4, 8))
+    k = np.tile(rng.standard_normal((1, 8)), (7, 1))
+    v = rng.standard_normal((7, 5))
+    o, lse = orc.attend_rows(q, k, v, 0.3, None)
+    np.testing.assert_allclose(o, np.tile(v.mean(axis=0), (4, 1)), atol=1e-13)
+    np.testing.assert_allclose(lse, 0.3 * (q @ k[0]) + math.log(7), atol=1e-13)
+
+
+def test_identical_keys():
+    check_identical_keys()
+
+
+def check_single_key():
+    rng = _rng(4)
+    q, k, v = rng.standard_normal((3, 6)), rng.standard_normal((1, 6)), rng.standard_normal((1, 4))
+    o, lse = orc.attend_rows(q, k, v, 1.3, None)
+    np.testing.assert_allclose(o, np.tile(v, (3, 1)), atol=1e-14)
+    np.testing.assert_allclose(lse, 1.3 * (q @ k[0]), atol=1e-14)
+
+
+def test_single_key():
+    check_single_key()
+
+
+def check_sink():
+    """O_sink = O * sigmoid(LSE - sink); sink -> -inf gives O, sink -> +inf gives 0."""
+    rng = _rng(5)
+    q, k, v = rng.standard_normal((5, 4)), rng.standard_normal((9, 4)), rng.standard_normal((9, 3))
+    vis = orc.visible_band(5, 9, True)
+    o, lse = orc.attend_rows(q, k, v, 0.8, vis)
+    for sink in (-2.0, 0.3, 1.7):
+        os_, ls = orc.attend_rows(q, k, v, 0.8, vis, sink)
+        np.testing.assert_allclose(os_, o / (1 + np.exp(sink - lse))[:, None], atol=1e-13)
+        np.testing.assert_allclose(ls, lse, atol=0)
+    np.testing.assert_allclose(orc.attend_rows(q, k, v, 0.8, vis, -1e30)[0], o, atol=1e-14)
+    np.testing.assert_allclose(orc.attend_rows(q, k, v, 0.8, vis, 1e30)[0], 0.0, atol=1e-14)
+
+
+def test_sink():
+    check_sink()
+
+
+def test_empty_rows():
+    q, k, v = np.ones((2, 3)), np.ones((0, 3)), np.ones((0, 2))
+    o, lse = orc.attend_rows(q, k, v, 1.0)
+    assert (o == 0).all() and np.isneginf(lse).all()
+    vis = np.zeros((2, 4), bool)
+    o, lse = orc.attend_rows(q, np.ones((4, 3)), np.ones((4, 2)), 1.0, vis, 0.5)
+    assert (o == 0).all() and np.isneginf(lse).all()
+
+
+# ----------------------------------------------------------- split and combine
+def _random_plan(rng, lens, max_splits):
+    """A hand-made plan with arbitrary cut points (including single-key and
+    empty-key splits), independent of the planner rule."""
+    ptr, tri = [0], []
+    for b, n in enumerate(lens):
+        ns = int(rng.integers(1, max_splits + 1))
+        cuts = np.sort(rng.integers(0, n + 1, size=ns - 1)) if n else np.zeros(ns - 1, int)
+        edges = [0, *cuts.tolist(), n]
+        for s in range(ns):
+            tri.append((b, edges[s], edges[s + 1]))
+        ptr.append(ptr[-1] + ns)
+    plan = np.zeros(orc.plan_words(len(lens), max_splits), np.int32)
+    plan[0], plan[1] = len(tri), 0
+    plan[2:3 + len(lens)] = ptr
+    plan[3 + len(lens):3 + len(lens) + 3 * len(tri)] = np.array(tri).ravel()
+    return plan
+
+
+def check_split_combine():
+    rng = _rng(6)
+    for causal, with_sink in ((False, False), (True, True)):
+        lens = [1, 5, 37, 64]
+        p = inputs.paged(11, lens, sq=2, hq=4, hkv=2, d=8, page=4, causal=causal,
+                         with_sinks=with_sink)
+        q, kc, vc = (inputs.bits_to_f32(x) for x in (p.q, p.k_cache, p.v_cache))
+        ref_o, ref_l = orc.attention_paged(q, kc, vc, p.block_table, p.cache_seqlens, 4, p.scale,
+                                           causal, p.sinks)
+        for _ in range(3):
+            plan = _random_plan(rng, lens, 6)
+            op, lp = orc.attention_paged_split(q, kc, vc, p.block_table, p.cache_seqlens, 4,
+                                               p.scale, plan, 6, causal)
+            ptr, _ = orc.plan_unpack(plan, len(lens))
+            o, l = orc.combine(op, lp, ptr, len(lens), 2, 4, 6, p.sinks)
+            np.testing.assert_allclose(o, ref_o, atol=1e-12)
+            np.testing.assert_allclose(l, ref_l, atol=1e-12)
+
+
+def test_split_combine():
+    check_split_combine()
+
+
+# ------------------------------------------------------------- GQA and varlen
+def check_gqa_equals_mha():
+    d = inputs.varlen(7, [5, 9], hq=6, hkv=2, d=8, causal=True)
+    q, k, v = d.f32("q"), d.f32("k"), d.f32("v")
+    o, lse = orc.attention_varlen(q, k, v, d.cu_seqlens_q, d.cu_seqlens_k, d.scale, True)
+    o2, lse2 = orc.attention_varlen(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1),
+                                    d.cu_seqlens_q, d.cu_seqlens_k, d.scale, True)
+    np.testing.assert_allclose(o, o2, atol=0)
+    np.testing.assert_allclose(lse, lse2, atol=0)
+
+
+def test_gqa_equals_mha():
+    check_gqa_equals_mha()
+
+
+def check_varlen_equals_dense():
+    lq, lk = [3, 8, 1], [6, 8, 4]
+    d = inputs.varlen(8, lq, lk, hq=4, hkv=2, d=8, causal=True, window=(3, -1))
+    q, k, v = d.f32("q"), d.f32("k"), d.f32("v")
+    o, lse = orc.attention_varlen(q, k, v, d.cu_seqlens_q, d.cu_seqlens_k, d.scale, True, (3, -1))
+    for b in range(3):
+        a0, a1 = d.cu_seqlens_q[b], d.cu_seqlens_q[b + 1]
+        c0, c1 = d.cu_seqlens_k[b], d.cu_seqlens_k[b + 1]
+        ob, lb = orc.attention_dense(q[None, a0:a1], k[None, c0:c1], v[None, c0:c1], d.scale,
+                                     True, (3, -1))
+        np.testing.assert_allclose(o[a0:a1], ob[0], atol=0)
+        np.testing.assert_allclose(lse[:, a0:a1], lb[0], atol=0)
+
+
+def test_varlen_equals_dense():
+    check_varlen_equals_dense()
+
+
+# ------------------------------------------------------------------ paged KV
+def check_paged_equals_contiguous():
+    p = inputs.paged(9, [13, 40, 1], sq=3, hq=4, hkv=2, d=8, page=8, causal=True)
+    q, kc, vc = (inputs.bits_to_f32(x) for x in (p.q, p.k_cache, p.v_cache))
+    o, lse = orc.attention_paged(q, kc, vc, p.block_table, p.cache_seqlens, 8, p.scale, True)
+    for b, n in enumerate(p.cache_seqlens):
+        # contiguous copy made by explicit loops, not by the oracle's gather
+        kk = np.stack([kc[p.block_table[b, j // 8], j % 8] for j in range(n)])
+        vv = np.stack([vc[p.block_table[b, j // 8], j % 8] for j in range(n)])
+        ob, lb = orc.attention_dense(q[b:b + 1], kk[None], vv[None], p.scale, True)
+        np.testing.assert_allclose(o[b], ob[0], atol=0)
+        np.testing.assert_allclose(lse[b], lb[0], atol=0)
+    # page-pool permutation invariance
+    rng = _rng(10)
+    perm = rng.permutation(kc.shape[0])
+    inv = np.argsort(perm)
+    table = np.where(p.block_table >= 0, inv[np.maximum(p.block_table, 0)], -1)
+    o2, l2 = orc.attention_paged(q, kc[perm], vc[perm], table, p.cache_seqlens, 8, p.scale, True)
+    np.testing.assert_allclose(o2, o, atol=0)
+    np.testing.assert_allclose(l2, lse, atol=0)
+
+
+def test_paged_equals_contiguous():
+    check_paged_equals_contiguous()
+
+
+def test_mate_mla_example_shape():
+    """MATE minimal MLA example: q (1,32,8,576), k_cache (4,16,2,576),
+    block_table zeros (1,4), cache_seqlens [32], head_dim_v 512. Every logical
+    page maps to physical page 0, so keys 16..31 repeat keys 0..15: O equals
+    attention over those 16 keys and LSE is larger by log 2."""
+    rng = _rng(12)
+    q = rng.standard_normal((1, 32, 8, 576))
+    kc = rng.standard_normal((4, 16, 2, 576))
+    table = np.zeros((1, 4), np.int32)
+    scale = 1 / math.sqrt(576)
+    o, lse = orc.mla_decode_paged(q, kc, table, [32], 16, scale)
+    k16 = kc[0][None]                     # (1, 16, 2, 576)
+    o16, l16 = orc.attention_dense(q, k16, k16[..., :512], scale)
+    np.testing.assert_allclose(o, o16, atol=1e-13)
+    np.testing.assert_allclose(lse, l16 + math.log(2), atol=1e-13)
+
+
+def check_gather():
+    rng = _rng(13)
+    cache = rng.integers(0, 65535, size=(7, 4, 2, 3)).astype(np.uint16)
+    table = np.array([[5, 0, 3, -1], [6, 1, 2, 4]], np.int32)
+    rows = orc.gather_paged(cache, table, 1, 14, 4)
+    for j in range(14):
+        assert np.array_equal(rows[j], cache[table[1, j // 4], j % 4])
+
+
+def test_gather():
+    check_gather()
+
+
+# ------------------------------------------------------------------------ MLA
+def test_mla_equals_generic():
+    p = inputs.paged(14, [20, 7], sq=2, hq=4, hkv=1, d=24, dv=16, page=8, shared_kv=True)
+    q, kc = inputs.bits_to_f32(p.q), inputs.bits_to_f32(p.k_cache)
+    o, lse = orc.mla_decode_paged(q, kc, p.block_table, p.cache_seqlens, 8, p.scale, dv=16)
+    o2, l2 = orc.attention_paged(q, kc, np.ascontiguousarray(kc[..., :16]), p.block_table,
+                                 p.cache_seqlens, 8, p.scale)
+    np.testing.assert_allclose(o, o2, atol=0)
+    np.testing.assert_allclose(lse, l2, atol=0)
+
+
+# --------------------------------------------------------------------- sparse
+def check_sparse():
+    """Indices = whole causal prefix (shorter than topk) equals dense
+    bottom-right causal; index order is irrelevant; -1 slots are ignored."""
+    s = inputs.sparse_mla(15, batch=2, sq=5, sk=12, hq=4, d=24, dv=16, topk=16)
+    q, kv = inputs.bits_to_f32(s.q), inputs.bits_to_f32(s.kv)
+    o, lse = orc.mla_sparse(q, kv, s.indices, s.scale, 3, s.sinks, dv=16)
+    od, ld = orc.attention_dense(q, kv, np.ascontiguousarray(kv[..., :16]), s.scale, True,
+                                 sinks=s.sinks)
+    np.testing.assert_allclose(o, od, atol=1e-13)
+    np.testing.assert_allclose(lse, ld, atol=1e-13)
+    rng = _rng(16)
+    idx2 = s.indices.copy()
+    for b in range(2):
+        for t in range(5):
+            idx2[b, t, 0] = rng.permutation(idx2[b, t, 0])
+    o2, l2 = orc.mla_sparse(q, kv, idx2, s.scale, 3, s.sinks, dv=16)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    np.testing.assert_allclose(l2, lse, atol=1e-13)
+    # mode 0 with indices beyond the causal limit: those keys now count
+    idx3 = np.full_like(s.indices, -1)
+    idx3[..., 0] = 11
+    o3, _ = orc.mla_sparse(q, kv, idx3, s.scale, 0, None, dv=16)
+    np.testing.assert_allclose(o3[:, :, :, :], np.broadcast_to(kv[:, 11:12, :, :16], o3.shape),
+                               atol=0)
+    o4, l4 = orc.mla_sparse(q, kv, idx3, s.scale, 3, None, dv=16)
+    assert (o4[:, :4] == 0).all() and np.isneginf(l4[:, :, :4]).all()  # t < 4 cannot see key 11
+
+
+def test_sparse():
+    check_sparse()
+
+
+# ----------------------------------------------------------- library routine
+def test_matches_torch_sdpa_float64():
+    torch = pytest.importorskip("torch")
+    d = inputs.varlen(17, [33], hq=4, hkv=4, d=16, causal=True, dtype="f32")
+    q, k, v = (torch.from_numpy(d.f32(n).astype(np.float64)).permute(1, 0, 2)[None]
+               for n in ("q", "k", "v"))
+    for causal in (False, True):
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=causal,
+                                                               scale=d.scale)
+        o, _ = orc.attention_varlen(d.f32("q"), d.f32("k"), d.f32("v"), d.cu_seqlens_q,
+                                    d.cu_seqlens_k, d.scale, causal)
+        np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+# ---------------------------------------------------------------- brute force
+def check_brute_force():
+    rng = _rng(18)
+    for causal, window, sink in ((False, (-1, -1), False), (True, (-1, -1), True),
+                                 (False, (2, 1), False), (True, (1, -1), True)):
+        bsz, sq, sk, hq, hkv, dd, dv = 2, 5, 7, 4, 2, 3, 2
+        q = rng.standard_normal((bsz, sq, hq, dd))
+        k = rng.standard_normal((bsz, sk, hkv, dd))
+        v = rng.standard_normal((bsz, sk, hkv, dv))
+        sinks = rng.standard_normal(hq) if sink else None
+        o, lse = orc.attention_dense(q, k, v, 0.9, causal, window, sinks)
+        ob, lb = brute.dense(q, k, v, 0.9, causal, window, sinks)
+        np.testing.assert_allclose(o, np.array(ob, dtype=float), atol=1e-12)
+        np.testing.assert_allclose(lse, np.array(lb, dtype=float), atol=1e-12)
+
+
+def test_brute_force():
+    check_brute_force()
+
+
+# -------------------------------------------------------------------- planner
+def _check_plan(plan, lens, page, max_splits):
+    bsz = len(lens)
+    ptr, tri = orc.plan_unpack(plan, bsz)
+    assert ptr[0] == 0 and ptr[-1] == plan[0] == len(tri)
+    for b, n in enumerate(lens):
+        ns = ptr[b + 1] - ptr[b]
+        assert 0 <= ns <= max_splits
+        assert (ns == 0) == (n <= 0)
+        seg = tri[ptr[b]:ptr[b + 1]]
+        assert (seg[:, 0] == b).all()
+        if ns:
+            assert seg[0, 1] == 0 and seg[-1, 2] == n                       # cover
+            assert (seg[1:, 1] == seg[:-1, 2]).all()                         # contiguous
+            assert (seg[:, 2] > seg[:, 1]).all()                             # non-empty
+            assert (seg[:, 1] % page == 0).all()                             # page aligned
+
+
+def test_planner_properties():
+    rng = _rng(19)
+    for _ in range(200):
+        bsz = int(rng.integers(1, 40))
+        page = int(rng.choice([16, 64]))
+        lens = rng.integers(0, 40000, size=bsz)
+        ms = int(rng.integers(1, 17))
+        plan = orc.plan_splits(lens, page, int(rng.integers(1, 9)), 256, int(rng.integers(1, 8)),
+                               ms, int(rng.integers(1, 9)))
+        _check_plan(plan, lens, page, ms)
+
+
+def test_planner_rule_example():
+    """Hand-worked instance of the rule: lens [1000, 64, 0], page 64,
+    units_per_block 2, 4 CUs x 1 wave, max 3 splits, min 2 blocks:
+    nblk = [16, 1, 0], total = 34, bps = max(2, ceil(34/4)) = 9,
+    ns0 = min(3, ceil(16/9)) = 2, pps0 = 8 -> splits [0,512) [512,1000);
+    ns1 = 1 -> [0,64); ns2 = 0."""
+    plan = orc.plan_splits([1000, 64, 0], 64, 2, 4, 1, 3, 2)
+    assert plan[:2 + 4 + 9].tolist() == [3, 9, 0, 2, 3, 3,
+                                              0, 0, 512, 0, 512, 1000, 1, 0, 64]
+
+
+# --------------------------------------------------------------- mutation test
+def _mutants():
+    base_rows = orc.attend_rows
+    base_vis = orc.visible_band
+    base_combine = orc.combine
+    base_gather = orc.gather_paged
+
+    def no_scale(q, k, v, scale, visible=None, sink=None):
+        return base_rows(q, k, v, 1.0, visible, sink)
+
+    def sink_dropped(q, k, v, scale, visible=None, sink=None):
+        return base_rows(q, k, v, scale, visible, None)
+
+    def lse_without_max(q, k, v, scale, visible=None, sink=None):
+        o, lse = base_rows(q, k, v, scale, visible, sink)
+        qq, kk = np.asarray(q, float), np.asarray(k, float)
+        if kk.shape[0] == 0:
+            return o, lse
+        s = scale * (qq @ kk.T)
+        if visible is not None:
+            s = np.where(visible, s, -np.inf)
+        return o, lse - s.max(axis=1)
+
+    def transposed_kv(q, k, v, scale, visible=None, sink=None):
+        k = np.asarray(k)
+        v = np.asarray(v)
+        return base_rows(q, k[::-1], v, scale, visible, sink)
+
+    def causal_top_left(lq, lk, causal, window_left=-1, window_right=-1, q_pos=None, k_pos=None):
+        return base_vis(lk, lk, causal, window_left, window_right,
+                        q_pos=np.arange(lq) if q_pos is None else q_pos, k_pos=k_pos)[:lq]
+
+    def window_sides_swapped(lq, lk, causal, window_left=-1, window_right=-1, q_pos=None,
+                             k_pos=None):
+        return base_vis(lq, lk, causal, window_right, window_left, q_pos, k_pos)
+
+    def combine_unweighted(o_partial, lse_partial, split_ptr, batch, seqlen_q, hq, max_splits,
+                           sinks=None):
+        return base_combine(o_partial, np.zeros_like(lse_partial), split_ptr, batch, seqlen_q, hq,
+                            max_splits, sinks)
+
+    def gather_swapped(cache, block_table, b, n, page_size):
+        j = np.arange(n)
+        return cache[np.asarray(block_table)[b, j % page_size % block_table.shape[1]],
+                     j // page_size % cache.shape[1]]
+
+    return [("attend_rows", no_scale), ("attend_rows", sink_dropped),
+            ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
+            ("visible_band", causal_top_left), ("visible_band", window_sides_swapped),
+            ("combine", combine_unweighted), ("gather_paged", gather_swapped)]
+
+
+PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical_keys,
+        check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
+        check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
+        check_brute_force]
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_pins_catch_planted_mistakes(monkeypatch, i):
+    name, fn = _mutants()[i]
+    monkeypatch.setattr(orc, name, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {fn.__name__} of {name} passed every pin"
