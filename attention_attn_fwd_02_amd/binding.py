@@ -1,0 +1,302 @@
+"""ctypes binding of libattn_mi355.so.
+
+Argument marshalling only: every function here checks that the torch tensors
+match the shapes and dtypes of the C ABI (include/attn.h), passes their device
+pointers and the current HIP stream, and turns a non-zero status into a Python
+exception. All arithmetic runs in the library's kernels. There is no fallback:
+when the library is missing or no GPU is present, calls raise.
+
+Function names are those of the C ABI.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn_mi355.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EEMPTY, ATTN_EHIP = range(5)
+ATTN_BF16, ATTN_F32 = 0, 1
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_device_info": (_I, [_I, ctypes.POINTER(_I)]),
+    "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                             _P, _P, _P, _P]),
+    "attn_plan_words": (ctypes.c_size_t, [_I, _I]),
+    "attn_plan_splits": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                               _P, _I, _P, _P, _P]),
+    "attn_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P]),
+    "mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
+    "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "attn_debug_gather_paged": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB_PATH):
+    """Loads the library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise AttnError(f"{path} is missing: build it with attention_attn_fwd_02_amd.build")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def _check(status: int):
+    if status == ATTN_OK:
+        return
+    msg = load().attn_last_error().decode()
+    name = load().attn_status_string(status).decode()
+    text = f"{name}: {msg}"
+    if status in (ATTN_EINVAL, ATTN_EEMPTY):
+        raise ValueError(text)
+    if status == ATTN_EUNSUPPORTED:
+        raise NotImplementedError(text)
+    raise AttnError(text)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(*ts, dtype=None):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise ValueError(f"expected {dtype}, got {t.dtype}")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------- prefill
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                    causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
+                    return_lse=True):
+    """q (Tq,Hq,D), k (Tk,Hkv,D), v (Tk,Hkv,Dv) bf16 or fp32; cu_seqlens int32
+    (B+1). Returns (out (Tq,Hq,Dv), lse (Hq,Tq) fp32 or None)."""
+    _dev(q, k, v)
+    _dev(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v dtypes differ")
+    tq, hq, d = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=q.dtype)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                                  _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k),
+                                  hq, hkv, d, dv, _dtype_code(q), float(scale), int(bool(causal)),
+                                  int(window[0]), int(window[1]), _ptr(sinks), _ptr(out),
+                                  _ptr(lse), _stream()))
+    return out, lse
+
+
+# -------------------------------------------------------------------- planner
+def attn_plan_words(batch, max_splits):
+    return int(load().attn_plan_words(int(batch), int(max_splits)))
+
+
+def attn_plan_splits(cache_seqlens, page_size, units_per_block, num_cu, waves, max_splits,
+                     min_blocks, plan=None):
+    _dev(cache_seqlens, dtype=torch.int32)
+    batch = cache_seqlens.numel()
+    if plan is None:
+        plan = torch.zeros(attn_plan_words(batch, max_splits), dtype=torch.int32,
+                           device=cache_seqlens.device)
+    _dev(plan, dtype=torch.int32)
+    _check(load().attn_plan_splits(_ptr(cache_seqlens), batch, int(page_size),
+                                   int(units_per_block), int(num_cu), int(waves), int(max_splits),
+                                   int(min_blocks), _ptr(plan), _stream()))
+    return plan
+
+
+def attn_device_info(device=0):
+    n = _I(0)
+    _check(load().attn_device_info(int(device), ctypes.byref(n)))
+    return n.value
+
+
+# --------------------------------------------------------------------- decode
+def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits, scale,
+                      causal=False, o_partial=None, lse_partial=None):
+    """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) bf16. Returns partials
+    (B*max_splits, Sq*Hq, Dv) and (B*max_splits, Sq*Hq) fp32."""
+    _dev(q, k_cache, v_cache, dtype=torch.bfloat16)
+    _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
+    b, sq, hq, d = q.shape
+    page, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    if o_partial is None:
+        o_partial = torch.empty((b * max_splits, sq * hq, dv), dtype=torch.float32,
+                                device=q.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((b * max_splits, sq * hq), dtype=torch.float32, device=q.device)
+    _dev(o_partial, lse_partial, dtype=torch.float32)
+    _check(load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                    block_table.shape[1], _ptr(cache_seqlens), b, sq, hq, hkv, d,
+                                    dv, page, ATTN_BF16, float(scale), int(bool(causal)),
+                                    _ptr(plan), int(max_splits), _ptr(o_partial),
+                                    _ptr(lse_partial), _stream()))
+    return o_partial, lse_partial
+
+
+def attn_combine(o_partial, lse_partial, plan, batch, seqlen_q, hq, max_splits, sinks=None,
+                 out_dtype=torch.bfloat16, out=None, lse=None, return_lse=True):
+    _dev(o_partial, lse_partial, dtype=torch.float32)
+    _dev(plan, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    dv = o_partial.shape[2]
+    if out is None:
+        out = torch.empty((batch, seqlen_q, hq, dv), dtype=out_dtype, device=o_partial.device)
+    if lse is None and return_lse:
+        lse = torch.empty((batch, hq, seqlen_q), dtype=torch.float32, device=o_partial.device)
+    _dev(out)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_combine(_ptr(o_partial), _ptr(lse_partial), _ptr(plan), int(batch),
+                               int(seqlen_q), int(hq), dv, int(max_splits), _ptr(sinks),
+                               _dtype_code(out), _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, scale,
+                     causal=False, o_partial=None, lse_partial=None):
+    """q (B,Sq,Hq,576), kv_cache (P,page,1,576) bf16; partials with Dv = 512."""
+    _dev(q, kv_cache, dtype=torch.bfloat16)
+    _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
+    b, sq, hq, d = q.shape
+    if d != 576 or kv_cache.shape[3] != 576 or kv_cache.shape[2] != 1:
+        raise NotImplementedError("MLA decode expects 576-wide rows and one KV head")
+    if o_partial is None:
+        o_partial = torch.empty((b * max_splits, sq * hq, 512), dtype=torch.float32,
+                                device=q.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((b * max_splits, sq * hq), dtype=torch.float32, device=q.device)
+    _dev(o_partial, lse_partial, dtype=torch.float32)
+    _check(load().mla_decode_paged(_ptr(q), _ptr(kv_cache), _ptr(block_table),
+                                   block_table.shape[1], _ptr(cache_seqlens), b, sq, hq,
+                                   kv_cache.shape[1], float(scale), int(bool(causal)), _ptr(plan),
+                                   int(max_splits), _ptr(o_partial), _ptr(lse_partial),
+                                   _stream()))
+    return o_partial, lse_partial
+
+
+def mla_sparse_fwd(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, out=None, lse=None,
+                   return_lse=True):
+    """q (B,Sq,Hq,576), kv (B,Sk,1,576) bf16, indices (B,Sq,1,topk) int32."""
+    _dev(q, kv, dtype=torch.bfloat16)
+    _dev(sparse_indices, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    b, sq, hq, d = q.shape
+    sk = kv.shape[1]
+    if d != 576 or kv.shape[3] != 576 or kv.shape[2] != 1:
+        raise NotImplementedError("sparse MLA expects 576-wide rows and one KV head")
+    topk = sparse_indices.shape[-1]
+    if out is None:
+        out = torch.empty((b, sq, hq, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    _check(load().mla_sparse_fwd(_ptr(q), _ptr(kv), _ptr(sparse_indices), topk, b, sq, sk, hq,
+                                 float(scale), int(sparse_mode), _ptr(sinks), _ptr(out), _ptr(lse),
+                                 _stream()))
+    return out, lse
+
+
+def attn_debug_gather_paged(cache, block_table, cache_seqlens, b, max_rows):
+    """Logical rows of sequence b from a paged cache (P, page, ...) of 16-bit
+    elements, copied by the kernels' own page-address computation."""
+    _dev(cache)
+    _dev(block_table, cache_seqlens, dtype=torch.int32)
+    if cache.element_size() != 2:
+        raise ValueError("16-bit cache expected")
+    row_elems = cache[0, 0].numel()
+    dst = torch.zeros((max_rows, row_elems), dtype=cache.dtype, device=cache.device)
+    _check(load().attn_debug_gather_paged(_ptr(cache), _ptr(block_table), block_table.shape[1],
+                                          _ptr(cache_seqlens), int(b), cache.shape[1], row_elems,
+                                          int(max_rows), _ptr(dst), _stream()))
+    return dst
+
+
+# ------------------------------------------------------- composed decode calls
+# The split planner sizes splits so that the decode grid holds about
+# num_cu * waves workgroups; these are its defaults for the two decode shapes.
+GQA_ROWS_PER_WG = 16
+MLA_ROWS_PER_WG = 64
+
+
+def _num_cu(device):
+    return attn_device_info(device.index if device.index is not None else 0)
+
+
+def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=False, sinks=None,
+                 max_splits=16, waves=4, min_blocks=4, num_cu=None, out_dtype=torch.bfloat16):
+    """plan -> attn_decode_paged -> attn_combine. Returns (out (B,Sq,Hq,Dv),
+    lse (B,Hq,Sq), plan)."""
+    b, sq, hq, _ = q.shape
+    hkv = k_cache.shape[2]
+    rows = sq * (hq // max(1, hkv))
+    upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
+    plan = attn_plan_splits(cache_seqlens, k_cache.shape[1], upb, num_cu or _num_cu(q.device),
+                            waves, max_splits, min_blocks)
+    op, lp = attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
+                               scale, causal)
+    out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits, sinks, out_dtype)
+    return out, lse, plan
+
+
+def mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal=False, max_splits=16,
+               waves=2, min_blocks=4, num_cu=None):
+    """plan -> mla_decode_paged -> attn_combine (dv = 512)."""
+    b, sq, hq, _ = q.shape
+    upb = (sq * hq + MLA_ROWS_PER_WG - 1) // MLA_ROWS_PER_WG
+    plan = attn_plan_splits(cache_seqlens, kv_cache.shape[1], upb, num_cu or _num_cu(q.device),
+                            waves, max_splits, min_blocks)
+    op, lp = mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, scale,
+                              causal)
+    out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
+    return out, lse, plan

@@ -1,0 +1,275 @@
+// C ABI of libattn_mi355.so (declared in include/attn.h): host-side argument
+// checks, instance selection and launches on the caller's stream. Checks run
+// before anything is enqueued; device tensor contents are never inspected.
+#include <hip/hip_runtime.h>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return ATTN_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int32_t status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_EINVAL: return "ATTN_EINVAL";
+    case ATTN_EUNSUPPORTED: return "ATTN_EUNSUPPORTED";
+    case ATTN_EEMPTY: return "ATTN_EEMPTY";
+    case ATTN_EHIP: return "ATTN_EHIP";
+    default: return "ATTN_UNKNOWN";
+  }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int32_t attn_device_info(int32_t device, int32_t* num_cu) {
+  REQUIRE(num_cu, ATTN_EINVAL, "num_cu is NULL");
+  int v = 0;
+  hipError_t e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_status(e, "hipDeviceGetAttribute");
+  *num_cu = v;
+  return ok();
+}
+
+int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_k, int32_t hq, int32_t hkv, int32_t d, int32_t dv,
+                        int32_t dtype, float scale, int32_t causal, int32_t window_left,
+                        int32_t window_right, const float* sinks, void* out, float* lse,
+                        void* stream) {
+  REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0, ATTN_EEMPTY,
+          "empty dimension (batch=%d max_seqlen_q=%d hq=%d hkv=%d d=%d dv=%d)", batch,
+          max_seqlen_q, hq, hkv, d, dv);
+  REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
+  REQUIRE(q && k && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL,
+          "null tensor pointer");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
+  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_F32, ATTN_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
+          "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
+  attn::VarlenArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  const int rows = dtype == ATTN_BF16 ? attn::varlen_bf16_rows(d) : attn::varlen_f32_rows(d);
+  a.nqt = (max_seqlen_q + rows - 1) / rows;
+  REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
+  hipError_t e = dtype == ATTN_BF16 ? attn::launch_varlen_bf16(a, d, as_stream(stream))
+                                    : attn::launch_varlen_f32(a, d, as_stream(stream));
+  return hip_status(e, "attn_fwd_varlen launch");
+}
+
+size_t attn_plan_words(int32_t batch, int32_t max_splits) {
+  if (batch <= 0 || max_splits <= 0) return 0;
+  return 3 + (size_t)batch + 3 * (size_t)batch * max_splits;
+}
+
+int32_t attn_plan_splits(const int32_t* cache_seqlens, int32_t batch, int32_t page_size,
+                         int32_t units_per_block, int32_t num_cu, int32_t waves,
+                         int32_t max_splits, int32_t min_blocks, int32_t* plan, void* stream) {
+  REQUIRE(batch > 0, ATTN_EEMPTY, "batch is 0");
+  REQUIRE(cache_seqlens && plan, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(page_size > 0 && units_per_block > 0 && num_cu > 0 && waves > 0 && min_blocks > 0,
+          ATTN_EINVAL, "page_size, units_per_block, num_cu, waves, min_blocks must be > 0");
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  return hip_status(attn::launch_plan(cache_seqlens, batch, page_size, units_per_block, num_cu,
+                                      waves, max_splits, min_blocks, plan, as_stream(stream)),
+                    "attn_plan_splits launch");
+}
+
+int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                          int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                          int32_t dtype, float scale, int32_t causal, const int32_t* plan,
+                          int32_t max_splits, float* o_partial, float* lse_partial,
+                          void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
+              max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(q && k_cache && v_cache && block_table && cache_seqlens && plan && o_partial &&
+              lse_partial,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
+          d, dv);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  attn::DecodeArgs a;
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.page = page_size;
+  a.causal = causal ? 1 : 0;
+  a.max_splits = max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  return hip_status(attn::launch_decode_gqa(a, as_stream(stream)), "attn_decode_paged launch");
+}
+
+int32_t attn_combine(const float* o_partial, const float* lse_partial, const int32_t* plan,
+                     int32_t batch, int32_t seqlen_q, int32_t hq, int32_t dv, int32_t max_splits,
+                     const float* sinks, int32_t out_dtype, void* out, float* lse,
+                     void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && dv > 0, ATTN_EEMPTY, "empty dimension");
+  REQUIRE(o_partial && lse_partial && plan && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(out_dtype == ATTN_BF16 || out_dtype == ATTN_F32, ATTN_EUNSUPPORTED, "out_dtype %d",
+          out_dtype);
+  REQUIRE(dv % 4 == 0 && dv <= 1024, ATTN_EUNSUPPORTED, "dv must be a multiple of 4, <= 1024");
+  attn::CombineArgs a;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.plan = plan;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.dv = dv;
+  a.max_splits = max_splits;
+  a.out_bf16 = out_dtype == ATTN_BF16;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(attn::launch_combine(a, as_stream(stream)), "attn_combine launch");
+}
+
+int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                         int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t batch,
+                         int32_t seqlen_q, int32_t hq, int32_t page_size, float scale,
+                         int32_t causal, const int32_t* plan, int32_t max_splits,
+                         float* o_partial, float* lse_partial, void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && page_size > 0 && max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(q && kv_cache && block_table && cache_seqlens && plan && o_partial && lse_partial,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  attn::DecodeArgs a;
+  a.q = q;
+  a.kc = kv_cache;
+  a.vc = nullptr;
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.hkv = 1;
+  a.page = page_size;
+  a.causal = causal ? 1 : 0;
+  a.max_splits = max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  return hip_status(attn::launch_decode_mla(a, as_stream(stream)), "mla_decode_paged launch");
+}
+
+int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indices, int32_t topk,
+                       int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t hq, float scale,
+                       int32_t sparse_mode, const float* sinks, void* out, float* lse,
+                       void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && seqlen_k > 0 && hq > 0 && topk > 0, ATTN_EEMPTY,
+          "empty dimension");
+  REQUIRE(q && kv && sparse_indices && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
+  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
+  REQUIRE((long)batch * seqlen_q * ((hq + 63) / 64) < (1L << 31), ATTN_EUNSUPPORTED,
+          "grid too large");
+  attn::SparseArgs a;
+  a.q = q;
+  a.kv = kv;
+  a.idx = sparse_indices;
+  a.topk = topk;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.sk = seqlen_k;
+  a.hq = hq;
+  a.mode = sparse_mode;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(attn::launch_sparse_mla(a, as_stream(stream)), "mla_sparse_fwd launch");
+}
+
+int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t b,
+                                int32_t page_size, int32_t row_elems, int32_t max_rows, void* dst,
+                                void* stream) {
+  REQUIRE(cache && block_table && cache_seqlens && dst, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(page_size > 0 && max_pages_per_seq > 0 && row_elems > 0 && b >= 0, ATTN_EEMPTY,
+          "empty dimension");
+  REQUIRE(row_elems % 8 == 0, ATTN_EUNSUPPORTED, "row_elems must be a multiple of 8");
+  REQUIRE(max_rows >= 0, ATTN_EINVAL, "max_rows < 0");
+  return hip_status(attn::launch_gather(cache, block_table, max_pages_per_seq, cache_seqlens, b,
+                                        page_size, row_elems, max_rows, dst, as_stream(stream)),
+                    "attn_debug_gather_paged launch");
+}
+
+}  // extern "C"

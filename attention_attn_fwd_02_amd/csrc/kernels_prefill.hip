@@ -1,0 +1,256 @@
+// Packed variable-length attention (prefill) for gfx950.
+// [MATE "Attention" page, FMHA: flash_attn_varlen_func; CANN flash_attn:
+//  cu_seqlens_q / cu_seqlens_kv; lite_boost flash_attention: causal and
+//  window_size]
+#include "attn_core.h"
+#include "launch.h"
+
+namespace attn {
+
+namespace {
+
+// Work order shared by the prefill grids: longest query tiles first (with a
+// causal mask the last tile of a sequence sees the most keys), and the query
+// heads of one GQA group placed 8 workgroup ids apart so that they run on the
+// same XCD (workgroups are dispatched round-robin over the 8 XCDs) and share
+// their K/V tiles through that XCD's L2.
+struct PrefillWork {
+  int b, h, kvh, qt;
+};
+
+__device__ __forceinline__ bool decode_prefill_work(int p, int batch, int hq, int hkv, int nqt,
+                                                    PrefillWork& w) {
+  const int grp = hq / hkv;
+  const int rest = (p / (8 * grp)) * 8 + (p & 7);
+  const int hg = (p >> 3) % grp;
+  const int logical = rest * grp + hg;
+  if (logical >= nqt * batch * hq) return false;
+  int t = logical / grp;
+  w.kvh = t % hkv;
+  t /= hkv;
+  w.b = t % batch;
+  w.qt = nqt - 1 - t / batch;
+  w.h = w.kvh * grp + hg;
+  return true;
+}
+
+int prefill_grid(int batch, int hq, int hkv, int nqt) {
+  const int unit = 8 * (hq / hkv);
+  const long total = (long)nqt * batch * hq;
+  return (int)(((total + unit - 1) / unit) * unit);
+}
+
+// Key range and masking of one query tile [row0, row_last] of a sequence with
+// Lq queries and Lk keys; diagonal of query t is t + (Lk - Lq).
+struct Band {
+  int lo, hi;       // keys to visit
+  int delta, wl, wr;  // wr is -1 (unbounded) or the effective right bound
+};
+
+__device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk, int causal,
+                                          int wl, int wr, int bn) {
+  Band bd;
+  bd.delta = lk - lq;
+  bd.wl = wl;
+  bd.wr = causal ? (wr < 0 ? 0 : min(wr, 0)) : wr;
+  bd.hi = lk;
+  if (bd.wr >= 0) bd.hi = min(bd.hi, row_last + bd.delta + bd.wr + 1);
+  bd.lo = 0;
+  if (wl >= 0) bd.lo = max(0, row0 + bd.delta - wl);
+  bd.lo = (bd.lo / bn) * bn;
+  return bd;
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS)
+k_varlen_bf16(VarlenArgs a) {
+  using Core = TileCore<C>;
+  using M = typename Core::M;
+  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_BYTES / 2];
+  PrefillWork w;
+  if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
+  const int q0 = a.cu_q[w.b];
+  const int lq = a.cu_q[w.b + 1] - q0;
+  const int row0 = w.qt * C::ROWS;
+  if (row0 >= lq) return;
+  const int k0 = a.cu_k[w.b];
+  const int lk = a.cu_k[w.b + 1] - k0;
+  const int row_last = min(lq, row0 + C::ROWS) - 1;
+  const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int trow = row0 + wave * C::R + M::row(lane);
+  const bool row_ok = trow < lq;
+  const bf16_t* q = static_cast<const bf16_t*>(a.q);
+  Core core;
+  core.init();
+  core.load_q(row_ok ? q + ((size_t)(q0 + trow) * a.hq + w.h) * C::D : nullptr, lane);
+
+  const size_t kst = (size_t)a.hkv * C::D, vst = (size_t)a.hkv * C::DV;
+  const bf16_t* kb = static_cast<const bf16_t*>(a.k) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
+  const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * vst + (size_t)w.kvh * C::DV;
+  auto kptr = [&](int j) -> const bf16_t* { return j < lk ? kb + (size_t)j * kst : nullptr; };
+  auto vptr = [&](int j) -> const bf16_t* { return j < lk ? vb + (size_t)j * vst : nullptr; };
+  const int tdiag = trow + bd.delta;
+  auto vis = [&](int j) {
+    return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
+  };
+  auto need = [&](int j0) {
+    return j0 + C::BN > lk || (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
+           (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
+  };
+  run_keys(core, lds, bd.lo, bd.hi, a.scale_log2, kptr, vptr, need, vis);
+
+  float lse;
+  const float inv = core.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse);
+  if (row_ok) {
+    core.store(static_cast<bf16_t*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * C::DV, inv,
+               lane);
+    if (a.lse && M::grp(lane) == 0) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 variant: VALU arithmetic in fp32 throughout (no bf16 rounding of
+// inputs or probabilities). LPR lanes share one query row, each holding 64 of
+// its head dimensions; K/V tiles of 32 keys are staged in LDS.
+template <int D>
+struct F32Cfg {
+  static constexpr int LPR = D / 64;
+  static constexpr int THREADS = 64;
+  static constexpr int ROWS = THREADS / LPR;
+  static constexpr int BN = 32;
+};
+
+template <int D>
+__global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
+  using C = F32Cfg<D>;
+  __shared__ __attribute__((aligned(16))) float ks[C::BN][D];
+  __shared__ __attribute__((aligned(16))) float vs[C::BN][D];
+  PrefillWork w;
+  if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
+  const int q0 = a.cu_q[w.b];
+  const int lq = a.cu_q[w.b + 1] - q0;
+  const int row0 = w.qt * C::ROWS;
+  if (row0 >= lq) return;
+  const int k0 = a.cu_k[w.b];
+  const int lk = a.cu_k[w.b + 1] - k0;
+  const int row_last = min(lq, row0 + C::ROWS) - 1;
+  const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
+
+  const int tid = threadIdx.x;
+  const int part = tid % C::LPR;
+  const int trow = row0 + tid / C::LPR;
+  const bool row_ok = trow < lq;
+  const float* q = static_cast<const float*>(a.q);
+  const float* kg = static_cast<const float*>(a.k);
+  const float* vg = static_cast<const float*>(a.v);
+  float qr[64], o[64];
+#pragma unroll
+  for (int d = 0; d < 64; ++d) {
+    qr[d] = row_ok ? q[((size_t)(q0 + trow) * a.hq + w.h) * D + part * 64 + d] : 0.f;
+    o[d] = 0.f;
+  }
+  float m_run = kNegInf, l_run = 0.f;
+  const int tdiag = trow + bd.delta;
+  for (int j0 = bd.lo; j0 < bd.hi; j0 += C::BN) {
+    for (int e = tid; e < C::BN * D; e += 64) {
+      const int r = e / D, c = e % D;
+      const int j = j0 + r;
+      const bool ok = j < lk;
+      ks[r][c] = ok ? kg[((size_t)(k0 + j) * a.hkv + w.kvh) * D + c] : 0.f;
+      vs[r][c] = ok ? vg[((size_t)(k0 + j) * a.hkv + w.kvh) * D + c] : 0.f;
+    }
+    __syncthreads();
+    float s[C::BN];
+    float mx = kNegInf;
+    for (int j = 0; j < C::BN; ++j) {
+      const f32x4* kr = reinterpret_cast<const f32x4*>(&ks[j][part * 64]);
+      float acc = 0.f;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const f32x4 kv = kr[d];
+        acc = fmaf(qr[4 * d], kv[0], acc);
+        acc = fmaf(qr[4 * d + 1], kv[1], acc);
+        acc = fmaf(qr[4 * d + 2], kv[2], acc);
+        acc = fmaf(qr[4 * d + 3], kv[3], acc);
+      }
+      if (C::LPR == 2) acc += __shfl_xor(acc, 1);
+      const int jj = j0 + j;
+      const bool ok = jj < lk && (bd.wr < 0 || jj <= tdiag + bd.wr) && (bd.wl < 0 || jj >= tdiag - bd.wl);
+      s[j] = ok ? acc * a.scale_log2 : kNegInf;
+    }
+#pragma unroll
+    for (int j = 0; j < C::BN; ++j) mx = fmaxf(mx, s[j]);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < 64; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int j = 0; j < C::BN; ++j) s[j] = fast_exp2(s[j] - m_use);
+    for (int j = 0; j < C::BN; ++j) {
+      const float p = s[j];
+      l_run += p;
+      const f32x4* vr = reinterpret_cast<const f32x4*>(&vs[j][part * 64]);
+#pragma unroll
+      for (int d = 0; d < 16; ++d) {
+        const f32x4 vv = vr[d];
+        o[4 * d] = fmaf(p, vv[0], o[4 * d]);
+        o[4 * d + 1] = fmaf(p, vv[1], o[4 * d + 1]);
+        o[4 * d + 2] = fmaf(p, vv[2], o[4 * d + 2]);
+        o[4 * d + 3] = fmaf(p, vv[3], o[4 * d + 3]);
+      }
+    }
+    __syncthreads();
+  }
+  const bool empty = !(l_run > 0.f);
+  const float lse = empty ? kNegInf : (m_run + fast_log2(l_run)) * kLn2;
+  float inv = empty ? 0.f : 1.f / l_run;
+  if (a.sinks && !empty) {
+    const float sink2 = a.sinks[w.h] * kLog2e;
+    const float ms = fmaxf(m_run, sink2);
+    const float f = fast_exp2(m_run - ms);
+    inv = f / (l_run * f + fast_exp2(sink2 - ms));
+  }
+  if (row_ok) {
+    float* orow = static_cast<float*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * D + part * 64;
+#pragma unroll
+    for (int d = 0; d < 64; d += 4) {
+      const f32x4 v = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+      *reinterpret_cast<f32x4*>(orow + d) = v;
+    }
+    if (a.lse && part == 0) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
+  }
+}
+
+using CfgP64 = TileCfg<32, 64, 64, 4, 64, false>;
+using CfgP128 = TileCfg<32, 128, 128, 4, 64, false>;
+
+}  // namespace
+
+int varlen_bf16_rows(int d) { return d == 64 ? CfgP64::ROWS : CfgP128::ROWS; }
+int varlen_f32_rows(int d) { return d == 64 ? F32Cfg<64>::ROWS : F32Cfg<128>::ROWS; }
+
+hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (d == 64)
+    hipLaunchKernelGGL(k_varlen_bf16<CfgP64>, dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_varlen_bf16<CfgP128>, dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (d == 64)
+    hipLaunchKernelGGL(k_varlen_f32<64>, dim3(grid), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_varlen_f32<128>, dim3(grid), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,74 @@
+// Kernel argument blocks and launchers (host side). The C ABI in attn_api.hip
+// validates arguments and then calls these; each returns hipSuccess or the
+// launch error.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct VarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch, hq, hkv, nqt;   // nqt: query tiles per sequence (grid bound)
+  int32_t causal, wl, wr;
+  float scale_log2;              // softmax scale * log2(e)
+  const float* sinks;
+  void* out;
+  float* lse;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kc;
+  const void* vc;               // unused when K and V share the cache row
+  const int32_t* block_table;
+  const int32_t* lens;
+  const int32_t* plan;
+  int32_t max_pages, batch, sq, hq, hkv, page, causal, max_splits;
+  float scale_log2;
+  float* o_part;
+  float* lse_part;
+};
+
+struct SparseArgs {
+  const void* q;
+  const void* kv;
+  const int32_t* idx;
+  int32_t topk, batch, sq, sk, hq, mode;
+  float scale_log2;
+  const float* sinks;
+  void* out;
+  float* lse;
+};
+
+struct CombineArgs {
+  const float* o_part;
+  const float* lse_part;
+  const int32_t* plan;
+  int32_t batch, sq, hq, dv, max_splits, out_bf16;
+  const float* sinks;
+  void* out;
+  float* lse;
+};
+
+// rows per workgroup of each instance (sizes the grids)
+int varlen_bf16_rows(int d);
+int varlen_f32_rows(int d);
+
+hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
+hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t launch_plan(const int32_t* lens, int batch, int page, int upb, int num_cu, int waves,
+                       int max_splits, int min_blocks, int32_t* plan, hipStream_t s);
+hipError_t launch_gather(const void* cache, const int32_t* block_table, int max_pages,
+                         const int32_t* lens, int b, int page, int row_elems, int max_rows,
+                         void* dst, hipStream_t s);
+
+}  // namespace attn

@@ -16,7 +16,10 @@ shared cache), then the page permutation, then sparse indices, then sinks.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
+
 import numpy as np
 
 # One seed per workload of the benchmark set.
@@ -26,7 +29,7 @@ SEED_PAGED_DECODE = 1003
 SEED_MLA_DECODE = 1004
 SEED_SPARSE_MLA = 1005
 
-_CHUNK = 1 << 24  # elements drawn per call when filling large tensors
+_CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -45,13 +48,30 @@ def bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     """N(0,1) float32 draws rounded to bfloat16, returned as uint16 bits.
-    Large tensors are drawn in fixed-size chunks in C order, so the stream of
-    draws does not depend on memory limits."""
+
+    One 63-bit key is taken from the workload's generator (so the fixed draw
+    order of the workload is kept); the tensor is then filled in C order in
+    blocks of _CHUNK elements, block i drawn from its own PCG64 stream seeded
+    with SeedSequence([key, i]). Blocks are independent, so they are filled by
+    a thread pool and the values do not depend on the thread count."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, _CHUNK):
-        e = min(n, s + _CHUNK)
-        out[s:e] = bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+    key = int(rng.integers(0, 2**63 - 1))
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([key, i])))
+        u = g.standard_normal(e - s, dtype=np.float32).view(np.uint32)
+        u += np.uint32(0x7FFF) + ((u >> 16) & np.uint32(1))
+        out[s:e] = u >> 16
+
+    nblk = (n + _CHUNK - 1) // _CHUNK
+    if nblk <= 1:
+        for i in range(nblk):
+            fill(i)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, nblk)) as ex:
+            list(ex.map(fill, range(nblk)))
     return out.reshape(shape)
 
 

@@ -1,0 +1,207 @@
+/*
+ * attn.h - C ABI of libattn_mi355.so: fused scaled-dot-product attention
+ * forward for AMD Instinct MI355X (gfx950).
+ *
+ * Every entry point computes, tile by tile and without materialising the
+ * score matrix,
+ *     S = scale * Q K^T,  O = softmax(S) V,  LSE = log sum exp(S - max S) + max S
+ * (attention and softmax_lse formulas of the CANN ops-transformer "flash_attn"
+ * page), with the masks and layouts described per function.
+ *
+ * Conventions shared by all calls
+ *  - Tensor arguments are DEVICE pointers, allocated and owned by the caller,
+ *    dense row-major in the shapes given. The library never allocates device
+ *    memory and keeps no pointer after the call returns.
+ *  - Scalar arguments (sizes, flags, scale) are host values.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *    enqueues work on it and returns without synchronising.
+ *  - bfloat16 tensors hold raw 16-bit patterns; results are rounded to
+ *    bfloat16 to nearest-even. LSE is float32, natural log.
+ *  - Query head h reads KV head h / (Hq / Hkv) (grouping (N2, N1/N2) of the
+ *    MindSpore "sparse_flash_attention" page).
+ *  - Causal masks are bottom-right aligned: query t of a sequence with Lq
+ *    queries and Lk keys sees key j iff j <= t + (Lk - Lq) (rightDownCausal
+ *    mode of the same page). A row that sees no key gets O = 0, LSE = -inf.
+ *  - Errors: host-side argument checks return an error before any device
+ *    work is enqueued. A zero-sized required dimension is ATTN_EEMPTY (the
+ *    flash_attn page rejects empty tensors). The CONTENTS of device tensors
+ *    (cu_seqlens, block_table, cache_seqlens, indices, plan) are not checked:
+ *    out-of-range values are undefined behaviour, as on the flash_attn page.
+ *    attn_last_error() returns a thread-local message for the last failure.
+ */
+#ifndef ATTN_MI355_H
+#define ATTN_MI355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* bad argument (null pointer, inconsistent sizes) */
+  ATTN_EUNSUPPORTED = 2,  /* valid but not implemented (head dims, dtype)    */
+  ATTN_EEMPTY = 3,        /* a required dimension is zero                    */
+  ATTN_EHIP = 4           /* HIP runtime error (launch, device query)        */
+} attn_status;
+
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+
+/* Human-readable name of a status code. Never NULL. */
+const char* attn_status_string(int32_t status);
+
+/* Message describing the last failing call on this thread ("" if none). */
+const char* attn_last_error(void);
+
+/* Number of compute units of `device` (host output). */
+int32_t attn_device_info(int32_t device, int32_t* num_cu);
+
+/*
+ * attn_fwd_varlen - packed variable-length attention (prefill).
+ * [MATE "Attention" page, FMHA: flash_attn_varlen_func; CANN flash_attn:
+ *  cu_seqlens_q / cu_seqlens_kv; lite_boost flash_attention: causal,
+ *  window_size]
+ *
+ *  q   (Tq, hq, d)     k (Tk, hkv, d)     v (Tk, hkv, dv)     dtype elements
+ *  cu_seqlens_q, cu_seqlens_k: int32 (batch+1) prefix sums, [0] = 0; sequence
+ *      b owns query rows [cu_q[b], cu_q[b+1]) and key rows [cu_k[b], cu_k[b+1]).
+ *  max_seqlen_q: host upper bound of the per-sequence query length (sizes the
+ *      grid; rows past it are not computed). max_seqlen_k: host upper bound
+ *      of the key length (informational, must be >= 0).
+ *  window_left / window_right: inclusive band around the causal diagonal,
+ *      -1 = unbounded; causal != 0 is the same as window_right = 0.
+ *  sinks: NULL or float32 (hq) sink logits (scaled-score domain): the output
+ *      becomes sum e^{S-m} V / (sum e^{S-m} + e^{sink-m}), m = max(sink, max S)
+ *      [CANN flash_attn sink formulas]; LSE stays sink-free.
+ *  out (Tq, hq, dv) dtype;  lse: NULL or float32 (hq, Tq).
+ *  Supported: dtype BF16 with d = dv in {64, 128}; dtype F32 with d = dv in
+ *  {64, 128}. Others return ATTN_EUNSUPPORTED.
+ */
+int32_t attn_fwd_varlen(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                        int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t dtype,
+                        float scale, int32_t causal, int32_t window_left, int32_t window_right,
+                        const float* sinks, void* out, float* lse, void* stream);
+
+/*
+ * Split-KV plan for paged decode.
+ * [MATE: get_scheduler_metadata / get_mla_metadata precompute the work split;
+ *  CANN flash_attn_metadata does the same before the main call. The rule
+ *  below is this library's own.]
+ *
+ *  attn_plan_words: number of int32 words of a plan buffer.
+ *  attn_plan_splits: enqueues one small kernel that reads cache_seqlens
+ *  (device int32, batch) and writes `plan` (device int32, attn_plan_words):
+ *    plan[0] = total splits, plan[1] = pages per split target (bps),
+ *    plan[2 .. 2+batch] = split_ptr (exclusive prefix sum, batch+1 words),
+ *    then one (batch, kv_start, kv_end) triple per split, batch-major.
+ *  Rule: nblk = ceil(len / page_size) (0 if len <= 0);
+ *        bps  = max(min_blocks, ceil(sum nblk * units_per_block / (num_cu * waves)));
+ *        ns   = min(max_splits, max(1, ceil(nblk / bps))), pps = ceil(nblk / ns),
+ *        ns   = ceil(nblk / pps); split s = tokens [s*pps*page, min((s+1)*pps*page, len)).
+ *  Empty sequences get no split. max_splits must be in [1, 16].
+ *  The same plan must be passed unchanged to the decode and combine calls.
+ */
+size_t attn_plan_words(int32_t batch, int32_t max_splits);
+int32_t attn_plan_splits(const int32_t* cache_seqlens, int32_t batch, int32_t page_size,
+                         int32_t units_per_block, int32_t num_cu, int32_t waves,
+                         int32_t max_splits, int32_t min_blocks, int32_t* plan, void* stream);
+
+/*
+ * attn_decode_paged - split-KV attention of a few query tokens against a
+ * paged KV cache; writes per-split partial results for attn_combine.
+ * [MATE FMHA: flash_attn_with_kvcache with k_cache (pages, page_size, Hkv, D),
+ *  block_table and cache_seqlens; a non-empty block_table enables paged
+ *  attention (CANN flash_attn)]
+ *
+ *  q (batch, seqlen_q, hq, d); k_cache (P, page_size, hkv, d);
+ *  v_cache (P, page_size, hkv, dv); block_table int32 (batch, max_pages_per_seq):
+ *  logical page i of sequence b is physical page block_table[b*max_pages_per_seq+i];
+ *  cache_seqlens int32 (batch): keys 0..len-1 (the cache already holds the
+ *  current tokens). causal: bottom-right over (seqlen_q, len).
+ *  plan: from attn_plan_splits with the same cache_seqlens and max_splits.
+ *  o_partial float32 (batch*max_splits, seqlen_q*hq, dv), lse_partial float32
+ *  (batch*max_splits, seqlen_q*hq): split s of b writes slot b*max_splits+s,
+ *  row t*hq+h, normalised within the split. Unused slots are untouched.
+ *  Supported: BF16, d = dv = 128, page_size a multiple of 16.
+ */
+int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                          int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                          int32_t dtype, float scale, int32_t causal, const int32_t* plan,
+                          int32_t max_splits, float* o_partial, float* lse_partial,
+                          void* stream);
+
+/*
+ * attn_combine - LSE-weighted merge of split results.
+ * [MATE FMHA: flash_attn_combine merges partial outputs and LSE buffers;
+ *  CANN flash_attn: softmax_lse definition]
+ *  For each output row: M = max_s LSE_s, w_s = e^{LSE_s - M},
+ *  LSE = M + log sum w_s, O = sum w_s O_s / sum w_s. With sinks (float32 hq,
+ *  or NULL) the sink of the row's head adds e^{sink - M*} to the denominator,
+ *  M* = max(M, sink); LSE stays sink-free. No split or all LSE_s = -inf gives
+ *  O = 0, LSE = -inf.
+ *  out (batch, seqlen_q, hq, dv) in out_dtype (BF16 or F32);
+ *  lse: NULL or float32 (batch, hq, seqlen_q).
+ */
+int32_t attn_combine(const float* o_partial, const float* lse_partial, const int32_t* plan,
+                     int32_t batch, int32_t seqlen_q, int32_t hq, int32_t dv, int32_t max_splits,
+                     const float* sinks, int32_t out_dtype, void* out, float* lse, void* stream);
+
+/*
+ * mla_decode_paged - MLA-absorbed split-KV decode: one KV head, each cached
+ * row holds the 512-wide latent followed by the 64-wide rope part (d = 576);
+ * the key is the whole row and the value is its first 512 entries.
+ * [MATE MLA example: flash_mla_with_kvcache(q (B,Sq,Hq,576), k_cache
+ *  (P,page,Hkv,576), head_dim_v=512); MindSpore sparse_flash_attention:
+ *  MLA-absorb concat of nope and rope along D; CANN flash_attn: shared KV]
+ *  q (batch, seqlen_q, hq, 576) bf16; kv_cache (P, page_size, 1, 576) bf16;
+ *  other arguments and the partial layout (dv = 512) as attn_decode_paged;
+ *  follow with attn_combine(dv = 512). hq must be a multiple of 16 and
+ *  page_size a multiple of 16.
+ */
+int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                         int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t batch,
+                         int32_t seqlen_q, int32_t hq, int32_t page_size, float scale,
+                         int32_t causal, const int32_t* plan, int32_t max_splits,
+                         float* o_partial, float* lse_partial, void* stream);
+
+/*
+ * mla_sparse_fwd - top-k sparse MLA attention with optional sinks.
+ * [MindSpore sparse_flash_attention: sparse_indices (B, Q_S, N2, 2048) select
+ *  K~ = V~ rows, N2 = 1, D = 512 + 64 rope, sparse_mode 0 (all) / 3
+ *  (rightDownCausal); CANN flash_attn sink formulas]
+ *  q (batch, seqlen_q, hq, 576) bf16; kv (batch, seqlen_k, 1, 576) bf16;
+ *  sparse_indices int32 (batch, seqlen_q, 1, topk): key rows of each query
+ *  token, shared by all its heads; entries < 0 or >= seqlen_k are skipped,
+ *  mode 3 also skips keys after t + (seqlen_k - seqlen_q); duplicates count
+ *  each time; order is irrelevant. sinks: NULL or float32 (hq).
+ *  out (batch, seqlen_q, hq, 512) bf16; lse: NULL or float32 (batch, hq, seqlen_q).
+ *  hq must be a multiple of 16.
+ */
+int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indices, int32_t topk,
+                       int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t hq, float scale,
+                       int32_t sparse_mode, const float* sinks, void* out, float* lse,
+                       void* stream);
+
+/*
+ * attn_debug_gather_paged - copies logical rows [0, cache_seqlens[b]) of one
+ * sequence out of a paged cache (P, page_size, row_elems) of 16-bit elements
+ * into dst (len, row_elems), using the same page-address computation as the
+ * decode kernels. For bit-exact tests of the gather. row_elems must be a
+ * multiple of 8.
+ */
+int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,
+                                int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t b,
+                                int32_t page_size, int32_t row_elems, int32_t max_rows, void* dst,
+                                void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355_H */

@@ -379,18 +379,28 @@ def mla_sparse(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, dv=512, 
 
     q (B, Sq, Hq, D), kv (B, Sk, 1, D), sparse_indices (B, Sq, 1, topk) int32.
     All query heads of a token share its index list (N2 = 1).
-    tokens: optional list of (b, t) to evaluate (others left NaN).
-    Returns O (B, Sq, Hq, dv), LSE (B, Hq, Sq).
+    Returns O (B, Sq, Hq, dv), LSE (B, Hq, Sq); when tokens (a list of (b, t))
+    is given, only those are evaluated and O (n, Hq, dv), LSE (n, Hq) are
+    returned in the order of the list.
     """
     bsz, sq, hq, _ = q.shape
     sk = kv.shape[1]
-    o = np.full((bsz, sq, hq, dv), np.nan)
-    lse = np.full((bsz, hq, sq), np.nan)
-    todo = [(b, t) for b in range(bsz) for t in range(sq)] if tokens is None else tokens
-    for b, t in todo:
+    if tokens is None:
+        o = np.zeros((bsz, sq, hq, dv))
+        lse = np.zeros((bsz, hq, sq))
+        todo = [(b, t) for b in range(bsz) for t in range(sq)]
+    else:
+        o = np.zeros((len(tokens), hq, dv))
+        lse = np.zeros((len(tokens), hq))
+        todo = tokens
+    for i, (b, t) in enumerate(todo):
         keys = sparse_key_set(sparse_indices[b, t, 0], sq, sk, t, sparse_mode)
         rows = kv[b, keys, 0]
         ob, lb = attend_rows(q[b, t], rows, rows[:, :dv], scale, None, sinks)
-        o[b, t] = ob
-        lse[b, :, t] = lb
+        if tokens is None:
+            o[b, t] = ob
+            lse[b, :, t] = lb
+        else:
+            o[i] = ob
+            lse[i] = lb
     return o, lse

@@ -1,0 +1,183 @@
+"""GPU parity of the split planner, the paged gather, split-KV decode (GQA
+and MLA shapes) and the combine, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from attention_attn_fwd_02_amd import binding as B
+from attention_attn_fwd_02_amd import inputs
+from oracle import attention as orc
+from tests.gpu_util import TOL_O_BF16, compare, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------- planner
+PLAN_CASES = [
+    # lens, page, upb, num_cu, waves, max_splits, min_blocks
+    ("decode_lens", None, 64, 8, 256, 4, 16, 4),
+    ("mla_lens", None, 64, 4, 256, 2, 16, 4),
+    ("with_zeros", [0, 1, 64, 65, 0, 40000, 12], 64, 1, 4, 1, 3, 2),
+    ("many_seqs", list(range(0, 5000 * 97, 97)), 16, 3, 256, 8, 16, 1),
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_plan_bit_exact(case):
+    name, lens, page, upb, ncu, waves, ms, mb = case
+    if lens is None:
+        w = inputs.paged_decode() if name == "decode_lens" else inputs.mla_decode()
+        lens = w.cache_seqlens
+    lens = np.asarray(lens, dtype=np.int32)
+    log("case plan", name, len(lens))
+    plan = B.attn_plan_splits(dev(lens), page, upb, ncu, waves, ms, mb)
+    ref = orc.plan_splits(lens, page, upb, ncu, waves, ms, mb)
+    got = host(plan)
+    n = 3 + len(lens) + 3 * int(ref[0])
+    assert np.array_equal(got[:n], ref[:n]), f"plan mismatch at {np.nonzero(got[:n] != ref[:n])[0][:8]}"
+
+
+# -------------------------------------------------------------------- gather
+def test_gather_bit_exact():
+    w = inputs.paged(77, [1000, 64, 3, 130], sq=1, hq=4, hkv=2, d=64, page=16)
+    cache = dev(w.k_cache)
+    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
+    for b, n in enumerate(w.cache_seqlens):
+        got = B.attn_debug_gather_paged(cache, bt, lens, b, int(n))
+        torch.cuda.synchronize()
+        ref = orc.gather_paged(w.k_cache, w.block_table, b, int(n), 16).reshape(int(n), -1)
+        assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), ref)
+
+
+# ---------------------------------------------------------------------- GQA
+def run_decode(w, max_splits=16, waves=4, min_blocks=4):
+    return B.paged_decode(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                          dev(w.cache_seqlens), w.scale, w.causal,
+                          None if w.sinks is None else dev(w.sinks), max_splits=max_splits,
+                          waves=waves, min_blocks=min_blocks)
+
+
+def oracle_decode(w, batches=None):
+    q, kc, vc = (inputs.bits_to_f32(x) for x in (w.q, w.k_cache, w.v_cache))
+    return orc.attention_paged(q, kc, vc, w.block_table, w.cache_seqlens, w.page_size, w.scale,
+                               w.causal, w.sinks, batches=batches)
+
+
+DECODE_CASES = [
+    # name, lens, sq, hq, hkv, page, causal, sinks, max_splits, waves, min_blocks
+    ("ragged_pages", [1, 63, 64, 65, 700, 2049], 1, 32, 8, 64, False, False, 16, 4, 4),
+    ("many_splits", [5000, 130, 4097], 1, 8, 2, 16, False, False, 16, 64, 1),
+    ("one_split", [300, 1200], 1, 8, 8, 64, False, False, 1, 4, 4),
+    ("causal_sq3", [90, 400, 3], 3, 16, 4, 16, True, False, 8, 16, 1),
+    ("sinks", [1000, 17], 2, 8, 2, 32, False, True, 4, 8, 1),
+    ("gqa16_rows32", [333, 1000], 2, 16, 1, 64, True, False, 16, 8, 2),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_decode_gqa(case):
+    name, lens, sq, hq, hkv, page, causal, sinks, ms, waves, mb = case
+    log("case decode", name)
+    w = inputs.paged(5000 + len(name), lens, sq=sq, hq=hq, hkv=hkv, d=128, page=page,
+                     causal=causal, with_sinks=sinks)
+    o, lse, plan = run_decode(w, ms, waves, mb)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(w)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+    ref_plan = orc.plan_splits(w.cache_seqlens, page, hkv * ((sq * hq // hkv + 15) // 16),
+                               B.attn_device_info(0), waves, ms, mb)
+    n = 3 + len(lens) + 3 * int(ref_plan[0])
+    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+
+
+def test_decode_gqa_unreferenced_pages_poisoned():
+    """Pool pages that no block_table entry names are filled with NaN; a
+    read past a sequence's valid pages would make the output non-finite."""
+    lens = [100, 64, 7]
+    w = inputs.paged(91, lens, sq=1, hq=8, hkv=2, d=128, page=16)
+    extra = 5
+    nan = np.uint16(0x7FC0)
+    kc = np.concatenate([w.k_cache, np.full((extra,) + w.k_cache.shape[1:], nan, np.uint16)])
+    vc = np.concatenate([w.v_cache, np.full((extra,) + w.v_cache.shape[1:], nan, np.uint16)])
+    # move every page up by `extra` so the poisoned ones sit in front
+    kc = np.roll(kc, extra, axis=0)
+    vc = np.roll(vc, extra, axis=0)
+    bt = np.where(w.block_table >= 0, w.block_table + extra, -1).astype(np.int32)
+    w2 = inputs.Paged(w.q, kc, vc, bt, w.cache_seqlens, 16, 128, w.scale, False)
+    o, lse, _ = run_decode(w2)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(w)
+    compare("poisoned_pool", o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_decode_gqa_full():
+    """Full workload: batch 64, lengths U[1024, 32768], page 64, Hq=32, Hkv=8,
+    D=128, up to 16 splits. Eight sequences are checked element by element
+    (the shortest, the longest and six seeded picks); every row of every
+    sequence must be finite with max S <= LSE-like bounds checked by the
+    oracle rows."""
+    w = inputs.paged_decode()
+    log("case decode_gqa_full seed", inputs.SEED_PAGED_DECODE)
+    o, lse, plan = run_decode(w)
+    torch.cuda.synchronize()
+    lens = w.cache_seqlens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                   *np.random.default_rng(7).choice(len(lens), 6, replace=False).tolist()})
+    ro, rl = oracle_decode(w, batches=pick)
+    mask = np.zeros(ro.shape, bool)
+    mask[pick] = True
+    compare("decode_gqa_full", o, lse, ro, rl, TOL_O_BF16, mask=mask)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    ref_plan = orc.plan_splits(lens, 64, 8, B.attn_device_info(0), 4, 16, 4)
+    n = 3 + len(lens) + 3 * int(ref_plan[0])
+    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+
+
+# ----------------------------------------------------------------------- MLA
+def run_mla(w, max_splits=16, waves=2, min_blocks=4):
+    return B.mla_decode(dev(w.q), dev(w.k_cache), dev(w.block_table), dev(w.cache_seqlens),
+                        w.scale, w.causal, max_splits=max_splits, waves=waves,
+                        min_blocks=min_blocks)
+
+
+def oracle_mla(w, batches=None):
+    q, kc = inputs.bits_to_f32(w.q), inputs.bits_to_f32(w.k_cache)
+    return orc.mla_decode_paged(q, kc, w.block_table, w.cache_seqlens, w.page_size, w.scale,
+                                w.causal, 512, batches)
+
+
+MLA_CASES = [
+    ("mla_small", [100, 1, 700], 2, 16, 64, False, 16, 2, 1),
+    ("mla_causal_sq4", [65, 300], 4, 32, 16, True, 8, 8, 1),
+    ("mla_hq128", [2000, 513], 1, 128, 64, False, 16, 2, 2),
+]
+
+
+@pytest.mark.parametrize("case", MLA_CASES, ids=[c[0] for c in MLA_CASES])
+def test_mla_decode(case):
+    name, lens, sq, hq, page, causal, ms, waves, mb = case
+    log("case", name)
+    w = inputs.paged(6000 + len(name), lens, sq=sq, hq=hq, hkv=1, d=576, dv=512, page=page,
+                     shared_kv=True, causal=causal)
+    o, lse, _ = run_mla(w, ms, waves, mb)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mla(w)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_mla_decode_full():
+    """Full workload: batch 64, 2 query tokens, Hq=128, one 576-wide KV head,
+    V = first 512 entries, page 64, lengths U[2048, 16384]; six sequences
+    checked element by element."""
+    w = inputs.mla_decode()
+    log("case mla_decode_full seed", inputs.SEED_MLA_DECODE)
+    o, lse, _ = run_mla(w)
+    torch.cuda.synchronize()
+    lens = w.cache_seqlens
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                   *np.random.default_rng(8).choice(len(lens), 4, replace=False).tolist()})
+    ro, rl = oracle_mla(w, batches=pick)
+    mask = np.zeros(ro.shape, bool)
+    mask[pick] = True
+    compare("mla_decode_full", o, lse, ro, rl, TOL_O_BF16, mask=mask)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
