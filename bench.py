@@ -1,0 +1,314 @@
+"""Benchmark of the fused attention forward on one MI355X.
+
+Headline: varlen causal GQA prefill (8 sequences with lengths U[512, 4096],
+Hq=32, Hkv=8, D=128, bf16), in attention TFLOP/s. One step = one
+attn_fwd_varlen call over the whole packed batch (the single kernel of the
+prefill path). The same JSON line carries the decode-side measurements as
+`secondary` entries: paged GQA decode (KV-read GB/s, step = plan + split
+decode + combine), MLA-absorbed paged decode and sparse MLA with sinks.
+
+Inputs are seeded synthetic tensors already resident in HBM when timing
+starts. Every timed region is bracketed by torch.cuda.synchronize() and
+timed with HIP events on the stream the kernels are launched on.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,...]
+                [--no-cpu] [--no-secondary]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD published spec)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD published spec)
+
+PREFILL_WORKLOAD = ("varlen causal GQA prefill: 8 sequences, lengths U[512,4096] packed with "
+                    "cu_seqlens, Hq=32, Hkv=8, D=128, bf16 Q/K/V ~ N(0,1), scale 1/sqrt(128), "
+                    "bf16 O + fp32 LSE (seed 1002)")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(x):
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def time_steps(fn, steps, warmup):
+    """Runs fn warmup times untimed, then `steps` times between two HIP events
+    on the current stream; returns milliseconds per step."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def prefill_flops(lens, hq=32, d=128):
+    # 4*D per (query row, visible key): 2*D for QK^T and 2*D for P.V; a causal
+    # row t sees t+1 keys.
+    return sum(4.0 * d * hq * (int(L) * (int(L) + 1) / 2) for L in lens)
+
+
+def bench_prefill(steps, warmup):
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.varlen_prefill()
+    lens = np.diff(w.cu_seqlens_q)
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    cq, ck = dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
+    out = None
+    lse = None
+
+    def step():
+        B.attn_fwd_varlen(q, k, v, cq, ck, int(lens.max()), int(lens.max()), w.scale, True,
+                          out=out_buf, lse=lse_buf)
+
+    import torch
+    out_buf = torch.empty((int(lens.sum()), 32, 128), dtype=torch.bfloat16, device="cuda")
+    lse_buf = torch.empty((32, int(lens.sum())), dtype=torch.float32, device="cuda")
+    ms = time_steps(step, steps, warmup)
+    flops = prefill_flops(lens)
+    tflops = flops / (ms * 1e-3) / 1e12
+    in_bytes = (w.q.nbytes + w.k.nbytes + w.v.nbytes)
+    out_bytes = out_buf.numel() * 2 + lse_buf.numel() * 4
+    return dict(ms=ms, tflops=tflops, flops=flops, lens=lens.tolist(), w=w,
+                bytes=in_bytes + out_bytes)
+
+
+def bench_decode(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.paged_decode()
+    q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
+    ncu = B.attn_device_info(0)
+    b, sq, hq, d = w.q.shape
+    hkv = w.k_cache.shape[2]
+    ms_, waves, mb = 16, 4, 4
+    upb = hkv * ((sq * hq // hkv + 15) // 16)
+    plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
+    op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
+    lp = torch.empty((b * ms_, sq * hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((b, sq, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+
+    def full():
+        B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb, plan=plan)
+        B.attn_decode_paged(q, kc, vc, bt, lens, plan, ms_, w.scale, False, op, lp)
+        B.attn_combine(op, lp, plan, b, sq, hq, ms_, None, torch.bfloat16, out, lse)
+
+    def decode_only():
+        B.attn_decode_paged(q, kc, vc, bt, lens, plan, ms_, w.scale, False, op, lp)
+
+    ms_full = time_steps(full, steps, warmup)
+    ms_dec = time_steps(decode_only, steps, warmup)
+    total_len = int(w.cache_seqlens.astype(np.int64).sum())
+    nblk = int(((w.cache_seqlens + 63) // 64).sum())
+    kv_bytes = total_len * hkv * (128 + 128) * 2
+    alg_bytes = kv_bytes + w.q.nbytes + out.numel() * 2 + lse.numel() * 4 + nblk * 4
+    return dict(ms=ms_full, ms_kernel=ms_dec, bytes=alg_bytes, kv_bytes=kv_bytes,
+                gbs=alg_bytes / (ms_full * 1e-3) / 1e9, gbs_kernel=alg_bytes / (ms_dec * 1e-3) / 1e9,
+                splits=int(plan[0].item()))
+
+
+def bench_mla(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.mla_decode()
+    q, kc = dev(w.q), dev(w.k_cache)
+    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
+    ncu = B.attn_device_info(0)
+    b, sq, hq, d = w.q.shape
+    ms_, waves, mb = 16, 2, 4
+    upb = (sq * hq + 63) // 64
+    plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
+    op = torch.empty((b * ms_, sq * hq, 512), dtype=torch.float32, device="cuda")
+    lp = torch.empty((b * ms_, sq * hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((b, sq, hq, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+
+    def full():
+        B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb, plan=plan)
+        B.mla_decode_paged(q, kc, bt, lens, plan, ms_, w.scale, False, op, lp)
+        B.attn_combine(op, lp, plan, b, sq, hq, ms_, None, torch.bfloat16, out, lse)
+
+    def decode_only():
+        B.mla_decode_paged(q, kc, bt, lens, plan, ms_, w.scale, False, op, lp)
+
+    ms_full = time_steps(full, steps, warmup)
+    ms_dec = time_steps(decode_only, steps, warmup)
+    total_len = int(w.cache_seqlens.astype(np.int64).sum())
+    flops = total_len * sq * hq * 2.0 * (576 + 512)
+    alg_bytes = total_len * 1152 + w.q.nbytes + out.numel() * 2 + lse.numel() * 4
+    return dict(ms=ms_full, ms_kernel=ms_dec, flops=flops, bytes=alg_bytes,
+                tflops=flops / (ms_full * 1e-3) / 1e12, gbs=alg_bytes / (ms_full * 1e-3) / 1e9,
+                tflops_kernel=flops / (ms_dec * 1e-3) / 1e12, splits=int(plan[0].item()))
+
+
+def bench_sparse(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    s = inputs.sparse_mla()
+    q, kv, idx, sinks = dev(s.q), dev(s.kv), dev(s.indices), dev(s.sinks)
+    b, sq, hq, d = s.q.shape
+    out = torch.empty((b, sq, hq, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.mla_sparse_fwd(q, kv, idx, s.scale, 3, sinks, out, lse)
+
+    ms = time_steps(step, max(1, steps // 4), max(1, warmup // 2))
+    valid = int((s.indices >= 0).sum())     # every drawn index lies in its causal prefix
+    flops = valid * hq * 2.0 * (576 + 512)
+    gathered = valid * 1152
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12,
+                gathered_gbs=gathered / (ms * 1e-3) / 1e9)
+
+
+def cpu_baseline(pre):
+    """The float64 oracle as it stands, timed on the host on a bounded sample
+    of the prefill workload: its first three sequences, all 32 heads."""
+    from threadpoolctl import threadpool_info
+    from oracle import attention as orc
+    w = pre["w"]
+    seqs = [0, 1, 2]
+    q, k, v = w.f32("q"), w.f32("k"), w.f32("v")
+    t0 = time.perf_counter()
+    orc.attention_varlen(q, k, v, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True, seqs=seqs)
+    dt = time.perf_counter() - t0
+    lens = [pre["lens"][i] for i in seqs]
+    flops = prefill_flops(lens)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle on sequences 0-2 (lengths {lens}) of the prefill "
+                      f"workload, all 32 heads; {dt:.1f} s wall; BLAS threads {threads}, "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default="prefill,decode,mla,sparse")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    from attention_attn_fwd_02_amd import binding as B
+    B.load()
+    only = set(args.only.split(","))
+    if args.no_secondary:
+        only &= {"prefill"}
+
+    log("prefill ...")
+    pre = bench_prefill(args.steps, args.warmup)
+    log(f"prefill {pre['ms']:.3f} ms  {pre['tflops']:.1f} TFLOP/s")
+    secondary = []
+    if "decode" in only:
+        log("paged decode ...")
+        dec = bench_decode(args.steps, args.warmup)
+        log(f"decode {dec['ms']:.3f} ms (kernel {dec['ms_kernel']:.3f}) {dec['gbs']:.0f} GB/s")
+        secondary.append({
+            "metric": "KV-read GB/s (paged decode)", "value": dec["gbs"], "unit": "GB/s",
+            "ms_per_step": dec["ms"],
+            "workload": "paged GQA decode: batch 64, 1 query token, cache_seqlens U[1024,32768], "
+                        "page 64, Hq=32, Hkv=8, D=128, bf16; plan + split decode (<=16 splits) + "
+                        f"combine per step; {dec['splits']} splits (seed 1003)",
+            "roofline": {"bound": "hbm", "achieved": dec["gbs_kernel"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": dec["gbs_kernel"] / PEAK_HBM_GBS,
+                         "traffic": None, "kernel": "k_decode (GQA)",
+                         "kernel_ms": dec["ms_kernel"]},
+            "frac_of_hbm_peak_whole_op": dec["gbs"] / PEAK_HBM_GBS})
+    if "mla" in only:
+        log("mla decode ...")
+        mla = bench_mla(args.steps, args.warmup)
+        log(f"mla {mla['ms']:.3f} ms {mla['tflops']:.1f} TFLOP/s {mla['gbs']:.0f} GB/s")
+        secondary.append({
+            "metric": "MLA paged decode TFLOP/s", "value": mla["tflops"], "unit": "TFLOP/s",
+            "ms_per_step": mla["ms"], "kv_read_gbs": mla["gbs"],
+            "frac_of_hbm_peak": mla["gbs"] / PEAK_HBM_GBS,
+            "workload": "MLA-absorbed paged decode: batch 64, 2 query tokens, Hq=128, Hkv=1, "
+                        "D=576 (V = first 512), page 64, cache_seqlens U[2048,16384], bf16; plan "
+                        f"+ split decode + combine; {mla['splits']} splits (seed 1004)",
+            "roofline": {"bound": "mfma", "achieved": mla["tflops_kernel"],
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": mla["tflops_kernel"] / PEAK_BF16_TFLOPS, "traffic": None,
+                         "kernel": "k_decode (MLA)", "kernel_ms": mla["ms_kernel"]}})
+    if "sparse" in only:
+        log("sparse mla ...")
+        sp = bench_sparse(args.steps, args.warmup)
+        log(f"sparse {sp['ms']:.3f} ms {sp['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "sparse MLA + sink TFLOP/s", "value": sp["tflops"], "unit": "TFLOP/s",
+            "ms_per_step": sp["ms"], "gathered_gbs": sp["gathered_gbs"],
+            "workload": "top-2048 sparse MLA with per-head sinks: 4 x 4096 query tokens, 32768 "
+                        "keys, Hq=64, D=576 (V = first 512), bf16 (seed 1005)",
+            "roofline": {"bound": "mfma", "achieved": sp["tflops"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": sp["tflops"] / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "k_sparse"}})
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(pre)
+        log(f"cpu {cpu['value']:.6f} TFLOP/s")
+
+    rec = {
+        "metric": "attention TFLOP/s (varlen prefill) and KV-read GB/s (paged decode), 1 MI355X",
+        "value": pre["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": PREFILL_WORKLOAD, "global_batch": 8,
+                   "seq_len": f"U[512,4096] (drawn {pre['lens']})", "heads_q": 32, "heads_kv": 8,
+                   "head_dim": 128, "causal": True, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
+                     "traffic": None, "kernel": "k_varlen_bf16 (D=128)",
+                     "algorithmic_flops_per_launch": pre["flops"]},
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
