@@ -4,6 +4,7 @@
 //  window_size]
 #include "attn_core.h"
 #include "launch.h"
+#include "prefill_bf16.h"
 
 namespace attn {
 
@@ -62,11 +63,11 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 }
 
 template <class C>
-__global__ void __launch_bounds__(C::THREADS)
+__global__ void __launch_bounds__(C::THREADS, 2)
 k_varlen_bf16(VarlenArgs a) {
-  using Core = TileCore<C>;
-  using M = typename Core::M;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_BYTES / 2];
+  using T = PrefillTile<C>;
+  __shared__ __attribute__((aligned(1024))) char stage0[2 * C::TILE_BYTES];  // K tile, V tile
+  __shared__ __attribute__((aligned(1024))) char stage1[2 * C::TILE_BYTES];
   PrefillWork w;
   if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
   const int q0 = a.cu_q[w.b];
@@ -80,34 +81,66 @@ k_varlen_bf16(VarlenArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int trow = row0 + wave * C::R + M::row(lane);
+  const int trow = row0 + wave * C::R + (lane & 31);
   const bool row_ok = trow < lq;
-  const bf16_t* q = static_cast<const bf16_t*>(a.q);
-  Core core;
-  core.init();
-  core.load_q(row_ok ? q + ((size_t)(q0 + trow) * a.hq + w.h) * C::D : nullptr, lane);
+  T t;
+  t.init();
+  t.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + ((size_t)(q0 + trow) * a.hq + w.h) * C::D
+                  : nullptr,
+           lane);
+  // Q must be in registers before any LDS-DMA is in flight: the compiler
+  // cannot count the DMA operations, so any vmcnt wait it placed for Q inside
+  // the key loop would also drain the prefetch of the next tile.
+  wait_vmcnt<0>();
 
-  const size_t kst = (size_t)a.hkv * C::D, vst = (size_t)a.hkv * C::DV;
+  const size_t kst = (size_t)a.hkv * C::D;
   const bf16_t* kb = static_cast<const bf16_t*>(a.k) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
-  const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * vst + (size_t)w.kvh * C::DV;
-  auto kptr = [&](int j) -> const bf16_t* { return j < lk ? kb + (size_t)j * kst : nullptr; };
-  auto vptr = [&](int j) -> const bf16_t* { return j < lk ? vb + (size_t)j * vst : nullptr; };
+  const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
+  const int last = lk - 1;  // rows past the sequence re-read its last key (then masked)
+  auto issue = [&](char* buf, int j0) {
+    T::template dma_tile<false>(
+        buf, [&](int r) { return kb + (size_t)min(j0 + r, last) * kst; }, wave, lane);
+    T::template dma_tile<true>(
+        buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)min(j0 + r, last) * kst; }, wave,
+        lane);
+  };
   const int tdiag = trow + bd.delta;
-  auto vis = [&](int j) {
-    return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
+  const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
+  auto process = [&](int i, char* __restrict__ cur, char* __restrict__ nxt) {
+    if (i + 1 < ntiles) {
+      issue(nxt, bd.lo + (i + 1) * C::BN);
+      wait_vmcnt<2 * C::DMA_PER_WAVE>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_no_fence();
+    const int j0 = bd.lo + i * C::BN;
+    const bool need = j0 + C::BN > lk ||
+                      (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
+                      (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
+    if (need) {
+      t.template tile<true>(cur, cur + C::TILE_BYTES, a.scale_log2, lane, [&](int jr) {
+        const int j = j0 + jr;
+        return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
+      });
+    } else {
+      t.template tile<false>(cur, cur + C::TILE_BYTES, a.scale_log2, lane, [](int) { return true; });
+    }
+    // every wave must finish reading `cur` before the next DMA into it
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    barrier_no_fence();
   };
-  auto need = [&](int j0) {
-    return j0 + C::BN > lk || (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
-           (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
-  };
-  run_keys(core, lds, bd.lo, bd.hi, a.scale_log2, kptr, vptr, need, vis);
+  if (ntiles > 0) issue(stage0, bd.lo);
+  for (int i = 0; i < ntiles; i += 2) {
+    process(i, stage0, stage1);
+    if (i + 1 < ntiles) process(i + 1, stage1, stage0);
+  }
 
   float lse;
-  const float inv = core.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse);
+  const float inv = t.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse);
   if (row_ok) {
-    core.store(static_cast<bf16_t*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * C::DV, inv,
-               lane);
-    if (a.lse && M::grp(lane) == 0) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
+    t.store(static_cast<bf16_t*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * C::DV, inv, lane);
+    if (a.lse && lane < 32) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
   }
 }
 
@@ -227,8 +260,8 @@ __global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
   }
 }
 
-using CfgP64 = TileCfg<32, 64, 64, 4, 64, false>;
-using CfgP128 = TileCfg<32, 128, 128, 4, 64, false>;
+using CfgP64 = PrefillCfg<64, 4, 64>;
+using CfgP128 = PrefillCfg<128, 4, 64>;
 
 }  // namespace
 

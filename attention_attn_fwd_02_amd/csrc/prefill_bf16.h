@@ -1,0 +1,226 @@
+// bf16 prefill tile engine for gfx950 (32 query rows per wave, 32x32x16 MFMA).
+//
+// Per workgroup: NW waves x 32 rows share one key sequence. Key tiles of BN
+// rows are copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no register
+// staging) into one of two buffers while the other buffer is consumed.
+//
+// LDS layouts (16-byte chunks, c = chunk index along the head dimension):
+//   K: [row / 8][c][row % 8]            -> A-operand reads of 32 consecutive
+//      rows at one chunk touch 8 distinct 16 B slots per 128 B: no conflicts.
+//   V: [row / 8][c / 2][row % 8][c % 2] -> a ds_read_b64_tr_b16 block (4 rows
+//      x 32 B) covers 128 contiguous bytes: no conflicts.
+// Both layouts make every DMA instruction write 1 KB contiguously (64 lanes x
+// 16 B) while each global row segment stays 128 B contiguous, and both give
+// per-lane base addresses plus compile-time offsets for all MFMA operands.
+//
+// Softmax runs in the base-2 domain on unscaled scores s: p = 2^(s*c - m),
+// c = scale*log2(e). The reference m is only raised when a row max exceeds it
+// by more than kRescaleSlack, so the O/l rescale is rare (p <= 2^slack keeps
+// fp32 and bf16 far from overflow); the final O = acc / l and
+// LSE = (m + log2 l) ln 2 are exact for any reference m.
+#pragma once
+#include "device_common.h"
+
+namespace attn {
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// 16 bytes per lane from gsrc into LDS at lds_dst_uniform + 16*lane
+// (global_load_lds_dwordx4; the LDS base goes through M0 and must be
+// wave-uniform). The instruction has no register results. It is issued from
+// asm so that the compiler does not add conservative vmcnt waits before LDS
+// reads of the other buffer: callers wait on vmcnt themselves before the
+// barrier that publishes a tile.
+__device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst_uniform) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_dst_uniform);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
+}
+
+// s_waitcnt with vmcnt = n and the other counters left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the caller
+// has already waited for exactly the memory operations the other waves need
+// (LDS-DMA of the current tile), so DMA for the next tile stays in flight.
+// The empty asm with a memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr float kRescaleSlack = 8.0f;
+
+template <int D_, int NW_, int BN_>
+struct PrefillCfg {
+  static constexpr int D = D_, DV = D_, NW = NW_, BN = BN_;
+  static constexpr int R = 32;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int ROWS = NW * R;
+  static constexpr int NCH = D / 8;                    // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * 2;        // one K (or V) tile
+  static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;
+  static constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;  // per wave, per K or V tile
+  static constexpr int NQ = D / 16;                    // Q fragments per row
+  static constexpr int NSB = BN / 32;                  // S^T blocks per tile
+  static constexpr int NPC = BN / 16;                  // P chunks per tile
+  static constexpr int NOB = DV / 32;                  // O^T blocks
+  static_assert(DMA_PER_TILE % NW == 0, "tile must split evenly over the waves");
+  static_assert(BN % 32 == 0 && D % 64 == 0, "shape");
+};
+
+template <class C>
+struct PrefillTile {
+  using M = Mfma<32>;
+  bf16x8 qf[C::NQ];
+  f32x16 o[C::NOB];
+  float m_ref;  // reference max (base-2 scaled domain), -inf until a key is seen
+  float l_run;  // this lane's share of sum 2^(s*c - m_ref)
+
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int i = 0; i < C::NOB; ++i) o[i] = f32x16{};
+    m_ref = kNegInf;
+    l_run = 0.f;
+  }
+
+  __device__ __forceinline__ void load_q(const bf16_t* qrow, int lane) {
+    const int g = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * 16 + g * 8);
+      qf[i] = as_bf16x8(v);
+    }
+  }
+
+  // Issues this wave's share of the DMA for one K or V tile whose key rows
+  // start at row(0); row(r) returns the global row pointer of key r (always a
+  // valid address). V tiles use the chunk-pair layout.
+  template <bool VLAYOUT, class RowPtr>
+  __device__ __forceinline__ static void dma_tile(char* buf, RowPtr row, int wave, int lane) {
+#pragma unroll
+    for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
+      const int inst = wave * C::DMA_PER_WAVE + n;
+      int r, c;
+      if constexpr (!VLAYOUT) {
+        // instruction -> (8-row block, half of the chunks); lane -> (row%8, chunk)
+        constexpr int IPB = C::NCH / 8;  // instructions per 8-row block
+        const int rb = inst / IPB, h = inst % IPB;
+        r = rb * 8 + (lane & 7);
+        c = h * 8 + (lane >> 3);
+      } else {
+        constexpr int IPB = C::NCH / 8;
+        const int rb = inst / IPB, pg = inst % IPB;
+        r = rb * 8 + ((lane & 15) >> 1);
+        c = 2 * (pg * 4 + (lane >> 4)) + (lane & 1);
+      }
+      lds_dma16(row(r) + c * 8, buf + inst * 1024);
+    }
+  }
+
+  // One key tile from LDS. MASK selects the masked variant; vis(j) is the
+  // visibility of tile-relative key j for this lane's row.
+  template <bool MASK, class Vis>
+  __device__ __forceinline__ void tile(const char* kbuf, const char* vbuf, float cscale, int lane,
+                                       Vis vis) {
+    const int g = lane >> 5;
+    // S^T = K Q^T
+    const char* kb = kbuf + ((((lane & 31) >> 3) * C::NCH + g) * 128 + (lane & 7) * 16);
+    f32x16 s[C::NSB];
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      bf16x8 kf[C::NQ];
+#pragma unroll
+      for (int dq = 0; dq < C::NQ; ++dq)
+        kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (sb * 4 * C::NCH + dq * 2) * 128));
+      s[sb] = f32x16{};
+#pragma unroll
+      for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], qf[dq], s[sb]);
+    }
+    // row max of raw scores (masked -> -inf)
+    float mx = kNegInf;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (MASK) {
+          if (!vis(sb * 32 + M::mrow(g, r))) s[sb][r] = kNegInf;
+        }
+        mx = fmaxf(mx, s[sb][r]);
+      }
+    }
+    mx = M::group_max(mx) * cscale;
+    // lazy reference update (wave-uniform branch)
+    const bool raise = mx > m_ref + kRescaleSlack;
+    if (__ballot(raise) != 0) {
+      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // m_ref = -inf -> 0
+      m_ref = raise ? mx : m_ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+    }
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
+    // probabilities packed to bf16 in B-operand order
+    uint32_t pk[C::NSB * 8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use));
+        lsum += p0 + p1;
+        pk[sb * 8 + r / 2] = pack_bf16x2(p0, p1);
+      }
+    }
+    l_run += lsum;
+    // O^T += V^T P^T (V read transposed)
+    const char* vb = vbuf + (((lane >> 4) & 1) * 256 + g * 128 + (lane & 15) * 8);
+#pragma unroll
+    for (int c = 0; c < C::NPC; ++c) {
+      const u32x4 pv = {pk[c * 4], pk[c * 4 + 1], pk[c * 4 + 2], pk[c * 4 + 3]};
+      const bf16x8 b = as_bf16x8(pv);
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob) {
+        const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(
+            vb + ((c * 2 + 0) * (C::NCH / 2) + ob * 2) * 256));
+        const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(
+            vb + ((c * 2 + 1) * (C::NCH / 2) + ob * 2) * 256));
+        o[ob] = M::mma(join_bf16x8(lo, hi), b, o[ob]);
+      }
+    }
+  }
+
+  __device__ __forceinline__ float finish(bool has_sink, float sink2, float& lse) const {
+    const float l = M::group_sum(l_run);
+    const bool empty = !(l > 0.f);
+    lse = empty ? kNegInf : (m_ref + fast_log2(l)) * kLn2;
+    if (!has_sink) return empty ? 0.f : 1.f / l;
+    if (empty) return 0.f;
+    const float ms = fmaxf(m_ref, sink2);
+    const float f = fast_exp2(m_ref - ms);
+    return f / (l * f + fast_exp2(sink2 - ms));
+  }
+
+  __device__ __forceinline__ void store(bf16_t* orow, float inv, int lane) const {
+    const int g = lane >> 5;
+#pragma unroll
+    for (int ob = 0; ob < C::NOB; ++ob) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 4) {
+        const int col = ob * 32 + M::mrow(g, r);
+        const u32x2 w = {pack_bf16x2(o[ob][r] * inv, o[ob][r + 1] * inv),
+                         pack_bf16x2(o[ob][r + 2] * inv, o[ob][r + 3] * inv)};
+        *reinterpret_cast<u32x2*>(orow + col) = w;
+      }
+    }
+  }
+};
+
+}  // namespace attn
