@@ -239,6 +239,8 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
   REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
   REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
   REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
+  REQUIRE(topk <= attn::sparse_max_topk(), ATTN_EUNSUPPORTED, "topk %d above %d", topk,
+          attn::sparse_max_topk());
   REQUIRE((long)batch * seqlen_q * ((hq + 63) / 64) < (1L << 31), ATTN_EUNSUPPORTED,
           "grid too large");
   attn::SparseArgs a;

@@ -1,278 +1,256 @@
-// Tiled online-softmax attention engine for gfx950 (bf16 MFMA, fp32 accumulate).
-//
-// One workgroup owns NW*R query rows that share one key sequence; each wave
-// owns R rows. Keys are consumed in tiles of BN rows staged through LDS:
+// Streaming tile engine for the decode-side kernels on gfx950 (paged GQA
+// decode, MLA-absorbed decode, top-k sparse MLA): 16 query rows per wave on
+// v_mfma_f32_16x16x32_bf16, keys streamed through an LDS ring.
 //
 //   S^T = K Q^T   (A = K tile from LDS, B = this wave's Q rows in registers)
-//   online softmax per row in the base-2 domain: m' = max(m, max_j s_j),
-//       p_j = 2^(s_j - m'), l = l 2^(m - m') + sum p_j, O *= 2^(m - m')
-//   O^T += V^T P^T (A = V tile read transposed from LDS, B = P in registers)
+//   online softmax per row in the base-2 domain with a lazily raised
+//   reference max (see prefill_bf16.h)
+//   O^T += V^T P^T (A = V read transposed from LDS, B = P from the S^T
+//   registers, which are already in B-operand order)
 //
-// Computing the transposed products makes every lane own exactly one query
-// row: the row statistics are per-lane scalars (reduced across the 2 or 4 lane
-// groups that share the row), and the S^T accumulator registers are already
-// laid out as the B operand of the P.V product, so P never leaves registers.
-// V stays row-major in LDS and is read with ds_read_b64_tr_b16, which also
-// lets a shared K/V row (MLA) be staged once.
+// Keys are consumed in tiles of BN = 32 rows. Each tile is copied global ->
+// LDS with global_load_lds_dwordx4 into a ring of STAGES buffers, so up to
+// STAGES-1 tiles are in flight per workgroup; the caller supplies the global
+// row address of every key of a tile (row(r), always a valid address) and,
+// after the ring, waits only on the DMA of the tile it is about to read.
 //
-// The score matrix is never materialised; the result per row is
-// O = sum_j e^{S_j - m} v_j / sum_j e^{S_j - m} and LSE = m + log sum e^{S_j - m}
-// (attention and softmax_lse formulas of the CANN "flash_attn" page), with the
-// optional sink of its sink formulas applied in finish().
+// LDS layouts (16-byte units, c = chunk index along the row; 64 banks x 4 B):
+//   K: [row / 16][c][(row % 16) ^ 8*(c & 1)]
+//      16 lanes reading 16 rows of one chunk cover 256 contiguous bytes; the
+//      parity swizzle makes the transposed V reads of a shared K/V row (MLA)
+//      conflict-free too: two 16-lane blocks reading chunks 2k and 2k+1 of
+//      8 rows land in opposite 128-byte halves.
+//   V (when not shared): [row / 8][c / 2][row % 8][c % 2]
+//      two 16-lane ds_read_b64_tr_b16 blocks (8 consecutive rows, one chunk
+//      pair) cover 256 contiguous bytes.
 #pragma once
 #include "device_common.h"
+#include "prefill_bf16.h"  // lds_dma16, wait_vmcnt, barrier_no_fence, kRescaleSlack
 
 namespace attn {
 
-template <int R_, int D_, int DV_, int NW_, int BN_, bool VSHARED_, bool KEYMASK_ = false>
-struct TileCfg {
-  static constexpr int R = R_, D = D_, DV = DV_, NW = NW_, BN = BN_;
-  static constexpr bool VSHARED = VSHARED_;   // V row = first DV entries of the K row
-  static constexpr bool KEYMASK = KEYMASK_;   // per-key validity flags staged with the tile
+template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_>
+struct StreamCfg {
+  static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
+  static constexpr bool VSHARED = VSHARED_;
+  static constexpr int BN = 32, R = 16;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * R;
-  static constexpr int KS = D + 8;                     // K row stride in LDS (elements)
-  static constexpr int VS = VSHARED ? KS : DV + 16;    // V row stride in LDS (elements)
-  static constexpr int K_ELEMS = BN * KS;
-  static constexpr int V_ELEMS = VSHARED ? 0 : BN * VS;
-  static constexpr int FLAG_BYTES = KEYMASK ? BN * 4 : 0;
-  static constexpr int LDS_BYTES = (K_ELEMS + V_ELEMS) * 2 + FLAG_BYTES;
-  static constexpr int KCH = D / 8;                    // 16-byte chunks per K row
-  static constexpr int VCH = DV / 8;
-  static constexpr int NKL = (BN * KCH + THREADS - 1) / THREADS;
-  static constexpr int NVL = VSHARED ? 0 : (BN * VCH + THREADS - 1) / THREADS;
-  static_assert(D % Mfma<R>::KSTEP == 0, "head dim must be a multiple of the MFMA depth");
-  static_assert(DV % Mfma<R>::SB == 0, "value dim must be a multiple of the MFMA width");
-  static_assert(BN % Mfma<R>::SB == 0 && BN % Mfma<R>::PVK == 0, "tile must hold whole MFMA blocks");
+  static constexpr int NCH = D / 8;
+  static constexpr int K_BYTES = BN * D * 2;
+  static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * 2;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int K_DMA = K_BYTES / 1024;
+  static constexpr int V_DMA = V_BYTES / 1024;
+  static constexpr int DMA_PER_WAVE = (K_DMA + V_DMA) / NW;
+  static constexpr int NQ = D / 32;      // Q fragments per row
+  static constexpr int NSB = BN / 16;    // S^T blocks per tile
+  static constexpr int NOB = DV / 16;    // O^T blocks
+  static_assert(D % 32 == 0 && DV % 16 == 0 && NCH % 4 == 0, "head dims");
+  static_assert((K_DMA + V_DMA) % NW == 0, "tile DMA must split evenly over the waves");
+  static_assert(VSHARED || (NCH / 2) % 4 == 0, "V layout needs whole instructions per row block");
+  static_assert(VSHARED ? DV <= D : DV == D, "value width");
+  static_assert(DMA_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
 };
 
 template <class C>
-struct TileCore {
-  using M = Mfma<C::R>;
-  using acc_t = typename M::acc_t;
-  static constexpr int NQ = C::D / M::KSTEP;    // Q fragments (B operands) per row
-  static constexpr int NSB = C::BN / M::SB;     // S^T blocks per tile
-  static constexpr int NPC = C::BN / M::PVK;    // P chunks (B operands of P.V) per tile
-  static constexpr int NOB = C::DV / M::SB;     // O^T blocks
-  static constexpr int NP = NSB * M::SREG / 2;  // packed bf16 pairs of P
-
-  struct Stage {
-    u32x4 k[C::NKL];
-    u32x4 v[C::NVL > 0 ? C::NVL : 1];
-    uint32_t kflag;  // bit i: K chunk i came from a valid key
-  };
-
-  bf16x8 qf[NQ];
-  acc_t o[NOB];
-  float m_run;  // running max of this row, base-2 scaled domain
-  float l_run;  // this lane's share of the running denominator
+struct StreamTile {
+  using M = Mfma<16>;
+  bf16x8 qf[C::NQ];
+  f32x4 o[C::NOB];
+  float m_ref;
+  float l_run;
 
   __device__ __forceinline__ void init() {
 #pragma unroll
-    for (int i = 0; i < NOB; ++i) o[i] = acc_t{};
-    m_run = kNegInf;
+    for (int i = 0; i < C::NOB; ++i) o[i] = f32x4{};
+    m_ref = kNegInf;
     l_run = 0.f;
   }
 
-  // qrow: this lane's query row (D elements) or nullptr for a padding row.
   __device__ __forceinline__ void load_q(const bf16_t* qrow, int lane) {
-    const int g = M::grp(lane);
+    const int g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < NQ; ++i) {
+    for (int i = 0; i < C::NQ; ++i) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * M::KSTEP + g * 8);
+      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * 32 + g * 8);
       qf[i] = as_bf16x8(v);
     }
   }
 
-  // Global -> registers for the tile starting at key j0. kptr(j) / vptr(j)
-  // return the row of key j or nullptr (invalid key: zeros are staged, so a
-  // masked key never injects NaN/Inf garbage into P.V).
-  template <class KP, class VP>
-  __device__ __forceinline__ void gload(Stage& st, int j0, int tid, KP kptr, VP vptr) const {
-    st.kflag = 0;
+  // This wave's share of the DMA of one tile into `stage`. krow(r) / vrow(r)
+  // give the global address of the K / V row of key r of the tile (r in
+  // [0, BN)); vrow is unused when V shares the K row.
+  template <class KRow, class VRow>
+  __device__ __forceinline__ static void dma_tile(char* stage, KRow krow, VRow vrow, int wave,
+                                                  int lane) {
 #pragma unroll
-    for (int i = 0; i < C::NKL; ++i) {
-      const int q = tid + i * C::THREADS;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < C::BN * C::KCH) {
-        const int r = q / C::KCH, c = q % C::KCH;
-        const bf16_t* p = kptr(j0 + r);
-        if (p) {
-          v = *reinterpret_cast<const u32x4*>(p + c * 8);
-          st.kflag |= 1u << i;
-        }
-      }
-      st.k[i] = v;
-    }
-#pragma unroll
-    for (int i = 0; i < C::NVL; ++i) {
-      const int q = tid + i * C::THREADS;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < C::BN * C::VCH) {
-        const int r = q / C::VCH, c = q % C::VCH;
-        const bf16_t* p = vptr(j0 + r);
-        if (p) v = *reinterpret_cast<const u32x4*>(p + c * 8);
-      }
-      st.v[i] = v;
-    }
-  }
-
-  __device__ __forceinline__ void sstore(const Stage& st, bf16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < C::NKL; ++i) {
-      const int q = tid + i * C::THREADS;
-      if (q < C::BN * C::KCH) {
-        const int r = q / C::KCH, c = q % C::KCH;
-        *reinterpret_cast<u32x4*>(lds + r * C::KS + c * 8) = st.k[i];
-        if (C::KEYMASK && c == 0)
-          reinterpret_cast<float*>(lds + C::K_ELEMS + C::V_ELEMS)[r] =
-              (st.kflag >> i) & 1u ? 0.f : kNegInf;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::NVL; ++i) {
-      const int q = tid + i * C::THREADS;
-      if (q < C::BN * C::VCH) {
-        const int r = q / C::VCH, c = q % C::VCH;
-        *reinterpret_cast<u32x4*>(lds + C::K_ELEMS + r * C::VS + c * 8) = st.v[i];
+    for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
+      // wave is 0 for single-wave workgroups and a uniform (SGPR) value
+      // otherwise, so the K/V choice below is a scalar branch or constant.
+      const int inst = (C::NW == 1 ? 0 : wave) * C::DMA_PER_WAVE + n;
+      const bool is_k = C::V_DMA == 0 || (C::NW == 1 ? n < C::K_DMA : inst < C::K_DMA);
+      if (is_k) {
+        constexpr int IPB = C::NCH / 4;  // instructions per 16-row block
+        const int rb = inst / IPB, cq = inst % IPB;
+        const int c = cq * 4 + (lane >> 4);
+        const int r = rb * 16 + ((lane & 15) ^ ((c & 1) * 8));
+        lds_dma16(krow(r) + c * 8, stage + inst * 1024);
+      } else {
+        const int vi = inst - C::K_DMA;
+        const int blk = 4 * vi + (lane >> 4);
+        const int r = (blk / (C::NCH / 2)) * 8 + ((lane & 15) >> 1);
+        const int c = (blk % (C::NCH / 2)) * 2 + (lane & 1);
+        lds_dma16(vrow(r) + c * 8, stage + C::K_BYTES + vi * 1024);
       }
     }
   }
 
-  // One key tile. cscale = softmax scale * log2(e). vis(j) decides whether
-  // key j (absolute index) is visible to this lane's row; it is only
-  // consulted when need_mask is true.
-  template <class Vis>
-  __device__ __forceinline__ void tile(const bf16_t* lds, int j0, bool need_mask, Vis vis,
-                                       float cscale, int lane) {
-    const int g = M::grp(lane);
-    const int rr = M::row(lane);
-    acc_t s[NSB];
+  // S^T for one tile.
+  __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
+    const int g = lane >> 4;
+    const char* kb = stage + (g * 256 + ((lane & 15) ^ ((g & 1) * 8)) * 16);
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      s[sb] = acc_t{};
-      const bf16_t* krow = lds + (sb * M::SB + rr) * C::KS + g * 8;
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      s[sb] = f32x4{};
 #pragma unroll
-      for (int dq = 0; dq < NQ; ++dq) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + dq * M::KSTEP);
+      for (int dq = 0; dq < C::NQ; ++dq) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + dq * 4) * 256);
         s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
       }
     }
-    // scale, mask, row max
-    float mx = kNegInf;
-    const float* kbias = reinterpret_cast<const float*>(lds + C::K_ELEMS + C::V_ELEMS);
+  }
+
+  // Masking (vis(j) for tile-relative key j, only when need_mask), row max,
+  // lazy update of the reference; returns the exponent offset.
+  template <class Vis>
+  __device__ __forceinline__ float prep(f32x4 (&s)[C::NSB], float cscale, int lane, bool need_mask,
+                                        Vis vis) {
+    const int g = lane >> 4;
+    if (need_mask) {
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
+      for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < M::SREG; ++r) {
-        float x = s[sb][r] * cscale;
-        if (need_mask) {
-          const int jl = sb * M::SB + M::mrow(g, r);
-          if (C::KEYMASK) x += kbias[jl];
-          if (!vis(j0 + jl)) x = kNegInf;
-        }
-        s[sb][r] = x;
-        mx = fmaxf(mx, x);
+        for (int r = 0; r < 4; ++r)
+          if (!vis(sb * 16 + g * 4 + r)) s[sb][r] = kNegInf;
       }
     }
-    mx = M::group_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= alpha;
+    float mx = kNegInf;
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) o[ob] *= alpha;
-    // probabilities, packed to bf16 pairs in B-operand order
-    uint32_t pk[NP];
+    for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[sb][r]);
+    }
+    mx = M::group_max(mx) * cscale;
+    const bool raise = mx > m_ref + kRescaleSlack;
+    if (__ballot(raise) != 0) {
+      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;
+      m_ref = raise ? mx : m_ref;
+      l_run *= alpha;
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+    }
+    return m_ref == kNegInf ? 0.f : m_ref;
+  }
+
+  __device__ __forceinline__ void probs(const f32x4 (&s)[C::NSB], float cscale, float m_use,
+                                        uint32_t (&pk)[C::NSB * 2]) {
     float lsum = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
+    for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < M::SREG; r += 2) {
-        const float p0 = fast_exp2(s[sb][r] - m_use);
-        const float p1 = fast_exp2(s[sb][r + 1] - m_use);
+      for (int r = 0; r < 4; r += 2) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use));
         lsum += p0 + p1;
-        pk[(sb * M::SREG + r) / 2] = pack_bf16x2(p0, p1);
+        pk[sb * 2 + r / 2] = pack_bf16x2(p0, p1);
       }
     }
     l_run += lsum;
-    // O^T += V^T P^T
-    const bf16_t* vt = lds + (C::VSHARED ? 0 : C::K_ELEMS);
-    const int i16 = lane & 15;
+  }
+
+  // O^T += V^T P^T for one tile (one 32-key chunk).
+  __device__ __forceinline__ void pv(const char* stage, int lane, const uint32_t (&pk)[C::NSB * 2]) {
+    const int g = lane >> 4, i = lane & 15;
+    const u32x4 pv4 = {pk[0], pk[1], pk[2], pk[3]};
+    const bf16x8 b = as_bf16x8(pv4);
+    if constexpr (C::VSHARED) {
+      const int par = (i >> 1) & 1;
+      const char* vb = stage + (par * 256 + ((g * 4 + (i >> 2)) ^ (par * 8)) * 16 + (i & 1) * 8);
 #pragma unroll
-    for (int c = 0; c < NPC; ++c) {
-      const u32x4 pb = {pk[c * 4], pk[c * 4 + 1], pk[c * 4 + 2], pk[c * 4 + 3]};
-      const bf16x8 b = as_bf16x8(pb);
-      const bf16_t* vrow = vt + (c * M::PVK + g * 4 + (i16 >> 2)) * C::VS + M::tr_col(lane) +
-                           (i16 & 3) * 4;
+      for (int ob = 0; ob < C::NOB; ++ob) {
+        const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(vb + (0 * C::NCH + ob * 2) * 256));
+        const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(vb + (1 * C::NCH + ob * 2) * 256));
+        o[ob] = M::mma(join_bf16x8(lo, hi), b, o[ob]);
+      }
+    } else {
+      const char* vb = stage + C::K_BYTES + ((g >> 1) * (C::NCH / 2) * 256 + (g & 1) * 128 + i * 8);
 #pragma unroll
-      for (int ob = 0; ob < NOB; ++ob) {
-        const s16x4 lo = lds_read_tr(vrow + ob * M::SB);
-        const s16x4 hi = lds_read_tr(vrow + (M::PVK / 2) * C::VS + ob * M::SB);
+      for (int ob = 0; ob < C::NOB; ++ob) {
+        const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(vb + (0 * (C::NCH / 2) + ob) * 256));
+        const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(vb + (2 * (C::NCH / 2) + ob) * 256));
         o[ob] = M::mma(join_bf16x8(lo, hi), b, o[ob]);
       }
     }
   }
 
-  // Final normalisation. Returns the factor that turns the accumulator into
-  // the output row, and the row's LSE (natural log, sink-free, -inf for a row
-  // that saw no key). With a sink (base-2 scaled logit sink2) the denominator
-  // gains 2^(sink2 - m) measured against m* = max(m, sink2).
   __device__ __forceinline__ float finish(bool has_sink, float sink2, float& lse) const {
     const float l = M::group_sum(l_run);
     const bool empty = !(l > 0.f);
-    lse = empty ? kNegInf : (m_run + fast_log2(l)) * kLn2;
+    lse = empty ? kNegInf : (m_ref + fast_log2(l)) * kLn2;
     if (!has_sink) return empty ? 0.f : 1.f / l;
     if (empty) return 0.f;
-    const float ms = fmaxf(m_run, sink2);
-    const float f = fast_exp2(m_run - ms);
+    const float ms = fmaxf(m_ref, sink2);
+    const float f = fast_exp2(m_ref - ms);
     return f / (l * f + fast_exp2(sink2 - ms));
   }
 
-  // Writes this lane's share of the output row: NOB blocks x SREG values,
-  // four consecutive columns at a time. OutT is bf16_t or float.
   template <class OutT>
   __device__ __forceinline__ void store(OutT* orow, float inv, int lane) const {
-    const int g = M::grp(lane);
+    const int g = lane >> 4;
 #pragma unroll
-    for (int ob = 0; ob < NOB; ++ob) {
-#pragma unroll
-      for (int r = 0; r < M::SREG; r += 4) {
-        const int col = ob * M::SB + M::mrow(g, r);
-        const float a0 = o[ob][r] * inv, a1 = o[ob][r + 1] * inv;
-        const float a2 = o[ob][r + 2] * inv, a3 = o[ob][r + 3] * inv;
-        if constexpr (sizeof(OutT) == 2) {
-          const u32x2 w = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
-          *reinterpret_cast<u32x2*>(orow + col) = w;
-        } else {
-          const f32x4 w = {a0, a1, a2, a3};
-          *reinterpret_cast<f32x4*>(orow + col) = w;
-        }
+    for (int ob = 0; ob < C::NOB; ++ob) {
+      const int col = ob * 16 + g * 4;
+      const float a0 = o[ob][0] * inv, a1 = o[ob][1] * inv;
+      const float a2 = o[ob][2] * inv, a3 = o[ob][3] * inv;
+      if constexpr (sizeof(OutT) == 2) {
+        const u32x2 w = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)};
+        *reinterpret_cast<u32x2*>(orow + col) = w;
+      } else {
+        const f32x4 w = {a0, a1, a2, a3};
+        *reinterpret_cast<f32x4*>(orow + col) = w;
       }
     }
   }
 };
 
-// Runs the whole key loop [lo, hi) for one workgroup with register-staged
-// prefetch of the next tile while the current one is computed.
-// need(j0) -> bool says whether tile j0 may contain keys that some row of
-// the workgroup must not see.
-template <class C, class KP, class VP, class Need, class Vis>
-__device__ __forceinline__ void run_keys(TileCore<C>& core, bf16_t* lds, int lo, int hi,
-                                         float cscale, KP kptr, VP vptr, Need need, Vis vis) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  if (lo >= hi) return;
-  typename TileCore<C>::Stage st;
-  core.gload(st, lo, tid, kptr, vptr);
-  for (int j0 = lo; j0 < hi; j0 += C::BN) {
-    core.sstore(st, lds, tid);
-    __syncthreads();
-    if (j0 + C::BN < hi) core.gload(st, j0 + C::BN, tid, kptr, vptr);
-    core.tile(lds, j0, need(j0), vis, cscale, lane);
-    __syncthreads();
+// Streams tiles [0, ntiles) through the LDS ring `ring` (STAGES buffers of
+// STAGE_BYTES). issue(stage_ptr, t) enqueues the DMA of tile t; compute(t,
+// stage_ptr) consumes it. Exactly DMA_PER_WAVE DMA instructions per wave per
+// tile must be issued by issue(). Waits only for the tile about to be read.
+template <class C, class Issue, class Compute>
+__device__ __forceinline__ void stream_tiles(char* ring, int ntiles, Issue issue, Compute compute) {
+  auto stage = [&](int t) { return ring + (t % C::STAGES) * C::STAGE_BYTES; };
+#pragma unroll
+  for (int t = 0; t < C::STAGES - 1; ++t)
+    if (t < ntiles) issue(stage(t), t);
+  for (int i = 0; i < ntiles; ++i) {
+    // tiles issued after tile i: min(ntiles-1-i, STAGES-2)
+    const int after = min(ntiles - 1 - i, C::STAGES - 2);
+    if constexpr (C::STAGES >= 4) {
+      if (after >= 2) wait_vmcnt<2 * C::DMA_PER_WAVE>();
+      else if (after == 1) wait_vmcnt<C::DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+    } else if constexpr (C::STAGES == 3) {
+      if (after >= 1) wait_vmcnt<C::DMA_PER_WAVE>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own LDS reads of tile i-1 retired
+    barrier_no_fence();                  // tile i visible; every wave is done with tile i-1
+    if (i + C::STAGES - 1 < ntiles) issue(stage(i + C::STAGES - 1), i + C::STAGES - 1);
+    compute(i, stage(i));
   }
 }
 

@@ -28,12 +28,15 @@ inline int round_grid(long total, int grp) {
 // One workgroup = (sequence b, split s, KV head kvh, row tile mt). Rows of a
 // KV head are (query token t, query head of the group): row r -> t = r / G,
 // head kvh*G + r % G. Keys are the split's range [kv0, kv1) of the sequence.
+// A 32-key tile spans at most two cache pages (page sizes are multiples of
+// 16 and splits start on page boundaries); their physical page numbers are
+// wave-uniform and come from scalar loads of the block table.
 template <class C>
 __global__ void __launch_bounds__(C::THREADS)
 k_decode(DecodeArgs a) {
-  using Core = TileCore<C>;
-  using M = typename Core::M;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_BYTES / 2];
+  using T = StreamTile<C>;
+  using M = Mfma<16>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   const int grp = a.hq / a.hkv;
   const int nrows = a.sq * grp;
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
@@ -54,53 +57,97 @@ k_decode(DecodeArgs a) {
   const int delta = lk - a.sq;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = mt * C::ROWS + wave * C::R + M::row(lane);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = mt * C::ROWS + wave * C::R + (lane & 15);
   const bool row_ok = r < nrows;
   const int tq = row_ok ? r / grp : 0;
   const int h = kvh * grp + (row_ok ? r % grp : 0);
-  const bf16_t* q = static_cast<const bf16_t*>(a.q);
-  Core core;
-  core.init();
-  core.load_q(row_ok ? q + (((size_t)b * a.sq + tq) * a.hq + h) * C::D : nullptr, lane);
+  T tile;
+  tile.init();
+  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
+                     : nullptr,
+              lane);
+  wait_vmcnt<0>();  // Q in registers before any DMA is in flight
 
-  const bf16_t* kc = static_cast<const bf16_t*>(a.kc);
-  const bf16_t* vc = static_cast<const bf16_t*>(a.vc);
-  auto kptr = [&](int j) -> const bf16_t* {
-    return j < kv1 ? kc + paged_row_offset(a.block_table, a.max_pages, b, j, a.page, a.hkv, kvh,
-                                           C::D)
-                   : nullptr;
-  };
-  auto vptr = [&](int j) -> const bf16_t* {
-    return j < kv1 ? vc + paged_row_offset(a.block_table, a.max_pages, b, j, a.page, a.hkv, kvh,
-                                           C::DV)
-                   : nullptr;
+  const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + (size_t)kvh * C::D;
+  const bf16_t* vc =
+      (C::VSHARED ? static_cast<const bf16_t*>(a.kc) : static_cast<const bf16_t*>(a.vc)) +
+      (size_t)kvh * C::DV;
+  const int* btb = a.block_table + (size_t)b * a.max_pages;
+  const int kv_last = kv1 - 1;
+  const size_t tok_k = (size_t)a.hkv * C::D, tok_v = (size_t)a.hkv * C::DV;
+  auto issue = [&](char* st, int ti) {
+    // Uniform per tile: the (at most two) pages it touches and the address
+    // of tile row 0 as if it were on each of them; row r of the tile is
+    // base + r * row_stride on its page. Rows past the split (last tile
+    // only) re-read the split's last key, which is masked.
+    const int j0 = kv0 + ti * C::BN;
+    const int lp0 = j0 / a.page;
+    const int lp1 = min(j0 + C::BN - 1, kv_last) / a.page;
+    const int bnd = (lp0 + 1) * a.page - j0;  // first tile row on page lp1
+    const long s0 = (long)btb[lp0] * a.page + (j0 - lp0 * a.page);
+    const long s1 = (long)btb[lp1] * a.page + (j0 - lp1 * a.page);
+    const int rmax = kv_last - j0;
+    const bf16_t* k0p = kc + s0 * tok_k;
+    const bf16_t* k1p = kc + s1 * tok_k;
+    const bf16_t* v0p = vc + s0 * tok_v;
+    const bf16_t* v1p = vc + s1 * tok_v;
+    if (rmax >= C::BN - 1) {
+      T::dma_tile(
+          st, [&](int rr) { return (rr < bnd ? k0p : k1p) + (size_t)rr * tok_k; },
+          [&](int rr) { return (rr < bnd ? v0p : v1p) + (size_t)rr * tok_v; }, wave, lane);
+    } else {
+      T::dma_tile(
+          st,
+          [&](int rr) {
+            rr = min(rr, rmax);
+            return (rr < bnd ? k0p : k1p) + (size_t)rr * tok_k;
+          },
+          [&](int rr) {
+            rr = min(rr, rmax);
+            return (rr < bnd ? v0p : v1p) + (size_t)rr * tok_v;
+          },
+          wave, lane);
+    }
   };
   const int first_t = (mt * C::ROWS) / grp;
-  auto vis = [&](int j) { return j < kv1 && (!a.causal || j <= tq + delta); };
-  auto need = [&](int j0) {
-    return j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
-  };
-  run_keys(core, lds, kv0, kv1, a.scale_log2, kptr, vptr, need, vis);
+  const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
+  stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+    const int j0 = kv0 + ti * C::BN;
+    const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
+    f32x4 sc[C::NSB];
+    tile.qk(st, lane, sc);
+    const float m_use = tile.prep(sc, a.scale_log2, lane, need, [&](int jr) {
+      const int j = j0 + jr;
+      return j < kv1 && (!a.causal || j <= tq + delta);
+    });
+    uint32_t pk[C::NSB * 2];
+    tile.probs(sc, a.scale_log2, m_use, pk);
+    tile.pv(st, lane, pk);
+  });
 
   float lse;
-  const float inv = core.finish(false, 0.f, lse);
+  const float inv = tile.finish(false, 0.f, lse);
   if (row_ok) {
-    const size_t slot = (size_t)b * a.max_splits + s;
-    const size_t row = slot * nrows * a.hkv + (size_t)tq * a.hq + h;
-    core.store(a.o_part + row * C::DV, inv, lane);
-    if (M::grp(lane) == 0) a.lse_part[row] = lse;
+    const size_t slot_id = (size_t)b * a.max_splits + s;
+    const size_t row = slot_id * nrows * a.hkv + (size_t)tq * a.hq + h;
+    tile.store(a.o_part + row * C::DV, inv, lane);
+    if (lane < 16) a.lse_part[row] = lse;
   }
 }
 
 // One workgroup = (sequence b, query token t, head tile mt); all heads of a
-// token share its index list, so the gathered key rows are staged once.
+// token share its index list. The list is staged in LDS once (invalid
+// entries -> -1); rows of invalid keys are fetched from row 0 (a valid
+// address) and masked.
+constexpr int kMaxTopk = 4096;
+
 template <class C>
 __global__ void __launch_bounds__(C::THREADS)
 k_sparse(SparseArgs a) {
-  using Core = TileCore<C>;
-  using M = typename Core::M;
-  __shared__ __attribute__((aligned(16))) bf16_t lds[C::LDS_BYTES / 2];
+  using T = StreamTile<C>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
+  __shared__ int sidx[kMaxTopk];
   const int mtiles = (a.hq + C::ROWS - 1) / C::ROWS;
   const int p = blockIdx.x;
   const int mt = p % mtiles;
@@ -108,41 +155,59 @@ k_sparse(SparseArgs a) {
   const int b = p / (mtiles * a.sq);
   if (b >= a.batch) return;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int h = mt * C::ROWS + wave * C::R + M::row(lane);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = mt * C::ROWS + wave * C::R + (lane & 15);
   const bool row_ok = h < a.hq;
-  const bf16_t* q = static_cast<const bf16_t*>(a.q);
-  Core core;
-  core.init();
-  core.load_q(row_ok ? q + (((size_t)b * a.sq + t) * a.hq + h) * C::D : nullptr, lane);
 
+  const int ntiles = (a.topk + C::BN - 1) / C::BN;
   const int32_t* ix = a.idx + ((size_t)b * a.sq + t) * a.topk;
   const int limit = a.mode == 3 ? min(a.sk - 1, t + a.sk - a.sq) : a.sk - 1;
+  for (int k = threadIdx.x; k < ntiles * C::BN; k += C::THREADS) {
+    const int id = k < a.topk ? ix[k] : -1;
+    sidx[k] = (id >= 0 && id <= limit) ? id : -1;
+  }
+  T tile;
+  tile.init();
+  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + t) * a.hq + h) * C::D
+                     : nullptr,
+              lane);
+  wait_vmcnt<0>();
+  __syncthreads();
+
   const bf16_t* kvb = static_cast<const bf16_t*>(a.kv) + (size_t)b * a.sk * C::D;
-  auto kptr = [&](int j) -> const bf16_t* {
-    if (j >= a.topk) return nullptr;
-    const int id = ix[j];
-    return (id >= 0 && id <= limit) ? kvb + (size_t)id * C::D : nullptr;
+  auto issue = [&](char* st, int ti) {
+    const int* tix = sidx + ti * C::BN;
+    auto krow = [&](int rr) { return kvb + (size_t)max(tix[rr], 0) * C::D; };
+    T::dma_tile(st, krow, krow, wave, lane);
   };
-  auto vis = [](int) { return true; };
-  auto need = [](int) { return true; };
-  run_keys(core, lds, 0, a.topk, a.scale_log2, kptr, kptr, need, vis);
+  stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+    const int* tix = sidx + ti * C::BN;
+    f32x4 sc[C::NSB];
+    tile.qk(st, lane, sc);
+    const float m_use =
+        tile.prep(sc, a.scale_log2, lane, true, [&](int jr) { return tix[jr] >= 0; });
+    uint32_t pk[C::NSB * 2];
+    tile.probs(sc, a.scale_log2, m_use, pk);
+    tile.pv(st, lane, pk);
+  });
 
   float lse;
   const float sink2 = (a.sinks && row_ok) ? a.sinks[h] * kLog2e : 0.f;
-  const float inv = core.finish(a.sinks != nullptr, sink2, lse);
+  const float inv = tile.finish(a.sinks != nullptr, sink2, lse);
   if (row_ok) {
-    core.store(static_cast<bf16_t*>(a.out) + (((size_t)b * a.sq + t) * a.hq + h) * C::DV, inv,
+    tile.store(static_cast<bf16_t*>(a.out) + (((size_t)b * a.sq + t) * a.hq + h) * C::DV, inv,
                lane);
-    if (a.lse && M::grp(lane) == 0) a.lse[((size_t)b * a.hq + h) * a.sq + t] = lse;
+    if (a.lse && lane < 16) a.lse[((size_t)b * a.hq + h) * a.sq + t] = lse;
   }
 }
 
-using CfgDecodeGqa = TileCfg<16, 128, 128, 1, 32, false>;
-using CfgDecodeMla = TileCfg<16, 576, 512, 4, 32, true>;
-using CfgSparseMla = TileCfg<16, 576, 512, 4, 32, true, true>;
+using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
+using CfgDecodeMla = StreamCfg<576, 512, 4, 3, true>;
+using CfgSparseMla = StreamCfg<576, 512, 4, 3, true>;
 
 }  // namespace
+
+int sparse_max_topk() { return kMaxTopk; }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   using C = CfgDecodeGqa;

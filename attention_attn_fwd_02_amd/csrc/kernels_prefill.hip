@@ -80,7 +80,7 @@ k_varlen_bf16(VarlenArgs a) {
   const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int trow = row0 + wave * C::R + (lane & 31);
   const bool row_ok = trow < lq;
   T t;
@@ -97,7 +97,10 @@ k_varlen_bf16(VarlenArgs a) {
   const bf16_t* kb = static_cast<const bf16_t*>(a.k) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
   const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
   const int last = lk - 1;  // rows past the sequence re-read its last key (then masked)
-  auto issue = [&](char* buf, int j0) {
+  // Two stages, each holding one K tile and one V tile. While tile i is
+  // computed from one stage, the DMA of tile i+1 fills the other.
+  auto issue = [&](char* buf, int i) {
+    const int j0 = bd.lo + i * C::BN;
     T::template dma_tile<false>(
         buf, [&](int r) { return kb + (size_t)min(j0 + r, last) * kst; }, wave, lane);
     T::template dma_tile<true>(
@@ -106,9 +109,9 @@ k_varlen_bf16(VarlenArgs a) {
   };
   const int tdiag = trow + bd.delta;
   const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
-  auto process = [&](int i, char* __restrict__ cur, char* __restrict__ nxt) {
+  auto process = [&](int i, char* cur, char* nxt) {
     if (i + 1 < ntiles) {
-      issue(nxt, bd.lo + (i + 1) * C::BN);
+      issue(nxt, i + 1);
       wait_vmcnt<2 * C::DMA_PER_WAVE>();
     } else {
       wait_vmcnt<0>();
@@ -118,19 +121,20 @@ k_varlen_bf16(VarlenArgs a) {
     const bool need = j0 + C::BN > lk ||
                       (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
                       (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
-    if (need) {
-      t.template tile<true>(cur, cur + C::TILE_BYTES, a.scale_log2, lane, [&](int jr) {
-        const int j = j0 + jr;
-        return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
-      });
-    } else {
-      t.template tile<false>(cur, cur + C::TILE_BYTES, a.scale_log2, lane, [](int) { return true; });
-    }
+    f32x16 s[C::NSB];
+    t.qk(cur, lane, s);
+    const float m_use = t.prep(s, a.scale_log2, lane, need, [&](int jr) {
+      const int j = j0 + jr;
+      return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
+    });
+    uint32_t pk[C::NSB * 8];
+    t.probs(s, a.scale_log2, m_use, pk);
+    t.pv(cur + C::TILE_BYTES, lane, pk);
     // every wave must finish reading `cur` before the next DMA into it
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     barrier_no_fence();
   };
-  if (ntiles > 0) issue(stage0, bd.lo);
+  if (ntiles > 0) issue(stage0, 0);
   for (int i = 0; i < ntiles; i += 2) {
     process(i, stage0, stage1);
     if (i + 1 < ntiles) process(i + 1, stage1, stage0);

@@ -58,6 +58,7 @@ struct CombineArgs {
 // rows per workgroup of each instance (sizes the grids)
 int varlen_bf16_rows(int d);
 int varlen_f32_rows(int d);
+int sparse_max_topk();
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);

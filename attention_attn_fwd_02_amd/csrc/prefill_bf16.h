@@ -4,14 +4,18 @@
 // rows are copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no register
 // staging) into one of two buffers while the other buffer is consumed.
 //
-// LDS layouts (16-byte chunks, c = chunk index along the head dimension):
-//   K: [row / 8][c][row % 8]            -> A-operand reads of 32 consecutive
-//      rows at one chunk touch 8 distinct 16 B slots per 128 B: no conflicts.
-//   V: [row / 8][c / 2][row % 8][c % 2] -> a ds_read_b64_tr_b16 block (4 rows
-//      x 32 B) covers 128 contiguous bytes: no conflicts.
-// Both layouts make every DMA instruction write 1 KB contiguously (64 lanes x
-// 16 B) while each global row segment stays 128 B contiguous, and both give
-// per-lane base addresses plus compile-time offsets for all MFMA operands.
+// LDS layouts (16-byte units, c = chunk index along the head dimension). The
+// LDS has 64 banks of 4 bytes (256 B per cycle) and serves 16 lanes of a
+// 16-byte read per cycle; both layouts put the 16 lanes of every read in 256
+// distinct bytes:
+//   K: [row / 16][c][row % 16]               A-operand reads (16 consecutive
+//      rows at one chunk) are 256 contiguous bytes.
+//   V: [row / 8][c / 4][(row / 4) % 2][row % 4][c % 4]
+//      the two 16-lane blocks of a ds_read_b64_tr_b16 that share a cycle
+//      (4 rows x 32 B each) interleave into 256 contiguous bytes.
+// Every DMA instruction writes 1 KB contiguously (64 lanes x 16 B); each row
+// segment it reads from global memory is 64 B (K) or 128 B (V) contiguous.
+// All MFMA operand addresses are a per-lane base plus a compile-time offset.
 //
 // Softmax runs in the base-2 domain on unscaled scores s: p = 2^(s*c - m),
 // c = scale*log2(e). The reference m is only raised when a row max exceeds it
@@ -109,54 +113,63 @@ struct PrefillTile {
       const int inst = wave * C::DMA_PER_WAVE + n;
       int r, c;
       if constexpr (!VLAYOUT) {
-        // instruction -> (8-row block, half of the chunks); lane -> (row%8, chunk)
-        constexpr int IPB = C::NCH / 8;  // instructions per 8-row block
-        const int rb = inst / IPB, h = inst % IPB;
-        r = rb * 8 + (lane & 7);
-        c = h * 8 + (lane >> 3);
+        // instruction -> (16-row block, 4 chunks); lane -> (row % 16, chunk)
+        constexpr int IPB = C::NCH / 4;
+        const int rb = inst / IPB, cq = inst % IPB;
+        r = rb * 16 + (lane & 15);
+        c = cq * 4 + (lane >> 4);
       } else {
-        constexpr int IPB = C::NCH / 8;
-        const int rb = inst / IPB, pg = inst % IPB;
-        r = rb * 8 + ((lane & 15) >> 1);
-        c = 2 * (pg * 4 + (lane >> 4)) + (lane & 1);
+        // instruction -> two 512 B blocks (8 rows x 4 chunks); lane -> (row, chunk)
+        const int blk = 2 * inst + (lane >> 5);
+        r = (blk / (C::NCH / 4)) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 2) & 3);
+        c = (blk % (C::NCH / 4)) * 4 + (lane & 3);
       }
       lds_dma16(row(r) + c * 8, buf + inst * 1024);
     }
   }
 
-  // One key tile from LDS. MASK selects the masked variant; vis(j) is the
-  // visibility of tile-relative key j for this lane's row.
-  template <bool MASK, class Vis>
-  __device__ __forceinline__ void tile(const char* kbuf, const char* vbuf, float cscale, int lane,
-                                       Vis vis) {
+  // The key loop is software pipelined: iteration i finishes tile i (its
+  // softmax and P.V) while computing S for tile i+1, all in one basic block,
+  // so the MFMA work of one tile and the VALU work of the other can overlap
+  // inside a wave. The pieces:
+
+  // S^T = K Q^T for one tile.
+  __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[C::NSB]) const {
     const int g = lane >> 5;
-    // S^T = K Q^T
-    const char* kb = kbuf + ((((lane & 31) >> 3) * C::NCH + g) * 128 + (lane & 7) * 16);
-    f32x16 s[C::NSB];
+    const char* kb = kbuf + ((((lane >> 4) & 1) * C::NCH + g) * 256 + (lane & 15) * 16);
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
       bf16x8 kf[C::NQ];
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq)
-        kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (sb * 4 * C::NCH + dq * 2) * 128));
+        kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (sb * 2 * C::NCH + dq * 2) * 256));
       s[sb] = f32x16{};
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], qf[dq], s[sb]);
     }
-    // row max of raw scores (masked -> -inf)
+  }
+
+  // Masking (only when need_mask), row max and the lazy update of the
+  // reference max. Returns the reference to subtract in the exponent.
+  template <class Vis>
+  __device__ __forceinline__ float prep(f32x16 (&s)[C::NSB], float cscale, int lane, bool need_mask,
+                                        Vis vis) {
+    const int g = lane >> 5;
+    if (need_mask) {
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!vis(sb * 32 + M::mrow(g, r))) s[sb][r] = kNegInf;
+      }
+    }
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if constexpr (MASK) {
-          if (!vis(sb * 32 + M::mrow(g, r))) s[sb][r] = kNegInf;
-        }
-        mx = fmaxf(mx, s[sb][r]);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
     }
     mx = M::group_max(mx) * cscale;
-    // lazy reference update (wave-uniform branch)
     const bool raise = mx > m_ref + kRescaleSlack;
     if (__ballot(raise) != 0) {
       const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // m_ref = -inf -> 0
@@ -165,9 +178,12 @@ struct PrefillTile {
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
     }
-    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
-    // probabilities packed to bf16 in B-operand order
-    uint32_t pk[C::NSB * 8];
+    return m_ref == kNegInf ? 0.f : m_ref;
+  }
+
+  // p = 2^(s*c - m), packed to bf16 pairs in B-operand order; l += sum p.
+  __device__ __forceinline__ void probs(const f32x16 (&s)[C::NSB], float cscale, float m_use,
+                                        uint32_t (&pk)[C::NSB * 8]) {
     float lsum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
@@ -180,18 +196,22 @@ struct PrefillTile {
       }
     }
     l_run += lsum;
-    // O^T += V^T P^T (V read transposed)
-    const char* vb = vbuf + (((lane >> 4) & 1) * 256 + g * 128 + (lane & 15) * 8);
+  }
+
+  // O^T += V^T P^T with V read transposed.
+  __device__ __forceinline__ void pv(const char* vbuf, int lane, const uint32_t (&pk)[C::NSB * 8]) {
+    const int g = lane >> 5;
+    const char* vb = vbuf + (g * 256 + ((lane & 15) >> 2) * 64 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
 #pragma unroll
     for (int c = 0; c < C::NPC; ++c) {
-      const u32x4 pv = {pk[c * 4], pk[c * 4 + 1], pk[c * 4 + 2], pk[c * 4 + 3]};
-      const bf16x8 b = as_bf16x8(pv);
+      const u32x4 pv4 = {pk[c * 4], pk[c * 4 + 1], pk[c * 4 + 2], pk[c * 4 + 3]};
+      const bf16x8 b = as_bf16x8(pv4);
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob) {
         const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(
-            vb + ((c * 2 + 0) * (C::NCH / 2) + ob * 2) * 256));
+            vb + ((c * 2 + 0) * (C::NCH / 4) + ob) * 512));
         const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(
-            vb + ((c * 2 + 1) * (C::NCH / 2) + ob * 2) * 256));
+            vb + ((c * 2 + 1) * (C::NCH / 4) + ob) * 512));
         o[ob] = M::mma(join_bf16x8(lo, hi), b, o[ob]);
       }
     }
