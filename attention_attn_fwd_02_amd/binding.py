@@ -264,7 +264,8 @@ def attn_debug_gather_paged(cache, block_table, cache_seqlens, b, max_rows):
 
 # ------------------------------------------------------- composed decode calls
 # The split planner sizes splits so that the decode grid holds about
-# num_cu * waves workgroups; these are its defaults for the two decode shapes.
+# num_cu * waves workgroups; the defaults below were tuned on MI355X for the
+# two decode shapes (GQA: 8 per CU, MLA: 4 per CU).
 GQA_ROWS_PER_WG = 16
 MLA_ROWS_PER_WG = 64
 
@@ -274,7 +275,7 @@ def _num_cu(device):
 
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=False, sinks=None,
-                 max_splits=16, waves=4, min_blocks=4, num_cu=None, out_dtype=torch.bfloat16):
+                 max_splits=16, waves=8, min_blocks=2, num_cu=None, out_dtype=torch.bfloat16):
     """plan -> attn_decode_paged -> attn_combine. Returns (out (B,Sq,Hq,Dv),
     lse (B,Hq,Sq), plan)."""
     b, sq, hq, _ = q.shape
@@ -290,7 +291,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=
 
 
 def mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal=False, max_splits=16,
-               waves=2, min_blocks=4, num_cu=None):
+               waves=4, min_blocks=2, num_cu=None):
     """plan -> mla_decode_paged -> attn_combine (dv = 512)."""
     b, sq, hq, _ = q.shape
     upb = (sq * hq + MLA_ROWS_PER_WG - 1) // MLA_ROWS_PER_WG

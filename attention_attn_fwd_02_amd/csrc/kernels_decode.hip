@@ -40,19 +40,19 @@ k_decode(DecodeArgs a) {
   const int grp = a.hq / a.hkv;
   const int nrows = a.sq * grp;
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
+  // Work items follow the plan's split list (batch-major, total = plan[0]):
+  // item = (split, kv head, row tile). Real items come first, so they spread
+  // over all XCDs; the row tiles of one (split, kv head) read the same keys
+  // and are placed on one XCD.
   const int logical = xcd_group(blockIdx.x, mtiles);
-  if (logical >= a.batch * a.max_splits * a.hkv * mtiles) return;
+  const int total = a.plan[0];
+  if (logical >= total * a.hkv * mtiles) return;
   const int mt = logical % mtiles;
-  int t = logical / mtiles;
-  const int kvh = t % a.hkv;
-  t /= a.hkv;
-  const int s = t % a.max_splits;
-  const int b = t / a.max_splits;
-  const int* split_ptr = a.plan + 2;
-  const int sp = split_ptr[b];
-  if (s >= split_ptr[b + 1] - sp) return;
-  const int* tri = a.plan + 3 + a.batch + 3 * (sp + s);
-  const int kv0 = tri[1], kv1 = tri[2];
+  const int kvh = (logical / mtiles) % a.hkv;
+  const int split = logical / (mtiles * a.hkv);
+  const int* tri = a.plan + 3 + a.batch + 3 * split;
+  const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
+  const int s = split - a.plan[2 + b];
   const int lk = a.lens[b];
   const int delta = lk - a.sq;
 

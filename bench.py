@@ -104,7 +104,7 @@ def bench_decode(steps, warmup):
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
     hkv = w.k_cache.shape[2]
-    ms_, waves, mb = 16, 4, 4
+    ms_, waves, mb = 16, 8, 2
     upb = hkv * ((sq * hq // hkv + 15) // 16)
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
@@ -140,7 +140,7 @@ def bench_mla(steps, warmup):
     bt, lens = dev(w.block_table), dev(w.cache_seqlens)
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
-    ms_, waves, mb = 16, 2, 4
+    ms_, waves, mb = 16, 4, 2
     upb = (sq * hq + 63) // 64
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 512), dtype=torch.float32, device="cuda")
@@ -187,6 +187,26 @@ def bench_sparse(steps, warmup):
                 gathered_gbs=gathered / (ms * 1e-3) / 1e9)
 
 
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter profile of this
+    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the same counters read on a
+    plain copy of known size), or None when no such profile matches the
+    current kernel build."""
+    path = os.path.join(ROOT, "profiles", "k_varlen_bf16_d128_traffic.txt")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from attention_attn_fwd_02_amd import binding as B
+    import hashlib
+    with open(B.LIB_PATH, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()[:16]
+    if rec.get("library_sha256_16") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def cpu_baseline(pre):
     """The float64 oracle as it stands, timed on the host on a bounded sample
     of the prefill workload: its first three sequences, all 32 heads."""
@@ -216,6 +236,9 @@ def main():
     ap.add_argument("--only", default="prefill,decode,mla,sparse")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy, so that a "
+                         "counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -230,10 +253,17 @@ def main():
     only = set(args.only.split(","))
     if args.no_secondary:
         only &= {"prefill"}
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.int16, device="cuda")   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log("prefill ...")
     pre = bench_prefill(args.steps, args.warmup)
     log(f"prefill {pre['ms']:.3f} ms  {pre['tflops']:.1f} TFLOP/s")
+    traffic = measured_traffic()
     secondary = []
     if "decode" in only:
         log("paged decode ...")
@@ -302,8 +332,9 @@ def main():
                    "head_dim": 128, "causal": True, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": pre["tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": pre["tflops"] / PEAK_BF16_TFLOPS,
-                     "traffic": None, "kernel": "k_varlen_bf16 (D=128)",
-                     "algorithmic_flops_per_launch": pre["flops"]},
+                     "traffic": traffic, "kernel": "k_varlen_bf16 (D=128)",
+                     "algorithmic_flops_per_launch": pre["flops"],
+                     "algorithmic_bytes_per_launch": pre["bytes"]},
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
