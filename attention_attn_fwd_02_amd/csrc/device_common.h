@@ -68,10 +68,20 @@ template <> struct Mfma<32> {
   }
   // column offset of this lane's 16-lane block inside an A-operand tile
   __device__ static __forceinline__ int tr_col(int l) { return ((l >> 4) & 1) * 16; }
+  // Reductions over the two lane groups of a row (lanes l and l ^ 32):
+  // v_permlane32_swap exchanges the upper half of its first operand with the
+  // lower half of its second, so with both set to x the two results hold
+  // x[l] and x[l ^ 32] (in some order) in every lane.
   __device__ static __forceinline__ float group_max(float x) {
-    return fmaxf(x, __shfl_xor(x, 32));
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
   }
-  __device__ static __forceinline__ float group_sum(float x) { return x + __shfl_xor(x, 32); }
+  __device__ static __forceinline__ float group_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  }
 };
 
 template <> struct Mfma<16> {
@@ -89,13 +99,20 @@ template <> struct Mfma<16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ int tr_col(int) { return 0; }
+  // Reductions over the four lane groups of a row (lanes l ^ 16, l ^ 32):
+  // v_permlane16_swap pairs 16-lane rows 0<->1 and 2<->3, then
+  // v_permlane32_swap pairs the two halves (see Mfma<32>).
   __device__ static __forceinline__ float group_max(float x) {
-    x = fmaxf(x, __shfl_xor(x, 16));
-    return fmaxf(x, __shfl_xor(x, 32));
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    x = fmaxf(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+    return Mfma<32>::group_max(x);
   }
   __device__ static __forceinline__ float group_sum(float x) {
-    x += __shfl_xor(x, 16);
-    return x + __shfl_xor(x, 32);
+    const auto a = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
+                                                    __builtin_bit_cast(uint32_t, x), false, false);
+    x = __builtin_bit_cast(float, (uint32_t)a[0]) + __builtin_bit_cast(float, (uint32_t)a[1]);
+    return Mfma<32>::group_sum(x);
   }
 };
 

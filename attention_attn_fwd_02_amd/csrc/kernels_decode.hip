@@ -117,10 +117,9 @@ k_decode(DecodeArgs a) {
     const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
     f32x4 sc[C::NSB];
     tile.qk(st, lane, sc);
-    const float m_use = tile.prep(sc, a.scale_log2, lane, need, [&](int jr) {
-      const int j = j0 + jr;
-      return j < kv1 && (!a.causal || j <= tq + delta);
-    });
+    const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
+    const float m_use = tile.prep(sc, a.scale_log2, lane, need,
+                                  [&](int jr) { return j0 + jr <= hi_vis; });
     uint32_t pk[C::NSB * 2];
     tile.probs(sc, a.scale_log2, m_use, pk);
     tile.pv(st, lane, pk);

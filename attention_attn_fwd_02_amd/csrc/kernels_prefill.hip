@@ -63,7 +63,7 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 }
 
 template <class C>
-__global__ void __launch_bounds__(C::THREADS, 2)
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES)
 k_varlen_bf16(VarlenArgs a) {
   using T = PrefillTile<C>;
   __shared__ __attribute__((aligned(1024))) char stage0[2 * C::TILE_BYTES];  // K tile, V tile
@@ -123,9 +123,11 @@ k_varlen_bf16(VarlenArgs a) {
                       (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
+    const int hi_vis = min(lk - 1, bd.wr < 0 ? lk - 1 : tdiag + bd.wr);  // last visible key
+    const int lo_vis = bd.wl < 0 ? 0 : tdiag - bd.wl;                     // first visible key
     const float m_use = t.prep(s, a.scale_log2, lane, need, [&](int jr) {
       const int j = j0 + jr;
-      return j < lk && (bd.wr < 0 || j <= tdiag + bd.wr) && (bd.wl < 0 || j >= tdiag - bd.wl);
+      return (j <= hi_vis) & (j >= lo_vis);
     });
     uint32_t pk[C::NSB * 8];
     t.probs(s, a.scale_log2, m_use, pk);
@@ -265,7 +267,7 @@ __global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
 }
 
 using CfgP64 = PrefillCfg<64, 4, 64>;
-using CfgP128 = PrefillCfg<128, 4, 64>;
+using CfgP128 = PrefillCfg<128, 4, 32, 3>;
 
 }  // namespace
 

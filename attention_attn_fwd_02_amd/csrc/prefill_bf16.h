@@ -60,9 +60,10 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D_, int NW_, int BN_>
+template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2>
 struct PrefillCfg {
   static constexpr int D = D_, DV = D_, NW = NW_, BN = BN_;
+  static constexpr int MIN_WAVES = MIN_WAVES_;  // waves per SIMD the registers must allow
   static constexpr int R = 32;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * R;
