@@ -29,25 +29,37 @@
 
 namespace attn {
 
-template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_>
+// DSPLIT = 2 pairs the waves of a workgroup (waves 2p and 2p+1): both own
+// the same 16 query rows, each holds half of every Q row and half of every
+// output row, computes the partial S^T over its half of the head dimension,
+// and the two partials are summed through LDS so that both waves continue
+// with identical scores. Only the even wave of a pair issues DMA. This halves
+// the registers a wave needs for wide heads (MLA: 576 / 512), so two waves
+// fit on each SIMD and hide each other's LDS latency.
+template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1>
 struct StreamCfg {
   static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
   static constexpr bool VSHARED = VSHARED_;
+  static constexpr int DSPLIT = DSPLIT_;
   static constexpr int BN = 32, R = 16;
   static constexpr int THREADS = NW * 64;
-  static constexpr int ROWS = NW * R;
+  static constexpr int ROWS = NW / DSPLIT * R;
+  static constexpr int DMA_WAVES = NW / DSPLIT;
   static constexpr int NCH = D / 8;
   static constexpr int K_BYTES = BN * D * 2;
   static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * 2;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_DMA = K_BYTES / 1024;
   static constexpr int V_DMA = V_BYTES / 1024;
-  static constexpr int DMA_PER_WAVE = (K_DMA + V_DMA) / NW;
-  static constexpr int NQ = D / 32;      // Q fragments per row
-  static constexpr int NSB = BN / 16;    // S^T blocks per tile
-  static constexpr int NOB = DV / 16;    // O^T blocks
-  static_assert(D % 32 == 0 && DV % 16 == 0 && NCH % 4 == 0, "head dims");
-  static_assert((K_DMA + V_DMA) % NW == 0, "tile DMA must split evenly over the waves");
+  static constexpr int DMA_PER_WAVE = (K_DMA + V_DMA) / DMA_WAVES;
+  static constexpr int NQ = D / 32 / DSPLIT;    // Q fragments held per wave
+  static constexpr int NSB = BN / 16;           // S^T blocks per tile
+  static constexpr int NOB = DV / 16 / DSPLIT;  // O^T blocks held per wave
+  // partial-S^T exchange buffer: [wave][sb][lane] x f32x4
+  static constexpr int XCHG_BYTES = DSPLIT == 2 ? NW * NSB * 64 * 16 : 0;
+  static_assert(DSPLIT == 1 || DSPLIT == 2, "DSPLIT");
+  static_assert(D % (32 * DSPLIT) == 0 && DV % (16 * DSPLIT) == 0 && NCH % 4 == 0, "head dims");
+  static_assert((K_DMA + V_DMA) % DMA_WAVES == 0, "tile DMA must split evenly over the waves");
   static_assert(VSHARED || (NCH / 2) % 4 == 0, "V layout needs whole instructions per row block");
   static_assert(VSHARED ? DV <= D : DV == D, "value width");
   static_assert(DMA_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
@@ -60,8 +72,10 @@ struct StreamTile {
   f32x4 o[C::NOB];
   float m_ref;
   float l_run;
+  int half;  // half of the head dimension this wave holds (0 unless DSPLIT = 2)
 
-  __device__ __forceinline__ void init() {
+  __device__ __forceinline__ void init(int wave) {
+    half = C::DSPLIT == 2 ? (wave & 1) : 0;
 #pragma unroll
     for (int i = 0; i < C::NOB; ++i) o[i] = f32x4{};
     m_ref = kNegInf;
@@ -73,23 +87,26 @@ struct StreamTile {
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * 32 + g * 8);
+      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + (half * C::NQ + i) * 32 + g * 8);
       qf[i] = as_bf16x8(v);
     }
   }
 
   // This wave's share of the DMA of one tile into `stage`. krow(r) / vrow(r)
   // give the global address of the K / V row of key r of the tile (r in
-  // [0, BN)); vrow is unused when V shares the K row.
+  // [0, BN)); vrow is unused when V shares the K row. With DSPLIT = 2 the odd
+  // waves issue nothing.
   template <class KRow, class VRow>
   __device__ __forceinline__ static void dma_tile(char* stage, KRow krow, VRow vrow, int wave,
                                                   int lane) {
+    if (C::DSPLIT == 2 && (wave & 1)) return;
+    const int dw = C::DMA_WAVES == 1 ? 0 : wave / C::DSPLIT;
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
-      // wave is 0 for single-wave workgroups and a uniform (SGPR) value
+      // dw is 0 for single-DMA-wave workgroups and a uniform (SGPR) value
       // otherwise, so the K/V choice below is a scalar branch or constant.
-      const int inst = (C::NW == 1 ? 0 : wave) * C::DMA_PER_WAVE + n;
-      const bool is_k = C::V_DMA == 0 || (C::NW == 1 ? n < C::K_DMA : inst < C::K_DMA);
+      const int inst = dw * C::DMA_PER_WAVE + n;
+      const bool is_k = C::V_DMA == 0 || (C::DMA_WAVES == 1 ? n < C::K_DMA : inst < C::K_DMA);
       if (is_k) {
         constexpr int IPB = C::NCH / 4;  // instructions per 16-row block
         const int rb = inst / IPB, cq = inst % IPB;
@@ -115,9 +132,27 @@ struct StreamTile {
       s[sb] = f32x4{};
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + dq * 4) * 256);
+        const u32x4 a =
+            *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + (half * C::NQ + dq) * 4) * 256);
         s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
       }
+    }
+  }
+
+  // DSPLIT = 2: adds the partner wave's partial S^T. The exchange buffer is
+  // reused every tile; the caller's per-tile barrier (after lgkmcnt(0))
+  // orders the partner's reads of tile i before the writes of tile i+1.
+  // Float addition commutes, so both waves of a pair obtain the same sums.
+  __device__ __forceinline__ void exchange(char* xchg, int wave, int lane, f32x4 (&s)[C::NSB]) const {
+    if constexpr (C::DSPLIT == 2) {
+      f32x4* mine = reinterpret_cast<f32x4*>(xchg) + wave * C::NSB * 64 + lane;
+      const f32x4* other = reinterpret_cast<const f32x4*>(xchg) + (wave ^ 1) * C::NSB * 64 + lane;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) mine[sb * 64] = s[sb];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own writes done
+      barrier_no_fence();
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) s[sb] += other[sb * 64];
     }
   }
 
@@ -176,7 +211,8 @@ struct StreamTile {
     const bf16x8 b = as_bf16x8(pv4);
     if constexpr (C::VSHARED) {
       const int par = (i >> 1) & 1;
-      const char* vb = stage + (par * 256 + ((g * 4 + (i >> 2)) ^ (par * 8)) * 16 + (i & 1) * 8);
+      const char* vb = stage + (par * 256 + ((g * 4 + (i >> 2)) ^ (par * 8)) * 16 + (i & 1) * 8) +
+                       half * C::NOB * 2 * 256;
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob) {
         const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(vb + (0 * C::NCH + ob * 2) * 256));
@@ -210,7 +246,7 @@ struct StreamTile {
     const int g = lane >> 4;
 #pragma unroll
     for (int ob = 0; ob < C::NOB; ++ob) {
-      const int col = ob * 16 + g * 4;
+      const int col = (half * C::NOB + ob) * 16 + g * 4;
       const float a0 = o[ob][0] * inv, a1 = o[ob][1] * inv;
       const float a2 = o[ob][2] * inv, a3 = o[ob][3] * inv;
       if constexpr (sizeof(OutT) == 2) {

@@ -37,6 +37,7 @@ k_decode(DecodeArgs a) {
   using T = StreamTile<C>;
   using M = Mfma<16>;
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char xchg[C::XCHG_BYTES > 0 ? C::XCHG_BYTES : 16];
   const int grp = a.hq / a.hkv;
   const int nrows = a.sq * grp;
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
@@ -58,12 +59,12 @@ k_decode(DecodeArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = mt * C::ROWS + wave * C::R + (lane & 15);
+  const int r = mt * C::ROWS + (wave / C::DSPLIT) * C::R + (lane & 15);
   const bool row_ok = r < nrows;
   const int tq = row_ok ? r / grp : 0;
   const int h = kvh * grp + (row_ok ? r % grp : 0);
   T tile;
-  tile.init();
+  tile.init(wave);
   tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
                      : nullptr,
               lane);
@@ -117,6 +118,7 @@ k_decode(DecodeArgs a) {
     const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
     f32x4 sc[C::NSB];
     tile.qk(st, lane, sc);
+    tile.exchange(xchg, wave, lane, sc);
     const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
     const float m_use = tile.prep(sc, a.scale_log2, lane, need,
                                   [&](int jr) { return j0 + jr <= hi_vis; });
@@ -131,7 +133,7 @@ k_decode(DecodeArgs a) {
     const size_t slot_id = (size_t)b * a.max_splits + s;
     const size_t row = slot_id * nrows * a.hkv + (size_t)tq * a.hq + h;
     tile.store(a.o_part + row * C::DV, inv, lane);
-    if (lane < 16) a.lse_part[row] = lse;
+    if (lane < 16 && tile.half == 0) a.lse_part[row] = lse;
   }
 }
 
@@ -147,6 +149,7 @@ k_sparse(SparseArgs a) {
   using T = StreamTile<C>;
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   __shared__ int sidx[kMaxTopk];
+  __shared__ __attribute__((aligned(16))) char xchg[C::XCHG_BYTES > 0 ? C::XCHG_BYTES : 16];
   const int mtiles = (a.hq + C::ROWS - 1) / C::ROWS;
   const int p = blockIdx.x;
   const int mt = p % mtiles;
@@ -155,7 +158,7 @@ k_sparse(SparseArgs a) {
   if (b >= a.batch) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int h = mt * C::ROWS + wave * C::R + (lane & 15);
+  const int h = mt * C::ROWS + (wave / C::DSPLIT) * C::R + (lane & 15);
   const bool row_ok = h < a.hq;
 
   const int ntiles = (a.topk + C::BN - 1) / C::BN;
@@ -166,7 +169,7 @@ k_sparse(SparseArgs a) {
     sidx[k] = (id >= 0 && id <= limit) ? id : -1;
   }
   T tile;
-  tile.init();
+  tile.init(wave);
   tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + t) * a.hq + h) * C::D
                      : nullptr,
               lane);
@@ -183,6 +186,7 @@ k_sparse(SparseArgs a) {
     const int* tix = sidx + ti * C::BN;
     f32x4 sc[C::NSB];
     tile.qk(st, lane, sc);
+    tile.exchange(xchg, wave, lane, sc);
     const float m_use =
         tile.prep(sc, a.scale_log2, lane, true, [&](int jr) { return tix[jr] >= 0; });
     uint32_t pk[C::NSB * 2];
@@ -196,13 +200,13 @@ k_sparse(SparseArgs a) {
   if (row_ok) {
     tile.store(static_cast<bf16_t*>(a.out) + (((size_t)b * a.sq + t) * a.hq + h) * C::DV, inv,
                lane);
-    if (a.lse && lane < 16) a.lse[((size_t)b * a.hq + h) * a.sq + t] = lse;
+    if (a.lse && lane < 16 && tile.half == 0) a.lse[((size_t)b * a.hq + h) * a.sq + t] = lse;
   }
 }
 
 using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
-using CfgDecodeMla = StreamCfg<576, 512, 4, 3, true>;
-using CfgSparseMla = StreamCfg<576, 512, 4, 3, true>;
+using CfgDecodeMla = StreamCfg<576, 512, 8, 3, true, 2>;
+using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
 
