@@ -243,6 +243,8 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
           attn::sparse_max_topk());
   REQUIRE((long)batch * seqlen_q * ((hq + 63) / 64) < (1L << 31), ATTN_EUNSUPPORTED,
           "grid too large");
+  REQUIRE((long)seqlen_k * 576 * 2 <= (1L << 32), ATTN_EUNSUPPORTED,
+          "seqlen_k %d above %ld (row byte offsets are 32-bit)", seqlen_k, (1L << 32) / 1152);
   attn::SparseArgs a;
   a.q = q;
   a.kv = kv;

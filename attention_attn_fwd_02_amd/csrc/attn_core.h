@@ -123,6 +123,53 @@ struct StreamTile {
     }
   }
 
+  // Source of one DMA instruction in the saddr form: wave-uniform base and
+  // the lane's byte offset from it.
+  struct Src {
+    const char* s;
+    uint32_t v;
+  };
+
+  // Lane parts of the saddr form (tile-independent): the byte offset of this
+  // lane's 16 bytes from the first row of a 16-row block whose rows are
+  // kstride / vstride bytes apart, for the K and the (separate) V DMA.
+  __device__ __forceinline__ static uint32_t k_lane_row(int lane) {
+    return (uint32_t)((lane & 15) ^ (((lane >> 4) & 1) * 8));
+  }
+  __device__ __forceinline__ static uint32_t k_lane_off(int lane, uint32_t kstride) {
+    return k_lane_row(lane) * kstride + (lane >> 4) * 16;
+  }
+  __device__ __forceinline__ static uint32_t v_lane_off(int lane, uint32_t vstride) {
+    return (uint32_t)((lane & 15) >> 1) * vstride + ((lane >> 4) * 2 + (lane & 1)) * 16;
+  }
+
+  // The same DMA as dma_tile in the saddr form. Every instruction reads rows
+  // of one 16-row block rb of the tile. ksrc(rb, colb) returns the source of
+  // a K instruction whose uniform column offset is colb bytes (the lane adds
+  // its row and (lane >> 4) * 16); vsrc(rb, sub, colb) that of a V
+  // instruction covering rows sub*8 .. sub*8+7 of block rb.
+  template <class KSrc, class VSrc>
+  __device__ __forceinline__ static void dma_tile_sv(char* stage, KSrc ksrc, VSrc vsrc, int wave) {
+    if (C::DSPLIT == 2 && (wave & 1)) return;
+    const int dw = C::DMA_WAVES == 1 ? 0 : wave / C::DSPLIT;
+#pragma unroll
+    for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
+      const int inst = dw * C::DMA_PER_WAVE + n;
+      const bool is_k = C::V_DMA == 0 || (C::DMA_WAVES == 1 ? n < C::K_DMA : inst < C::K_DMA);
+      if (is_k) {
+        constexpr int IPB = C::NCH / 4;
+        const Src a = ksrc(inst / IPB, (inst % IPB) * 64);
+        lds_dma16_sv(a.s, a.v, stage + inst * 1024);
+      } else {
+        constexpr int H = C::NCH / 2;
+        const int vi = inst - C::K_DMA;
+        const int q = 4 * vi / H;  // 8-row group of the instruction
+        const Src a = vsrc(q >> 1, q & 1, ((4 * vi) % H) * 32);
+        lds_dma16_sv(a.s, a.v, stage + C::K_BYTES + vi * 1024);
+      }
+    }
+  }
+
   // S^T for one tile.
   __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
     const int g = lane >> 4;

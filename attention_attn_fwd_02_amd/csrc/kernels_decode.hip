@@ -77,38 +77,41 @@ k_decode(DecodeArgs a) {
   const int* btb = a.block_table + (size_t)b * a.max_pages;
   const int kv_last = kv1 - 1;
   const size_t tok_k = (size_t)a.hkv * C::D, tok_v = (size_t)a.hkv * C::DV;
+  const uint32_t kstride = (uint32_t)(tok_k * 2), vstride = (uint32_t)(tok_v * 2);
+  const uint32_t klane = T::k_lane_off(lane, kstride);
+  const uint32_t vlane = T::v_lane_off(lane, vstride);
+  const char* kcb = reinterpret_cast<const char*>(kc);
+  const char* vcb = reinterpret_cast<const char*>(vc);
   auto issue = [&](char* st, int ti) {
-    // Uniform per tile: the (at most two) pages it touches and the address
-    // of tile row 0 as if it were on each of them; row r of the tile is
-    // base + r * row_stride on its page. Rows past the split (last tile
-    // only) re-read the split's last key, which is masked.
+    // A 16-row block of a tile lies on one page (pages are multiples of 16
+    // rows and splits start on page boundaries). slot0 / slot1: cache slot
+    // of tile row 0 and of tile row 16 (clamped to the split's last key).
     const int j0 = kv0 + ti * C::BN;
-    const int lp0 = j0 / a.page;
-    const int lp1 = min(j0 + C::BN - 1, kv_last) / a.page;
-    const int bnd = (lp0 + 1) * a.page - j0;  // first tile row on page lp1
-    const long s0 = (long)btb[lp0] * a.page + (j0 - lp0 * a.page);
-    const long s1 = (long)btb[lp1] * a.page + (j0 - lp1 * a.page);
+    const int j1 = min(j0 + 16, kv_last);
+    const int lp0 = j0 / a.page, lp1 = j1 / a.page;
+    int p0, p1;
+    sload2_uniform(btb + lp0, btb + lp1, p0, p1);
+    const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
+    const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
     const int rmax = kv_last - j0;
-    const bf16_t* k0p = kc + s0 * tok_k;
-    const bf16_t* k1p = kc + s1 * tok_k;
-    const bf16_t* v0p = vc + s0 * tok_v;
-    const bf16_t* v1p = vc + s1 * tok_v;
     if (rmax >= C::BN - 1) {
-      T::dma_tile(
-          st, [&](int rr) { return (rr < bnd ? k0p : k1p) + (size_t)rr * tok_k; },
-          [&](int rr) { return (rr < bnd ? v0p : v1p) + (size_t)rr * tok_v; }, wave, lane);
-    } else {
-      T::dma_tile(
+      T::dma_tile_sv(
           st,
-          [&](int rr) {
-            rr = min(rr, rmax);
-            return (rr < bnd ? k0p : k1p) + (size_t)rr * tok_k;
+          [&](int rb, int colb) {
+            return typename T::Src{kcb + (rb ? slot1 : slot0) * (long)kstride + colb, klane};
           },
-          [&](int rr) {
-            rr = min(rr, rmax);
-            return (rr < bnd ? v0p : v1p) + (size_t)rr * tok_v;
+          [&](int rb, int sub, int colb) {
+            return typename T::Src{
+                vcb + (rb ? slot1 : slot0) * (long)vstride + sub * 8 * (long)vstride + colb, vlane};
           },
-          wave, lane);
+          wave);
+    } else {
+      // last tile of the split: rows past its last key re-read that key,
+      // which is masked
+      auto row = [&](int rr) { rr = min(rr, rmax); return (rr >> 4 ? slot1 : slot0) + (rr & 15); };
+      T::dma_tile(
+          st, [&](int rr) { return kc + row(rr) * tok_k; },
+          [&](int rr) { return vc + row(rr) * tok_v; }, wave, lane);
     }
   };
   const int first_t = (mt * C::ROWS) / grp;
@@ -176,11 +179,21 @@ k_sparse(SparseArgs a) {
   wait_vmcnt<0>();
   __syncthreads();
 
-  const bf16_t* kvb = static_cast<const bf16_t*>(a.kv) + (size_t)b * a.sk * C::D;
+  // K rows are gathered: the uniform base is the sequence's first row and
+  // the lane offset the byte offset of its row (fits 32 bits: sk * D * 2 is
+  // checked on the host), plus its 16-byte column.
+  static_assert(C::VSHARED, "sparse path reads V from the K rows");
+  const char* kvb =
+      reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.kv) + (size_t)b * a.sk * C::D);
+  const int lrow = (int)T::k_lane_row(lane);
+  const uint32_t lcol = (lane >> 4) * 16;
   auto issue = [&](char* st, int ti) {
     const int* tix = sidx + ti * C::BN;
-    auto krow = [&](int rr) { return kvb + (size_t)max(tix[rr], 0) * C::D; };
-    T::dma_tile(st, krow, krow, wave, lane);
+    const uint32_t r0 = (uint32_t)max(tix[lrow], 0) * (uint32_t)(C::D * 2) + lcol;
+    const uint32_t r1 = (uint32_t)max(tix[16 + lrow], 0) * (uint32_t)(C::D * 2) + lcol;
+    T::dma_tile_sv(
+        st, [&](int rb, int colb) { return typename T::Src{kvb + colb, rb ? r1 : r0}; },
+        [&](int, int, int) { return typename T::Src{kvb, 0u}; }, wave);
   };
   stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
     const int* tix = sidx + ti * C::BN;

@@ -40,6 +40,29 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst_unifor
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
 
+// Same DMA with the source split into a wave-uniform base (SGPR pair) and the
+// lane's 32-bit byte offset from it (the global "saddr" form), so the
+// per-lane part can be computed once and reused for every tile.
+__device__ __forceinline__ void lds_dma16_sv(const void* sbase_uniform, uint32_t voff,
+                                             void* lds_dst_uniform) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_dst_uniform);
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase_uniform), "{m0}"(m0)
+               : "memory");
+}
+
+// Two wave-uniform 32-bit loads through the scalar cache, waited for inside
+// the asm. The compiler would otherwise emit vector loads here (the DMA asm
+// above clobbers memory), and its vmcnt wait for them would also wait for
+// every DMA in flight.
+__device__ __forceinline__ void sload2_uniform(const int* p0, const int* p1, int& v0, int& v1) {
+  asm volatile(
+      "s_load_dword %0, %2, 0x0\n\t"
+      "s_load_dword %1, %3, 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1)
+      : "s"(p0), "s"(p1));
+}
+
 // s_waitcnt with vmcnt = n and the other counters left unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -120,6 +120,9 @@ def test_mla_and_sparse_host_checks(lib):
                               None) == B.ATTN_EEMPTY
     assert lib.mla_sparse_fwd(None, P, P, 16, 1, 1, 10, 64, 0.1, 3, None, P, None,
                               None) == B.ATTN_EINVAL
+    # per-sequence row byte offsets must fit 32 bits
+    assert lib.mla_sparse_fwd(P, P, P, 16, 1, 1, 3728271, 64, 0.1, 0, None, P, None,
+                              None) == B.ATTN_EUNSUPPORTED
 
 
 def test_combine_host_checks(lib):
