@@ -58,7 +58,7 @@ struct StreamCfg {
   // partial-S^T exchange buffer: [wave][sb][lane] x f32x4
   static constexpr int XCHG_BYTES = DSPLIT == 2 ? NW * NSB * 64 * 16 : 0;
   static_assert(DSPLIT == 1 || DSPLIT == 2, "DSPLIT");
-  static_assert(D % (32 * DSPLIT) == 0 && DV % (16 * DSPLIT) == 0 && NCH % 4 == 0, "head dims");
+  static_assert(D % 64 == 0 && DV % (16 * DSPLIT) == 0, "head dims");
   static_assert((K_DMA + V_DMA) % DMA_WAVES == 0, "tile DMA must split evenly over the waves");
   static_assert(VSHARED || (NCH / 2) % 4 == 0, "V layout needs whole instructions per row block");
   static_assert(VSHARED ? DV <= D : DV == D, "value width");
@@ -82,12 +82,23 @@ struct StreamTile {
     l_run = 0.f;
   }
 
+  // Fragment dq of this wave covers the head-dimension chunks (8 elements
+  // each) c = (f >> 1) * 8 + 2 * g + (f & 1), f = dq * DSPLIT + half, for
+  // lane group g = lane >> 4: all four groups of one fragment read chunks of
+  // one parity, so the K reads of the swizzled layout stay conflict-free (a
+  // uniform XOR of the row slot only relabels banks). With DSPLIT = 2 the
+  // two waves of a pair hold the even and the odd chunks.
+  __device__ __forceinline__ static int q_chunk(int dq, int half, int g) {
+    const int f = dq * C::DSPLIT + half;
+    return (f >> 1) * 8 + 2 * g + (f & 1);
+  }
+
   __device__ __forceinline__ void load_q(const bf16_t* qrow, int lane) {
     const int g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + (half * C::NQ + i) * 32 + g * 8);
+      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + q_chunk(i, half, g) * 8);
       qf[i] = as_bf16x8(v);
     }
   }
@@ -173,14 +184,18 @@ struct StreamTile {
   // S^T for one tile.
   __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
     const int g = lane >> 4;
-    const char* kb = stage + (g * 256 + ((lane & 15) ^ ((g & 1) * 8)) * 16);
+    // chunk parity p = f & 1; chunk c = (f >> 1) * 8 + 2g + p sits at
+    // c * 256 + ((row % 16) ^ 8p) * 16 within a 16-row block
+    const char* kb0 = stage + g * 512 + (lane & 15) * 16;
+    const char* kb1 = stage + g * 512 + 256 + ((lane & 15) ^ 8) * 16;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
       s[sb] = f32x4{};
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + (half * C::NQ + dq) * 4) * 256);
+        const int f = dq * C::DSPLIT + half;
+        const char* kb = (f & 1) ? kb1 : kb0;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + (f >> 1) * 8) * 256);
         s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
       }
     }
