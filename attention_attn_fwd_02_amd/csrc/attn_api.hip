@@ -82,6 +82,8 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_F32, ATTN_EUNSUPPORTED, "dtype %d", dtype);
   REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
           "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
   attn::VarlenArgs a;
   a.q = q;
   a.k = k;
@@ -146,6 +148,8 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
           d, dv);
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
   attn::DecodeArgs a;
   a.q = q;
   a.kc = k_cache;

@@ -66,8 +66,8 @@ template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES)
 k_varlen_bf16(VarlenArgs a) {
   using T = PrefillTile<C>;
-  __shared__ __attribute__((aligned(1024))) char stage0[2 * C::TILE_BYTES];  // K tile, V tile
-  __shared__ __attribute__((aligned(1024))) char stage1[2 * C::TILE_BYTES];
+  // ring of STAGES buffers, each one K tile followed by one V tile
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * 2 * C::TILE_BYTES];
   PrefillWork w;
   if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
   const int q0 = a.cu_q[w.b];
@@ -97,26 +97,51 @@ k_varlen_bf16(VarlenArgs a) {
   const bf16_t* kb = static_cast<const bf16_t*>(a.k) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
   const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
   const int last = lk - 1;  // rows past the sequence re-read its last key (then masked)
-  // Two stages, each holding one K tile and one V tile. While tile i is
-  // computed from one stage, the DMA of tile i+1 fills the other.
+  // STAGES-1 tiles are in flight while one is computed; a single barrier per
+  // tile both publishes tile i and retires every wave's reads of tile i-1,
+  // whose buffer then receives tile i+STAGES-1.
+  const long row_bytes = (long)kst * 2;
+  const uint32_t koff = T::template dma_lane_off<false>(lane, (uint32_t)row_bytes);
+  const uint32_t voff = T::template dma_lane_off<true>(lane, (uint32_t)row_bytes);
   auto issue = [&](char* buf, int i) {
     const int j0 = bd.lo + i * C::BN;
-    T::template dma_tile<false>(
-        buf, [&](int r) { return kb + (size_t)min(j0 + r, last) * kst; }, wave, lane);
-    T::template dma_tile<true>(
-        buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)min(j0 + r, last) * kst; }, wave,
-        lane);
+    if (j0 + C::BN - 1 <= last) {
+      T::template dma_tile_sv<false>(buf, reinterpret_cast<const char*>(kb) + j0 * row_bytes,
+                                     row_bytes, koff, wave);
+      T::template dma_tile_sv<true>(buf + C::TILE_BYTES,
+                                    reinterpret_cast<const char*>(vb) + j0 * row_bytes, row_bytes,
+                                    voff, wave);
+    } else {
+      T::template dma_tile<false>(
+          buf, [&](int r) { return kb + (size_t)min(j0 + r, last) * kst; }, wave, lane);
+      T::template dma_tile<true>(
+          buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)min(j0 + r, last) * kst; }, wave,
+          lane);
+    }
   };
   const int tdiag = trow + bd.delta;
   const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
-  auto process = [&](int i, char* cur, char* nxt) {
-    if (i + 1 < ntiles) {
-      issue(nxt, i + 1);
-      wait_vmcnt<2 * C::DMA_PER_WAVE>();
+  auto stage = [&](int i) { return ring + i * (2 * C::TILE_BYTES); };  // i < STAGES
+  constexpr int PER_TILE = 2 * C::DMA_PER_WAVE;  // DMA instructions per wave per tile
+  static_assert(PER_TILE * (C::STAGES - 1) < 64, "vmcnt range");
+#pragma unroll
+  for (int i = 0; i < C::STAGES - 1; ++i)
+    if (i < ntiles) issue(stage(i), i);
+  auto process = [&](int i, char* cur, char* refill) {
+    const int after = min(ntiles - 1 - i, C::STAGES - 2);  // tiles issued after tile i
+    if constexpr (C::STAGES >= 4) {
+      if (after >= 2) wait_vmcnt<2 * PER_TILE>();
+      else if (after == 1) wait_vmcnt<PER_TILE>();
+      else wait_vmcnt<0>();
+    } else if constexpr (C::STAGES == 3) {
+      if (after >= 1) wait_vmcnt<PER_TILE>();
+      else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own reads of tile i-1 retired
     barrier_no_fence();
+    if (i + C::STAGES - 1 < ntiles) issue(refill, i + C::STAGES - 1);
     const int j0 = bd.lo + i * C::BN;
     const bool need = j0 + C::BN > lk ||
                       (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
@@ -132,14 +157,14 @@ k_varlen_bf16(VarlenArgs a) {
     uint32_t pk[C::NSB * 8];
     t.probs(s, a.scale_log2, m_use, pk);
     t.pv(cur + C::TILE_BYTES, lane, pk);
-    // every wave must finish reading `cur` before the next DMA into it
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    barrier_no_fence();
   };
-  if (ntiles > 0) issue(stage0, 0);
-  for (int i = 0; i < ntiles; i += 2) {
-    process(i, stage0, stage1);
-    if (i + 1 < ntiles) process(i + 1, stage1, stage0);
+  // unrolled by STAGES so that every buffer address is a constant
+  for (int i = 0; i < ntiles; i += C::STAGES) {
+#pragma unroll
+    for (int k = 0; k < C::STAGES; ++k)
+      if (i + k < ntiles)
+        process(i + k, ring + k * (2 * C::TILE_BYTES),
+                ring + ((k + C::STAGES - 1) % C::STAGES) * (2 * C::TILE_BYTES));
   }
 
   float lse;

@@ -83,10 +83,11 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2>
+template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2, int STAGES_ = 3>
 struct PrefillCfg {
   static constexpr int D = D_, DV = D_, NW = NW_, BN = BN_;
   static constexpr int MIN_WAVES = MIN_WAVES_;  // waves per SIMD the registers must allow
+  static constexpr int STAGES = STAGES_;        // K+V tile buffers in the LDS ring
   static constexpr int R = 32;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * R;
@@ -152,10 +153,35 @@ struct PrefillTile {
     }
   }
 
-  // The key loop is software pipelined: iteration i finishes tile i (its
-  // softmax and P.V) while computing S for tile i+1, all in one basic block,
-  // so the MFMA work of one tile and the VALU work of the other can overlap
-  // inside a wave. The pieces:
+  // The same DMA in the saddr form for a tile whose BN rows are all valid
+  // and row_bytes apart from `tile` (a wave-uniform pointer to row 0):
+  // every instruction's uniform part (its row block and chunk group) goes
+  // into the scalar base and the lane's part is lane_off, computed once by
+  // dma_lane_off.
+  template <bool VLAYOUT>
+  __device__ __forceinline__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes) {
+    if constexpr (!VLAYOUT) return (uint32_t)(lane & 15) * row_bytes + (lane >> 4) * 16;
+    return (uint32_t)(((lane >> 4) & 1) * 4 + ((lane >> 2) & 3)) * row_bytes +
+           ((lane >> 5) * 4 + (lane & 3)) * 16;
+  }
+  template <bool VLAYOUT>
+  __device__ __forceinline__ static void dma_tile_sv(char* buf, const char* tile, long row_bytes,
+                                                     uint32_t lane_off, int wave) {
+#pragma unroll
+    for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
+      const int inst = wave * C::DMA_PER_WAVE + n;
+      long u;
+      if constexpr (!VLAYOUT) {
+        constexpr int IPB = C::NCH / 4;
+        u = (inst / IPB) * 16 * row_bytes + (inst % IPB) * 64;
+      } else {
+        // blk = 2 inst + (lane >> 5); NCH / 4 is even, so blk / (NCH / 4) is uniform
+        constexpr int BPR = C::NCH / 4;
+        u = ((2 * inst) / BPR) * 8 * row_bytes + ((2 * inst) % BPR) * 64;
+      }
+      lds_dma16_sv(tile + u, lane_off, buf + inst * 1024);
+    }
+  }
 
   // S^T = K Q^T for one tile.
   __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[C::NSB]) const {
