@@ -265,9 +265,10 @@ def attn_debug_gather_paged(cache, block_table, cache_seqlens, b, max_rows):
 # ------------------------------------------------------- composed decode calls
 # The split planner sizes splits so that the decode grid holds about
 # num_cu * waves workgroups; the defaults below were tuned on MI355X for the
-# two decode shapes (GQA: 8 per CU, MLA: 4 per CU).
+# two decode shapes (GQA: 8 per CU; MLA: 3 per CU, at most 8 splits, at
+# least 8 pages per split).
 GQA_ROWS_PER_WG = 16
-MLA_ROWS_PER_WG = 64
+MLA_ROWS_PER_WG = 128
 
 
 def _num_cu(device):
@@ -290,8 +291,8 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=
     return out, lse, plan
 
 
-def mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal=False, max_splits=16,
-               waves=4, min_blocks=2, num_cu=None):
+def mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal=False, max_splits=8,
+               waves=3, min_blocks=8, num_cu=None):
     """plan -> mla_decode_paged -> attn_combine (dv = 512)."""
     b, sq, hq, _ = q.shape
     upb = (sq * hq + MLA_ROWS_PER_WG - 1) // MLA_ROWS_PER_WG

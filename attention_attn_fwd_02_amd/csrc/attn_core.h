@@ -29,6 +29,13 @@
 
 namespace attn {
 
+// Source of one DMA instruction in the saddr form: wave-uniform base and the
+// lane's byte offset from it.
+struct DmaSrc {
+  const char* s;
+  uint32_t v;
+};
+
 // DSPLIT = 2 pairs the waves of a workgroup (waves 2p and 2p+1): both own
 // the same 16 query rows, each holds half of every Q row and half of every
 // output row, computes the partial S^T over its half of the head dimension,
@@ -134,12 +141,7 @@ struct StreamTile {
     }
   }
 
-  // Source of one DMA instruction in the saddr form: wave-uniform base and
-  // the lane's byte offset from it.
-  struct Src {
-    const char* s;
-    uint32_t v;
-  };
+  using Src = DmaSrc;
 
   // Lane parts of the saddr form (tile-independent): the byte offset of this
   // lane's 16 bytes from the first row of a 16-row block whose rows are

@@ -5,6 +5,7 @@
 //  sparse_mode, MLA-absorb concat; CANN flash_attn: paged attention via
 //  block_table, shared KV, sink formulas]
 #include "attn_core.h"
+#include "attn_wide.h"
 #include "launch.h"
 #include "paged.h"
 
@@ -140,6 +141,109 @@ k_decode(DecodeArgs a) {
   }
 }
 
+// MLA-absorbed decode on the wide tile: one workgroup = (split, row tile mt)
+// of 128 rows (query token, head) of the single latent KV head; the rest as in
+// k_decode.
+template <class C>
+__global__ void __launch_bounds__(C::THREADS)
+k_decode_wide(DecodeArgs a) {
+  using T = WideTile<C>;
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char xchg[C::XCHG_BYTES];
+  __shared__ __attribute__((aligned(16))) char qlds[C::QLDS_BYTES > 0 ? C::QLDS_BYTES : 16];
+  const int nrows = a.sq * a.hq;
+  const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
+  const int logical = xcd_group(blockIdx.x, mtiles);
+  const int total = a.plan[0];
+  if (logical >= total * mtiles) return;
+  const int mt = logical % mtiles;
+  const int split = logical / mtiles;
+  const int* tri = a.plan + 3 + a.batch + 3 * split;
+  const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
+  const int s = split - a.plan[2 + b];
+  const int lk = a.lens[b];
+  const int delta = lk - a.sq;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = mt * C::ROWS + (wave >> 1) * C::R + (lane & 31);
+  const bool row_ok = r < nrows;
+  const int tq = row_ok ? r / a.hq : 0;
+  const int h = row_ok ? r % a.hq : 0;
+  T tile;
+  tile.init(wave);
+  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
+                     : nullptr,
+              qlds, wave, lane);
+  wait_vmcnt<0>();  // Q in registers before any DMA is in flight
+
+  const int* btb = a.block_table + (size_t)b * a.max_pages;
+  const int kv_last = kv1 - 1;
+  const uint32_t kstride = (uint32_t)(C::D * 2);
+  const char* kcb = static_cast<const char*>(a.kc);
+  auto issue = [&](char* st, int ti) {
+    // 16-row blocks lie on one page each (see k_decode)
+    const int j0 = kv0 + ti * C::BN;
+    const int j1 = min(j0 + 16, kv_last);
+    const int lp0 = j0 / a.page, lp1 = j1 / a.page;
+    int p0, p1;
+    sload2_uniform(btb + lp0, btb + lp1, p0, p1);
+    const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
+    const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
+    const int rmax = kv_last - j0;
+    if (rmax >= C::BN - 1) {
+      const uint32_t klane = T::dma_lane_off(fresh_lane(), kstride);
+      T::dma_tile_sv(
+          st,
+          [&](int rb, int colb) {
+            return DmaSrc{kcb + (rb ? slot1 : slot0) * (long)kstride + colb, klane};
+          },
+          wave);
+    } else {
+      const int lane = fresh_lane();
+      // last tile of the split: slot1 is tile row min(16, rmax); lane rows
+      // past the split's last key re-read that key (masked), so the lane's
+      // row offset from its block's first row is clamped to lim
+      const int lim0 = min(rmax, 15), lim1 = max(rmax - 16, 0);
+      T::dma_tile_sv(
+          st,
+          [&](int rb, int colb) {
+            const uint32_t lr = min(T::dma_lane_row(lane), (uint32_t)(rb ? lim1 : lim0));
+            return DmaSrc{kcb + (rb ? slot1 : slot0) * (long)kstride + colb,
+                          lr * kstride + (lane >> 4) * 16};
+          },
+          wave);
+    }
+  };
+  const int first_t = (mt * C::ROWS) / a.hq;
+  const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
+  stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+    const int j0 = kv0 + ti * C::BN;
+    const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
+    f32x16 sc;
+    tile.qk(st, qlds, wave, sc);
+    tile.exchange(xchg, wave, sc);
+    const float m_use = tile.prep(sc, a.scale_log2, need, [&](int jr) {
+      // row of this lane, recomputed here rather than kept across the loop
+      const int rr = mt * C::ROWS + (wave >> 1) * C::R + (fresh_lane() & 31);
+      const int hi_vis = a.causal ? min(kv1 - 1, rr / a.hq + delta) : kv1 - 1;
+      return j0 + jr <= hi_vis;
+    });
+    uint32_t pk[8];
+    tile.probs(sc, a.scale_log2, m_use, pk);
+    tile.pv(st, pk);
+  });
+
+  float lse;
+  const float inv = tile.finish(false, 0.f, lse);
+  if (row_ok) {
+    const size_t slot_id = (size_t)b * a.max_splits + s;
+    const size_t row = slot_id * nrows + (size_t)tq * a.hq + h;
+    tile.store(a.o_part + row * C::DV, inv, lane);
+    if (lane < 32 && tile.half == 0) a.lse_part[row] = lse;
+  }
+}
+
 // One workgroup = (sequence b, query token t, head tile mt); all heads of a
 // token share its index list. The list is staged in LDS once (invalid
 // entries -> -1); rows of invalid keys are fetched from row 0 (a valid
@@ -218,7 +322,7 @@ k_sparse(SparseArgs a) {
 }
 
 using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
-using CfgDecodeMla = StreamCfg<576, 512, 8, 3, true, 2>;
+using CfgDecodeMla = WideCfg<576, 512, 3, 0>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
@@ -239,7 +343,7 @@ hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s) {
   const int nrows = a.sq * a.hq;
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * mt, mt);
-  hipLaunchKernelGGL(k_decode<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL(k_decode_wide<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -140,8 +140,8 @@ def bench_mla(steps, warmup):
     bt, lens = dev(w.block_table), dev(w.cache_seqlens)
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
-    ms_, waves, mb = 16, 4, 2
-    upb = (sq * hq + 63) // 64
+    ms_, waves, mb = 8, 3, 8
+    upb = (sq * hq + B.MLA_ROWS_PER_WG - 1) // B.MLA_ROWS_PER_WG
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 512), dtype=torch.float32, device="cuda")
     lp = torch.empty((b * ms_, sq * hq), dtype=torch.float32, device="cuda")
