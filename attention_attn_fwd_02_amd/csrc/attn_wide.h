@@ -21,9 +21,21 @@
 //   (128 bytes); sw places blocks 0/1 (and 2/3) in complementary halves of
 //   the 64 banks.
 #pragma once
+#include <utility>
 #include "attn_core.h"
 
 namespace attn {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, with i usable as a
+// constant expression (schedule-group sizes must be constants).
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // QLDS of each wave's Q fragments are kept in LDS instead of registers (the
 // register file holds 2 waves per SIMD only just: 128 accumulator registers
@@ -45,6 +57,9 @@ struct WideCfg {
   static constexpr int XCHG_BYTES = NW * 4 * 64 * 16;  // [wave][quarter][lane] x f32x4
   static constexpr int NQR = NQ - QLDS;                // Q fragments held in registers
   static constexpr int QLDS_BYTES = NW * QLDS * 1024;  // [wave][fragment][lane] x 16 B
+  static constexpr int QK_PREFETCH = 3;                 // K fragments read ahead in Q K^T
+  static constexpr int PV_PREFETCH = 2;                 // V fragments read ahead in P V
+  static constexpr bool SCHED_GROUPS = true;
   static_assert(D % 64 == 0 && NCH % 8 == 0, "chunk classes need D % 64 == 0");
   static_assert(DV % 64 == 0 && DV <= D, "value width");
   static_assert(K_DMA % DMA_WAVES == 0, "tile DMA must split evenly over the waves");
@@ -151,18 +166,36 @@ struct WideTile {
     // fragment parity p: chunk a + 4g with a % 4 = half + 2p, sw = 8 half ^ 4p
     const char* kb0 = stage + (rb * C::NCH + half + 4 * g) * 256 + (slot ^ (8 * half)) * 16;
     const char* kb1 = stage + (rb * C::NCH + half + 2 + 4 * g) * 256 + (slot ^ (8 * half ^ 4)) * 16;
+    auto kload = [&](int t) {
+      const char* kb = (t & 1) ? kb1 : kb0;
+      return *reinterpret_cast<const u32x4*>(kb + 8 * (t >> 1) * 256);
+    };
+    // K fragments are read PF ahead of their MFMA; the schedule groups below
+    // keep the compiler from sinking the reads next to their uses.
+    constexpr int PF = C::QK_PREFETCH;
+    u32x4 ka[C::NQ];
+#pragma unroll
+    for (int t = 0; t < PF; ++t) ka[t] = kload(t);
     s = f32x16{};
 #pragma unroll
     for (int t = 0; t < C::NQ; ++t) {
-      const char* kb = (t & 1) ? kb1 : kb0;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(kb + 8 * (t >> 1) * 256);
+      if (t + PF < C::NQ) ka[t + PF] = kload(t + PF);
       bf16x8 q;
       if (t < C::NQR)
         q = qf[t];
       else
         q = as_bf16x8(*reinterpret_cast<const u32x4*>(
             qlds + (wave * C::QLDS + t - C::NQR) * 1024 + lane * 16));
-      s = M::mma(as_bf16x8(a), q, s);
+      s = M::mma(as_bf16x8(ka[t]), q, s);
+    }
+    if constexpr (C::SCHED_GROUPS) {
+      __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF LDS reads
+      static_for<C::NQ>([&](auto I) {
+        constexpr int t = decltype(I)::value;
+        constexpr int reads = (t + PF < C::NQ) + (t + 1 >= C::NQR && t + 1 < C::NQ);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        if constexpr (reads > 0) __builtin_amdgcn_sched_group_barrier(0x100, reads, 0);
+      });
     }
   }
 
@@ -238,17 +271,31 @@ struct WideTile {
     const int klo = g * 4 + (i >> 2);
     const char* lo_b = stage + cc * 256 + ((klo ^ fs) * 16) + (i & 1) * 8;
     const char* hi_b = stage + cc * 256 + (((klo + 8) ^ fs) * 16) + (i & 1) * 8;
+    // instruction n = c * NOB + ob; V fragments are read PF ahead
+    constexpr int N = 2 * C::NOB, PF = C::PV_PREFETCH;
+    auto vload = [&](int n) {
+      const int off = ((n / C::NOB) * C::NCH + 4 * (n % C::NOB)) * 256;
+      const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(lo_b + off));
+      const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(hi_b + off));
+      return join_bf16x8(lo, hi);
+    };
+    bf16x8 va[N];
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int n = 0; n < PF; ++n) va[n] = vload(n);
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      if (n + PF < N) va[n + PF] = vload(n + PF);
+      const int c = n / C::NOB, ob = n % C::NOB;
       const u32x4 p4 = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
-      const bf16x8 bop = as_bf16x8(p4);
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) {
-        const int off = (c * C::NCH + 4 * ob) * 256;
-        const s16x4 lo = lds_read_tr(reinterpret_cast<const bf16_t*>(lo_b + off));
-        const s16x4 hi = lds_read_tr(reinterpret_cast<const bf16_t*>(hi_b + off));
-        o[ob] = M::mma(join_bf16x8(lo, hi), bop, o[ob]);
-      }
+      o[ob] = M::mma(va[n], as_bf16x8(p4), o[ob]);
+    }
+    if constexpr (C::SCHED_GROUPS) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 1);  // PF fragments (2 reads each)
+      static_for<N>([&](auto I) {
+        constexpr int n = decltype(I)::value;
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if constexpr (n + PF < N) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      });
     }
   }
 

@@ -322,7 +322,7 @@ k_sparse(SparseArgs a) {
 }
 
 using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
-using CfgDecodeMla = WideCfg<576, 512, 3, 0>;
+using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
