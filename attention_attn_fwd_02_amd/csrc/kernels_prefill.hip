@@ -2,7 +2,6 @@
 // [MATE "Attention" page, FMHA: flash_attn_varlen_func; CANN flash_attn:
 //  cu_seqlens_q / cu_seqlens_kv; lite_boost flash_attention: causal and
 //  window_size]
-#include "attn_core.h"
 #include "launch.h"
 #include "prefill_bf16.h"
 
