@@ -182,7 +182,9 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
  *  each time; order is irrelevant. sinks: NULL or float32 (hq).
  *  out (batch, seqlen_q, hq, 512) bf16; lse: NULL or float32 (batch, hq, seqlen_q).
  *  hq must be a multiple of 16; topk at most 4096; seqlen_k at most
- *  3728270 (row byte offsets inside one sequence are 32-bit).
+ *  3728270 (row byte offsets inside one sequence are 32-bit). Skipped
+ *  entries are fetched from row 0 of the sequence and masked, so row 0 must
+ *  hold finite values.
  */
 int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indices, int32_t topk,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t hq, float scale,

@@ -90,20 +90,34 @@ def test_decode_gqa(case):
     assert np.array_equal(host(plan)[:n], ref_plan[:n])
 
 
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def poison_pool(w, extra):
+    """Copies of the caches with `extra` NaN pages placed in front of the
+    pool (no block_table entry names them) and NaN in every row past a
+    sequence's length inside its last page. A read of any row outside
+    [0, len) that reached the softmax or P.V would make the output NaN."""
+    def one(c):
+        c = np.concatenate([np.full((extra,) + c.shape[1:], NAN_BF16, np.uint16), c])
+        for b, L in enumerate(w.cache_seqlens):
+            L = int(L)
+            if L % w.page_size:
+                last = int(w.block_table[b, (L - 1) // w.page_size]) + extra
+                c[last, L % w.page_size:] = NAN_BF16
+        return c
+    bt = np.where(w.block_table >= 0, w.block_table + extra, -1).astype(np.int32)
+    vc = None if w.v_cache is None else one(w.v_cache)
+    return inputs.Paged(w.q, one(w.k_cache), vc, bt, w.cache_seqlens, w.page_size, w.dv,
+                        w.scale, w.causal)
+
+
 def test_decode_gqa_unreferenced_pages_poisoned():
-    """Pool pages that no block_table entry names are filled with NaN; a
-    read past a sequence's valid pages would make the output non-finite."""
+    """Unreferenced pool pages and the rows past each sequence's length are
+    NaN (see poison_pool)."""
     lens = [100, 64, 7]
     w = inputs.paged(91, lens, sq=1, hq=8, hkv=2, d=128, page=16)
-    extra = 5
-    nan = np.uint16(0x7FC0)
-    kc = np.concatenate([w.k_cache, np.full((extra,) + w.k_cache.shape[1:], nan, np.uint16)])
-    vc = np.concatenate([w.v_cache, np.full((extra,) + w.v_cache.shape[1:], nan, np.uint16)])
-    # move every page up by `extra` so the poisoned ones sit in front
-    kc = np.roll(kc, extra, axis=0)
-    vc = np.roll(vc, extra, axis=0)
-    bt = np.where(w.block_table >= 0, w.block_table + extra, -1).astype(np.int32)
-    w2 = inputs.Paged(w.q, kc, vc, bt, w.cache_seqlens, 16, 128, w.scale, False)
+    w2 = poison_pool(w, 5)
     o, lse, _ = run_decode(w2)
     torch.cuda.synchronize()
     ro, rl = oracle_decode(w)
@@ -150,6 +164,10 @@ MLA_CASES = [
     ("mla_small", [100, 1, 700], 2, 16, 64, False, 16, 2, 1),
     ("mla_causal_sq4", [65, 300], 4, 32, 16, True, 8, 8, 1),
     ("mla_hq128", [2000, 513], 1, 128, 64, False, 16, 2, 2),
+    # 192 rows: two row tiles, the second half empty; causal, 16-row pages
+    ("mla_causal_2tiles", [37, 1000, 129], 3, 64, 16, True, 8, 3, 1),
+    # many short splits on 32-row pages, sequence shorter than one tile
+    ("mla_many_splits", [4000, 31, 2048], 2, 128, 32, False, 16, 8, 1),
 ]
 
 
@@ -163,6 +181,18 @@ def test_mla_decode(case):
     torch.cuda.synchronize()
     ro, rl = oracle_mla(w)
     compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_mla_decode_poisoned():
+    """MLA over a pool with NaN outside every sequence's rows (see poison_pool);
+    lengths end mid-tile and mid-page."""
+    w = inputs.paged(6100, [100, 47, 300], sq=2, hq=64, hkv=1, d=576, dv=512, page=16,
+                     shared_kv=True)
+    w2 = poison_pool(w, 3)
+    o, lse, _ = run_mla(w2, 8, 4, 1)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mla(w)
+    compare("mla_poisoned", o, lse, ro, rl, TOL_O_BF16)
 
 
 def test_mla_decode_full():
