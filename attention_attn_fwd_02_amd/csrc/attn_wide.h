@@ -21,21 +21,9 @@
 //   (128 bytes); sw places blocks 0/1 (and 2/3) in complementary halves of
 //   the 64 banks.
 #pragma once
-#include <utility>
 #include "attn_core.h"
 
 namespace attn {
-
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, with i usable as a
-// constant expression (schedule-group sizes must be constants).
-template <class F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-  (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // QLDS of each wave's Q fragments are kept in LDS instead of registers (the
 // register file holds 2 waves per SIMD only just: 128 accumulator registers
