@@ -23,6 +23,9 @@ Sources (the reference pages):
          the minimal dense MLA example.
   [LB]   MindSpore Lite "lite_boost.layers.flash_attention" page: causal and
          window_size=(-1,-1) arguments, softmax_scale default 1/sqrt(D).
+  [MOJO] Modular "flash_attention_split_kv" page: attention of the current
+         queries over the previous KV cache followed by the current K/V,
+         passed separately instead of concatenated.
 
 Readings where the pages are silent (each is listed in the design notes):
   * causal is bottom-right aligned: key j is visible to query t iff
@@ -217,6 +220,36 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
 # --------------------------------------------------------------------------
 # Split planner, split-KV partials and the LSE-weighted combine
 # --------------------------------------------------------------------------
+def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
+                             block_table, cache_seqlens, page_size, scale, causal=False,
+                             window=(-1, -1), sinks=None, seqs=None):
+    """Packed queries over a paged cache of earlier tokens plus the current
+    K/V rows.                                   [MOJO flash_attention_split_kv]
+
+    q (Tq, Hq, D); k, v (Tk, Hkv, D|Dv) hold the current tokens (sequence b
+    owns rows cu_seqlens_k[b]:cu_seqlens_k[b+1]); k_cache / v_cache
+    (P, page, Hkv, D|Dv) with block_table hold the cache_seqlens[b] earlier
+    tokens [MATE flash_attn_with_kvcache paging]. The key sequence of b is the
+    cache rows 0..Lc-1 followed by the current rows, Lk = Lc + Ln; masks are
+    those of attention_varlen over that sequence (bottom-right causal).
+    Written as its definition: the concatenated K/V, then attention_varlen.
+    Returns O (Tq, Hq, Dv) and LSE (Hq, Tq).
+    """
+    bsz = len(cu_seqlens_q) - 1
+    ks, vs, cu = [], [], [0]
+    for b in range(bsz):
+        lc = int(cache_seqlens[b])
+        kb = np.concatenate([gather_paged(k_cache, block_table, b, lc, page_size),
+                             k[cu_seqlens_k[b]:cu_seqlens_k[b + 1]]])
+        vb = np.concatenate([gather_paged(v_cache, block_table, b, lc, page_size),
+                             v[cu_seqlens_k[b]:cu_seqlens_k[b + 1]]])
+        ks.append(kb)
+        vs.append(vb)
+        cu.append(cu[-1] + len(kb))
+    return attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cu_seqlens_q,
+                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs)
+
+
 def plan_words(batch, max_splits):
     """int32 words of a plan buffer: header (2), split_ptr (B+1) and up to
     B*max_splits (batch, kv_start, kv_end) triples."""

@@ -248,6 +248,94 @@ def test_paged_equals_contiguous():
     check_paged_equals_contiguous()
 
 
+# ------------------------------------------------- cache + current K/V (split-KV)
+def _kvcache_case(seed, lq, ln, lc, hq=4, hkv=2, d=4, page=4):
+    """Tiny varlen problem: per sequence lq[b] queries, ln[b] current K/V rows
+    and lc[b] cached rows in a shuffled page pool (float values)."""
+    rng = _rng(seed)
+    bsz = len(lq)
+    q = rng.standard_normal((sum(lq), hq, d))
+    k = rng.standard_normal((sum(ln), hkv, d))
+    v = rng.standard_normal((sum(ln), hkv, d))
+    npg = [(n + page - 1) // page for n in lc]
+    pool = sum(npg) + 2
+    kc = rng.standard_normal((pool, page, hkv, d))
+    vc = rng.standard_normal((pool, page, hkv, d))
+    perm = rng.permutation(pool)
+    table = np.full((bsz, max(max(npg), 1)), -1, np.int64)
+    at = 0
+    for b, n in enumerate(npg):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(ln)])
+    return q, k, v, cq, ck, kc, vc, table, np.asarray(lc), page
+
+
+def check_kvcache_brute_force():
+    """Brute force with its own key list: cache rows read slot by slot, then
+    the current rows, bottom-right causal over the whole key sequence."""
+    q, k, v, cq, ck, kc, vc, table, lc, page = _kvcache_case(41, [3, 1, 4], [2, 0, 4], [5, 3, 0])
+    o, lse = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.7, True)
+    grp = q.shape[1] // k.shape[1]
+    for b in range(len(lc)):
+        nq, nn, nc = cq[b + 1] - cq[b], ck[b + 1] - ck[b], int(lc[b])
+        for h in range(q.shape[1]):
+            g = h // grp
+            keys = [list(kc[table[b, j // page], j % page, g]) for j in range(nc)]
+            vals = [list(vc[table[b, j // page], j % page, g]) for j in range(nc)]
+            keys += [list(k[ck[b] + j, g]) for j in range(nn)]
+            vals += [list(v[ck[b] + j, g]) for j in range(nn)]
+            lk = nc + nn
+            qs = [list(q[cq[b] + t, h]) for t in range(nq)]
+            ob, lb = brute.rows(qs, keys, vals, 0.7, visible=lambda t, j: j <= t + lk - nq)
+            for t in range(nq):
+                if math.isinf(lb[t]):
+                    assert np.isneginf(lse[h, cq[b] + t]) and not o[cq[b] + t, h].any()
+                    continue
+                assert abs(lse[h, cq[b] + t] - lb[t]) <= 1e-12
+                np.testing.assert_allclose(o[cq[b] + t, h], ob[t], atol=1e-12)
+
+
+def check_kvcache_special_cases():
+    # an empty cache is plain varlen attention over the current rows
+    q, k, v, cq, ck, kc, vc, table, lc, page = _kvcache_case(42, [4, 2], [4, 5], [0, 0])
+    o, lse = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.5, True)
+    o2, l2 = orc.attention_varlen(q, k, v, cq, ck, 0.5, True)
+    np.testing.assert_allclose(o, o2, atol=0)
+    np.testing.assert_allclose(lse, l2, atol=0)
+    # chunked prefill: a sequence's first rows cached (slot by slot), the rest
+    # current, queries = the last rows; equals attention over the whole
+    # contiguous sequence with those queries (bottom-right causal)
+    rng = _rng(43)
+    total, lq, page, hq, hkv, d = 11, 4, 4, 2, 1, 4
+    kf = rng.standard_normal((total, hkv, d))
+    vf = rng.standard_normal((total, hkv, d))
+    qf = rng.standard_normal((lq, hq, d))
+    lcache = total - lq
+    npg = (lcache + page - 1) // page
+    kc = np.zeros((npg + 1, page, hkv, d))
+    vc = np.zeros((npg + 1, page, hkv, d))
+    table = np.array([[npg - i for i in range(npg)]])   # pages in reverse pool order
+    for j in range(lcache):
+        kc[table[0, j // page], j % page] = kf[j]
+        vc[table[0, j // page], j % page] = vf[j]
+    o, lse = orc.attention_varlen_kvcache(qf, kf[lcache:], vf[lcache:], np.array([0, lq]),
+                                          np.array([0, lq]), kc, vc, table,
+                                          np.array([lcache]), page, 0.6, True)
+    o2, l2 = orc.attention_varlen(qf, kf, vf, np.array([0, lq]), np.array([0, total]), 0.6, True)
+    np.testing.assert_allclose(o, o2, atol=1e-14)
+    np.testing.assert_allclose(lse, l2, atol=1e-14)
+
+
+def test_kvcache_brute_force():
+    check_kvcache_brute_force()
+
+
+def test_kvcache_special_cases():
+    check_kvcache_special_cases()
+
+
 def test_mate_mla_example_shape():
     """MATE minimal MLA example: q (1,32,8,576), k_cache (4,16,2,576),
     block_table zeros (1,4), cache_seqlens [32], head_dim_v 512. Every logical
@@ -443,19 +531,41 @@ def _mutants():
         return cache[np.asarray(block_table)[b, j % page_size % block_table.shape[1]],
                      j // page_size % cache.shape[1]]
 
+    base_kvc = orc.attention_varlen_kvcache
+
+    def kvcache_order_swapped(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
+                              block_table, cache_seqlens, page_size, scale, causal=False,
+                              window=(-1, -1), sinks=None, seqs=None):
+        # current rows placed before the cached ones
+        bsz = len(cu_seqlens_q) - 1
+        ks, vs, cu = [], [], [0]
+        for b in range(bsz):
+            lc = int(cache_seqlens[b])
+            kb = np.concatenate([k[cu_seqlens_k[b]:cu_seqlens_k[b + 1]],
+                                 orc.gather_paged(k_cache, block_table, b, lc, page_size)])
+            vb = np.concatenate([v[cu_seqlens_k[b]:cu_seqlens_k[b + 1]],
+                                 orc.gather_paged(v_cache, block_table, b, lc, page_size)])
+            ks.append(kb)
+            vs.append(vb)
+            cu.append(cu[-1] + len(kb))
+        return orc.attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cu_seqlens_q,
+                                    np.asarray(cu), scale, causal, window, sinks, seqs)
+
+    del base_kvc
     return [("attend_rows", no_scale), ("attend_rows", sink_dropped),
             ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
             ("visible_band", causal_top_left), ("visible_band", window_sides_swapped),
-            ("combine", combine_unweighted), ("gather_paged", gather_swapped)]
+            ("combine", combine_unweighted), ("gather_paged", gather_swapped),
+            ("attention_varlen_kvcache", kvcache_order_swapped)]
 
 
 PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical_keys,
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
-        check_brute_force]
+        check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases]
 
 
-@pytest.mark.parametrize("i", range(8))
+@pytest.mark.parametrize("i", range(9))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
