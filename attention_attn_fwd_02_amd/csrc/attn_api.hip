@@ -100,12 +100,72 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   a.sinks = sinks;
   a.out = out;
   a.lse = lse;
+  a.kc = nullptr;
+  a.vc = nullptr;
+  a.block_table = nullptr;
+  a.cache_lens = nullptr;
+  a.max_pages = 0;
+  a.page = 0;
   const int rows = dtype == ATTN_BF16 ? attn::varlen_bf16_rows(d) : attn::varlen_f32_rows(d);
   a.nqt = (max_seqlen_q + rows - 1) / rows;
   REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_varlen_bf16(a, d, as_stream(stream))
                                     : attn::launch_varlen_f32(a, d, as_stream(stream));
   return hip_status(e, "attn_fwd_varlen launch");
+}
+
+int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* cache_seqlens, int32_t page_size, int32_t batch,
+                                int32_t max_seqlen_q, int32_t hq, int32_t hkv, int32_t d,
+                                int32_t dv, int32_t dtype, float scale, int32_t causal,
+                                int32_t window_left, int32_t window_right, const float* sinks,
+                                void* out, float* lse, void* stream) {
+  REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 &&
+              page_size > 0 && max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  // k and v may be NULL when no sequence has current rows (they are then never read)
+  REQUIRE(q && cu_seqlens_q && cu_seqlens_k && k_cache && v_cache && block_table &&
+              cache_seqlens && out,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
+  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "cache + current attention supports bf16 only");
+  REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
+          "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
+  attn::VarlenArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.cache_lens = cache_seqlens;
+  a.max_pages = max_pages_per_seq;
+  a.page = page_size;
+  const int rows = attn::varlen_bf16_rows(d);
+  a.nqt = (max_seqlen_q + rows - 1) / rows;
+  REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
+  return hip_status(attn::launch_varlen_kvcache_bf16(a, d, as_stream(stream)),
+                    "attn_fwd_varlen_kvcache launch");
 }
 
 size_t attn_plan_words(int32_t batch, int32_t max_splits) {

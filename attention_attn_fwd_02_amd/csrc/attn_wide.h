@@ -55,17 +55,6 @@ struct WideCfg {
   static_assert(QLDS >= 0 && QLDS < NQ, "QLDS");
 };
 
-// Lane id recomputed where it is used (volatile, so not hoisted out of the
-// key loop): lane-dependent addresses are then rebuilt with a few VALU
-// operations per tile instead of occupying registers across the loop, which
-// at 256 registers per wave would be spilled and reloaded through scratch
-// memory (and scratch loads share vmcnt with the tile DMA).
-__device__ __forceinline__ int fresh_lane() {
-  int l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
 template <class C>
 struct WideTile {
   using M = Mfma<32>;

@@ -140,6 +140,17 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Lane id recomputed where it is used (volatile, so not hoisted out of the
+// key loop): lane-dependent addresses are then rebuilt with a few VALU
+// operations per tile instead of occupying registers across the loop, which
+// near the register limit would be spilled and reloaded through scratch
+// memory (and scratch loads share vmcnt with the tile DMA).
+__device__ __forceinline__ int fresh_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ bf16x8 join_bf16x8(s16x4 lo, s16x4 hi) {
   u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
   u32x4 r = {a[0], a[1], b[0], b[1]};

@@ -61,7 +61,11 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
   return bd;
 }
 
-template <class C>
+// KVC: the keys of sequence b are its cache_lens[b] cached rows (paged:
+// row j at block_table[b][j / page], slot j % page) followed by its current
+// rows [cu_k[b], cu_k[b+1]). Page sizes are multiples of 16, so each 16-row
+// block of a tile that lies wholly in the cache sits on one page.
+template <class C, bool KVC>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES)
 k_varlen_bf16(VarlenArgs a) {
   using T = PrefillTile<C>;
@@ -74,7 +78,8 @@ k_varlen_bf16(VarlenArgs a) {
   const int row0 = w.qt * C::ROWS;
   if (row0 >= lq) return;
   const int k0 = a.cu_k[w.b];
-  const int lk = a.cu_k[w.b + 1] - k0;
+  const int lc = KVC ? a.cache_lens[w.b] : 0;  // cached keys come first
+  const int lk = lc + a.cu_k[w.b + 1] - k0;
   const int row_last = min(lq, row0 + C::ROWS) - 1;
   const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
 
@@ -102,20 +107,72 @@ k_varlen_bf16(VarlenArgs a) {
   const long row_bytes = (long)kst * 2;
   const uint32_t koff = T::template dma_lane_off<false>(lane, (uint32_t)row_bytes);
   const uint32_t voff = T::template dma_lane_off<true>(lane, (uint32_t)row_bytes);
+  // cache bases of this KV head (KVC only)
+  const char* kcb = KVC ? static_cast<const char*>(a.kc) + (size_t)w.kvh * C::D * 2 : nullptr;
+  const char* vcb = KVC ? static_cast<const char*>(a.vc) + (size_t)w.kvh * C::D * 2 : nullptr;
+  const int* btb = KVC ? a.block_table + (size_t)w.b * a.max_pages : nullptr;
   auto issue = [&](char* buf, int i) {
-    const int j0 = bd.lo + i * C::BN;
-    if (j0 + C::BN - 1 <= last) {
-      T::template dma_tile_sv<false>(buf, reinterpret_cast<const char*>(kb) + j0 * row_bytes,
-                                     row_bytes, koff, wave);
-      T::template dma_tile_sv<true>(buf + C::TILE_BYTES,
-                                    reinterpret_cast<const char*>(vb) + j0 * row_bytes, row_bytes,
-                                    voff, wave);
-    } else {
-      T::template dma_tile<false>(
-          buf, [&](int r) { return kb + (size_t)min(j0 + r, last) * kst; }, wave, lane);
-      T::template dma_tile<true>(
-          buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)min(j0 + r, last) * kst; }, wave,
-          lane);
+    const int j0 = bd.lo + i * C::BN;  // key index of tile row 0 (cache rows first)
+    if (!KVC || j0 >= lc) {
+      const int c0 = j0 - lc;  // current row of tile row 0
+      if (j0 + C::BN - 1 <= last) {
+        T::template dma_tile_sv<false>(buf, reinterpret_cast<const char*>(kb) + c0 * row_bytes,
+                                       row_bytes, koff, wave);
+        T::template dma_tile_sv<true>(buf + C::TILE_BYTES,
+                                      reinterpret_cast<const char*>(vb) + c0 * row_bytes,
+                                      row_bytes, voff, wave);
+      } else {
+        // the cache variant holds more state across the key loop: its lane
+        // constants are rebuilt here rather than kept live
+        const int ln = KVC ? fresh_lane() : lane;
+        T::template dma_tile<false>(
+            buf, [&](int r) { return kb + (size_t)(min(j0 + r, last) - lc) * kst; }, wave, ln);
+        T::template dma_tile<true>(
+            buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)(min(j0 + r, last) - lc) * kst; },
+            wave, ln);
+      }
+      return;
+    }
+    if constexpr (KVC) {
+      // cache slot of the first row of each 16-row block of the tile (blocks
+      // past the cache clamp to its last row and are not used)
+      constexpr int NB = C::BN / 16;
+      long sl[NB];
+      static_for<NB / 2>([&](auto I) {
+        constexpr int b = 2 * decltype(I)::value;
+        const int ja = min(j0 + 16 * b, lc - 1), jb = min(j0 + 16 * (b + 1), lc - 1);
+        int pa, pb;
+        sload2_uniform(btb + ja / a.page, btb + jb / a.page, pa, pb);
+        sl[b] = (long)pa * a.page + ja % a.page;
+        sl[b + 1] = (long)pb * a.page + jb % a.page;
+      });
+      auto slot = [&](int rb) {
+        long v = sl[0];
+        static_for<NB - 1>([&](auto I) {
+          if (rb == decltype(I)::value + 1) v = sl[decltype(I)::value + 1];
+        });
+        return v;
+      };
+      if (j0 + C::BN - 1 < lc) {
+        auto kblk = [&](int rb) { return kcb + slot(rb) * row_bytes; };
+        auto vblk = [&](int rb) { return vcb + slot(rb) * row_bytes; };
+        T::template dma_tile_blk<false>(buf, kblk, row_bytes, koff, wave);
+        T::template dma_tile_blk<true>(buf + C::TILE_BYTES, vblk, row_bytes, voff, wave);
+      } else {
+        // the tile straddles the end of the cache (or is the last tile):
+        // per-lane rows, cached ones through the block slots above
+        const int ln = fresh_lane();
+        auto row = [&](const char* cb, const bf16_t* cur, int r) -> const bf16_t* {
+          const int j = min(j0 + r, last);
+          if (j < lc)
+            return reinterpret_cast<const bf16_t*>(cb + slot((j - j0) >> 4) * row_bytes) +
+                   (size_t)((j - j0) & 15) * kst;
+          return cur + (size_t)(j - lc) * kst;
+        };
+        T::template dma_tile<false>(buf, [&](int r) { return row(kcb, kb, r); }, wave, ln);
+        T::template dma_tile<true>(buf + C::TILE_BYTES, [&](int r) { return row(vcb, vb, r); },
+                                   wave, ln);
+      }
     }
   };
   const int tdiag = trow + bd.delta;
@@ -301,9 +358,19 @@ int varlen_f32_rows(int d) { return d == 64 ? F32Cfg<64>::ROWS : F32Cfg<128>::RO
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s) {
   const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
   if (d == 64)
-    hipLaunchKernelGGL(k_varlen_bf16<CfgP64>, dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_varlen_bf16<CfgP64, false>), dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(k_varlen_bf16<CfgP128>, dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
+    hipLaunchKernelGGL((k_varlen_bf16<CfgP128, false>), dim3(grid), dim3(CfgP128::THREADS), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (d == 64)
+    hipLaunchKernelGGL((k_varlen_bf16<CfgP64, true>), dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_varlen_bf16<CfgP128, true>), dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,13 @@ struct VarlenArgs {
   const float* sinks;
   void* out;
   float* lse;
+  // keys of sequence b = cache rows [0, cache_lens[b]) followed by its current
+  // rows (attn_fwd_varlen_kvcache); unused by attn_fwd_varlen
+  const void* kc;
+  const void* vc;
+  const int32_t* block_table;
+  const int32_t* cache_lens;
+  int32_t max_pages, page;
 };
 
 struct DecodeArgs {
@@ -62,6 +69,7 @@ int sparse_max_topk();
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
+hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s);

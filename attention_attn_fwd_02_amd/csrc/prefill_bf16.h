@@ -164,23 +164,34 @@ struct PrefillTile {
     return (uint32_t)(((lane >> 4) & 1) * 4 + ((lane >> 2) & 3)) * row_bytes +
            ((lane >> 5) * 4 + (lane & 3)) * 16;
   }
-  template <bool VLAYOUT>
-  __device__ __forceinline__ static void dma_tile_sv(char* buf, const char* tile, long row_bytes,
-                                                     uint32_t lane_off, int wave) {
+  // blk(rb): wave-uniform byte pointer of tile row 16 rb; rows of one
+  // 16-row block are row_bytes apart (different blocks may lie on different
+  // pages).
+  template <bool VLAYOUT, class Blk>
+  __device__ __forceinline__ static void dma_tile_blk(char* buf, Blk blk, long row_bytes,
+                                                      uint32_t lane_off, int wave) {
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       const int inst = wave * C::DMA_PER_WAVE + n;
-      long u;
+      const char* src;
       if constexpr (!VLAYOUT) {
         constexpr int IPB = C::NCH / 4;
-        u = (inst / IPB) * 16 * row_bytes + (inst % IPB) * 64;
+        src = blk(inst / IPB) + (inst % IPB) * 64;
       } else {
-        // blk = 2 inst + (lane >> 5); NCH / 4 is even, so blk / (NCH / 4) is uniform
+        // blk = 2 inst + (lane >> 5); NCH / 4 is even, so the 8-row group
+        // (2 inst) / (NCH / 4) is uniform
         constexpr int BPR = C::NCH / 4;
-        u = ((2 * inst) / BPR) * 8 * row_bytes + ((2 * inst) % BPR) * 64;
+        const int q8 = (2 * inst) / BPR;
+        src = blk(q8 >> 1) + (q8 & 1) * 8 * row_bytes + ((2 * inst) % BPR) * 64;
       }
-      lds_dma16_sv(tile + u, lane_off, buf + inst * 1024);
+      lds_dma16_sv(src, lane_off, buf + inst * 1024);
     }
+  }
+  template <bool VLAYOUT>
+  __device__ __forceinline__ static void dma_tile_sv(char* buf, const char* tile, long row_bytes,
+                                                     uint32_t lane_off, int wave) {
+    dma_tile_blk<VLAYOUT>(
+        buf, [&](int rb) { return tile + rb * 16 * row_bytes; }, row_bytes, lane_off, wave);
   }
 
   // S^T = K Q^T for one tile.

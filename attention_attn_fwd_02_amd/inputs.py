@@ -166,6 +166,52 @@ def varlen_prefill(seed: int = SEED_VARLEN_PREFILL, nseq: int = 8, lo: int = 512
 
 
 @dataclasses.dataclass
+class DenseKV(Dense):
+    """A Dense problem whose keys also have an earlier part in a paged cache:
+    k_cache (P,page,Hkv,D), v_cache (P,page,Hkv,Dv) bits, block_table
+    (B, max_pages) int32 (-1 past a sequence's pages), cache_seqlens (B)."""
+    k_cache: np.ndarray = None
+    v_cache: np.ndarray = None
+    block_table: np.ndarray = None
+    cache_seqlens: np.ndarray = None
+    page_size: int = 0
+
+
+def varlen_kvcache(seed: int, lens_q, lens_new, lens_cache, hq: int = 32, hkv: int = 8,
+                   d: int = 128, page: int = 64, causal: bool = True, window=(-1, -1),
+                   scale: float | None = None, with_sinks: bool = False,
+                   spare_pages: int = 0) -> DenseKV:
+    """Chunked prefill: per sequence lens_q queries and lens_new current K/V
+    rows (packed as in varlen), after lens_cache earlier rows held in a paged
+    bf16 cache. The pool has spare_pages pages that no sequence references.
+    Draw order: Q, K, V, K cache, V cache, page permutation, sinks."""
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_new = np.asarray(lens_new, dtype=np.int64)
+    lens_cache = np.asarray(lens_cache, dtype=np.int64)
+    tq, tk = int(lens_q.sum()), int(lens_new.sum())
+    q = _normal_bf16(rng, (tq, hq, d))
+    k = _normal_bf16(rng, (tk, hkv, d))
+    v = _normal_bf16(rng, (tk, hkv, d))
+    nblk = (lens_cache + page - 1) // page
+    pool = max(1, int(nblk.sum()) + spare_pages)
+    k_cache = _normal_bf16(rng, (pool, page, hkv, d))
+    v_cache = _normal_bf16(rng, (pool, page, hkv, d))
+    perm = rng.permutation(pool).astype(np.int32)
+    table = np.full((len(lens_cache), max(1, int(nblk.max()))), -1, dtype=np.int32)
+    off = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[off:off + n]
+        off += n
+    sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_new)]).astype(np.int32)
+    return DenseKV(q, k, v, cu_q, cu_k, "bf16", scale if scale is not None else 1.0 / np.sqrt(d),
+                   causal, tuple(window), sinks, k_cache, v_cache, table,
+                   lens_cache.astype(np.int32), page)
+
+
+@dataclasses.dataclass
 class Paged:
     """Decode against a paged cache. q (B,Sq,Hq,D) bits; k_cache (P,page,Hkv,D)
     bits; v_cache (P,page,Hkv,Dv) bits, or None when K and V share one cache

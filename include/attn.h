@@ -87,6 +87,43 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v,
                         const float* sinks, void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_kvcache - packed queries over a paged cache of earlier
+ * tokens followed by the current K/V rows, without concatenating them
+ * (chunked / append prefill).
+ * [Modular flash_attention_split_kv: the previous KV cache and the current
+ *  K/V are separate inputs; MATE flash_attn_with_kvcache: paged k_cache with
+ *  block_table and cache_seqlens]
+ *
+ *  q (Tq, hq, d); k (Tk, hkv, d), v (Tk, hkv, dv): the current tokens, as in
+ *      attn_fwd_varlen (cu_seqlens_q, cu_seqlens_k); k and v may be NULL when
+ *      Tk = 0 (queries over cached keys only).
+ *  k_cache (P, page_size, hkv, d), v_cache (P, page_size, hkv, dv); int32
+ *      block_table (batch, max_pages_per_seq); int32 cache_seqlens (batch):
+ *      sequence b has cache_seqlens[b] earlier tokens, row j at page
+ *      block_table[b][j / page_size], slot j % page_size; the current tokens
+ *      are not in the cache.
+ *  The keys of b are its cached rows 0 .. Lc-1 followed by its current rows,
+ *  Lk = Lc + Ln; causal and window masks are those of attn_fwd_varlen over
+ *  that sequence (bottom-right: query t sits at position t + Lk - Lq).
+ *  out (Tq, hq, dv); lse NULL or float32 (hq, Tq); sinks as attn_fwd_varlen.
+ *  Supported: dtype BF16, d = dv in {64, 128}, page_size a multiple of 16.
+ *  Block-table entries past ceil(Lc / page_size) are never read. Device
+ *  values are not checked: the caller keeps 0 <= cache_seqlens[b] <=
+ *  max_pages_per_seq * page_size and every referenced entry a page of the
+ *  pool. Host arguments are checked as for attn_fwd_varlen (EEMPTY, EINVAL,
+ *  EUNSUPPORTED) before anything is enqueued.
+ */
+int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
+                                const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* cache_seqlens, int32_t page_size, int32_t batch,
+                                int32_t max_seqlen_q, int32_t hq, int32_t hkv, int32_t d,
+                                int32_t dv, int32_t dtype, float scale, int32_t causal,
+                                int32_t window_left, int32_t window_right, const float* sinks,
+                                void* out, float* lse, void* stream);
+
+/*
  * Split-KV plan for paged decode.
  * [MATE: get_scheduler_metadata / get_mla_metadata precompute the work split;
  *  CANN flash_attn_metadata does the same before the main call. The rule

@@ -29,7 +29,7 @@ def lib():
 def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
-              "attn_combine", "mla_decode_paged", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "mla_sparse_fwd", "attn_debug_gather_paged",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -76,6 +76,30 @@ def test_varlen_host_checks(lib):
 def test_error_message_set(lib):
     assert varlen(lib, hq=6, hkv=4) == B.ATTN_EINVAL
     assert b"multiple" in lib.attn_last_error()
+
+
+def test_varlen_kvcache_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, cq=P, ck=P, kc=P, vc=P, bt=P, mp=4, lens=P, page=64, batch=2,
+                 mq=8, hq=8, hkv=2, d=128, dv=128, dtype=0, scale=0.1, causal=1, wl=-1, wr=-1)
+        a.update(kw)
+        return lib.attn_fwd_varlen_kvcache(
+            a["q"], a["k"], a["v"], a["cq"], a["ck"], a["kc"], a["vc"], a["bt"], a["mp"],
+            a["lens"], a["page"], a["batch"], a["mq"], a["hq"], a["hkv"], a["d"], a["dv"],
+            a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None, P, None, None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(mp=0) == B.ATTN_EEMPTY
+    assert call(page=0) == B.ATTN_EEMPTY
+    assert call(bt=None) == B.ATTN_EINVAL
+    assert call(lens=None) == B.ATTN_EINVAL
+    assert call(kc=None) == B.ATTN_EINVAL
+    assert call(hq=6, hkv=4) == B.ATTN_EINVAL
+    assert call(wr=-3) == B.ATTN_EINVAL
+    assert call(dtype=1) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=128) == B.ATTN_EUNSUPPORTED
+    assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
+    assert call(page=24) == B.ATTN_EUNSUPPORTED
+    assert b"page_size" in lib.attn_last_error()
 
 
 def test_plan_host_checks(lib):
