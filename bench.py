@@ -9,7 +9,11 @@ decode + combine), MLA-absorbed paged decode and sparse MLA with sinks.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Every timed region is bracketed by torch.cuda.synchronize() and
-timed with HIP events on the stream the kernels are launched on.
+timed with HIP events on the stream the kernels are launched on. Before the
+W warmup steps of each workload, its step runs untimed for --ramp-ms
+milliseconds: from idle the GPU takes about 40 ms of continuous work to
+leave its low clocks (prefill steps run 25 % slower over the first 10 ms),
+so a few warmup steps alone would time the clock ramp, not the kernels.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--only prefill,...]
                 [--no-cpu] [--no-secondary]
@@ -45,10 +49,29 @@ def dev(x):
     return torch.from_numpy(x).cuda()
 
 
-def time_steps(fn, steps, warmup):
-    """Runs fn warmup times untimed, then `steps` times between two HIP events
-    on the current stream; returns milliseconds per step."""
+RAMP_MS = [200.0]
+
+
+def ramp(fn, ms):
+    """Untimed: runs fn back to back for about `ms` milliseconds (host clock,
+    synchronising every 4 calls), at most 20000 calls."""
     import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms and n < 20000:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+        n += 4
+
+
+def time_steps(fn, steps, warmup):
+    """Ramps the clocks (ramp), runs fn warmup times untimed, then `steps`
+    times between two HIP events on the current stream; returns milliseconds
+    per step."""
+    import torch
+    ramp(fn, RAMP_MS[0])
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -317,6 +340,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--ramp-ms", type=float, default=200.0,
+                    help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only", default="prefill,decode,mla,sparse")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -329,6 +354,7 @@ def main():
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command, stored with the traffic record")
     args = ap.parse_args()
+    RAMP_MS[0] = max(0.0, args.ramp_ms)
     if args.traffic_from:
         write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_command)
         return
@@ -418,6 +444,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_ramp_ms": RAMP_MS[0],
         "ms_per_step": pre["ms"],
         "cold_cache": {"ms_per_step_median": pre["ms_cold"],
                        "value": pre["flops"] / (pre["ms_cold"] * 1e-3) / 1e12,
