@@ -78,7 +78,8 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
           "null tensor pointer");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
-  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_F32, ATTN_EUNSUPPORTED, "dtype %d", dtype);
   REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
           "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
@@ -132,7 +133,8 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
           ATTN_EINVAL, "null tensor pointer");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
-  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "cache + current attention supports bf16 only");
   REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
           "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
@@ -203,7 +205,8 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
-  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
   REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
           d, dv);
@@ -269,7 +272,8 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
           ATTN_EINVAL, "null tensor pointer");
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
-  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
   REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   attn::DecodeArgs a;
@@ -301,7 +305,8 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
           "empty dimension");
   REQUIRE(q && kv && sparse_indices && out, ATTN_EINVAL, "null tensor pointer");
   REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
-  REQUIRE(std::isfinite(scale), ATTN_EINVAL, "scale is not finite");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
   REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
   REQUIRE(topk <= attn::sparse_max_topk(), ATTN_EUNSUPPORTED, "topk %d above %d", topk,
           attn::sparse_max_topk());

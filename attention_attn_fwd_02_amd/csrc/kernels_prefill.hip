@@ -184,17 +184,11 @@ k_varlen_bf16(VarlenArgs a) {
   for (int i = 0; i < C::STAGES - 1; ++i)
     if (i < ntiles) issue(stage(i), i);
   auto process = [&](int i, char* cur, char* refill) {
-    const int after = min(ntiles - 1 - i, C::STAGES - 2);  // tiles issued after tile i
-    if constexpr (C::STAGES >= 4) {
-      if (after >= 2) wait_vmcnt<2 * PER_TILE>();
-      else if (after == 1) wait_vmcnt<PER_TILE>();
-      else wait_vmcnt<0>();
-    } else if constexpr (C::STAGES == 3) {
-      if (after >= 1) wait_vmcnt<PER_TILE>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // tile i has landed once at most `after` later tiles are outstanding
+    const int after = min(ntiles - 1 - i, C::STAGES - 2);
+    static_for<C::STAGES - 1>([&](auto I) {
+      if (after == decltype(I)::value) wait_vmcnt<decltype(I)::value * PER_TILE>();
+    });
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): own reads of tile i-1 retired
     barrier_no_fence();
     if (i + C::STAGES - 1 < ntiles) issue(refill, i + C::STAGES - 1);
@@ -204,12 +198,13 @@ k_varlen_bf16(VarlenArgs a) {
                       (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
-    const int hi_vis = min(lk - 1, bd.wr < 0 ? lk - 1 : tdiag + bd.wr);  // last visible key
-    const int lo_vis = bd.wl < 0 ? 0 : tdiag - bd.wl;                     // first visible key
-    const float m_use = t.prep(s, a.scale_log2, lane, need, [&](int jr) {
-      const int j = j0 + jr;
-      return (j <= hi_vis) & (j >= lo_vis);
-    });
+    if (need) {
+      // visible keys of this lane's row, as tile indices
+      const int hi = min(lk - 1, bd.wr < 0 ? lk - 1 : tdiag + bd.wr) - j0;
+      if (bd.wl < 0) T::template mask<false>(s, lane, 0, hi);
+      else T::template mask<true>(s, lane, tdiag - bd.wl - j0, hi);
+    }
+    const float m_use = t.prep(s, a.scale_log2);
     uint32_t pk[C::NSB * 8];
     t.probs(s, a.scale_log2, m_use, pk);
     t.pv(cur + C::TILE_BYTES, lane, pk);

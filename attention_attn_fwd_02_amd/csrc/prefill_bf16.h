@@ -2,19 +2,23 @@
 //
 // Per workgroup: NW waves x 32 rows share one key sequence. Key tiles of BN
 // rows are copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no register
-// staging) into one of two buffers while the other buffer is consumed.
+// staging) through a ring of STAGES buffers, STAGES-1 tiles in flight.
 //
 // LDS layouts (16-byte units, c = chunk index along the head dimension). The
 // LDS has 64 banks of 4 bytes (256 B per cycle) and serves 16 lanes of a
-// 16-byte read per cycle; both layouts put the 16 lanes of every read in 256
-// distinct bytes:
-//   K: [row / 16][c][row % 16]               A-operand reads (16 consecutive
-//      rows at one chunk) are 256 contiguous bytes.
+// 16-byte read per cycle; both layouts put the 16 lanes of every read in 64
+// distinct banks:
+//   K: [row / 16][c / 4][row % 16][(c % 4) ^ ((row % 16) / 4)]
+//      an A-operand read (16 consecutive rows at one chunk) takes the 16
+//      combinations of row % 4 (16-bank group) and the swizzled slot
+//      (4-bank group).
 //   V: [row / 8][c / 4][(row / 4) % 2][row % 4][c % 4]
 //      the two 16-lane blocks of a ds_read_b64_tr_b16 that share a cycle
 //      (4 rows x 32 B each) interleave into 256 contiguous bytes.
-// Every DMA instruction writes 1 KB contiguously (64 lanes x 16 B); each row
-// segment it reads from global memory is 64 B (K) or 128 B (V) contiguous.
+// Every DMA instruction writes 1 KB contiguously (64 lanes x 16 B). Its
+// global reads are coalesced: each group of 4 consecutive lanes reads one
+// 64-byte row segment (K: 16 rows x 64 B per instruction; V: 8 rows x 2
+// segments).
 // All MFMA operand addresses are a per-lane base plus a compile-time offset.
 //
 // Softmax runs in the base-2 domain on unscaled scores s: p = 2^(s*c - m),
@@ -109,12 +113,16 @@ struct PrefillTile {
   bf16x8 qf[C::NQ];
   f32x16 o[C::NOB];
   float m_ref;  // reference max (base-2 scaled domain), -inf until a key is seen
+  float m_use;  // exponent offset: m_ref, or 0 while m_ref is -inf
+  float thr;    // raw score above which the reference may have to rise
   float l_run;  // this lane's share of sum 2^(s*c - m_ref)
 
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int i = 0; i < C::NOB; ++i) o[i] = f32x16{};
     m_ref = kNegInf;
+    m_use = 0.f;
+    thr = kNegInf;
     l_run = 0.f;
   }
 
@@ -138,11 +146,12 @@ struct PrefillTile {
       const int inst = wave * C::DMA_PER_WAVE + n;
       int r, c;
       if constexpr (!VLAYOUT) {
-        // instruction -> (16-row block, 4 chunks); lane -> (row % 16, chunk)
+        // instruction -> (16-row block, 4 chunks); 4 lanes per row, the
+        // chunk slot swizzled by the row's quarter of the block
         constexpr int IPB = C::NCH / 4;
         const int rb = inst / IPB, cq = inst % IPB;
-        r = rb * 16 + (lane & 15);
-        c = cq * 4 + (lane >> 4);
+        r = rb * 16 + (lane >> 2);
+        c = cq * 4 + ((lane & 3) ^ ((lane >> 4) & 3));
       } else {
         // instruction -> two 512 B blocks (8 rows x 4 chunks); lane -> (row, chunk)
         const int blk = 2 * inst + (lane >> 5);
@@ -160,7 +169,8 @@ struct PrefillTile {
   // dma_lane_off.
   template <bool VLAYOUT>
   __device__ __forceinline__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes) {
-    if constexpr (!VLAYOUT) return (uint32_t)(lane & 15) * row_bytes + (lane >> 4) * 16;
+    if constexpr (!VLAYOUT)
+      return (uint32_t)(lane >> 2) * row_bytes + ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
     return (uint32_t)(((lane >> 4) & 1) * 4 + ((lane >> 2) & 3)) * row_bytes +
            ((lane >> 5) * 4 + (lane & 3)) * 16;
   }
@@ -194,69 +204,91 @@ struct PrefillTile {
         buf, [&](int rb) { return tile + rb * 16 * row_bytes; }, row_bytes, lane_off, wave);
   }
 
-  // S^T = K Q^T for one tile.
+  // S^T = K Q^T for one tile. Lane (key k = lane % 32, group g = lane / 32)
+  // reads chunk 2 dq + g of key k: block (k / 16, dq / 2), row k % 16, slot
+  // (2 (dq % 2) + g) ^ ((k % 16) / 4); the two slot patterns of even and odd
+  // dq give two per-lane bases.
   __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[C::NSB]) const {
-    const int g = lane >> 5;
-    const char* kb = kbuf + ((((lane >> 4) & 1) * C::NCH + g) * 256 + (lane & 15) * 16);
+    constexpr int IPB = C::NCH / 4;
+    const int g = lane >> 5, r = lane & 15, sw = (r >> 2) & 3;
+    const char* base = kbuf + ((lane >> 4) & 1) * IPB * 1024 + r * 64;
+    const char* kb0 = base + (g ^ sw) * 16;
+    const char* kb1 = base + ((2 + g) ^ sw) * 16;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
       bf16x8 kf[C::NQ];
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq)
-        kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>(kb + (sb * 2 * C::NCH + dq * 2) * 256));
+        kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>((dq & 1 ? kb1 : kb0) +
+                                                           (sb * 2 * IPB + dq / 2) * 1024));
       s[sb] = f32x16{};
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], qf[dq], s[sb]);
     }
   }
 
-  // Masking (only when need_mask), row max and the lazy update of the
-  // reference max. Returns the reference to subtract in the exponent.
-  template <class Vis>
-  __device__ __forceinline__ float prep(f32x16 (&s)[C::NSB], float cscale, int lane, bool need_mask,
-                                        Vis vis) {
-    const int g = lane >> 5;
-    if (need_mask) {
+  // Masks the scores of keys this lane's row must not see: key = tile key
+  // index (sb * 32 + mrow(g, r)); the row sees keys lo <= key <= hi (tile
+  // indices, possibly out of range). HAS_LO = false skips the lower bound.
+  template <bool HAS_LO>
+  __device__ __forceinline__ static void mask(f32x16 (&s)[C::NSB], int lane, int lo, int hi) {
+    const int g4 = (lane >> 5) * 4;  // mrow(g, r) = (r/4)*8 + 4g + r%4
+    const int h = hi - g4, l = lo - g4;
 #pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
+    for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!vis(sb * 32 + M::mrow(g, r))) s[sb][r] = kNegInf;
+      for (int r = 0; r < 16; ++r) {
+        const int k = sb * 32 + (r >> 2) * 8 + (r & 3);
+        bool hide = k > h;
+        if constexpr (HAS_LO) hide |= k < l;
+        if (hide) s[sb][r] = kNegInf;
       }
     }
+  }
+
+  // Lazy update of the reference max: each lane compares the max of its own
+  // scores with the raw threshold thr = (m_ref + slack) / c (c > 0); only
+  // when some lane exceeds it is the row max formed across the lane pair and
+  // the reference raised (O and l rescaled). Returns the exponent offset.
+  __device__ __forceinline__ float prep(const f32x16 (&s)[C::NSB], float cscale) {
     float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
     }
-    mx = M::group_max(mx) * cscale;
-    const bool raise = mx > m_ref + kRescaleSlack;
-    if (__ballot(raise) != 0) {
-      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;  // m_ref = -inf -> 0
-      m_ref = raise ? mx : m_ref;
+    if (__ballot(mx > thr) != 0) {
+      const float rmx = M::group_max(mx) * cscale;
+      const bool raise = rmx > m_ref + kRescaleSlack;
+      const float alpha = raise ? fast_exp2(m_ref - rmx) : 1.f;  // m_ref = -inf -> 0
+      m_ref = raise ? rmx : m_ref;
       l_run *= alpha;
 #pragma unroll
       for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+      m_use = m_ref == kNegInf ? 0.f : m_ref;
+      thr = (m_ref + kRescaleSlack) / cscale;
     }
-    return m_ref == kNegInf ? 0.f : m_ref;
+    return m_use;
   }
 
-  // p = 2^(s*c - m), packed to bf16 pairs in B-operand order; l += sum p.
-  __device__ __forceinline__ void probs(const f32x16 (&s)[C::NSB], float cscale, float m_use,
+  // p = 2^(s*c - m), packed to bf16 pairs in B-operand order; l += sum p in
+  // float32 (summing the bf16-rounded p instead would move LSE by up to 2^-9
+  // on rows with few keys).
+  __device__ __forceinline__ void probs(const f32x16 (&s)[C::NSB], float cscale, float m_use_,
                                         uint32_t (&pk)[C::NSB * 8]) {
-    float lsum = 0.f;
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use));
-        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use));
-        lsum += p0 + p1;
+        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use_));
+        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use_));
         pk[sb * 8 + r / 2] = pack_bf16x2(p0, p1);
+        if ((r >> 1) & 1) l1 += p0 + p1;
+        else l0 += p0 + p1;
       }
     }
-    l_run += lsum;
+    l_run += l0 + l1;
   }
 
   // O^T += V^T P^T with V read transposed.

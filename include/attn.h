@@ -12,7 +12,9 @@
  *  - Tensor arguments are DEVICE pointers, allocated and owned by the caller,
  *    dense row-major in the shapes given. The library never allocates device
  *    memory and keeps no pointer after the call returns.
- *  - Scalar arguments (sizes, flags, scale) are host values.
+ *  - Scalar arguments (sizes, flags, scale) are host values. scale must be
+ *    positive and finite (ATTN_EINVAL otherwise): the kernels track the row
+ *    maximum of the scaled scores through the maximum of the raw ones.
  *  - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *    enqueues work on it and returns without synchronising.
  *  - bfloat16 tensors hold raw 16-bit patterns; results are rounded to

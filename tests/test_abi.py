@@ -67,6 +67,8 @@ def test_varlen_host_checks(lib):
     assert varlen(lib, hq=6, hkv=4) == B.ATTN_EINVAL
     assert varlen(lib, wl=-2) == B.ATTN_EINVAL
     assert varlen(lib, scale=float("nan")) == B.ATTN_EINVAL
+    assert varlen(lib, scale=0.0) == B.ATTN_EINVAL
+    assert varlen(lib, scale=-0.1) == B.ATTN_EINVAL
     assert varlen(lib, d=96, dv=96) == B.ATTN_EUNSUPPORTED
     assert varlen(lib, d=128, dv=64) == B.ATTN_EUNSUPPORTED
     assert varlen(lib, dtype=7) == B.ATTN_EUNSUPPORTED
