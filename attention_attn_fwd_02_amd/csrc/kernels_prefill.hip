@@ -86,6 +86,8 @@ k_varlen_bf16(VarlenArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int trow = row0 + wave * C::R + (lane & 31);
+  const int wrow0 = row0 + wave * C::R;             // this wave's first row
+  const int wrow1 = min(lq, wrow0 + C::R) - 1;      // and its last row in the sequence
   const bool row_ok = trow < lq;
   T t;
   t.init();
@@ -193,9 +195,15 @@ k_varlen_bf16(VarlenArgs a) {
     barrier_no_fence();
     if (i + C::STAGES - 1 < ntiles) issue(refill, i + C::STAGES - 1);
     const int j0 = bd.lo + i * C::BN;
+    // per wave: skip a tile none of its rows sees (on the causal diagonal or
+    // past a window, or rows past the sequence); mask only where some of its
+    // rows see part of the tile
+    if (wrow1 < wrow0 || (bd.wr >= 0 && j0 > wrow1 + bd.delta + bd.wr) ||
+        (bd.wl >= 0 && j0 + C::BN - 1 < wrow0 + bd.delta - bd.wl))
+      return;
     const bool need = j0 + C::BN > lk ||
-                      (bd.wr >= 0 && j0 + C::BN - 1 > row0 + bd.delta + bd.wr) ||
-                      (bd.wl >= 0 && j0 < row_last + bd.delta - bd.wl);
+                      (bd.wr >= 0 && j0 + C::BN - 1 > wrow0 + bd.delta + bd.wr) ||
+                      (bd.wl >= 0 && j0 < wrow1 + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
     if (need) {
