@@ -15,11 +15,15 @@
 // after the ring, waits only on the DMA of the tile it is about to read.
 //
 // LDS layouts (16-byte units, c = chunk index along the row; 64 banks x 4 B):
-//   K: [row / 16][c][(row % 16) ^ 8*(c & 1)]
+//   K, V shared with K (MLA): [row / 16][c][(row % 16) ^ 8*(c & 1)]
 //      16 lanes reading 16 rows of one chunk cover 256 contiguous bytes; the
 //      parity swizzle makes the transposed V reads of a shared K/V row (MLA)
 //      conflict-free too: two 16-lane blocks reading chunks 2k and 2k+1 of
 //      8 rows land in opposite 128-byte halves.
+//   K, separate V: [row / 16][c / 4][row % 16][(c % 4) ^ ((row % 16) / 4)]
+//      the DMA reads each 64-byte row segment with 4 consecutive lanes
+//      (coalesced); 16 lanes reading 16 rows of one chunk take the 16
+//      combinations of row % 4 (16-bank group) and swizzled slot (4 banks).
 //   V (when not shared): [row / 8][c / 2][row % 8][c % 2]
 //      two 16-lane ds_read_b64_tr_b16 blocks (8 consecutive rows, one chunk
 //      pair) cover 256 contiguous bytes.
@@ -128,8 +132,8 @@ struct StreamTile {
       if (is_k) {
         constexpr int IPB = C::NCH / 4;  // instructions per 16-row block
         const int rb = inst / IPB, cq = inst % IPB;
-        const int c = cq * 4 + (lane >> 4);
-        const int r = rb * 16 + ((lane & 15) ^ ((c & 1) * 8));
+        const int c = cq * 4 + (C::VSHARED ? (lane >> 4) : k_lane_col(lane) / 16);
+        const int r = rb * 16 + (int)k_lane_row(lane);
         lds_dma16(krow(r) + c * 8, stage + inst * 1024);
       } else {
         const int vi = inst - C::K_DMA;
@@ -147,10 +151,15 @@ struct StreamTile {
   // lane's 16 bytes from the first row of a 16-row block whose rows are
   // kstride / vstride bytes apart, for the K and the (separate) V DMA.
   __device__ __forceinline__ static uint32_t k_lane_row(int lane) {
-    return (uint32_t)((lane & 15) ^ (((lane >> 4) & 1) * 8));
+    if constexpr (C::VSHARED) return (uint32_t)((lane & 15) ^ (((lane >> 4) & 1) * 8));
+    return (uint32_t)(lane >> 2);
+  }
+  __device__ __forceinline__ static uint32_t k_lane_col(int lane) {
+    if constexpr (C::VSHARED) return (uint32_t)(lane >> 4) * 16;
+    return (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16;
   }
   __device__ __forceinline__ static uint32_t k_lane_off(int lane, uint32_t kstride) {
-    return k_lane_row(lane) * kstride + (lane >> 4) * 16;
+    return k_lane_row(lane) * kstride + k_lane_col(lane);
   }
   __device__ __forceinline__ static uint32_t v_lane_off(int lane, uint32_t vstride) {
     return (uint32_t)((lane & 15) >> 1) * vstride + ((lane >> 4) * 2 + (lane & 1)) * 16;
@@ -186,19 +195,41 @@ struct StreamTile {
   // S^T for one tile.
   __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
     const int g = lane >> 4;
-    // chunk parity p = f & 1; chunk c = (f >> 1) * 8 + 2g + p sits at
-    // c * 256 + ((row % 16) ^ 8p) * 16 within a 16-row block
-    const char* kb0 = stage + g * 512 + (lane & 15) * 16;
-    const char* kb1 = stage + g * 512 + 256 + ((lane & 15) ^ 8) * 16;
+    if constexpr (C::VSHARED) {
+      // chunk parity p = f & 1; chunk c = (f >> 1) * 8 + 2g + p sits at
+      // c * 256 + ((row % 16) ^ 8p) * 16 within a 16-row block
+      const char* kb0 = stage + g * 512 + (lane & 15) * 16;
+      const char* kb1 = stage + g * 512 + 256 + ((lane & 15) ^ 8) * 16;
 #pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-      s[sb] = f32x4{};
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        s[sb] = f32x4{};
 #pragma unroll
-      for (int dq = 0; dq < C::NQ; ++dq) {
-        const int f = dq * C::DSPLIT + half;
-        const char* kb = (f & 1) ? kb1 : kb0;
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + (f >> 1) * 8) * 256);
-        s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
+        for (int dq = 0; dq < C::NQ; ++dq) {
+          const int f = dq * C::DSPLIT + half;
+          const char* kb = (f & 1) ? kb1 : kb0;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(kb + (sb * C::NCH + (f >> 1) * 8) * 256);
+          s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
+        }
+      }
+    } else {
+      // chunk c = (f >> 1) * 8 + 2g + p: block c / 4 = 2 (f >> 1) + g / 2,
+      // slot (2 (g & 1) + p) ^ ((row % 16) / 4)
+      constexpr int IPB = C::NCH / 4;
+      const int r = lane & 15, sw = (r >> 2) & 3;
+      const char* base = stage + (g >> 1) * 1024 + r * 64;
+      const char* kb0 = base + ((2 * (g & 1)) ^ sw) * 16;
+      const char* kb1 = base + ((2 * (g & 1) + 1) ^ sw) * 16;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        s[sb] = f32x4{};
+#pragma unroll
+        for (int dq = 0; dq < C::NQ; ++dq) {
+          const int f = dq * C::DSPLIT + half;
+          const char* kb = (f & 1) ? kb1 : kb0;
+          const u32x4 a =
+              *reinterpret_cast<const u32x4*>(kb + (sb * IPB + (f >> 1) * 2) * 1024);
+          s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
+        }
       }
     }
   }
