@@ -83,8 +83,12 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
 
 // LSE-weighted combine [MATE flash_attn_combine; CANN softmax_lse]. Each
 // thread owns four output columns of one row; rows are (b, t, h) with the
-// partial layout slot = b*max_splits + s, row t*hq + h.
+// partial layout slot = b*max_splits + s, row t*hq + h. All of a row's split
+// LSEs and partial outputs are loaded before any is used (unrolled over the
+// largest split count, extra splits re-reading the last one with weight 0),
+// so a thread waits for one round trip to memory instead of one per split.
 constexpr int kCombineThreads = 256;
+constexpr int kMaxSplits = 16;
 
 __global__ void __launch_bounds__(kCombineThreads)
 k_combine(CombineArgs a) {
@@ -100,29 +104,39 @@ k_combine(CombineArgs a) {
   const int t = rr / a.hq, h = rr % a.hq;
   const int ns = a.plan[2 + b + 1] - a.plan[2 + b];
   const size_t slot0 = (size_t)b * a.max_splits;
-  float mx = kNegInf;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, a.lse_part[(slot0 + s) * rows_per_b + rr]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float lse = kNegInf;
-  if (mx != kNegInf) {
-    float ref = mx;
-    float extra = 0.f;
-    if (a.sinks) {
-      const float sg = a.sinks[h];
-      ref = fmaxf(mx, sg);
-      extra = __expf(sg - ref);
+  if (ns > 0) {
+    float ls[kMaxSplits];
+    f32x4 o[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      const size_t r = (slot0 + min(s, ns - 1)) * rows_per_b + rr;
+      ls[s] = a.lse_part[r];
+      o[s] = *reinterpret_cast<const f32x4*>(a.o_part + r * a.dv + col);
     }
-    float wsum = 0.f, wsum_ref = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float ls = a.lse_part[(slot0 + s) * rows_per_b + rr];
-      const float w = __expf(ls - ref);
-      wsum += w;
-      wsum_ref += __expf(ls - mx);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(a.o_part + ((slot0 + s) * rows_per_b + rr) * a.dv + col);
-      acc += w * o;
+    float mx = kNegInf;
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) mx = fmaxf(mx, ls[s]);
+    if (mx != kNegInf) {
+      float ref = mx;
+      float extra = 0.f;
+      if (a.sinks) {
+        const float sg = a.sinks[h];
+        ref = fmaxf(mx, sg);
+        extra = __expf(sg - ref);
+      }
+      float wsum = 0.f, wsum_ref = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxSplits; ++s) {
+        const float w = s < ns ? __expf(ls[s] - ref) : 0.f;
+        wsum += w;
+        wsum_ref += s < ns ? __expf(ls[s] - mx) : 0.f;
+        acc += w * o[s];
+      }
+      acc *= 1.f / (wsum + extra);
+      lse = mx + __logf(wsum_ref);
     }
-    acc *= 1.f / (wsum + extra);
-    lse = mx + __logf(wsum_ref);
   }
   const size_t orow = ((size_t)b * a.sq + t) * a.hq + h;
   if (a.out_bf16) {
