@@ -28,6 +28,7 @@ SEED_VARLEN_PREFILL = 1002
 SEED_PAGED_DECODE = 1003
 SEED_MLA_DECODE = 1004
 SEED_SPARSE_MLA = 1005
+SEED_CHUNKED_PREFILL = 1006
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -209,6 +210,18 @@ def varlen_kvcache(seed: int, lens_q, lens_new, lens_cache, hq: int = 32, hkv: i
     return DenseKV(q, k, v, cu_q, cu_k, "bf16", scale if scale is not None else 1.0 / np.sqrt(d),
                    causal, tuple(window), sinks, k_cache, v_cache, table,
                    lens_cache.astype(np.int32), page)
+
+
+def chunked_prefill(seed: int = SEED_CHUNKED_PREFILL, nseq: int = 8, chunk: int = 1024,
+                    lo: int = 1024, hi: int = 8192, hq: int = 32, hkv: int = 8, d: int = 128,
+                    page: int = 64) -> DenseKV:
+    """Chunked causal GQA prefill: nseq sequences, each a chunk of `chunk` new
+    tokens after a cached prefix of U[lo, hi] tokens in a paged cache."""
+    rng = np.random.default_rng(seed)
+    lens_cache = rng.integers(lo, hi, endpoint=True, size=nseq)
+    lens = np.full(nseq, chunk)
+    return varlen_kvcache(int(rng.integers(0, 2**63 - 1)), lens, lens, lens_cache, hq=hq,
+                          hkv=hkv, d=d, page=page, causal=True)
 
 
 @dataclasses.dataclass

@@ -3,9 +3,10 @@
 Headline: varlen causal GQA prefill (8 sequences with lengths U[512, 4096],
 Hq=32, Hkv=8, D=128, bf16), in attention TFLOP/s. One step = one
 attn_fwd_varlen call over the whole packed batch (the single kernel of the
-prefill path). The same JSON line carries the decode-side measurements as
+prefill path). The same JSON line carries the other workloads as
 `secondary` entries: paged GQA decode (KV-read GB/s, step = plan + split
-decode + combine), MLA-absorbed paged decode and sparse MLA with sinks.
+decode + combine), MLA-absorbed paged decode, chunked prefill over a paged
+cache and sparse MLA with sinks.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Every timed region is bracketed by torch.cuda.synchronize() and
@@ -237,6 +238,32 @@ def bench_sparse(steps, warmup):
                 gathered_gbs=gathered / (ms * 1e-3) / 1e9)
 
 
+def bench_chunked(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.chunked_prefill()
+    lq = np.diff(w.cu_seqlens_q)
+    lc = w.cache_seqlens.astype(np.int64)
+    t = dict(q=dev(w.q), k=dev(w.k), v=dev(w.v), cq=dev(w.cu_seqlens_q), ck=dev(w.cu_seqlens_k),
+             kc=dev(w.k_cache), vc=dev(w.v_cache), bt=dev(w.block_table),
+             lens=dev(w.cache_seqlens))
+    hq, d = w.q.shape[1], w.q.shape[2]
+    out = torch.empty((int(lq.sum()), hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, int(lq.sum())), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.attn_fwd_varlen_kvcache(t["q"], t["k"], t["v"], t["cq"], t["ck"], t["kc"], t["vc"],
+                                  t["bt"], t["lens"], int(lq.max()), w.scale, True, out=out,
+                                  lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    # query t of a chunk sees the cache and the chunk's rows 0..t
+    flops = sum(4.0 * d * hq * (int(n) * int(c) + int(n) * (int(n) + 1) / 2)
+                for n, c in zip(lq, lc))
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lc=lc.tolist())
+
+
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "k_varlen_bf16_d128_traffic.txt")
 # the sources the prefill kernel is compiled from (its translation unit)
 PREFILL_SOURCES = ("kernels_prefill.hip", "prefill_bf16.h", "device_common.h", "launch.h")
@@ -342,7 +369,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
-    ap.add_argument("--only", default="prefill,decode,mla,sparse")
+    ap.add_argument("--only", default="prefill,decode,mla,chunked,sparse")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,6 +445,19 @@ def main():
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": mla["tflops_kernel"] / PEAK_BF16_TFLOPS, "traffic": None,
                          "kernel": "k_decode (MLA)", "kernel_ms": mla["ms_kernel"]}})
+    if "chunked" in only:
+        log("chunked prefill ...")
+        ch = bench_chunked(args.steps, args.warmup)
+        log(f"chunked {ch['ms']:.3f} ms {ch['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "chunked prefill TFLOP/s (cache + new K/V)", "value": ch["tflops"],
+            "unit": "TFLOP/s", "ms_per_step": ch["ms"],
+            "workload": "chunked causal GQA prefill: 8 sequences, 1024 new tokens each after a "
+                        f"paged cache of U[1024,8192] tokens (drawn {ch['lc']}), page 64, "
+                        "Hq=32, Hkv=8, D=128, bf16; attn_fwd_varlen_kvcache (seed 1006)",
+            "roofline": {"bound": "mfma", "achieved": ch["tflops"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ch["tflops"] / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "k_varlen_bf16 (cache + current, D=128)"}})
     if "sparse" in only:
         log("sparse mla ...")
         sp = bench_sparse(args.steps, args.warmup)

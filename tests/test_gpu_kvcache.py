@@ -129,3 +129,16 @@ def test_kvcache_deterministic():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+def test_kvcache_chunked_workload():
+    """The benchmarked chunked-prefill workload (seed 1006: 8 chunks of 1024
+    tokens after caches of U[1024, 8192] tokens, page 64, Hq=32, Hkv=8,
+    D=128, causal), in the launch configuration bench.py times; sequences 0
+    and 4 compared element by element."""
+    w = inputs.chunked_prefill()
+    log("case kvcache_chunked_workload caches", w.cache_seqlens.tolist())
+    o, lse = run_kvcache(w)
+    torch.cuda.synchronize()
+    ro, rl = oracle_kvcache(w, seqs=[0, 4])
+    compare("kvcache_chunked_workload", o, lse, ro, rl, TOL_O_BF16)
