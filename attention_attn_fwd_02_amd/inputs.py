@@ -29,6 +29,7 @@ SEED_PAGED_DECODE = 1003
 SEED_MLA_DECODE = 1004
 SEED_SPARSE_MLA = 1005
 SEED_CHUNKED_PREFILL = 1006
+SEED_PAGED_DECODE_FP8 = 1007
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -265,6 +266,96 @@ def _paged_draw(rng, lens, sq, hq, hkv, d, dv, page, shared_kv, causal, scale, w
     sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
     return Paged(q, k_cache, v_cache, table, lens.astype(np.int32), page, dv,
                  scale if scale is not None else 1.0 / np.sqrt(d), causal, sinks)
+
+
+# FP8 codes: (exponent bits, mantissa bits, bias, largest finite value) of the
+# OCP formats e4m3fn and e5m2.
+_FP8 = {"e4m3": (4, 3, 7, 448.0), "e5m2": (5, 2, 15, 57344.0)}
+
+
+def fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
+    """Rounds values to the nearest code of an FP8 format (ties to even,
+    saturating at the largest finite value) and returns the uint8 codes."""
+    ebits, mbits, bias, vmax = _FP8[fmt]
+    x = np.clip(np.asarray(x, dtype=np.float64), -vmax, vmax)
+    neg = np.signbit(x)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, 1 - bias)                         # subnormals share the least exponent
+    q = np.round(a / np.exp2(e - mbits))                # mantissa with its leading bit
+    carry = q >= 2 ** (mbits + 1)
+    e = np.where(carry, e + 1, e)
+    q = np.where(carry, q / 2, q)
+    normal = q >= 2 ** mbits
+    efield = np.where(normal, e + bias, 0).astype(np.int64)
+    mfield = np.where(normal, q - 2 ** mbits, q).astype(np.int64)
+    return ((neg.astype(np.int64) << 7) | (efield << mbits) | mfield).astype(np.uint8)
+
+
+@dataclasses.dataclass
+class PagedFP8:
+    """Decode against a paged FP8 cache: q (B,Sq,Hq,D), k_cache (P,page,Hkv,D)
+    and v_cache (P,page,Hkv,Dv) uint8 codes of format fmt; descales float32
+    (B, Hkv) or None."""
+    q: np.ndarray
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    fmt: str
+    q_descale: np.ndarray | None
+    k_descale: np.ndarray | None
+    v_descale: np.ndarray | None
+    block_table: np.ndarray
+    cache_seqlens: np.ndarray
+    page_size: int
+    scale: float
+    causal: bool
+
+    @property
+    def batch(self):
+        return self.q.shape[0]
+
+
+def paged_fp8(seed: int, lens, fmt: str = "e4m3", sq: int = 1, hq: int = 32, hkv: int = 8,
+              d: int = 128, page: int = 64, causal: bool = False, descale: bool = True,
+              spare_pages: int = 0) -> PagedFP8:
+    """N(0,1) Q, K, V stored as FP8 codes of x / descale, with descales drawn
+    per (batch, KV head) from U[0.25, 4] (or none). Draw order: descales, Q,
+    K cache, V cache (N(0,1) float32 draws), page permutation."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, dtype=np.int64)
+    b = len(lens)
+    ds = [rng.uniform(0.25, 4.0, size=(b, hkv)).astype(np.float32) if descale else None
+          for _ in range(3)]
+    nblk = (lens + page - 1) // page
+    pool = max(1, int(nblk.sum()) + spare_pages)
+    grp = hq // hkv
+    qd = np.ones((b, hkv), np.float32) if ds[0] is None else ds[0]
+    q = rng.standard_normal((b, sq, hq, d), dtype=np.float32)
+    q8 = fp8_bits(q / np.repeat(qd, grp, axis=1)[:, None, :, None], fmt)
+    kc = rng.standard_normal((pool, page, hkv, d), dtype=np.float32)
+    vc = rng.standard_normal((pool, page, hkv, d), dtype=np.float32)
+    table, _ = _paged_table(rng, lens, page)
+    # each page belongs to one sequence: quantize it with that sequence's descales
+    owner = np.zeros(pool, np.int64)
+    for bi, n in enumerate(nblk):
+        owner[table[bi, :n]] = bi
+    kd = np.ones((b, hkv), np.float32) if ds[1] is None else ds[1]
+    vd = np.ones((b, hkv), np.float32) if ds[2] is None else ds[2]
+    k8 = fp8_bits(kc / kd[owner][:, None, :, None], fmt)
+    v8 = fp8_bits(vc / vd[owner][:, None, :, None], fmt)
+    return PagedFP8(q8, k8, v8, fmt, ds[0], ds[1], ds[2], table, lens.astype(np.int32), page,
+                    1.0 / np.sqrt(d), causal)
+
+
+def paged_decode_fp8(seed: int = SEED_PAGED_DECODE_FP8, batch: int = 64, lo: int = 1024,
+                     hi: int = 32768, page: int = 64, hq: int = 32, hkv: int = 8,
+                     d: int = 128, fmt: str = "e4m3") -> PagedFP8:
+    """GQA decode with an FP8 cache: the paged-decode shape (one query token,
+    cache_seqlens U[lo, hi], page 64, Hq=32, Hkv=8, D=128) with e4m3 Q/K/V
+    codes and per-(batch, KV head) descales."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(lo, hi, endpoint=True, size=batch)
+    return paged_fp8(int(rng.integers(0, 2**63 - 1)), lens, fmt, 1, hq, hkv, d, page)
 
 
 def paged_decode(seed: int = SEED_PAGED_DECODE, batch: int = 64, lo: int = 1024,

@@ -1,0 +1,87 @@
+"""FP8 inputs for the float64 oracle: the two 8-bit float formats and
+attention over descaled FP8 Q / K / V.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module. It shares nothing with the HIP path.
+
+Source: [MATE] "Attention" API page, FMHA forward dtype notes. The varlen and
+KV-cache forward paths take float8_e4m3fn and float8_e5m2 inputs; optional
+float32 q_descale, k_descale and v_descale tensors of shape
+(batch_size, num_heads_kv) scale them; FP8 inputs give bfloat16 outputs. The
+real value of an element is its FP8 value times the descale of its (batch,
+KV head); for Q that is the KV head its query head reads (the grouping
+(N2, N1/N2) of the MindSpore sparse_flash_attention page), which is the plain
+reading of a query descale indexed by num_heads_kv.
+
+The formats themselves are the OCP 8-bit floating-point formats the dtype
+names refer to (sign, exponent, mantissa bits; value
+(-1)^s 2^(e-bias) (1 + m/2^M) for e > 0 and (-1)^s 2^(1-bias) m/2^M for e = 0):
+  e4m3fn: 4 exponent bits (bias 7), 3 mantissa bits, no infinities, S.1111.111
+          is NaN, largest finite 448;
+  e5m2:   5 exponent bits (bias 15), 2 mantissa bits, exponent 31 is infinity
+          (mantissa 0) or NaN, largest finite 57344.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle.attention import _group, attend_rows, gather_paged, visible_band
+
+FORMATS = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}   # exponent bits, mantissa bits, bias
+
+
+def decode(bits, fmt):
+    """float64 values of uint8 FP8 codes, from the bit-field definition."""
+    ebits, mbits, bias = FORMATS[fmt]
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> mbits) & ((1 << ebits) - 1)
+    m = b & ((1 << mbits) - 1)
+    normal = sign * np.ldexp(1.0 + m / float(1 << mbits), (e - bias).astype(np.int64))
+    sub = sign * np.ldexp(m / float(1 << mbits), 1 - bias)
+    val = np.where(e == 0, sub, normal)
+    top = (1 << ebits) - 1
+    if fmt == "e4m3":
+        val = np.where((e == top) & (m == (1 << mbits) - 1), np.nan, val)
+    else:
+        val = np.where((e == top) & (m == 0), sign * np.inf, val)
+        val = np.where((e == top) & (m != 0), np.nan, val)
+    return val
+
+
+def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_table,
+                        cache_seqlens, page_size, scale, causal=False, sinks=None,
+                        batches=None):
+    """Decode against a paged FP8 cache.          [MATE FMHA FP8 dtype notes]
+
+    q8 (B, Sq, Hq, D), k8 (P, page, Hkv, D), v8 (P, page, Hkv, Dv) uint8 codes
+    of format fmt ("e4m3" or "e5m2"); descales float (B, Hkv) or None (= 1).
+    The real inputs are decode(x8) * descale[b, kv head]; the attention is
+    then the paged decode of the plain definition (sequence b sees keys
+    0..cache_seqlens[b]-1, bottom-right causal). Returns O (B, Sq, Hq, Dv)
+    and LSE (B, Hq, Sq).
+    """
+    bsz, sq, hq, _ = q8.shape
+    hkv = k8.shape[2]
+    g = _group(hq, hkv)
+    dv = v8.shape[3]
+    one = np.ones((bsz, hkv))
+    qd = one if q_descale is None else np.asarray(q_descale, np.float64)
+    kd = one if k_descale is None else np.asarray(k_descale, np.float64)
+    vd = one if v_descale is None else np.asarray(v_descale, np.float64)
+    o = np.full((bsz, sq, hq, dv), np.nan)
+    lse = np.full((bsz, hq, sq), np.nan)
+    for b in (range(bsz) if batches is None else batches):
+        lk = int(cache_seqlens[b])
+        kr = decode(gather_paged(k8, block_table, b, lk, page_size), fmt)
+        vr = decode(gather_paged(v8, block_table, b, lk, page_size), fmt)
+        vis = visible_band(sq, lk, causal)
+        for h in range(hq):
+            kh = h // g
+            qh = decode(q8[b, :, h], fmt) * qd[b, kh]
+            sink = None if sinks is None else float(sinks[h])
+            ob, lb = attend_rows(qh, kr[:, kh] * kd[b, kh], vr[:, kh] * vd[b, kh], scale, vis,
+                                 sink)
+            o[b, :, h] = ob
+            lse[b, h] = lb
+    return o, lse

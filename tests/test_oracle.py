@@ -13,6 +13,7 @@ import pytest
 from attention_attn_fwd_02_amd import inputs
 from oracle import attention as orc
 from oracle import brute
+from oracle import fp8 as ofp8
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.json")
 
@@ -334,6 +335,142 @@ def test_kvcache_brute_force():
 
 def test_kvcache_special_cases():
     check_kvcache_special_cases()
+
+
+# ------------------------------------------------------------------ FP8 inputs
+def check_fp8_decode_library():
+    """Every code of both formats against torch's float8 dtypes (a library
+    conversion): equal values, NaN exactly where torch has NaN."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    for fmt, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        ref = torch.from_numpy(codes).view(dt).to(torch.float64).numpy()
+        got = ofp8.decode(codes, fmt)
+        assert np.array_equal(np.isnan(ref), np.isnan(got)), fmt
+        fin = ~np.isnan(ref)
+        assert np.array_equal(ref[fin], got[fin]), fmt
+        assert np.array_equal(np.signbit(ref[fin]), np.signbit(got[fin])), fmt
+
+
+def check_fp8_decode_values():
+    """Codes whose values follow from the format definitions by hand."""
+    known = {"e4m3": {0x38: 1.0, 0xB8: -1.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+                      0x08: 2.0 ** -6, 0x3C: 1.5, 0x00: 0.0},
+             "e5m2": {0x3C: 1.0, 0xBC: -1.0, 0x7B: 57344.0, 0x7C: math.inf, 0xFC: -math.inf,
+                      0x01: 2.0 ** -16, 0x04: 2.0 ** -14, 0x3E: 1.5}}
+    for fmt, table in known.items():
+        for code, val in table.items():
+            assert ofp8.decode(np.array([code], np.uint8), fmt)[0] == val, (fmt, hex(code))
+    assert np.isnan(ofp8.decode(np.array([0x7F, 0xFF], np.uint8), "e4m3")).all()
+    assert np.isnan(ofp8.decode(np.array([0x7D, 0x7F], np.uint8), "e5m2")).all()
+    assert np.signbit(ofp8.decode(np.array([0x80], np.uint8), "e4m3")[0])
+
+
+def _fp8_case(seed, fmt, descale=True):
+    return inputs.paged_fp8(seed, [5, 3], fmt, sq=2, hq=4, hkv=2, d=4, page=4, causal=True,
+                            descale=descale)
+
+
+def check_fp8_attention_brute():
+    """Brute force on values dequantized by an independent path (torch's
+    float8 conversion times the descale of (batch, h // (Hq/Hkv)))."""
+    import torch
+    for fmt, dt in (("e4m3", torch.float8_e4m3fn), ("e5m2", torch.float8_e5m2)):
+        w = _fp8_case(61, fmt)
+        o, lse = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, fmt, w.q_descale,
+                                          w.k_descale, w.v_descale, w.block_table,
+                                          w.cache_seqlens, w.page_size, w.scale, True)
+        deq = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(dt).to(torch.float64).numpy()
+        bsz, sq, hq, _ = w.q.shape
+        grp = hq // w.k_cache.shape[2]
+        for b in range(bsz):
+            n = int(w.cache_seqlens[b])
+            rows = [(w.block_table[b, j // w.page_size], j % w.page_size) for j in range(n)]
+            for h in range(hq):
+                g = h // grp
+                qs = [list(deq(w.q[b, t, h]) * float(w.q_descale[b, g])) for t in range(sq)]
+                ks = [list(deq(w.k_cache[p, s, g]) * float(w.k_descale[b, g])) for p, s in rows]
+                vs = [list(deq(w.v_cache[p, s, g]) * float(w.v_descale[b, g])) for p, s in rows]
+                ob, lb = brute.rows(qs, ks, vs, w.scale, visible=lambda t, j: j <= t + n - sq)
+                for t in range(sq):
+                    assert abs(lse[b, h, t] - lb[t]) <= 1e-12
+                    np.testing.assert_allclose(o[b, t, h], ob[t], rtol=0, atol=1e-12)
+
+
+def check_fp8_descale_identities():
+    """Only the product of the Q and K descales enters the scores; the V
+    descale scales O and leaves LSE unchanged."""
+    w = _fp8_case(62, "e4m3")
+    args = (w.block_table, w.cache_seqlens, w.page_size, w.scale, True)
+    o, lse = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, "e4m3", w.q_descale,
+                                      w.k_descale, w.v_descale, *args)
+    o2, l2 = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, "e4m3", w.q_descale * 2,
+                                      w.k_descale / 2, w.v_descale.astype(np.float64) * 3,
+                                      *args)
+    np.testing.assert_allclose(l2, lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2, o * 3, rtol=1e-12, atol=1e-12)
+    # unit descales are the plain paged decode of the decoded codes
+    o1, l1 = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, "e4m3", None, None, None, *args)
+    o3, l3 = orc.attention_paged(ofp8.decode(w.q, "e4m3"), ofp8.decode(w.k_cache, "e4m3"),
+                                 ofp8.decode(w.v_cache, "e4m3"), *args)
+    np.testing.assert_allclose(o1, o3, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l3, rtol=0, atol=1e-14)
+
+
+def test_fp8_decode_library():
+    check_fp8_decode_library()
+
+
+def test_fp8_decode_values():
+    check_fp8_decode_values()
+
+
+def test_fp8_attention_brute():
+    check_fp8_attention_brute()
+
+
+def test_fp8_descale_identities():
+    check_fp8_descale_identities()
+
+
+FP8_PINS = [check_fp8_decode_library, check_fp8_decode_values, check_fp8_attention_brute,
+            check_fp8_descale_identities]
+
+
+def _fp8_mutants():
+    base_decode = ofp8.decode
+    base_attn = ofp8.attention_paged_fp8
+
+    def decode_bias_off(bits, fmt):
+        return base_decode(bits, fmt) * (2.0 if fmt == "e4m3" else 1.0)
+
+    def decode_no_inf(bits, fmt):
+        v = base_decode(bits, fmt)
+        return np.where(np.isinf(v), np.nan, v)
+
+    def q_descale_by_query_head(q8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, **kw):
+        qd = None if q_descale is None else np.asarray(q_descale)[:, ::-1]
+        return base_attn(q8, k8, v8, fmt, qd, k_descale, v_descale, *rest, **kw)
+
+    def v_descale_on_k(q8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, **kw):
+        return base_attn(q8, k8, v8, fmt, q_descale, v_descale, k_descale, *rest, **kw)
+
+    return [("decode", decode_bias_off), ("decode", decode_no_inf),
+            ("attention_paged_fp8", q_descale_by_query_head),
+            ("attention_paged_fp8", v_descale_on_k)]
+
+
+@pytest.mark.parametrize("i", range(4))
+def test_fp8_pins_catch_planted_mistakes(monkeypatch, i):
+    name, fn = _fp8_mutants()[i]
+    monkeypatch.setattr(ofp8, name, fn)
+    caught = []
+    for pin in FP8_PINS:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"mutant {fn.__name__} of {name} passed every pin"
 
 
 def test_mate_mla_example_shape():
