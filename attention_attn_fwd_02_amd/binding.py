@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn_mi355.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EEMPTY, ATTN_EHIP = range(5)
-ATTN_BF16, ATTN_F32 = 0, 1
+ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_FP8_E5M2 = 0, 1, 2, 3
+FP8_FORMATS = {"e4m3": ATTN_FP8_E4M3, "e5m2": ATTN_FP8_E5M2}
 
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -37,6 +38,8 @@ _SIGNATURES = {
     "attn_plan_splits": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                _P, _I, _P, _P, _P]),
+    "attn_decode_paged_fp8": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                                   _P, _P, _F, _I, _P, _I, _P, _P, _P]),
     "attn_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P]),
     "mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
     "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
@@ -218,6 +221,34 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max
     return o_partial, lse_partial
 
 
+def attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
+                          scale, fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
+                          causal=False, o_partial=None, lse_partial=None):
+    """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) uint8 FP8 codes of fmt ("e4m3" or
+    "e5m2"); descales float32 (B,Hkv) or None. Returns partials as
+    attn_decode_paged."""
+    _dev(q, k_cache, v_cache, dtype=torch.uint8)
+    _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
+    _dev(q_descale, k_descale, v_descale, dtype=torch.float32)
+    b, sq, hq, d = q.shape
+    page, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    for t in (q_descale, k_descale, v_descale):
+        if t is not None and tuple(t.shape) != (b, hkv):
+            raise ValueError("descales must be (batch, hkv)")
+    if o_partial is None:
+        o_partial = torch.empty((b * max_splits, sq * hq, dv), dtype=torch.float32,
+                                device=q.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((b * max_splits, sq * hq), dtype=torch.float32, device=q.device)
+    _dev(o_partial, lse_partial, dtype=torch.float32)
+    _check(load().attn_decode_paged_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), b, sq, hq, hkv, d, dv, page, FP8_FORMATS[fmt], _ptr(q_descale),
+        _ptr(k_descale), _ptr(v_descale), float(scale), int(bool(causal)), _ptr(plan),
+        int(max_splits), _ptr(o_partial), _ptr(lse_partial), _stream()))
+    return o_partial, lse_partial
+
+
 def attn_combine(o_partial, lse_partial, plan, batch, seqlen_q, hq, max_splits, sinks=None,
                  out_dtype=torch.bfloat16, out=None, lse=None, return_lse=True):
     _dev(o_partial, lse_partial, dtype=torch.float32)
@@ -322,6 +353,23 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=
     op, lp = attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
                                scale, causal)
     out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits, sinks, out_dtype)
+    return out, lse, plan
+
+
+def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale, fmt="e4m3",
+                     q_descale=None, k_descale=None, v_descale=None, causal=False,
+                     max_splits=16, waves=8, min_blocks=2, num_cu=None):
+    """plan -> attn_decode_paged_fp8 -> attn_combine (bfloat16 out)."""
+    b, sq, hq, _ = q.shape
+    hkv = k_cache.shape[2]
+    rows = sq * (hq // max(1, hkv))
+    upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
+    plan = attn_plan_splits(cache_seqlens, k_cache.shape[1], upb, num_cu or _num_cu(q.device),
+                            waves, max_splits, min_blocks)
+    op, lp = attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan,
+                                   max_splits, scale, fmt, q_descale, k_descale, v_descale,
+                                   causal)
+    out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
     return out, lse, plan
 
 

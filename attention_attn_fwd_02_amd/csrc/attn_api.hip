@@ -85,7 +85,7 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
           "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
-  attn::VarlenArgs a;
+  attn::VarlenArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -141,7 +141,7 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
-  attn::VarlenArgs a;
+  attn::VarlenArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -213,7 +213,7 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
-  attn::DecodeArgs a;
+  attn::DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;
   a.vc = v_cache;
@@ -234,6 +234,58 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   return hip_status(attn::launch_decode_gqa(a, as_stream(stream)), "attn_decode_paged launch");
 }
 
+int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int32_t max_pages_per_seq,
+                              const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                              int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                              int32_t fp8_format, const float* q_descale,
+                              const float* k_descale, const float* v_descale, float scale,
+                              int32_t causal, const int32_t* plan, int32_t max_splits,
+                              float* o_partial, float* lse_partial, void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
+              max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(q && k_cache && v_cache && block_table && cache_seqlens && plan && o_partial &&
+              lse_partial,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(fp8_format == ATTN_FP8_E4M3 || fp8_format == ATTN_FP8_E5M2, ATTN_EUNSUPPORTED,
+          "fp8_format %d (expected ATTN_FP8_E4M3 or ATTN_FP8_E5M2)", fp8_format);
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
+          d, dv);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.page = page_size;
+  a.causal = causal ? 1 : 0;
+  a.max_splits = max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  return hip_status(attn::launch_decode_gqa_fp8(a, fp8_format == ATTN_FP8_E4M3 ? 1 : 2,
+                                                as_stream(stream)),
+                    "attn_decode_paged_fp8 launch");
+}
+
 int32_t attn_combine(const float* o_partial, const float* lse_partial, const int32_t* plan,
                      int32_t batch, int32_t seqlen_q, int32_t hq, int32_t dv, int32_t max_splits,
                      const float* sinks, int32_t out_dtype, void* out, float* lse,
@@ -245,7 +297,7 @@ int32_t attn_combine(const float* o_partial, const float* lse_partial, const int
   REQUIRE(out_dtype == ATTN_BF16 || out_dtype == ATTN_F32, ATTN_EUNSUPPORTED, "out_dtype %d",
           out_dtype);
   REQUIRE(dv % 4 == 0 && dv <= 1024, ATTN_EUNSUPPORTED, "dv must be a multiple of 4, <= 1024");
-  attn::CombineArgs a;
+  attn::CombineArgs a{};
   a.o_part = o_partial;
   a.lse_part = lse_partial;
   a.plan = plan;
@@ -276,7 +328,7 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
           "scale must be positive and finite");
   REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
-  attn::DecodeArgs a;
+  attn::DecodeArgs a{};
   a.q = q;
   a.kc = kv_cache;
   a.vc = nullptr;
@@ -314,7 +366,7 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
           "grid too large");
   REQUIRE((long)seqlen_k * 576 * 2 <= (1L << 32), ATTN_EUNSUPPORTED,
           "seqlen_k %d above %ld (row byte offsets are 32-bit)", seqlen_k, (1L << 32) / 1152);
-  attn::SparseArgs a;
+  attn::SparseArgs a{};
   a.q = q;
   a.kv = kv;
   a.idx = sparse_indices;

@@ -47,18 +47,25 @@ struct DmaSrc {
 // with identical scores. Only the even wave of a pair issues DMA. This halves
 // the registers a wave needs for wide heads (MLA: 576 / 512), so two waves
 // fit on each SIMD and hide each other's LDS latency.
-template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1>
+//
+// FP8 = 1 (e4m3fn) or 2 (e5m2): Q, K and V hold 8-bit codes. Tiles reach LDS
+// as bytes (half the traffic) and every fragment is widened to bfloat16 as it
+// is read (exact), so the MFMAs, softmax and partial outputs are those of the
+// bfloat16 path; descales are applied to the scores and to O.
+template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1, int FP8_ = 0>
 struct StreamCfg {
   static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
   static constexpr bool VSHARED = VSHARED_;
   static constexpr int DSPLIT = DSPLIT_;
+  static constexpr int FP8 = FP8_;
+  static constexpr int EB = FP8 ? 1 : 2;  // bytes per element in memory and LDS
   static constexpr int BN = 32, R = 16;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW / DSPLIT * R;
   static constexpr int DMA_WAVES = NW / DSPLIT;
   static constexpr int NCH = D / 8;
-  static constexpr int K_BYTES = BN * D * 2;
-  static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * 2;
+  static constexpr int K_BYTES = BN * D * EB;
+  static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * EB;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_DMA = K_BYTES / 1024;
   static constexpr int V_DMA = V_BYTES / 1024;
@@ -74,6 +81,8 @@ struct StreamCfg {
   static_assert(VSHARED || (NCH / 2) % 4 == 0, "V layout needs whole instructions per row block");
   static_assert(VSHARED ? DV <= D : DV == D, "value width");
   static_assert(DMA_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(FP8 == 0 || (D == 128 && DV == 128 && !VSHARED && DSPLIT == 1),
+                "FP8 tiles: D = Dv = 128, separate V, whole head per wave");
 };
 
 template <class C>
@@ -111,6 +120,56 @@ struct StreamTile {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + q_chunk(i, half, g) * 8);
       qf[i] = as_bf16x8(v);
+    }
+  }
+
+  // FP8 Q: fragment dq holds chunk dq * 4 + g (8 codes), widened to bf16.
+  __device__ __forceinline__ void load_q8(const uint8_t* qrow, int lane) {
+    const int g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < C::NQ; ++i) {
+      u32x2 v = {0u, 0u};
+      if (qrow) v = *reinterpret_cast<const u32x2*>(qrow + (i * 4 + g) * 8);
+      qf[i] = fp8x8_to_bf16<C::FP8>(v);
+    }
+  }
+
+  // FP8 LDS layouts: tile rows of 128 bytes; the 16-byte unit u of row r is
+  // stored at unit u ^ f(r), with
+  //   K: f(r) = (r / 2) % 8              (16 consecutive rows of one block)
+  //   V: f(r) = (r / 2) % 4 + 4 (r / 16)  (rows 4g..4g+3 and 16+4g..16+4g+3)
+  // so that the 32 lanes of each read cycle hit 64 distinct banks. A DMA
+  // instruction fills 8 rows: lane l reads 16 bytes of row l / 8 (8 lanes
+  // per 128-byte row, coalesced); its unit depends on the instruction's rows
+  // through one bit, hence two lane offsets each for K and V.
+  __device__ __forceinline__ static int swz8_k(int r) { return (r >> 1) & 7; }
+  __device__ __forceinline__ static int swz8_v(int r) { return ((r >> 1) & 3) | ((r >> 4) << 2); }
+  // lane offsets for instructions whose 8-row groups r8 have (r8 & 1) = hi
+  // (K) or (r8 >> 1) = hi (V); rows `stride` bytes apart
+  __device__ __forceinline__ static uint32_t lane_off8(int lane, uint32_t stride, int hi) {
+    return (uint32_t)(lane >> 3) * stride + (uint32_t)((lane & 7) ^ (hi * 4 + (lane >> 4))) * 16;
+  }
+  // Saddr form: kbase(r8) / vbase(r8) give the wave-uniform pointer of tile
+  // row 8 r8 (r8 = 0..3; rows 8 r8 .. 8 r8 + 7 are `stride` bytes apart).
+  template <class KB, class VB>
+  __device__ __forceinline__ static void dma_tile8_sv(char* stage, KB kbase, VB vbase,
+                                                      uint32_t koff0, uint32_t koff1,
+                                                      uint32_t voff0, uint32_t voff1) {
+#pragma unroll
+    for (int r8 = 0; r8 < 4; ++r8)
+      lds_dma16_sv(kbase(r8), (r8 & 1) ? koff1 : koff0, stage + r8 * 1024);
+#pragma unroll
+    for (int r8 = 0; r8 < 4; ++r8)
+      lds_dma16_sv(vbase(r8), (r8 >> 1) ? voff1 : voff0, stage + C::K_BYTES + r8 * 1024);
+  }
+  // Per-lane form: krow(r) / vrow(r) are the byte addresses of tile row r.
+  template <class KRow, class VRow>
+  __device__ __forceinline__ static void dma_tile8(char* stage, KRow krow, VRow vrow, int lane) {
+#pragma unroll
+    for (int r8 = 0; r8 < 4; ++r8) {
+      const int r = r8 * 8 + (lane >> 3);
+      lds_dma16(krow(r) + ((lane & 7) ^ swz8_k(r)) * 16, stage + r8 * 1024);
+      lds_dma16(vrow(r) + ((lane & 7) ^ swz8_v(r)) * 16, stage + C::K_BYTES + r8 * 1024);
     }
   }
 
@@ -195,7 +254,23 @@ struct StreamTile {
   // S^T for one tile.
   __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
     const int g = lane >> 4;
-    if constexpr (C::VSHARED) {
+    if constexpr (C::FP8) {
+      // key r = lane % 16 of block sb, chunk dq * 4 + g: unit 2 dq + g / 2,
+      // half g % 2; stored at unit (2 dq) ^ (g / 2) ^ ((r / 2) % 8)
+      const int r = lane & 15;
+      const int fl = (g >> 1) ^ swz8_k(r);
+      const char* base = stage + r * 128 + (g & 1) * 8;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        s[sb] = f32x4{};
+#pragma unroll
+        for (int dq = 0; dq < C::NQ; ++dq) {
+          const u32x2 w =
+              *reinterpret_cast<const u32x2*>(base + sb * 16 * 128 + ((2 * dq) ^ fl) * 16);
+          s[sb] = M::mma(fp8x8_to_bf16<C::FP8>(w), qf[dq], s[sb]);
+        }
+      }
+    } else if constexpr (C::VSHARED) {
       // chunk parity p = f & 1; chunk c = (f >> 1) * 8 + 2g + p sits at
       // c * 256 + ((row % 16) ^ 8p) * 16 within a 16-row block
       const char* kb0 = stage + g * 512 + (lane & 15) * 16;
@@ -304,7 +379,20 @@ struct StreamTile {
     const int g = lane >> 4, i = lane & 15;
     const u32x4 pv4 = {pk[0], pk[1], pk[2], pk[3]};
     const bf16x8 b = as_bf16x8(pv4);
-    if constexpr (C::VSHARED) {
+    if constexpr (C::FP8) {
+      // The B operand (P) of lane group g holds keys 4g..4g+3 and
+      // 16+4g..16+4g+3 (the S^T accumulator layout of the two 16-key
+      // blocks); the A operand must list the same keys: lane i of block g
+      // receives V[key k_j][dv ob*16 + i], k_j = (j % 4) + 4g + 16 (j / 4),
+      // by addressing row k_{i/2}, bytes ob*16 + 8 (i % 2) .. + 7.
+      const int jj = i >> 1;
+      const int row = (jj & 3) + 4 * g + 16 * (jj >> 2);
+      const int fv = swz8_v(row);
+      const char* vb = stage + C::K_BYTES + row * 128 + (i & 1) * 8;
+#pragma unroll
+      for (int ob = 0; ob < C::NOB; ++ob)
+        o[ob] = M::mma(fp8x8_to_bf16<C::FP8>(lds_read_tr8(vb + (ob ^ fv) * 16)), b, o[ob]);
+    } else if constexpr (C::VSHARED) {
       const int par = (i >> 1) & 1;
       const char* vb = stage + (par * 256 + ((g * 4 + (i >> 2)) ^ (par * 8)) * 16 + (i & 1) * 8) +
                        half * C::NOB * 2 * 256;

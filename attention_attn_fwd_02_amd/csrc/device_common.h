@@ -4,6 +4,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 #include <utility>
 
 namespace attn {
@@ -128,6 +129,34 @@ __device__ __forceinline__ s16x4 lds_read_tr(const bf16_t* p) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Transposing read of 8-bit elements (ds_read_b64_tr_b8). Within each block of
+// 16 lanes, lane m addresses 8 bytes; lane i receives byte i % 8 of the bytes
+// lane 2j + i/8 addressed, for j = 0..7 (so if lane m addresses row m/2,
+// bytes 8(m%2) .. 8(m%2)+7 of an 8 x 16 byte tile, lane i gets column i).
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p)));
+}
+
+// Eight FP8 codes (bytes 0..7 of w) -> eight bfloat16 values, exactly (every
+// e4m3 / e5m2 value is a bfloat16 value): v_cvt_scalef32_pk_bf16_{fp8,bf8}
+// with scale 1, two codes per instruction. FMT 1 = e4m3fn, 2 = e5m2.
+template <int FMT>
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  auto cvt = [](uint32_t x, auto hi) {
+    if constexpr (FMT == 1)
+      return __builtin_bit_cast(uint32_t,
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, decltype(hi)::value));
+    else
+      return __builtin_bit_cast(uint32_t,
+                                __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(x, 1.0f, decltype(hi)::value));
+  };
+  const u32x4 r = {cvt(w[0], std::false_type{}), cvt(w[0], std::true_type{}),
+                   cvt(w[1], std::false_type{}), cvt(w[1], std::true_type{})};
+  return as_bf16x8(r);
+}
 
 // f(std::integral_constant<int, i>) for i = 0 .. N-1, with i usable as a
 // constant expression (schedule-group sizes must be constants).

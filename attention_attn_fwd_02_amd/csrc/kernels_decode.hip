@@ -66,10 +66,68 @@ k_decode(DecodeArgs a) {
   const int h = kvh * grp + (row_ok ? r % grp : 0);
   T tile;
   tile.init(wave);
-  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
-                     : nullptr,
-              lane);
+  const size_t qoff = (((size_t)b * a.sq + tq) * a.hq + h) * C::D;
+  if constexpr (C::FP8)
+    tile.load_q8(row_ok ? static_cast<const uint8_t*>(a.q) + qoff : nullptr, lane);
+  else
+    tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + qoff : nullptr, lane);
+  // FP8: descales of (b, kvh) scale the scores and O (1 when not given)
+  float cscale = a.scale_log2, vscale = 1.f;
+  if constexpr (C::FP8) {
+    const size_t di = (size_t)b * a.hkv + kvh;
+    cscale *= (a.q_descale ? a.q_descale[di] : 1.f) * (a.k_descale ? a.k_descale[di] : 1.f);
+    vscale = a.v_descale ? a.v_descale[di] : 1.f;
+  }
   wait_vmcnt<0>();  // Q in registers before any DMA is in flight
+
+  if constexpr (C::FP8) {
+    // FP8 cache: byte rows, one DMA instruction per 8 tile rows
+    const size_t tok = (size_t)a.hkv * C::D;  // bytes per token (K and V alike)
+    const char* kcb = static_cast<const char*>(a.kc) + (size_t)kvh * C::D;
+    const char* vcb = static_cast<const char*>(a.vc) + (size_t)kvh * C::DV;
+    const int* btb = a.block_table + (size_t)b * a.max_pages;
+    const int kv_last = kv1 - 1;
+    const uint32_t k0 = T::lane_off8(lane, (uint32_t)tok, 0), k1 = T::lane_off8(lane, (uint32_t)tok, 1);
+    auto issue = [&](char* st, int ti) {
+      const int j0 = kv0 + ti * C::BN;
+      const int j1 = min(j0 + 16, kv_last);
+      const int lp0 = j0 / a.page, lp1 = j1 / a.page;
+      int p0, p1;
+      sload2_uniform(btb + lp0, btb + lp1, p0, p1);
+      const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
+      const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
+      const int rmax = kv_last - j0;
+      if (rmax >= C::BN - 1) {
+        auto kb = [&](int r8) {
+          return kcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok;
+        };
+        auto vb = [&](int r8) {
+          return vcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok;
+        };
+        T::dma_tile8_sv(st, kb, vb, k0, k1, k0, k1);
+      } else {
+        // last tile of the split: rows past its last key re-read that key
+        auto row = [&](int rr) { rr = min(rr, rmax); return (rr >> 4 ? slot1 : slot0) + (rr & 15); };
+        T::dma_tile8(
+            st, [&](int rr) { return kcb + row(rr) * tok; },
+            [&](int rr) { return vcb + row(rr) * tok; }, lane);
+      }
+    };
+    const int first_t = (mt * C::ROWS) / grp;
+    const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
+    stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+      const int j0 = kv0 + ti * C::BN;
+      const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
+      f32x4 sc[C::NSB];
+      tile.qk(st, lane, sc);
+      const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
+      const float m_use = tile.prep(sc, cscale, lane, need,
+                                    [&](int jr) { return j0 + jr <= hi_vis; });
+      uint32_t pk[C::NSB * 2];
+      tile.probs(sc, cscale, m_use, pk);
+      tile.pv(st, lane, pk);
+    });
+  } else {
 
   const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + (size_t)kvh * C::D;
   const bf16_t* vc =
@@ -130,9 +188,10 @@ k_decode(DecodeArgs a) {
     tile.probs(sc, a.scale_log2, m_use, pk);
     tile.pv(st, lane, pk);
   });
+  }
 
   float lse;
-  const float inv = tile.finish(false, 0.f, lse);
+  const float inv = tile.finish(false, 0.f, lse) * vscale;
   if (row_ok) {
     const size_t slot_id = (size_t)b * a.max_splits + s;
     const size_t row = slot_id * nrows * a.hkv + (size_t)tq * a.hq + h;
@@ -322,6 +381,8 @@ k_sparse(SparseArgs a) {
 }
 
 using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
+template <int FMT>
+using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT>;
 using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
@@ -335,6 +396,18 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
   hipLaunchKernelGGL(k_decode<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s) {
+  using C = CfgDecodeGqa8<1>;
+  const int nrows = a.sq * (a.hq / a.hkv);
+  const int mt = (nrows + C::ROWS - 1) / C::ROWS;
+  const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

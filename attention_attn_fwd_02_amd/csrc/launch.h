@@ -39,6 +39,10 @@ struct DecodeArgs {
   float scale_log2;
   float* o_part;
   float* lse_part;
+  // FP8 caches: descales (batch, hkv) float32, NULL = 1
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
 };
 
 struct SparseArgs {
@@ -71,6 +75,7 @@ hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s);  // fmt 1 e4m3, 2 e5m2
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);

@@ -49,7 +49,7 @@ typedef enum {
   ATTN_EHIP = 4           /* HIP runtime error (launch, device query)        */
 } attn_status;
 
-typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1 } attn_dtype;
+typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1, ATTN_FP8_E4M3 = 2, ATTN_FP8_E5M2 = 3 } attn_dtype;
 
 /* Human-readable name of a status code. Never NULL. */
 const char* attn_status_string(int32_t status);
@@ -174,6 +174,33 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           int32_t dtype, float scale, int32_t causal, const int32_t* plan,
                           int32_t max_splits, float* o_partial, float* lse_partial,
                           void* stream);
+
+/*
+ * attn_decode_paged_fp8 - attn_decode_paged with FP8 query and cache.
+ * [MATE "Attention" page, FMHA forward dtype notes: float8_e4m3fn and
+ *  float8_e5m2 inputs of flash_attn_with_kvcache; optional float32 q_descale,
+ *  k_descale, v_descale of shape (batch_size, num_heads_kv); FP8 inputs give
+ *  bfloat16 outputs]
+ *
+ *  q (B, Sq, Hq, 128), k_cache / v_cache (P, page_size, Hkv, 128) hold 8-bit
+ *  codes of fp8_format: ATTN_FP8_E4M3 (e4m3fn: bias 7, no infinities, max
+ *  448) or ATTN_FP8_E5M2 (bias 15, IEEE-style infinities and NaN).
+ *  q_descale, k_descale, v_descale: NULL (= 1) or float32 (B, Hkv). The real
+ *  value of a code of sequence b and KV head g is code * descale[b][g]; query
+ *  head h uses the descale of its KV head g = h / (Hq / Hkv). Descales must
+ *  be positive and finite (not checked).
+ *  Everything else (block table, plan, partial layouts, masks, errors) is as
+ *  in attn_decode_paged; attn_combine then gives the bfloat16 O and the LSE.
+ *  Supported: d = dv = 128, page_size a multiple of 16.
+ */
+int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int32_t max_pages_per_seq,
+                              const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                              int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                              int32_t fp8_format, const float* q_descale,
+                              const float* k_descale, const float* v_descale, float scale,
+                              int32_t causal, const int32_t* plan, int32_t max_splits,
+                              float* o_partial, float* lse_partial, void* stream);
 
 /*
  * attn_combine - LSE-weighted merge of split results.

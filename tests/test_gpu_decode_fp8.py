@@ -1,0 +1,124 @@
+"""GPU parity of the FP8 paged decode (attn_decode_paged_fp8 + attn_combine)
+against the float64 oracle on the dequantized codes, through the C ABI.
+
+Tolerance: the FP8 codes widen to bfloat16 exactly and the arithmetic after
+that is the bfloat16 path's (fp32 scores and sums, P rounded to bfloat16, O
+rounded to bfloat16), so the bfloat16 bars apply with the output scaled by its
+V descale (up to 4 here): max-abs 2e-2 * v_descale on O, 1e-3 on LSE."""
+import numpy as np
+import pytest
+import torch
+
+from attention_attn_fwd_02_amd import binding as B
+from attention_attn_fwd_02_amd import inputs
+from oracle import attention as orc
+from oracle import fp8 as ofp8
+from tests.gpu_util import TOL_O_BF16, compare, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fp8(w, max_splits=16, waves=4, min_blocks=4, k_cache=None, v_cache=None,
+            block_table=None):
+    ds = [None if x is None else dev(x) for x in (w.q_descale, w.k_descale, w.v_descale)]
+    return B.paged_decode_fp8(dev(w.q), dev(w.k_cache if k_cache is None else k_cache),
+                              dev(w.v_cache if v_cache is None else v_cache),
+                              dev(w.block_table if block_table is None else block_table),
+                              dev(w.cache_seqlens), w.scale, w.fmt, *ds, causal=w.causal,
+                              max_splits=max_splits, waves=waves, min_blocks=min_blocks)
+
+
+def oracle_fp8(w, batches=None):
+    return ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, w.fmt, w.q_descale, w.k_descale,
+                                    w.v_descale, w.block_table, w.cache_seqlens, w.page_size,
+                                    w.scale, w.causal, batches=batches)
+
+
+def tol(w):
+    return TOL_O_BF16 * (1.0 if w.v_descale is None else float(w.v_descale.max()))
+
+
+FP8_CASES = [
+    # name, fmt, lens, sq, hq, hkv, page, causal, descale, max_splits, waves, min_blocks
+    ("e4m3_ragged", "e4m3", [1, 63, 64, 65, 700, 2049], 1, 32, 8, 64, False, True, 16, 4, 4),
+    ("e5m2_ragged", "e5m2", [1, 63, 64, 65, 700, 2049], 1, 32, 8, 64, False, True, 16, 4, 4),
+    ("e4m3_no_descale", "e4m3", [300, 1200], 1, 8, 8, 64, False, False, 1, 4, 4),
+    ("e4m3_many_splits_page16", "e4m3", [5000, 130, 4097], 1, 8, 2, 16, False, True, 16, 64, 1),
+    ("e5m2_causal_sq3", "e5m2", [90, 400, 3], 3, 16, 4, 16, True, True, 8, 16, 1),
+    ("e4m3_gqa16_rows32", "e4m3", [333, 1000], 2, 16, 1, 64, True, True, 16, 8, 2),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_decode_fp8(case):
+    name, fmt, lens, sq, hq, hkv, page, causal, descale, ms, waves, mb = case
+    log("case decode_fp8", name)
+    w = inputs.paged_fp8(7000 + len(name), lens, fmt, sq=sq, hq=hq, hkv=hkv, page=page,
+                         causal=causal, descale=descale)
+    o, lse, plan = run_fp8(w, ms, waves, mb)
+    torch.cuda.synchronize()
+    ro, rl = oracle_fp8(w)
+    compare(name, o, lse, ro, rl, tol(w))
+    ref_plan = orc.plan_splits(w.cache_seqlens, page, hkv * ((sq * hq // hkv + 15) // 16),
+                               B.attn_device_info(0), waves, ms, mb)
+    n = 3 + len(lens) + 3 * int(ref_plan[0])
+    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+
+
+def test_decode_fp8_extreme_codes():
+    """Codes drawn uniformly over every finite code of each format (largest
+    magnitudes and subnormals included) with small descales, so that the
+    widening of every exponent and of subnormals reaches the output."""
+    for fmt in ("e4m3", "e5m2"):
+        w = inputs.paged_fp8(7100, [200, 77], fmt, sq=1, hq=8, hkv=2, page=32)
+        rng = np.random.default_rng(7101)
+        finite = np.flatnonzero(np.isfinite(ofp8.decode(np.arange(256, dtype=np.uint8), fmt)))
+        pick = lambda shape: finite[rng.integers(0, len(finite), size=shape)].astype(np.uint8)
+        w.q, w.k_cache, w.v_cache = pick(w.q.shape), pick(w.k_cache.shape), pick(w.v_cache.shape)
+        top = float(np.nanmax(np.abs(ofp8.decode(finite.astype(np.uint8), fmt))))
+        # scores stay finite in fp32 and |V| * v_descale stays near 1
+        w.q_descale = np.full_like(w.q_descale, 1.0 / top)
+        w.k_descale = np.full_like(w.k_descale, 1.0 / top)
+        w.v_descale = np.full_like(w.v_descale, 1.0 / top)
+        log("case decode_fp8_extreme", fmt)
+        o, lse, _ = run_fp8(w)
+        torch.cuda.synchronize()
+        ro, rl = oracle_fp8(w)
+        compare(f"decode_fp8_extreme_{fmt}", o, lse, ro, rl, TOL_O_BF16)
+
+
+NAN_E4M3 = np.uint8(0x7F)
+
+
+def test_decode_fp8_poisoned_pool():
+    """NaN codes in pool pages no sequence references and in the cache rows
+    past each sequence's length inside its last page."""
+    lens, page, extra = [100, 64, 7], 16, 5
+    w = inputs.paged_fp8(7200, lens, "e4m3", sq=1, hq=8, hkv=2, page=page)
+
+    def poison(c):
+        c = np.concatenate([np.full((extra,) + c.shape[1:], NAN_E4M3, np.uint8), c])
+        for b, n in enumerate(lens):
+            if n % page:
+                c[int(w.block_table[b, (n - 1) // page]) + extra, n % page:] = NAN_E4M3
+        return c
+
+    bt = np.where(w.block_table >= 0, w.block_table + extra, -1).astype(np.int32)
+    log("case decode_fp8_poisoned_pool")
+    o, lse, _ = run_fp8(w, k_cache=poison(w.k_cache), v_cache=poison(w.v_cache), block_table=bt)
+    torch.cuda.synchronize()
+    ro, rl = oracle_fp8(w)
+    compare("decode_fp8_poisoned_pool", o, lse, ro, rl, tol(w))
+
+
+def test_decode_fp8_workload():
+    """The benchmarked FP8 decode workload (seed 1007: 64 sequences with cache
+    lengths U[1024, 32768], page 64, Hq=32, Hkv=8, D=128, e4m3 with descales),
+    in the launch configuration bench.py times; sequences 0, 17 and 63
+    compared element by element."""
+    w = inputs.paged_decode_fp8()
+    log("case decode_fp8_workload")
+    o, lse, _ = run_fp8(w, 16, 8, 2)
+    torch.cuda.synchronize()
+    ro, rl = oracle_fp8(w, batches=[0, 17, 63])
+    compare("decode_fp8_workload", o, lse, ro, rl, tol(w))
