@@ -268,28 +268,50 @@ def _paged_draw(rng, lens, sq, hq, hkv, d, dv, page, shared_kv, causal, scale, w
                  scale if scale is not None else 1.0 / np.sqrt(d), causal, sinks)
 
 
-# FP8 codes: (exponent bits, mantissa bits, bias, largest finite value) of the
-# OCP formats e4m3fn and e5m2.
-_FP8 = {"e4m3": (4, 3, 7, 448.0), "e5m2": (5, 2, 15, 57344.0)}
+# FP8 codes of the OCP formats e4m3fn and e5m2: (mantissa bits, bias,
+# largest finite value).
+_FP8 = {"e4m3": (3, 7, 448.0), "e5m2": (2, 15, 57344.0)}
 
 
 def fp8_bits(x: np.ndarray, fmt: str) -> np.ndarray:
-    """Rounds values to the nearest code of an FP8 format (ties to even,
-    saturating at the largest finite value) and returns the uint8 codes."""
-    ebits, mbits, bias, vmax = _FP8[fmt]
-    x = np.clip(np.asarray(x, dtype=np.float64), -vmax, vmax)
-    neg = np.signbit(x)
-    a = np.abs(x)
-    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    e = np.maximum(e, 1 - bias)                         # subnormals share the least exponent
-    q = np.round(a / np.exp2(e - mbits))                # mantissa with its leading bit
-    carry = q >= 2 ** (mbits + 1)
-    e = np.where(carry, e + 1, e)
-    q = np.where(carry, q / 2, q)
-    normal = q >= 2 ** mbits
-    efield = np.where(normal, e + bias, 0).astype(np.int64)
-    mfield = np.where(normal, q - 2 ** mbits, q).astype(np.int64)
-    return ((neg.astype(np.int64) << 7) | (efield << mbits) | mfield).astype(np.uint8)
+    """Rounds float32 values to the nearest code of an FP8 format (ties to
+    even, saturating at the largest finite value) and returns uint8 codes.
+    Normal results come from the float32 bit pattern rounded at the format's
+    mantissa width with the exponent rebiased; below the least normal value
+    the code is the multiple of the least subnormal, rounded half to even."""
+    mbits, bias, vmax = _FP8[fmt]
+    x = np.asarray(x, dtype=np.float32)
+    a = np.minimum(np.abs(x), np.float32(vmax))
+    u = a.view(np.uint32)
+    sh = 23 - mbits
+    r = (u + np.uint32((1 << (sh - 1)) - 1) + ((u >> sh) & 1)) >> sh   # exponent | mantissa
+    normal = (r.astype(np.int64) - ((127 - bias) << mbits))
+    sub = np.rint(a * np.float32(2.0 ** (bias - 1 + mbits))).astype(np.int64)
+    code = np.where(a < np.float32(2.0 ** (1 - bias)), sub, normal)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def _normal_fp8(rng: np.random.Generator, shape, fmt: str, mult) -> np.ndarray:
+    """N(0,1) float32 draws times a multiplier per row of the last dimension
+    (mult(r0, r1) gives those of rows [r0, r1) of the flattened tensor),
+    rounded to FP8 codes; blocks of _CHUNK elements drawn as in _normal_bf16
+    (one key, one stream per block)."""
+    n = int(np.prod(shape))
+    d = shape[-1]
+    assert _CHUNK % d == 0
+    out = np.empty(n, dtype=np.uint8)
+    key = int(rng.integers(0, 2**63 - 1))
+
+    def fill(i):
+        s, e = i * _CHUNK, min(n, (i + 1) * _CHUNK)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([key, i])))
+        x = g.standard_normal(e - s, dtype=np.float32).reshape(-1, d)
+        out[s:e] = fp8_bits(x * mult(s // d, e // d)[:, None], fmt).ravel()
+
+    nblk = (n + _CHUNK - 1) // _CHUNK
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(16, os.cpu_count() or 1, nblk))) as ex:
+        list(ex.map(fill, range(nblk)))
+    return out.reshape(shape)
 
 
 @dataclasses.dataclass
@@ -319,30 +341,40 @@ def paged_fp8(seed: int, lens, fmt: str = "e4m3", sq: int = 1, hq: int = 32, hkv
               d: int = 128, page: int = 64, causal: bool = False, descale: bool = True,
               spare_pages: int = 0) -> PagedFP8:
     """N(0,1) Q, K, V stored as FP8 codes of x / descale, with descales drawn
-    per (batch, KV head) from U[0.25, 4] (or none). Draw order: descales, Q,
-    K cache, V cache (N(0,1) float32 draws), page permutation."""
+    per (batch, KV head) from U[0.25, 4] (or none); a cache page is quantized
+    with the descales of the sequence that owns it. Draw order: descales, Q,
+    page permutation, K cache, V cache."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     b = len(lens)
     ds = [rng.uniform(0.25, 4.0, size=(b, hkv)).astype(np.float32) if descale else None
           for _ in range(3)]
+    one = np.ones((b, hkv), np.float32)
+    qd, kd, vd = (one if x is None else x for x in ds)
     nblk = (lens + page - 1) // page
     pool = max(1, int(nblk.sum()) + spare_pages)
     grp = hq // hkv
-    qd = np.ones((b, hkv), np.float32) if ds[0] is None else ds[0]
-    q = rng.standard_normal((b, sq, hq, d), dtype=np.float32)
-    q8 = fp8_bits(q / np.repeat(qd, grp, axis=1)[:, None, :, None], fmt)
-    kc = rng.standard_normal((pool, page, hkv, d), dtype=np.float32)
-    vc = rng.standard_normal((pool, page, hkv, d), dtype=np.float32)
+    # multiplier of flattened element i of q (B, Sq, Hq, D): 1 / qd[b, h // grp]
+    qinv = np.repeat(1.0 / qd, grp, axis=1).astype(np.float32)       # (B, Hq)
+
+    def qmult(r0, r1):                     # rows of q are (b, t, h)
+        r = np.arange(r0, r1)
+        return qinv[r // (sq * hq), r % hq]
+
+    q8 = _normal_fp8(rng, (b, sq, hq, d), fmt, qmult)
     table, _ = _paged_table(rng, lens, page)
-    # each page belongs to one sequence: quantize it with that sequence's descales
     owner = np.zeros(pool, np.int64)
     for bi, n in enumerate(nblk):
         owner[table[bi, :n]] = bi
-    kd = np.ones((b, hkv), np.float32) if ds[1] is None else ds[1]
-    vd = np.ones((b, hkv), np.float32) if ds[2] is None else ds[2]
-    k8 = fp8_bits(kc / kd[owner][:, None, :, None], fmt)
-    v8 = fp8_bits(vc / vd[owner][:, None, :, None], fmt)
+
+    def cmult(inv):                        # rows of a cache are (page, slot, kv head)
+        def f(r0, r1):
+            r = np.arange(r0, r1)
+            return inv[owner[r // (page * hkv)], r % hkv]
+        return f
+
+    k8 = _normal_fp8(rng, (pool, page, hkv, d), fmt, cmult((1.0 / kd).astype(np.float32)))
+    v8 = _normal_fp8(rng, (pool, page, hkv, d), fmt, cmult((1.0 / vd).astype(np.float32)))
     return PagedFP8(q8, k8, v8, fmt, ds[0], ds[1], ds[2], table, lens.astype(np.int32), page,
                     1.0 / np.sqrt(d), causal)
 

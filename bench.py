@@ -5,8 +5,8 @@ Hq=32, Hkv=8, D=128, bf16), in attention TFLOP/s. One step = one
 attn_fwd_varlen call over the whole packed batch (the single kernel of the
 prefill path). The same JSON line carries the other workloads as
 `secondary` entries: paged GQA decode (KV-read GB/s, step = plan + split
-decode + combine), MLA-absorbed paged decode, chunked prefill over a paged
-cache and sparse MLA with sinks.
+decode + combine) with a bf16 and with an FP8 cache, MLA-absorbed paged
+decode, chunked prefill over a paged cache and sparse MLA with sinks.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Every timed region is bracketed by torch.cuda.synchronize() and
@@ -179,6 +179,50 @@ def bench_decode(steps, warmup):
     return dict(ms=ms_full, ms_kernel=ms_dec, ms_cold=ms_cold, bytes=alg_bytes, kv_bytes=kv_bytes,
                 gbs=alg_bytes / (ms_full * 1e-3) / 1e9, gbs_kernel=alg_bytes / (ms_dec * 1e-3) / 1e9,
                 splits=int(plan[0].item()))
+
+
+FP8_DECODE_PLAN = (16, 16, 2)  # max_splits, waves, min_blocks for the FP8 decode
+
+
+def bench_decode_fp8(steps, warmup, plan_args=FP8_DECODE_PLAN):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.paged_decode_fp8()
+    q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    qd, kd, vd = dev(w.q_descale), dev(w.k_descale), dev(w.v_descale)
+    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
+    ncu = B.attn_device_info(0)
+    b, sq, hq, d = w.q.shape
+    hkv = w.k_cache.shape[2]
+    ms_, waves, mb = plan_args
+    upb = hkv * ((sq * hq // hkv + 15) // 16)
+    plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
+    op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
+    lp = torch.empty((b * ms_, sq * hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((b, sq, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+
+    def decode_only():
+        B.attn_decode_paged_fp8(q, kc, vc, bt, lens, plan, ms_, w.scale, w.fmt, qd, kd, vd,
+                                False, op, lp)
+
+    def full():
+        B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb, plan=plan)
+        decode_only()
+        B.attn_combine(op, lp, plan, b, sq, hq, ms_, None, torch.bfloat16, out, lse)
+
+    ms_full = time_steps(full, steps, warmup)
+    ms_dec = time_steps(decode_only, steps, warmup)
+    ms_cold = time_cold(full, 9)
+    total_len = int(w.cache_seqlens.astype(np.int64).sum())
+    nblk = int(((w.cache_seqlens + 63) // 64).sum())
+    kv_bytes = total_len * hkv * (128 + 128)               # one byte per code
+    alg_bytes = (kv_bytes + w.q.nbytes + out.numel() * 2 + lse.numel() * 4 + nblk * 4
+                 + 3 * b * hkv * 4)
+    return dict(ms=ms_full, ms_kernel=ms_dec, ms_cold=ms_cold, bytes=alg_bytes, kv_bytes=kv_bytes,
+                tokens=total_len, gbs=alg_bytes / (ms_full * 1e-3) / 1e9,
+                gbs_kernel=alg_bytes / (ms_dec * 1e-3) / 1e9, splits=int(plan[0].item()))
 
 
 def bench_mla(steps, warmup):
@@ -369,7 +413,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
-    ap.add_argument("--only", default="prefill,decode,mla,chunked,sparse")
+    ap.add_argument("--only", default="prefill,decode,decode_fp8,mla,chunked,sparse")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -428,6 +472,25 @@ def main():
                          "traffic": None, "kernel": "k_decode (GQA)",
                          "kernel_ms": dec["ms_kernel"]},
             "frac_of_hbm_peak_whole_op": dec["gbs"] / PEAK_HBM_GBS})
+    if "decode_fp8" in only:
+        log("paged decode fp8 ...")
+        d8 = bench_decode_fp8(args.steps, args.warmup)
+        log(f"decode_fp8 {d8['ms']:.3f} ms (kernel {d8['ms_kernel']:.3f}) {d8['gbs']:.0f} GB/s")
+        secondary.append({
+            "metric": "KV-read GB/s (paged decode, FP8 e4m3 Q/K/V)", "value": d8["gbs"],
+            "unit": "GB/s", "ms_per_step": d8["ms"],
+            "cached_tokens_per_s": d8["tokens"] / (d8["ms"] * 1e-3),
+            "cold_cache": {"ms_per_step_median": d8["ms_cold"],
+                           "value": d8["bytes"] / (d8["ms_cold"] * 1e-3) / 1e9},
+            "workload": "paged GQA decode with an FP8 cache: batch 64, 1 query token, "
+                        "cache_seqlens U[1024,32768], page 64, Hq=32, Hkv=8, D=128, e4m3 codes "
+                        "with per-(batch, KV head) descales, bf16 out; plan + split decode "
+                        f"(<=16 splits) + combine per step; {d8['splits']} splits (seed 1007)",
+            "roofline": {"bound": "hbm", "achieved": d8["gbs_kernel"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": d8["gbs_kernel"] / PEAK_HBM_GBS,
+                         "traffic": None, "kernel": "k_decode (GQA, FP8)",
+                         "kernel_ms": d8["ms_kernel"]},
+            "frac_of_hbm_peak_whole_op": d8["gbs"] / PEAK_HBM_GBS})
     if "mla" in only:
         log("mla decode ...")
         mla = bench_mla(args.steps, args.warmup)
