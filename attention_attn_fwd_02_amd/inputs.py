@@ -427,6 +427,54 @@ class Sparse:
         return self.q.shape[0]
 
 
+@dataclasses.dataclass
+class SparsePaged:
+    """Block-sparse MLA over a paged latent cache: q (B,Sq,Hq,D) bits,
+    kv_cache (P,page,1,D) bits, block_table (B, max_pages) int32 (-1 past a
+    sequence's pages), seqlens_kv (B) int32, indices (B,Sq,1,topk) int32 block
+    numbers (-1 unused), block_size keys per index."""
+    q: np.ndarray
+    kv_cache: np.ndarray
+    block_table: np.ndarray
+    seqlens_kv: np.ndarray
+    page_size: int
+    indices: np.ndarray
+    block_size: int
+    sinks: np.ndarray | None
+    dv: int
+    scale: float
+    sparse_mode: int
+
+
+def sparse_paged(seed: int, lens_kv, sq: int, topk: int, block_size: int = 1, page: int = 64,
+                 hq: int = 64, d: int = 576, dv: int = 512, sparse_mode: int = 3,
+                 with_sinks: bool = True, spare_pages: int = 0) -> SparsePaged:
+    """Per query token t of sequence b, topk distinct block numbers drawn
+    without replacement from the blocks that hold keys of its bottom-right
+    causal prefix [0, Lk_b - sq + t] (all of them, in random order, when there
+    are fewer), padded with -1. Draw order: Q, cache, page permutation,
+    indices, sinks."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens_kv, dtype=np.int64)
+    batch = len(lens)
+    nblk = (lens + page - 1) // page
+    pool = max(1, int(nblk.sum()) + spare_pages)
+    q = _normal_bf16(rng, (batch, sq, hq, d))
+    kv = _normal_bf16(rng, (pool, page, 1, d))
+    table, _ = _paged_table(rng, lens, page)
+    idx = np.full((batch, sq, 1, topk), -1, dtype=np.int32)
+    for b in range(batch):
+        for t in range(sq):
+            p = max(0, min(int(lens[b]), int(lens[b]) - sq + t + 1))
+            nb = (p + block_size - 1) // block_size
+            n = min(topk, nb)
+            if n:
+                idx[b, t, 0, :n] = rng.choice(nb, n, replace=False)
+    sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
+    return SparsePaged(q, kv, table, lens.astype(np.int32), page, idx, block_size, sinks, dv,
+                       1.0 / np.sqrt(d), sparse_mode)
+
+
 def sparse_mla(seed: int = SEED_SPARSE_MLA, batch: int = 4, sq: int = 4096, sk: int = 32768,
                hq: int = 64, d: int = 576, dv: int = 512, topk: int = 2048,
                sparse_mode: int = 3, with_sinks: bool = True,

@@ -406,6 +406,53 @@ def sparse_key_set(indices_row, seqlen_q, seqlen_k, t, sparse_mode):
     return idx[keep]
 
 
+def sparse_block_keys(indices_row, seqlen_q, seqlen_k, t, sparse_mode, block_size):
+    """Keys selected for query token t when each index names a block of
+    block_size consecutive keys [SFA sparse_indices with sparse_block_size,
+    PA_BSND]: index i >= 0 selects keys i*block_size .. i*block_size +
+    block_size - 1; keys at or past seqlen_k, and in mode 3 after
+    t + (seqlen_k - seqlen_q), are dropped; duplicates count each time."""
+    idx = np.asarray(indices_row, dtype=np.int64)
+    idx = idx[idx >= 0]
+    keys = (idx[:, None] * block_size + np.arange(block_size)[None, :]).ravel()
+    keep = keys < seqlen_k
+    if sparse_mode == 3:
+        keep &= keys <= t + (seqlen_k - seqlen_q)
+    return keys[keep]
+
+
+def mla_sparse_paged(q, kv_cache, block_table, seqlens_kv, page_size, sparse_indices, scale,
+                     sparse_mode=3, sinks=None, sparse_block_size=1, dv=512, tokens=None):
+    """Sparse MLA over a paged latent cache [SFA layout_kv PA_BSND: key
+    (block_num, block_size, 1, D) with block_table, actual_seq_lengths_kv;
+    sparse_block_size]. Sequence b has seqlens_kv[b] keys, key j at page
+    block_table[b, j // page_size], slot j % page_size; its selected keys are
+    sparse_block_keys(...); the rest as mla_sparse.
+    Returns O (B, Sq, Hq, dv), LSE (B, Hq, Sq), or per listed (b, t) token."""
+    bsz, sq, hq, _ = q.shape
+    if tokens is None:
+        o = np.zeros((bsz, sq, hq, dv))
+        lse = np.zeros((bsz, hq, sq))
+        todo = [(b, t) for b in range(bsz) for t in range(sq)]
+    else:
+        o = np.zeros((len(tokens), hq, dv))
+        lse = np.zeros((len(tokens), hq))
+        todo = tokens
+    for i, (b, t) in enumerate(todo):
+        lk = int(seqlens_kv[b])
+        keys = sparse_block_keys(sparse_indices[b, t, 0], sq, lk, t, sparse_mode,
+                                 sparse_block_size)
+        rows = gather_paged(kv_cache, block_table, b, lk, page_size)[keys, 0]
+        ob, lb = attend_rows(q[b, t], rows, rows[:, :dv], scale, None, sinks)
+        if tokens is None:
+            o[b, t] = ob
+            lse[b, :, t] = lb
+        else:
+            o[i] = ob
+            lse[i] = lb
+    return o, lse
+
+
 def mla_sparse(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, dv=512, tokens=None):
     """Top-k sparse MLA with optional per-head sinks [SFA formula with the
     selected K~ = V~ rows; CANN sink formulas].

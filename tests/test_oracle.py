@@ -547,6 +547,52 @@ def test_sparse():
     check_sparse()
 
 
+def check_sparse_paged():
+    """Block-sparse MLA over a paged cache [SFA PA_BSND, sparse_block_size]:
+    selecting every block of the causal prefix equals dense bottom-right
+    causal attention over the contiguous rows (blocks past the prefix hold
+    keys the mask drops); one block index m selects exactly keys m*s ..
+    m*s + s - 1; with block size 1 and the cache laid out contiguously it is
+    the dense-layout sparse path."""
+    lens, sq, d, dv, page, bs = [13, 9], 4, 24, 16, 4, 4
+    w = inputs.sparse_paged(71, lens, sq, topk=8, block_size=bs, page=page, hq=4, d=d, dv=dv)
+    q, kc = inputs.bits_to_f32(w.q), inputs.bits_to_f32(w.kv_cache)
+    o, lse = orc.mla_sparse_paged(q, kc, w.block_table, w.seqlens_kv, page, w.indices, w.scale,
+                                  3, w.sinks, bs, dv=dv)
+    for b, lk in enumerate(lens):
+        rows = orc.gather_paged(kc, w.block_table, b, lk, page)     # (lk, 1, d)
+        od, ld = orc.attention_dense(q[b:b + 1], rows[None], np.ascontiguousarray(
+            rows[None, ..., :dv]), w.scale, True, sinks=w.sinks)
+        np.testing.assert_allclose(o[b], od[0], atol=1e-13)
+        np.testing.assert_allclose(lse[b], ld[0], atol=1e-13)
+    # a single block index m: keys m*bs .. m*bs+bs-1 (mode 0, block inside the sequence)
+    idx1 = np.full_like(w.indices, -1)
+    idx1[..., 0] = 1
+    o1, l1 = orc.mla_sparse_paged(q, kc, w.block_table, w.seqlens_kv, page, idx1, w.scale, 0,
+                                  None, bs, dv=dv)
+    for b, lk in enumerate(lens):
+        rows = orc.gather_paged(kc, w.block_table, b, lk, page)[bs:2 * bs, 0]
+        for t in range(sq):
+            ob, lb = orc.attend_rows(q[b, t], rows, rows[:, :dv], w.scale)
+            np.testing.assert_allclose(o1[b, t], ob, atol=1e-13)
+            np.testing.assert_allclose(l1[b, :, t], lb, atol=1e-13)
+    # block size 1, pages in order: the dense-layout sparse path
+    s = inputs.sparse_mla(72, batch=1, sq=5, sk=12, hq=4, d=d, dv=dv, topk=6)
+    kv = inputs.bits_to_f32(s.kv)
+    cache = kv[0].reshape(3, 4, 1, d)
+    table = np.array([[0, 1, 2]], np.int32)
+    qs = inputs.bits_to_f32(s.q)
+    o2, l2 = orc.mla_sparse_paged(qs, cache, table, [12], 4, s.indices, s.scale, 3, s.sinks, 1,
+                                  dv=dv)
+    o3, l3 = orc.mla_sparse(qs, kv, s.indices, s.scale, 3, s.sinks, dv=dv)
+    np.testing.assert_allclose(o2, o3, atol=0)
+    np.testing.assert_allclose(l2, l3, atol=0)
+
+
+def test_sparse_paged():
+    check_sparse_paged()
+
+
 # ----------------------------------------------------------- library routine
 def test_matches_torch_sdpa_float64():
     torch = pytest.importorskip("torch")
@@ -689,7 +735,17 @@ def _mutants():
                                     np.asarray(cu), scale, causal, window, sinks, seqs)
 
     del base_kvc
-    return [("attend_rows", no_scale), ("attend_rows", sink_dropped),
+
+    def block_keys_unscaled(indices_row, seqlen_q, seqlen_k, t, sparse_mode, block_size):
+        idx = np.asarray(indices_row, dtype=np.int64)
+        idx = idx[idx >= 0]
+        keys = (idx[:, None] + np.arange(block_size)[None, :]).ravel()
+        keep = keys < seqlen_k
+        if sparse_mode == 3:
+            keep &= keys <= t + (seqlen_k - seqlen_q)
+        return keys[keep]
+
+    return [("sparse_block_keys", block_keys_unscaled), ("attend_rows", no_scale), ("attend_rows", sink_dropped),
             ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
             ("visible_band", causal_top_left), ("visible_band", window_sides_swapped),
             ("combine", combine_unweighted), ("gather_paged", gather_swapped),
@@ -699,10 +755,11 @@ def _mutants():
 PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical_keys,
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
-        check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases]
+        check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases,
+        check_sparse_paged]
 
 
-@pytest.mark.parametrize("i", range(9))
+@pytest.mark.parametrize("i", range(10))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
