@@ -43,6 +43,8 @@ _SIGNATURES = {
     "attn_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P]),
     "mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
     "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
+    "mla_sparse_paged_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I,
+                                  _P, _P, _P, _P]),
     "attn_debug_gather_paged": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P]),
 }
 
@@ -309,6 +311,31 @@ def mla_sparse_fwd(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, out=
     _check(load().mla_sparse_fwd(_ptr(q), _ptr(kv), _ptr(sparse_indices), topk, b, sq, sk, hq,
                                  float(scale), int(sparse_mode), _ptr(sinks), _ptr(out), _ptr(lse),
                                  _stream()))
+    return out, lse
+
+
+def mla_sparse_paged_fwd(q, kv_cache, block_table, seqlens_kv, sparse_indices, scale,
+                         sparse_block_size=1, sparse_mode=3, sinks=None, out=None, lse=None,
+                         return_lse=True):
+    """q (B,Sq,Hq,576) bf16, kv_cache (P,page,1,576) bf16, block_table
+    (B,max_pages) and seqlens_kv (B) int32, indices (B,Sq,1,topk) int32."""
+    _dev(q, kv_cache, dtype=torch.bfloat16)
+    _dev(block_table, seqlens_kv, sparse_indices, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    b, sq, hq, d = q.shape
+    if d != 576 or kv_cache.shape[3] != 576 or kv_cache.shape[2] != 1:
+        raise NotImplementedError("sparse MLA expects 576-wide rows and one KV head")
+    if out is None:
+        out = torch.empty((b, sq, hq, 512), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    _check(load().mla_sparse_paged_fwd(
+        _ptr(q), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1], _ptr(block_table),
+        block_table.shape[1], _ptr(seqlens_kv), _ptr(sparse_indices), sparse_indices.shape[-1],
+        int(sparse_block_size), b, sq, hq, float(scale), int(sparse_mode), _ptr(sinks), _ptr(out),
+        _ptr(lse), _stream()))
     return out, lse
 
 

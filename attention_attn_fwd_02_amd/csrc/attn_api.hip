@@ -360,8 +360,6 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
   REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
-  REQUIRE(topk <= attn::sparse_max_topk(), ATTN_EUNSUPPORTED, "topk %d above %d", topk,
-          attn::sparse_max_topk());
   REQUIRE((long)batch * seqlen_q * ((hq + 63) / 64) < (1L << 31), ATTN_EUNSUPPORTED,
           "grid too large");
   REQUIRE((long)seqlen_k * 576 * 2 <= (1L << 32), ATTN_EUNSUPPORTED,
@@ -381,6 +379,54 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
   a.out = out;
   a.lse = lse;
   return hip_status(attn::launch_sparse_mla(a, as_stream(stream)), "mla_sparse_fwd launch");
+}
+
+int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_blocks,
+                             int32_t page_size, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seqlens_kv,
+                             const int32_t* sparse_indices, int32_t topk,
+                             int32_t sparse_block_size, int32_t batch, int32_t seqlen_q,
+                             int32_t hq, float scale, int32_t sparse_mode, const float* sinks,
+                             void* out, float* lse, void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && topk > 0 && num_blocks > 0 && page_size > 0 &&
+              max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(q && kv_cache && block_table && seqlens_kv && sparse_indices && out, ATTN_EINVAL,
+          "null tensor pointer");
+  REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  int ls = 0;
+  while (ls < 8 && (1 << ls) < sparse_block_size) ++ls;
+  REQUIRE(sparse_block_size >= 1 && sparse_block_size <= 128 && (1 << ls) == sparse_block_size,
+          ATTN_EINVAL, "sparse_block_size %d is not a power of two in [1, 128]",
+          sparse_block_size);
+  REQUIRE((long)topk * sparse_block_size < (1L << 31), ATTN_EUNSUPPORTED, "too many keys");
+  REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
+  REQUIRE((long)batch * seqlen_q * ((hq + 63) / 64) < (1L << 31), ATTN_EUNSUPPORTED,
+          "grid too large");
+  REQUIRE((long)num_blocks * page_size * 576 * 2 <= (1L << 32), ATTN_EUNSUPPORTED,
+          "page pool above %ld rows (row byte offsets are 32-bit)", (1L << 32) / 1152);
+  attn::SparseArgs a{};
+  a.q = q;
+  a.kv = kv_cache;
+  a.idx = sparse_indices;
+  a.block_table = block_table;
+  a.seqlens = seqlens_kv;
+  a.max_pages = max_pages_per_seq;
+  a.page = page_size;
+  a.ls = ls;
+  a.topk = topk;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.sk = 0;
+  a.hq = hq;
+  a.mode = sparse_mode;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(attn::launch_sparse_mla(a, as_stream(stream)), "mla_sparse_paged_fwd launch");
 }
 
 int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,

@@ -304,12 +304,14 @@ k_decode_wide(DecodeArgs a) {
 }
 
 // One workgroup = (sequence b, query token t, head tile mt); all heads of a
-// token share its index list. The list is staged in LDS once (invalid
-// entries -> -1); rows of invalid keys are fetched from row 0 (a valid
-// address) and masked.
+// token share its key list. Index i names keys i*s .. i*s + s - 1 (s =
+// 2^ls, the sparse block size; s = 1: token indices). The keys are taken in
+// chunks of kMaxTopk: each chunk's physical rows (paged: through the block
+// table) are staged in LDS, invalid keys as -1, whose rows are fetched from
+// row 0 of the base (a valid address) and masked; the chunk is then streamed.
 constexpr int kMaxTopk = 4096;
 
-template <class C>
+template <class C, bool PAGED>
 __global__ void __launch_bounds__(C::THREADS)
 k_sparse(SparseArgs a) {
   using T = StreamTile<C>;
@@ -327,27 +329,24 @@ k_sparse(SparseArgs a) {
   const int h = mt * C::ROWS + (wave / C::DSPLIT) * C::R + (lane & 15);
   const bool row_ok = h < a.hq;
 
-  const int ntiles = (a.topk + C::BN - 1) / C::BN;
   const int32_t* ix = a.idx + ((size_t)b * a.sq + t) * a.topk;
-  const int limit = a.mode == 3 ? min(a.sk - 1, t + a.sk - a.sq) : a.sk - 1;
-  for (int k = threadIdx.x; k < ntiles * C::BN; k += C::THREADS) {
-    const int id = k < a.topk ? ix[k] : -1;
-    sidx[k] = (id >= 0 && id <= limit) ? id : -1;
-  }
+  const int lk = PAGED ? a.seqlens[b] : a.sk;
+  const int limit = a.mode == 3 ? min(lk - 1, t + lk - a.sq) : lk - 1;
+  const int nkeys = a.topk << a.ls;
   T tile;
   tile.init(wave);
   tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + t) * a.hq + h) * C::D
                      : nullptr,
               lane);
   wait_vmcnt<0>();
-  __syncthreads();
 
-  // K rows are gathered: the uniform base is the sequence's first row and
-  // the lane offset the byte offset of its row (fits 32 bits: sk * D * 2 is
-  // checked on the host), plus its 16-byte column.
+  // K rows are gathered: the uniform base is the sequence's first row (the
+  // pool's first row when paged) and the lane offset the byte offset of its
+  // row (fits 32 bits: checked on the host), plus its 16-byte column.
   static_assert(C::VSHARED, "sparse path reads V from the K rows");
-  const char* kvb =
-      reinterpret_cast<const char*>(static_cast<const bf16_t*>(a.kv) + (size_t)b * a.sk * C::D);
+  const char* kvb = reinterpret_cast<const char*>(
+      static_cast<const bf16_t*>(a.kv) + (PAGED ? 0 : (size_t)b * a.sk * C::D));
+  const int* btb = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
   const int lrow = (int)T::k_lane_row(lane);
   const uint32_t lcol = (lane >> 4) * 16;
   auto issue = [&](char* st, int ti) {
@@ -358,17 +357,36 @@ k_sparse(SparseArgs a) {
         st, [&](int rb, int colb) { return typename T::Src{kvb + colb, rb ? r1 : r0}; },
         [&](int, int, int) { return typename T::Src{kvb, 0u}; }, wave);
   };
-  stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
-    const int* tix = sidx + ti * C::BN;
-    f32x4 sc[C::NSB];
-    tile.qk(st, lane, sc);
-    tile.exchange(xchg, wave, lane, sc);
-    const float m_use =
-        tile.prep(sc, a.scale_log2, lane, true, [&](int jr) { return tix[jr] >= 0; });
-    uint32_t pk[C::NSB * 2];
-    tile.probs(sc, a.scale_log2, m_use, pk);
-    tile.pv(st, lane, pk);
-  });
+  const int bmask = (1 << a.ls) - 1;
+  for (int c0 = 0; c0 < nkeys; c0 += kMaxTopk) {
+    const int n = min(kMaxTopk, nkeys - c0);
+    const int ntiles = (n + C::BN - 1) / C::BN;
+    __syncthreads();  // every wave is done with the previous chunk's list and ring
+    for (int k = threadIdx.x; k < ntiles * C::BN; k += C::THREADS) {
+      int row = -1;
+      if (k < n) {
+        const int key = c0 + k;
+        const int id = ix[key >> a.ls];
+        if (id >= 0 && id <= (limit >> a.ls)) {
+          const int j = (id << a.ls) + (key & bmask);
+          if (j <= limit) row = PAGED ? btb[j / a.page] * a.page + j % a.page : j;
+        }
+      }
+      sidx[k] = row;
+    }
+    __syncthreads();
+    stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+      const int* tix = sidx + ti * C::BN;
+      f32x4 sc[C::NSB];
+      tile.qk(st, lane, sc);
+      tile.exchange(xchg, wave, lane, sc);
+      const float m_use =
+          tile.prep(sc, a.scale_log2, lane, true, [&](int jr) { return tix[jr] >= 0; });
+      uint32_t pk[C::NSB * 2];
+      tile.probs(sc, a.scale_log2, m_use, pk);
+      tile.pv(st, lane, pk);
+    });
+  }
 
   float lse;
   const float sink2 = (a.sinks && row_ok) ? a.sinks[h] * kLog2e : 0.f;
@@ -387,8 +405,6 @@ using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
-
-int sparse_max_topk() { return kMaxTopk; }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
   using C = CfgDecodeGqa;
@@ -424,7 +440,10 @@ hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s) {
   using C = CfgSparseMla;
   const int mt = (a.hq + C::ROWS - 1) / C::ROWS;
   const long grid = (long)a.batch * a.sq * mt;
-  hipLaunchKernelGGL(k_sparse<C>, dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
+  if (a.block_table)
+    hipLaunchKernelGGL((k_sparse<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_sparse<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

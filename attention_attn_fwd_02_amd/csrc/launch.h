@@ -47,8 +47,12 @@ struct DecodeArgs {
 
 struct SparseArgs {
   const void* q;
-  const void* kv;
+  const void* kv;               // (B, sk, 1, D), or the page pool when block_table is set
   const int32_t* idx;
+  const int32_t* block_table;   // NULL: dense layout; else (B, max_pages)
+  const int32_t* seqlens;       // paged: keys per sequence
+  int32_t max_pages, page;
+  int32_t ls;                   // log2 of the sparse block size
   int32_t topk, batch, sq, sk, hq, mode;
   float scale_log2;
   const float* sinks;
@@ -69,7 +73,6 @@ struct CombineArgs {
 // rows per workgroup of each instance (sizes the grids)
 int varlen_bf16_rows(int d);
 int varlen_f32_rows(int d);
-int sparse_max_topk();
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);

@@ -247,15 +247,41 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
  *  mode 3 also skips keys after t + (seqlen_k - seqlen_q); duplicates count
  *  each time; order is irrelevant. sinks: NULL or float32 (hq).
  *  out (batch, seqlen_q, hq, 512) bf16; lse: NULL or float32 (batch, hq, seqlen_q).
- *  hq must be a multiple of 16; topk at most 4096; seqlen_k at most
- *  3728270 (row byte offsets inside one sequence are 32-bit). Skipped
- *  entries are fetched from row 0 of the sequence and masked, so row 0 must
- *  hold finite values.
+ *  hq must be a multiple of 16; seqlen_k at most 3728270 (row byte offsets
+ *  inside one sequence are 32-bit). Skipped entries are fetched from row 0
+ *  of the sequence and masked, so row 0 must hold finite values.
  */
 int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indices, int32_t topk,
                        int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t hq, float scale,
                        int32_t sparse_mode, const float* sinks, void* out, float* lse,
                        void* stream);
+
+/*
+ * mla_sparse_paged_fwd - block-sparse MLA over a paged latent cache.
+ * [MindSpore sparse_flash_attention: layout_kv "PA_BSND" with key of shape
+ *  (block_num, block_size, N2, D) and block_table, actual_seq_lengths_kv,
+ *  sparse_block_size in [1, 128], a power of two]
+ *  q, out, lse, sinks, scale, sparse_mode as mla_sparse_fwd.
+ *  kv_cache (num_blocks, page_size, 1, 576) bf16; int32 block_table (batch,
+ *  max_pages_per_seq): key j of sequence b is row j % page_size of page
+ *  block_table[b][j / page_size]; int32 seqlens_kv (batch): keys of each
+ *  sequence (Lk_b).
+ *  sparse_indices int32 (batch, seqlen_q, 1, topk): index i >= 0 selects the
+ *  sparse_block_size keys i*s .. i*s + s - 1 (s = sparse_block_size; s = 1
+ *  selects token i); keys >= Lk_b, and in mode 3 keys after
+ *  t + (Lk_b - seqlen_q), are skipped; duplicates count each time.
+ *  Supported: hq a multiple of 16, num_blocks * page_size at most 3728270
+ *  rows (32-bit row byte offsets into the pool). Skipped keys are fetched
+ *  from pool row 0 and masked, so it must hold finite values. Device values
+ *  are not checked: referenced block-table entries must name pool pages.
+ */
+int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_blocks,
+                             int32_t page_size, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* seqlens_kv,
+                             const int32_t* sparse_indices, int32_t topk,
+                             int32_t sparse_block_size, int32_t batch, int32_t seqlen_q,
+                             int32_t hq, float scale, int32_t sparse_mode, const float* sinks,
+                             void* out, float* lse, void* stream);
 
 /*
  * attn_debug_gather_paged - copies logical rows [0, cache_seqlens[b]) of one

@@ -29,7 +29,7 @@ def lib():
 def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
-              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -168,6 +168,25 @@ def test_mla_and_sparse_host_checks(lib):
     # per-sequence row byte offsets must fit 32 bits
     assert lib.mla_sparse_fwd(P, P, P, 16, 1, 1, 3728271, 64, 0.1, 0, None, P, None,
                               None) == B.ATTN_EUNSUPPORTED
+
+
+def test_sparse_paged_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, kc=P, nb=100, page=64, bt=P, mp=4, lens=P, idx=P, topk=2048, bs=1, batch=2,
+                 sq=4, hq=64, scale=0.1, mode=3)
+        a.update(kw)
+        return lib.mla_sparse_paged_fwd(a["q"], a["kc"], a["nb"], a["page"], a["bt"], a["mp"],
+                                        a["lens"], a["idx"], a["topk"], a["bs"], a["batch"],
+                                        a["sq"], a["hq"], a["scale"], a["mode"], None, P, None,
+                                        None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(nb=0) == B.ATTN_EEMPTY
+    assert call(bt=None) == B.ATTN_EINVAL
+    assert call(mode=1) == B.ATTN_EINVAL
+    assert call(bs=3) == B.ATTN_EINVAL
+    assert call(bs=256) == B.ATTN_EINVAL
+    assert call(hq=8) == B.ATTN_EUNSUPPORTED
+    assert call(nb=60000, page=64) == B.ATTN_EUNSUPPORTED   # pool rows x 1152 B above 2^32
 
 
 def test_combine_host_checks(lib):

@@ -27,6 +27,8 @@ SPARSE_CASES = [
     ("mode0_all", 1, 9, 300, 32, 128, 0, False),
     ("topk_not_tile_multiple", 1, 7, 500, 64, 100, 3, True),
     ("hq128", 1, 3, 2000, 128, 256, 3, True),
+    # 5000 indices: the key list is staged in two chunks
+    ("topk_two_chunks", 1, 3, 8192, 16, 5000, 3, True),
 ]
 
 

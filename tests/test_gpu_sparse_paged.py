@@ -1,0 +1,89 @@
+"""GPU parity of mla_sparse_paged_fwd (block-sparse MLA over a paged latent
+cache, sparse_block_size) against the float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from attention_attn_fwd_02_amd import binding as B
+from attention_attn_fwd_02_amd import inputs
+from oracle import attention as orc
+from tests.gpu_util import TOL_O_BF16, compare, dev, log
+
+pytestmark = pytest.mark.gpu
+
+NAN_BF16 = np.uint16(0x7FC0)
+
+
+def run(w, kv_cache=None):
+    return B.mla_sparse_paged_fwd(dev(w.q), dev(w.kv_cache if kv_cache is None else kv_cache),
+                                  dev(w.block_table), dev(w.seqlens_kv), dev(w.indices), w.scale,
+                                  w.block_size, w.sparse_mode,
+                                  None if w.sinks is None else dev(w.sinks))
+
+
+def oracle(w):
+    return orc.mla_sparse_paged(inputs.bits_to_f32(w.q), inputs.bits_to_f32(w.kv_cache),
+                                w.block_table, w.seqlens_kv, w.page_size, w.indices, w.scale,
+                                w.sparse_mode, w.sinks, w.block_size, dv=w.dv)
+
+
+CASES = [
+    # name, lens_kv, sq, topk, block_size, page, hq, mode, sinks
+    ("tokens_page64", [300, 1000], 4, 64, 1, 64, 64, 3, True),
+    ("blocks4_page16", [513, 200], 3, 32, 4, 16, 32, 3, False),
+    # 80 blocks of 64 keys: 5120 keys, two staged chunks of the key list
+    ("blocks64_two_chunks", [6000, 2500], 2, 80, 64, 64, 64, 3, True),
+    ("blocks128_page32", [3000], 2, 40, 128, 32, 16, 3, False),
+    ("blocks8_mode0", [400, 64], 3, 16, 8, 64, 16, 0, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_sparse_paged(case):
+    name, lens, sq, topk, bs, page, hq, mode, sinks = case
+    log("case sparse_paged", name)
+    w = inputs.sparse_paged(8000 + len(name), lens, sq, topk, bs, page, hq=hq, sparse_mode=mode,
+                            with_sinks=sinks, spare_pages=2)
+    if mode == 0:
+        # indices past the causal limit (still inside the sequence) now count
+        w.indices[:, :, 0, -1] = (np.asarray(lens)[:, None] - 1) // bs
+    o, lse = run(w)
+    torch.cuda.synchronize()
+    ro, rl = oracle(w)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_sparse_paged_poisoned_pool():
+    """NaN in pool pages no sequence references (after the used ones, so pool
+    row 0 stays finite) and in the rows past each sequence's length inside its
+    last page, with blocks that straddle the end of the sequence."""
+    lens, page, bs = [250, 77], 32, 16
+    w = inputs.sparse_paged(8100, lens, 3, 24, bs, page, hq=16, spare_pages=3)
+    kc = w.kv_cache.copy()
+    used = set(int(p) for p in w.block_table.ravel() if p >= 0)
+    for p in range(kc.shape[0]):
+        if p not in used:
+            kc[p] = NAN_BF16
+    for b, n in enumerate(lens):
+        if n % page:
+            kc[int(w.block_table[b, (n - 1) // page]), n % page:] = NAN_BF16
+    log("case sparse_paged_poisoned_pool")
+    o, lse = run(w, kc)
+    torch.cuda.synchronize()
+    ro, rl = oracle(w)
+    compare("sparse_paged_poisoned_pool", o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_sparse_paged_matches_dense_layout():
+    """Block size 1 over pages laid out in order equals mla_sparse_fwd on the
+    contiguous cache, bit for bit (the same rows in the same order)."""
+    s = inputs.sparse_mla(8200, batch=1, sq=6, sk=1024, hq=64, topk=256)
+    kv = s.kv.reshape(16, 64, 1, 576)
+    table = np.arange(16, dtype=np.int32)[None]
+    o1, l1 = B.mla_sparse_fwd(dev(s.q), dev(s.kv), dev(s.indices), s.scale, 3, dev(s.sinks))
+    o2, l2 = B.mla_sparse_paged_fwd(dev(s.q), dev(kv), dev(table),
+                                    dev(np.array([1024], np.int32)), dev(s.indices), s.scale, 1,
+                                    3, dev(s.sinks))
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
