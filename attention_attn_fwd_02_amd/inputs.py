@@ -30,6 +30,7 @@ SEED_MLA_DECODE = 1004
 SEED_SPARSE_MLA = 1005
 SEED_CHUNKED_PREFILL = 1006
 SEED_PAGED_DECODE_FP8 = 1007
+SEED_SPARSE_PAGED = 1008
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -473,6 +474,16 @@ def sparse_paged(seed: int, lens_kv, sq: int, topk: int, block_size: int = 1, pa
     sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
     return SparsePaged(q, kv, table, lens.astype(np.int32), page, idx, block_size, sinks, dv,
                        1.0 / np.sqrt(d), sparse_mode)
+
+
+def sparse_paged_blocks(seed: int = SEED_SPARSE_PAGED, batch: int = 4, sq: int = 4096,
+                        sk: int = 32768, topk: int = 32, block_size: int = 64, page: int = 64,
+                        hq: int = 64) -> SparsePaged:
+    """Block-sparse MLA over a paged cache: the sparse-MLA shape (4 x 4096
+    query tokens, 32768 cached keys per sequence, Hq=64, D=576, sinks) with
+    32 blocks of 64 keys selected per token (2048 keys, as the token-sparse
+    workload), page 64, mode 3."""
+    return sparse_paged(seed, [sk] * batch, sq, topk, block_size, page, hq)
 
 
 def sparse_mla(seed: int = SEED_SPARSE_MLA, batch: int = 4, sq: int = 4096, sk: int = 32768,

@@ -6,7 +6,8 @@ attn_fwd_varlen call over the whole packed batch (the single kernel of the
 prefill path). The same JSON line carries the other workloads as
 `secondary` entries: paged GQA decode (KV-read GB/s, step = plan + split
 decode + combine) with a bf16 and with an FP8 cache, MLA-absorbed paged
-decode, chunked prefill over a paged cache and sparse MLA with sinks.
+decode, chunked prefill over a paged cache, sparse MLA with sinks and
+block-sparse MLA over a paged cache.
 
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Every timed region is bracketed by torch.cuda.synchronize() and
@@ -308,6 +309,35 @@ def bench_chunked(steps, warmup):
     return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lc=lc.tolist())
 
 
+def bench_sparse_paged(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.sparse_paged_blocks()
+    q, kc, bt = dev(w.q), dev(w.kv_cache), dev(w.block_table)
+    lens, idx, sinks = dev(w.seqlens_kv), dev(w.indices), dev(w.sinks)
+    b, sq, hq, d = w.q.shape
+    out = torch.empty((b, sq, hq, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.mla_sparse_paged_fwd(q, kc, bt, lens, idx, w.scale, w.block_size, 3, sinks, out, lse)
+
+    ms = time_steps(step, max(1, steps // 4), max(1, warmup // 2))
+    # every drawn block lies in its token's causal prefix; count its keys there
+    valid = 0
+    for bi in range(b):
+        lk = int(w.seqlens_kv[bi])
+        lim = lk - sq + np.arange(sq)                                   # last visible key
+        blk = w.indices[bi, :, 0, :].astype(np.int64)
+        first = blk * w.block_size
+        n = np.clip(lim[:, None] - first + 1, 0, w.block_size)
+        valid += int(np.where(blk >= 0, n, 0).sum())
+    flops = valid * hq * 2.0 * (576 + 512)
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12,
+                gathered_gbs=valid * 1152 / (ms * 1e-3) / 1e9)
+
+
 TRAFFIC_PATH = os.path.join(ROOT, "profiles", "k_varlen_bf16_d128_traffic.txt")
 # the sources the prefill kernel is compiled from (its translation unit)
 PREFILL_SOURCES = ("kernels_prefill.hip", "prefill_bf16.h", "device_common.h", "launch.h")
@@ -413,7 +443,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
-    ap.add_argument("--only", default="prefill,decode,decode_fp8,mla,chunked,sparse")
+    ap.add_argument("--only",
+                    default="prefill,decode,decode_fp8,mla,chunked,sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -533,6 +564,21 @@ def main():
             "roofline": {"bound": "mfma", "achieved": sp["tflops"], "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": sp["tflops"] / PEAK_BF16_TFLOPS,
                          "traffic": None, "kernel": "k_sparse"}})
+
+    if "sparse_paged" in only:
+        log("block-sparse paged mla ...")
+        sp2 = bench_sparse_paged(args.steps, args.warmup)
+        log(f"sparse_paged {sp2['ms']:.3f} ms {sp2['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "block-sparse paged MLA + sink TFLOP/s", "value": sp2["tflops"],
+            "unit": "TFLOP/s", "ms_per_step": sp2["ms"], "gathered_gbs": sp2["gathered_gbs"],
+            "workload": "block-sparse MLA over a paged latent cache: 4 x 4096 query tokens, "
+                        "32768 keys per sequence in pages of 64, 32 blocks of 64 keys per token "
+                        "(sparse_block_size 64), Hq=64, D=576 (V = first 512), sinks, bf16 "
+                        "(seed 1008)",
+            "roofline": {"bound": "mfma", "achieved": sp2["tflops"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": sp2["tflops"] / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "k_sparse (paged)"}})
 
     cpu = None
     if not args.no_cpu:

@@ -87,3 +87,21 @@ def test_sparse_paged_matches_dense_layout():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1, l2)
+
+
+def test_sparse_paged_workload():
+    """The benchmarked block-sparse workload (seed 1008: 4 x 4096 tokens,
+    32768 keys per sequence in pages of 64, 32 blocks of 64 keys per token,
+    Hq=64, sinks), in the launch configuration bench.py times; twelve tokens
+    spread over the batch compared element by element."""
+    w = inputs.sparse_paged_blocks()
+    log("case sparse_paged_workload")
+    o, lse = run(w)
+    torch.cuda.synchronize()
+    toks = [(b, t) for b in range(4) for t in (0, 1777, 4095)]
+    ro, rl = orc.mla_sparse_paged(inputs.bits_to_f32(w.q), inputs.bits_to_f32(w.kv_cache),
+                                  w.block_table, w.seqlens_kv, w.page_size, w.indices, w.scale,
+                                  3, w.sinks, w.block_size, dv=w.dv, tokens=toks)
+    og = torch.stack([o[b, t] for b, t in toks])
+    lg = torch.stack([lse[b, :, t] for b, t in toks])
+    compare("sparse_paged_workload", og, lg, ro, rl, TOL_O_BF16)
