@@ -47,14 +47,16 @@ NEG_INF = -np.inf
 # --------------------------------------------------------------------------
 # Row definition
 # --------------------------------------------------------------------------
-def attend_rows(q, k, v, scale, visible=None, sink=None):
+def attend_rows(q, k, v, scale, visible=None, sink=None, bias=None):
     """Attention of M query rows against N key rows.
 
     q (M, D), k (N, D), v (N, Dv): float arrays (widened to float64).
     visible (M, N) bool, True where key j may be seen by row i; None = all.
     sink: scalar or (M,) array of sink logits, or None.
+    bias: (M, N) additive mask added to the scaled scores, or None; a -inf
+    entry removes that key from the row              [MOJO input_mask_fn]
 
-    S = scale * q k^T                                  [CANN formula; SFA formula]
+    S = scale * q k^T (+ bias)                         [CANN formula; SFA formula]
     m = max_j S, lse = log sum_j exp(S - m) + m        [CANN softmax_lse formula]
     no sink:   O = sum_j exp(S_j - m) v_j / sum_j exp(S_j - m)
     with sink: m' = max(sink, m),
@@ -72,6 +74,8 @@ def attend_rows(q, k, v, scale, visible=None, sink=None):
     if m_rows == 0 or k.shape[0] == 0:
         return o, lse
     s = scale * (q @ k.T)
+    if bias is not None:
+        s = s + np.asarray(bias, dtype=np.float64)
     if visible is not None:
         s = np.where(visible, s, NEG_INF)
     m = s.max(axis=1)
@@ -120,14 +124,17 @@ def _group(hq, hkv):
 # Packed variable-length attention (prefill)
 # --------------------------------------------------------------------------
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
-                     window=(-1, -1), sinks=None, seqs=None):
+                     window=(-1, -1), sinks=None, seqs=None, mask=None):
     """Packed varlen attention.                [MATE FMHA flash_attn_varlen_func]
 
     q (Tq, Hq, D), k (Tk, Hkv, D), v (Tk, Hkv, Dv); cu_seqlens_* (B+1) prefix
     sums with a leading 0. Sequence b owns query rows cu_q[b]:cu_q[b+1] and key
     rows cu_k[b]:cu_k[b+1]. Query head h reads KV head h // (Hq/Hkv)
     [SFA (N2, N1/N2) grouping]. sinks: (Hq,) or None. seqs: optional subset of
-    sequences to evaluate (other rows are left NaN).
+    sequences to evaluate (other rows are left NaN). mask: optional additive
+    mask (Hm, Tq, L) with Hm = 1 (all heads) or Hq: query row r of sequence b
+    adds mask[h or 0, r, j] to its scaled score with key j of the sequence
+    [MOJO flash_attention_split_kv input_mask_fn].
 
     Returns O (Tq, Hq, Dv) float64 and LSE (Hq, Tq) float64 [CANN: TND LSE is
     (Q_N, Q_T)].
@@ -147,7 +154,9 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
         for h in range(hq):
             kh = h // g
             sink = None if sinks is None else float(sinks[h])
-            ob, lb = attend_rows(q[q0:q1, h], k[k0:k1, kh], v[k0:k1, kh], scale, vis, sink)
+            bias = None if mask is None else mask[h if mask.shape[0] > 1 else 0, q0:q1, :lk]
+            ob, lb = attend_rows(q[q0:q1, h], k[k0:k1, kh], v[k0:k1, kh], scale, vis, sink,
+                                 bias)
             o[q0:q1, h] = ob
             lse[h, q0:q1] = lb
     return o, lse
@@ -222,7 +231,7 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
 # --------------------------------------------------------------------------
 def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
                              block_table, cache_seqlens, page_size, scale, causal=False,
-                             window=(-1, -1), sinks=None, seqs=None):
+                             window=(-1, -1), sinks=None, seqs=None, mask=None):
     """Packed queries over a paged cache of earlier tokens plus the current
     K/V rows.                                   [MOJO flash_attention_split_kv]
 
@@ -231,7 +240,8 @@ def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cac
     (P, page, Hkv, D|Dv) with block_table hold the cache_seqlens[b] earlier
     tokens [MATE flash_attn_with_kvcache paging]. The key sequence of b is the
     cache rows 0..Lc-1 followed by the current rows, Lk = Lc + Ln; masks are
-    those of attention_varlen over that sequence (bottom-right causal).
+    those of attention_varlen over that sequence (bottom-right causal); mask
+    columns are key positions of that sequence (cache rows first).
     Written as its definition: the concatenated K/V, then attention_varlen.
     Returns O (Tq, Hq, Dv) and LSE (Hq, Tq).
     """
@@ -247,7 +257,7 @@ def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cac
         vs.append(vb)
         cu.append(cu[-1] + len(kb))
     return attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cu_seqlens_q,
-                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs)
+                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs, mask)
 
 
 def plan_words(batch, max_splits):

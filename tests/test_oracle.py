@@ -329,6 +329,58 @@ def check_kvcache_special_cases():
     np.testing.assert_allclose(lse, l2, atol=1e-14)
 
 
+def check_additive_mask():
+    """Additive mask [MOJO input_mask_fn]: zeros change nothing; a constant c
+    on every key of a row leaves O and adds c to LSE (softmax is shift
+    invariant); -inf entries equal removing those keys; a finite mask agrees
+    with brute force on exp(scale q.k + mask)."""
+    q, k, v, cq, ck, kc, vc, table, lc, page = _kvcache_case(44, [4, 3], [4, 3], [5, 2])
+    tq, hq = q.shape[0], q.shape[1]
+    ld = 12
+    base = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True)
+    z = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True,
+                                     mask=np.zeros((1, tq, ld)))
+    np.testing.assert_allclose(z[0], base[0], atol=0)
+    c = np.linspace(-1.5, 0.75, hq)[:, None, None] * np.ones((hq, tq, ld))
+    sh = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True,
+                                      mask=c)
+    np.testing.assert_allclose(sh[0], base[0], atol=1e-13)
+    np.testing.assert_allclose(sh[1], base[1] + c[:, :, 0], atol=1e-13)
+    # a random mask with -inf on key 0 of every row, against brute force that
+    # drops key 0 and adds the mask to each remaining score
+    rng = _rng(45)
+    m = rng.standard_normal((hq, tq, ld))
+    m[:, :, 0] = -np.inf
+    o, lse = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True,
+                                          mask=m)
+    grp = hq // k.shape[1]
+    for b in range(len(lc)):
+        nq, nn, nc = cq[b + 1] - cq[b], ck[b + 1] - ck[b], int(lc[b])
+        for h in range(hq):
+            g = h // grp
+            keys = [list(kc[table[b, j // page], j % page, g]) for j in range(nc)]
+            vals = [list(vc[table[b, j // page], j % page, g]) for j in range(nc)]
+            keys += [list(k[ck[b] + j, g]) for j in range(nn)]
+            vals += [list(v[ck[b] + j, g]) for j in range(nn)]
+            lk = nc + nn
+            for t in range(nq):
+                r = cq[b] + t
+                w = [math.exp(0.6 * sum(a * bb for a, bb in zip(q[r, h], keys[j])) + m[h, r, j])
+                     if (j <= t + lk - nq and j > 0) else 0.0 for j in range(lk)]
+                tot = math.fsum(w)
+                if tot == 0.0:
+                    assert np.isneginf(lse[h, r])
+                    continue
+                assert abs(lse[h, r] - math.log(tot)) <= 1e-12
+                ref = [math.fsum(w[j] * vals[j][e] for j in range(lk)) / tot
+                       for e in range(v.shape[2])]
+                np.testing.assert_allclose(o[r, h], ref, rtol=0, atol=1e-12)
+
+
+def test_additive_mask():
+    check_additive_mask()
+
+
 def test_kvcache_brute_force():
     check_kvcache_brute_force()
 
@@ -675,14 +727,14 @@ def _mutants():
     base_combine = orc.combine
     base_gather = orc.gather_paged
 
-    def no_scale(q, k, v, scale, visible=None, sink=None):
-        return base_rows(q, k, v, 1.0, visible, sink)
+    def no_scale(q, k, v, scale, visible=None, sink=None, bias=None):
+        return base_rows(q, k, v, 1.0, visible, sink, bias)
 
-    def sink_dropped(q, k, v, scale, visible=None, sink=None):
-        return base_rows(q, k, v, scale, visible, None)
+    def sink_dropped(q, k, v, scale, visible=None, sink=None, bias=None):
+        return base_rows(q, k, v, scale, visible, None, bias)
 
-    def lse_without_max(q, k, v, scale, visible=None, sink=None):
-        o, lse = base_rows(q, k, v, scale, visible, sink)
+    def lse_without_max(q, k, v, scale, visible=None, sink=None, bias=None):
+        o, lse = base_rows(q, k, v, scale, visible, sink, bias)
         qq, kk = np.asarray(q, float), np.asarray(k, float)
         if kk.shape[0] == 0:
             return o, lse
@@ -691,10 +743,10 @@ def _mutants():
             s = np.where(visible, s, -np.inf)
         return o, lse - s.max(axis=1)
 
-    def transposed_kv(q, k, v, scale, visible=None, sink=None):
+    def transposed_kv(q, k, v, scale, visible=None, sink=None, bias=None):
         k = np.asarray(k)
         v = np.asarray(v)
-        return base_rows(q, k[::-1], v, scale, visible, sink)
+        return base_rows(q, k[::-1], v, scale, visible, sink, bias)
 
     def causal_top_left(lq, lk, causal, window_left=-1, window_right=-1, q_pos=None, k_pos=None):
         return base_vis(lk, lk, causal, window_left, window_right,
@@ -718,7 +770,7 @@ def _mutants():
 
     def kvcache_order_swapped(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
                               block_table, cache_seqlens, page_size, scale, causal=False,
-                              window=(-1, -1), sinks=None, seqs=None):
+                              window=(-1, -1), sinks=None, seqs=None, mask=None):
         # current rows placed before the cached ones
         bsz = len(cu_seqlens_q) - 1
         ks, vs, cu = [], [], [0]
@@ -732,9 +784,15 @@ def _mutants():
             vs.append(vb)
             cu.append(cu[-1] + len(kb))
         return orc.attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cu_seqlens_q,
-                                    np.asarray(cu), scale, causal, window, sinks, seqs)
+                                    np.asarray(cu), scale, causal, window, sinks, seqs, mask)
 
     del base_kvc
+
+    def bias_scaled(q, k, v, scale, visible=None, sink=None, bias=None):
+        # the mask added before the scale: scale * (q k + mask)
+        if bias is not None:
+            bias = np.asarray(bias, dtype=np.float64) * scale
+        return base_rows(q, k, v, scale, visible, sink, bias)
 
     def block_keys_unscaled(indices_row, seqlen_q, seqlen_k, t, sparse_mode, block_size):
         idx = np.asarray(indices_row, dtype=np.int64)
@@ -745,7 +803,8 @@ def _mutants():
             keep &= keys <= t + (seqlen_k - seqlen_q)
         return keys[keep]
 
-    return [("sparse_block_keys", block_keys_unscaled), ("attend_rows", no_scale), ("attend_rows", sink_dropped),
+    return [("sparse_block_keys", block_keys_unscaled), ("attend_rows", bias_scaled),
+            ("attend_rows", no_scale), ("attend_rows", sink_dropped),
             ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
             ("visible_band", causal_top_left), ("visible_band", window_sides_swapped),
             ("combine", combine_unweighted), ("gather_paged", gather_swapped),
@@ -756,10 +815,10 @@ PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
         check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases,
-        check_sparse_paged]
+        check_sparse_paged, check_additive_mask]
 
 
-@pytest.mark.parametrize("i", range(10))
+@pytest.mark.parametrize("i", range(11))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
