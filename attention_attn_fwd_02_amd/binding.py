@@ -33,7 +33,7 @@ _SIGNATURES = {
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P, _P, _P, _P]),
     "attn_fwd_varlen_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
-                                     _I, _I, _I, _F, _I, _I, _I, _P, _P, _P, _P]),
+                                     _I, _I, _I, _F, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]),
     "attn_plan_words": (ctypes.c_size_t, [_I, _I]),
     "attn_plan_splits": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -145,17 +145,21 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
 
 def attn_fwd_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache, block_table,
                             cache_seqlens, max_seqlen_q, scale, causal=False, window=(-1, -1),
-                            sinks=None, out=None, lse=None, return_lse=True):
+                            sinks=None, out=None, lse=None, return_lse=True, mask=None):
     """Current tokens q (Tq,Hq,D), k (Tk,Hkv,D), v (Tk,Hkv,Dv) with cu_seqlens
     as attn_fwd_varlen, over earlier tokens in k_cache (P,page,Hkv,D) and
     v_cache (P,page,Hkv,Dv), block_table (B,max_pages) and cache_seqlens (B)
-    int32. bf16. Returns (out (Tq,Hq,Dv), lse (Hq,Tq) fp32 or None)."""
+    int32. bf16. mask: None or an additive bf16 mask (1 or Hq, Tq, ld), ld a
+    multiple of 64. Returns (out (Tq,Hq,Dv), lse (Hq,Tq) fp32 or None)."""
     _dev(q, k, v, k_cache, v_cache, dtype=torch.bfloat16)
     _dev(cu_seqlens_q, cu_seqlens_k, block_table, cache_seqlens, dtype=torch.int32)
     _dev(sinks, dtype=torch.float32)
+    _dev(mask, dtype=torch.bfloat16)
     tq, hq, d = q.shape
     hkv, dv = k.shape[1], v.shape[2]
     batch = cu_seqlens_q.numel() - 1
+    if mask is not None and (mask.dim() != 3 or mask.shape[1] != tq):
+        raise ValueError("mask must be (1 or Hq, Tq, ld)")
     if k_cache.shape[2:] != (hkv, d) or v_cache.shape[2:] != (hkv, dv):
         raise ValueError("cache heads or widths differ from k, v")
     if block_table.dim() != 2 or block_table.shape[0] != batch or cache_seqlens.numel() != batch:
@@ -170,8 +174,9 @@ def attn_fwd_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cach
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
         k_cache.shape[1], batch, int(max_seqlen_q), hq, hkv, d, dv, ATTN_BF16, float(scale),
-        int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(out), _ptr(lse),
-        _stream()))
+        int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(mask),
+        0 if mask is None else mask.shape[0], 0 if mask is None else mask.shape[2], _ptr(out),
+        _ptr(lse), _stream()))
     return out, lse
 
 

@@ -123,6 +123,7 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 int32_t max_seqlen_q, int32_t hq, int32_t hkv, int32_t d,
                                 int32_t dv, int32_t dtype, float scale, int32_t causal,
                                 int32_t window_left, int32_t window_right, const float* sinks,
+                                const void* mask, int32_t mask_heads, int32_t mask_ld,
                                 void* out, float* lse, void* stream) {
   REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 &&
               page_size > 0 && max_pages_per_seq > 0,
@@ -141,6 +142,13 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
+  if (mask) {
+    REQUIRE(mask_heads == 1 || mask_heads == hq, ATTN_EINVAL,
+            "mask_heads must be 1 or hq (got %d)", mask_heads);
+    REQUIRE(mask_ld > 0 && mask_ld % 64 == 0, ATTN_EINVAL,
+            "mask_ld must be a positive multiple of 64 (got %d)", mask_ld);
+    REQUIRE((long)mask_ld * 2 * 32 < (1L << 32), ATTN_EUNSUPPORTED, "mask_ld too large");
+  }
   attn::VarlenArgs a{};
   a.q = q;
   a.k = k;
@@ -157,6 +165,9 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
   a.sinks = sinks;
   a.out = out;
   a.lse = lse;
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  a.mask_ld = mask_ld;
   a.kc = k_cache;
   a.vc = v_cache;
   a.block_table = block_table;

@@ -65,12 +65,18 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 // row j at block_table[b][j / page], slot j % page) followed by its current
 // rows [cu_k[b], cu_k[b+1]). Page sizes are multiples of 16, so each 16-row
 // block of a tile that lies wholly in the cache sits on one page.
-template <class C, bool KVC>
+// MASK: an additive bf16 mask (mask_heads, Tq, mask_ld) is added to the scaled
+// scores; each wave streams its 32 rows x BN mask entries of every key tile
+// into the stage beside K and V (4 lanes per 64-byte row segment, coalesced).
+template <class C, bool KVC, bool MASK = false>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES)
 k_varlen_bf16(VarlenArgs a) {
   using T = PrefillTile<C>;
-  // ring of STAGES buffers, each one K tile followed by one V tile
-  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * 2 * C::TILE_BYTES];
+  constexpr int MASK_BAND = C::R * C::BN * 2;              // one wave's rows of a tile
+  constexpr int STAGE = 2 * C::TILE_BYTES + (MASK ? C::NW * MASK_BAND : 0);
+  constexpr int MASK_DMA = MASK ? C::BN / 16 : 0;          // mask instructions per wave
+  // ring of STAGES buffers, each one K tile, one V tile (and the mask tile)
+  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * STAGE];
   PrefillWork w;
   if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
   const int q0 = a.cu_q[w.b];
@@ -113,8 +119,28 @@ k_varlen_bf16(VarlenArgs a) {
   const char* kcb = KVC ? static_cast<const char*>(a.kc) + (size_t)w.kvh * C::D * 2 : nullptr;
   const char* vcb = KVC ? static_cast<const char*>(a.vc) + (size_t)w.kvh * C::D * 2 : nullptr;
   const int* btb = KVC ? a.block_table + (size_t)w.b * a.max_pages : nullptr;
+  // mask rows of this wave (rows past the sequence re-read its last row)
+  const char* mbase = nullptr;
+  uint32_t moff[MASK_DMA > 0 ? MASK_DMA : 1] = {};
+  if constexpr (MASK) {
+    constexpr int UPR = C::BN / 8, RPI = 64 / UPR;  // 16-byte units per row, rows per instr.
+    const int tq = a.cu_q[a.batch];
+    const int hm = a.mask_heads > 1 ? w.h : 0;
+    const int base_row = q0 + min(wrow0, lq - 1);
+    mbase = static_cast<const char*>(a.mask) + ((size_t)hm * tq + base_row) * a.mask_ld * 2;
+#pragma unroll
+    for (int n = 0; n < MASK_DMA; ++n) {
+      const int r = q0 + min(wrow0 + n * RPI + lane / UPR, lq - 1);
+      moff[n] = (uint32_t)(r - base_row) * (uint32_t)a.mask_ld * 2 + (lane % UPR) * 16;
+    }
+  }
   auto issue = [&](char* buf, int i) {
     const int j0 = bd.lo + i * C::BN;  // key index of tile row 0 (cache rows first)
+    if constexpr (MASK) {
+#pragma unroll
+      for (int n = 0; n < MASK_DMA; ++n)
+        lds_dma16_sv(mbase + j0 * 2, moff[n], buf + 2 * C::TILE_BYTES + wave * MASK_BAND + n * 1024);
+    }
     if (!KVC || j0 >= lc) {
       const int c0 = j0 - lc;  // current row of tile row 0
       if (j0 + C::BN - 1 <= last) {
@@ -179,8 +205,8 @@ k_varlen_bf16(VarlenArgs a) {
   };
   const int tdiag = trow + bd.delta;
   const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
-  auto stage = [&](int i) { return ring + i * (2 * C::TILE_BYTES); };  // i < STAGES
-  constexpr int PER_TILE = 2 * C::DMA_PER_WAVE;  // DMA instructions per wave per tile
+  auto stage = [&](int i) { return ring + i * STAGE; };  // i < STAGES
+  constexpr int PER_TILE = 2 * C::DMA_PER_WAVE + MASK_DMA;  // DMA instructions per wave per tile
   static_assert(PER_TILE * (C::STAGES - 1) < 64, "vmcnt range");
 #pragma unroll
   for (int i = 0; i < C::STAGES - 1; ++i)
@@ -206,15 +232,20 @@ k_varlen_bf16(VarlenArgs a) {
                       (bd.wl >= 0 && j0 < wrow1 + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
+    float cs = a.scale_log2;
+    if constexpr (MASK) {
+      T::add_mask(s, cur + 2 * C::TILE_BYTES + wave * MASK_BAND, cs, lane);
+      cs = 1.f;  // the scores are scaled
+    }
     if (need) {
       // visible keys of this lane's row, as tile indices
       const int hi = min(lk - 1, bd.wr < 0 ? lk - 1 : tdiag + bd.wr) - j0;
       if (bd.wl < 0) T::template mask<false>(s, lane, 0, hi);
       else T::template mask<true>(s, lane, tdiag - bd.wl - j0, hi);
     }
-    const float m_use = t.prep(s, a.scale_log2);
+    const float m_use = t.prep(s, cs);
     uint32_t pk[C::NSB * 8];
-    t.probs(s, a.scale_log2, m_use, pk);
+    t.probs(s, cs, m_use, pk);
     t.pv(cur + C::TILE_BYTES, lane, pk);
   };
   // unrolled by STAGES so that every buffer address is a constant
@@ -222,8 +253,7 @@ k_varlen_bf16(VarlenArgs a) {
 #pragma unroll
     for (int k = 0; k < C::STAGES; ++k)
       if (i + k < ntiles)
-        process(i + k, ring + k * (2 * C::TILE_BYTES),
-                ring + ((k + C::STAGES - 1) % C::STAGES) * (2 * C::TILE_BYTES));
+        process(i + k, ring + k * STAGE, ring + ((k + C::STAGES - 1) % C::STAGES) * STAGE);
   }
 
   float lse;
@@ -370,10 +400,18 @@ hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s) {
 
 hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s) {
   const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
-  if (d == 64)
+  if (a.mask) {
+    if (d == 64)
+      hipLaunchKernelGGL((k_varlen_bf16<CfgP64, true, true>), dim3(grid), dim3(CfgP64::THREADS), 0,
+                         s, a);
+    else
+      hipLaunchKernelGGL((k_varlen_bf16<CfgP128, true, true>), dim3(grid),
+                         dim3(CfgP128::THREADS), 0, s, a);
+  } else if (d == 64) {
     hipLaunchKernelGGL((k_varlen_bf16<CfgP64, true>), dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((k_varlen_bf16<CfgP128, true>), dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -26,6 +26,10 @@ struct VarlenArgs {
   const int32_t* block_table;
   const int32_t* cache_lens;
   int32_t max_pages, page;
+  // optional additive mask (mask_heads, Tq, mask_ld) bf16 added to the scaled
+  // scores; column = key position of the query's sequence
+  const void* mask;
+  int32_t mask_heads, mask_ld;
 };
 
 struct DecodeArgs {
@@ -76,7 +80,7 @@ int varlen_f32_rows(int d);
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
-hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);
+hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);  // mask: a.mask
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s);  // fmt 1 e4m3, 2 e5m2
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

@@ -246,6 +246,29 @@ struct PrefillTile {
     }
   }
 
+  // Additive mask: s <- s * c + mask * log2(e) (the base-2 scaled domain).
+  // The wave's mask band in LDS is row-major, 32 rows x BN bf16; this lane
+  // reads its row's keys mrow(g, r) in four 8-byte groups per 32-key block.
+  __device__ __forceinline__ static void add_mask(f32x16 (&s)[C::NSB], const char* mbuf,
+                                                  float cscale, int lane) {
+    const int g = lane >> 5;
+    const char* mrow = mbuf + (lane & 31) * (C::BN * 2) + g * 8;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+      for (int q8 = 0; q8 < 4; ++q8) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(mrow + (sb * 32 + q8 * 8) * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+          const int r = q8 * 4 + e;                  // mrow(g, r) = 8 q8 + 4 g + e
+          s[sb][r] = __builtin_fmaf(s[sb][r], cscale,
+                                    __builtin_bit_cast(float, bits) * kLog2e);
+        }
+      }
+    }
+  }
+
   // Lazy update of the reference max: each lane compares the max of its own
   // scores with the raw threshold thr = (m_ref + slack) / c (c > 0); only
   // when some lane exceeds it is the row max formed across the lane pair and

@@ -108,6 +108,13 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v,
  *  Lk = Lc + Ln; causal and window masks are those of attn_fwd_varlen over
  *  that sequence (bottom-right: query t sits at position t + Lk - Lq).
  *  out (Tq, hq, dv); lse NULL or float32 (hq, Tq); sinks as attn_fwd_varlen.
+ *  mask: NULL or a bf16 additive mask (mask_heads, Tq, mask_ld) [Modular
+ *  flash_attention_split_kv input_mask_fn: additive mask values]: query row
+ *  r (packed index) of head h adds mask[h or 0][r][j] to its scaled score
+ *  with key j of its sequence (cache rows first); -inf removes the key.
+ *  mask_heads is 1 (shared by all heads) or hq; mask_ld is a multiple of 64
+ *  and at least every sequence's Lk rounded up to 64 (columns up to that are
+ *  read); the mask is 16-byte aligned.
  *  Supported: dtype BF16, d = dv in {64, 128}, page_size a multiple of 16.
  *  Block-table entries past ceil(Lc / page_size) are never read. Device
  *  values are not checked: the caller keeps 0 <= cache_seqlens[b] <=
@@ -123,6 +130,7 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 int32_t max_seqlen_q, int32_t hq, int32_t hkv, int32_t d,
                                 int32_t dv, int32_t dtype, float scale, int32_t causal,
                                 int32_t window_left, int32_t window_right, const float* sinks,
+                                const void* mask, int32_t mask_heads, int32_t mask_ld,
                                 void* out, float* lse, void* stream);
 
 /*

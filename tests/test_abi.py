@@ -83,12 +83,14 @@ def test_error_message_set(lib):
 def test_varlen_kvcache_host_checks(lib):
     def call(**kw):
         a = dict(q=P, k=P, v=P, cq=P, ck=P, kc=P, vc=P, bt=P, mp=4, lens=P, page=64, batch=2,
-                 mq=8, hq=8, hkv=2, d=128, dv=128, dtype=0, scale=0.1, causal=1, wl=-1, wr=-1)
+                 mq=8, hq=8, hkv=2, d=128, dv=128, dtype=0, scale=0.1, causal=1, wl=-1, wr=-1,
+                 mask=None, mh=0, mld=0)
         a.update(kw)
         return lib.attn_fwd_varlen_kvcache(
             a["q"], a["k"], a["v"], a["cq"], a["ck"], a["kc"], a["vc"], a["bt"], a["mp"],
             a["lens"], a["page"], a["batch"], a["mq"], a["hq"], a["hkv"], a["d"], a["dv"],
-            a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None, P, None, None)
+            a["dtype"], a["scale"], a["causal"], a["wl"], a["wr"], None, a["mask"], a["mh"],
+            a["mld"], P, None, None)
     assert call(batch=0) == B.ATTN_EEMPTY
     assert call(mp=0) == B.ATTN_EEMPTY
     assert call(page=0) == B.ATTN_EEMPTY
@@ -102,6 +104,8 @@ def test_varlen_kvcache_host_checks(lib):
     assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
     assert b"page_size" in lib.attn_last_error()
+    assert call(mask=P, mh=3, mld=64) == B.ATTN_EINVAL
+    assert call(mask=P, mh=1, mld=100) == B.ATTN_EINVAL
 
 
 def test_plan_host_checks(lib):

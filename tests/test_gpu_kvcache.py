@@ -142,3 +142,61 @@ def test_kvcache_chunked_workload():
     torch.cuda.synchronize()
     ro, rl = oracle_kvcache(w, seqs=[0, 4])
     compare("kvcache_chunked_workload", o, lse, ro, rl, TOL_O_BF16)
+
+
+MASK_CASES = [
+    # name, lens_q, lens_cache, hq, hkv, d, page, causal, mask_heads, neg_inf_fraction
+    ("mask_heads_d128", [37, 200, 64], [100, 333, 0], 8, 2, 128, 64, True, 8, 0.0),
+    ("mask_shared_neginf_d128", [150, 3], [81, 500], 8, 2, 128, 16, True, 1, 0.2),
+    ("mask_d64_noncausal", [50, 130], [77, 250], 8, 1, 64, 16, False, 8, 0.1),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[c[0] for c in MASK_CASES])
+def test_kvcache_additive_mask(case):
+    """Additive bf16 mask on the scaled scores, N(0, 2^2) values with a share
+    of -inf entries, over keys of the cache and the current rows."""
+    name, lq, lc, hq, hkv, d, page, causal, mh, frac = case
+    log("case", name)
+    w = inputs.varlen_kvcache(5500 + len(name), lq, lq, lc, hq=hq, hkv=hkv, d=d, page=page,
+                              causal=causal)
+    tq = int(sum(lq))
+    ld = ((max(a + b for a, b in zip(lq, lc)) + 63) // 64) * 64 + 64
+    rng = np.random.default_rng(5600 + len(name))
+    m = (2.0 * rng.standard_normal((mh, tq, ld))).astype(np.float32)
+    m[rng.random(m.shape) < frac] = -np.inf
+    mbits = inputs.bf16_bits(m)
+    mvals = inputs.bits_to_f32(mbits).astype(np.float64)
+    o, lse = B.attn_fwd_varlen_kvcache(
+        dev(w.q), dev(w.k), dev(w.v), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k), dev(w.k_cache),
+        dev(w.v_cache), dev(w.block_table), dev(w.cache_seqlens), max(lq), w.scale, causal,
+        mask=dev(mbits))
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_varlen_kvcache(
+        w.f32("q"), w.f32("k"), w.f32("v"), w.cu_seqlens_q, w.cu_seqlens_k,
+        inputs.bits_to_f32(w.k_cache), inputs.bits_to_f32(w.v_cache), w.block_table,
+        w.cache_seqlens, w.page_size, w.scale, causal, mask=mvals)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_kvcache_mask_rows_fully_masked():
+    """Rows whose mask is -inf on every key are empty (O = 0, LSE = -inf);
+    the other rows are unaffected."""
+    lq, lc = [40, 70], [30, 100]
+    w = inputs.varlen_kvcache(5700, lq, lq, lc, hq=4, hkv=2, d=128, page=16, causal=True)
+    tq, ld = 110, 192
+    m = np.zeros((1, tq, ld), np.float32)
+    m[0, ::7] = -np.inf
+    mbits = inputs.bf16_bits(m)
+    log("case kvcache_mask_rows_fully_masked")
+    o, lse = B.attn_fwd_varlen_kvcache(
+        dev(w.q), dev(w.k), dev(w.v), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k), dev(w.k_cache),
+        dev(w.v_cache), dev(w.block_table), dev(w.cache_seqlens), max(lq), w.scale, True,
+        mask=dev(mbits))
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_varlen_kvcache(
+        w.f32("q"), w.f32("k"), w.f32("v"), w.cu_seqlens_q, w.cu_seqlens_k,
+        inputs.bits_to_f32(w.k_cache), inputs.bits_to_f32(w.v_cache), w.block_table,
+        w.cache_seqlens, w.page_size, w.scale, True, mask=inputs.bits_to_f32(mbits).astype(float))
+    assert np.isneginf(rl[:, ::7]).all()
+    compare("kvcache_mask_rows_fully_masked", o, lse, ro, rl, TOL_O_BF16)
