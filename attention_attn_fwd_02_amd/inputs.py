@@ -226,6 +226,11 @@ def chunked_prefill(seed: int = SEED_CHUNKED_PREFILL, nseq: int = 8, chunk: int 
                           hkv=hkv, d=d, page=page, causal=True)
 
 
+def chunked_mask(rows: int, ld: int, seed: int = SEED_CHUNKED_PREFILL) -> np.ndarray:
+    """A (1, rows, ld) additive mask of N(0,1) values rounded to bf16 bits."""
+    return _normal_bf16(np.random.default_rng(seed + 100), (1, rows, ld))
+
+
 @dataclasses.dataclass
 class Paged:
     """Decode against a paged cache. q (B,Sq,Hq,D) bits; k_cache (P,page,Hkv,D)

@@ -283,7 +283,7 @@ def bench_sparse(steps, warmup):
                 gathered_gbs=gathered / (ms * 1e-3) / 1e9)
 
 
-def bench_chunked(steps, warmup):
+def bench_chunked(steps, warmup, with_mask=False):
     import torch
     from attention_attn_fwd_02_amd import binding as B
     from attention_attn_fwd_02_amd import inputs
@@ -297,10 +297,16 @@ def bench_chunked(steps, warmup):
     out = torch.empty((int(lq.sum()), hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((hq, int(lq.sum())), dtype=torch.float32, device="cuda")
 
+    mask = None
+    if with_mask:
+        # one shared bf16 mask over every key of every row: N(0,1) values
+        ld = ((int((lq + lc).max()) + 63) // 64) * 64
+        mask = dev(inputs.chunked_mask(int(lq.sum()), ld))
+
     def step():
         B.attn_fwd_varlen_kvcache(t["q"], t["k"], t["v"], t["cq"], t["ck"], t["kc"], t["vc"],
                                   t["bt"], t["lens"], int(lq.max()), w.scale, True, out=out,
-                                  lse=lse)
+                                  lse=lse, mask=mask)
 
     ms = time_steps(step, steps, warmup)
     # query t of a chunk sees the cache and the chunk's rows 0..t
@@ -444,7 +450,8 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
-                    default="prefill,decode,decode_fp8,mla,chunked,sparse,sparse_paged")
+                    default="prefill,decode,decode_fp8,mla,chunked,chunked_mask,sparse,"
+                            "sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -552,6 +559,18 @@ def main():
             "roofline": {"bound": "mfma", "achieved": ch["tflops"], "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": ch["tflops"] / PEAK_BF16_TFLOPS,
                          "traffic": None, "kernel": "k_varlen_bf16 (cache + current, D=128)"}})
+    if "chunked_mask" in only:
+        log("chunked prefill with mask ...")
+        cm = bench_chunked(args.steps, args.warmup, with_mask=True)
+        log(f"chunked_mask {cm['ms']:.3f} ms {cm['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "chunked prefill TFLOP/s (cache + new K/V, additive mask)",
+            "value": cm["tflops"], "unit": "TFLOP/s", "ms_per_step": cm["ms"],
+            "workload": "the chunked-prefill workload (seed 1006) with one bf16 additive mask "
+                        "shared by all heads, N(0,1) over every (row, key), streamed beside K/V",
+            "roofline": {"bound": "mfma", "achieved": cm["tflops"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": cm["tflops"] / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "k_varlen_bf16 (cache + current, mask)"}})
     if "sparse" in only:
         log("sparse mla ...")
         sp = bench_sparse(args.steps, args.warmup)

@@ -200,3 +200,24 @@ def test_kvcache_mask_rows_fully_masked():
         w.cache_seqlens, w.page_size, w.scale, True, mask=inputs.bits_to_f32(mbits).astype(float))
     assert np.isneginf(rl[:, ::7]).all()
     compare("kvcache_mask_rows_fully_masked", o, lse, ro, rl, TOL_O_BF16)
+
+
+def test_kvcache_chunked_mask_workload():
+    """The benchmarked masked chunked-prefill workload (seed 1006 with the
+    shared N(0,1) bf16 mask), in the launch configuration bench.py times;
+    sequences 0 and 4 compared element by element."""
+    w = inputs.chunked_prefill()
+    lq = np.diff(w.cu_seqlens_q)
+    ld = ((int((lq + w.cache_seqlens).max()) + 63) // 64) * 64
+    mbits = inputs.chunked_mask(int(lq.sum()), ld)
+    log("case kvcache_chunked_mask_workload")
+    o, lse = B.attn_fwd_varlen_kvcache(
+        dev(w.q), dev(w.k), dev(w.v), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k), dev(w.k_cache),
+        dev(w.v_cache), dev(w.block_table), dev(w.cache_seqlens), int(lq.max()), w.scale, True,
+        mask=dev(mbits))
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_varlen_kvcache(
+        w.f32("q"), w.f32("k"), w.f32("v"), w.cu_seqlens_q, w.cu_seqlens_k,
+        inputs.bits_to_f32(w.k_cache), inputs.bits_to_f32(w.v_cache), w.block_table,
+        w.cache_seqlens, w.page_size, w.scale, True, seqs=[0, 4], mask=inputs.bits_to_f32(mbits))
+    compare("kvcache_chunked_mask_workload", o, lse, ro, rl, TOL_O_BF16)
