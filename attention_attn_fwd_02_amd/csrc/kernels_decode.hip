@@ -80,67 +80,22 @@ k_decode(DecodeArgs a) {
   }
   wait_vmcnt<0>();  // Q in registers before any DMA is in flight
 
-  if constexpr (C::FP8) {
-    // FP8 cache: byte rows, one DMA instruction per 8 tile rows
-    const size_t tok = (size_t)a.hkv * C::D;  // bytes per token (K and V alike)
-    const char* kcb = static_cast<const char*>(a.kc) + (size_t)kvh * C::D;
-    const char* vcb = static_cast<const char*>(a.vc) + (size_t)kvh * C::DV;
-    const int* btb = a.block_table + (size_t)b * a.max_pages;
-    const int kv_last = kv1 - 1;
-    const uint32_t k0 = T::lane_off8(lane, (uint32_t)tok, 0), k1 = T::lane_off8(lane, (uint32_t)tok, 1);
-    auto issue = [&](char* st, int ti) {
-      const int j0 = kv0 + ti * C::BN;
-      const int j1 = min(j0 + 16, kv_last);
-      const int lp0 = j0 / a.page, lp1 = j1 / a.page;
-      int p0, p1;
-      sload2_uniform(btb + lp0, btb + lp1, p0, p1);
-      const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
-      const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
-      const int rmax = kv_last - j0;
-      if (rmax >= C::BN - 1) {
-        auto kb = [&](int r8) {
-          return kcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok;
-        };
-        auto vb = [&](int r8) {
-          return vcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok;
-        };
-        T::dma_tile8_sv(st, kb, vb, k0, k1, k0, k1);
-      } else {
-        // last tile of the split: rows past its last key re-read that key
-        auto row = [&](int rr) { rr = min(rr, rmax); return (rr >> 4 ? slot1 : slot0) + (rr & 15); };
-        T::dma_tile8(
-            st, [&](int rr) { return kcb + row(rr) * tok; },
-            [&](int rr) { return vcb + row(rr) * tok; }, lane);
-      }
-    };
-    const int first_t = (mt * C::ROWS) / grp;
-    const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
-    stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
-      const int j0 = kv0 + ti * C::BN;
-      const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
-      f32x4 sc[C::NSB];
-      tile.qk(st, lane, sc);
-      const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
-      const float m_use = tile.prep(sc, cscale, lane, need,
-                                    [&](int jr) { return j0 + jr <= hi_vis; });
-      uint32_t pk[C::NSB * 2];
-      tile.probs(sc, cscale, m_use, pk);
-      tile.pv(st, lane, pk);
-    });
-  } else {
-
-  const bf16_t* kc = static_cast<const bf16_t*>(a.kc) + (size_t)kvh * C::D;
-  const bf16_t* vc =
-      (C::VSHARED ? static_cast<const bf16_t*>(a.kc) : static_cast<const bf16_t*>(a.vc)) +
-      (size_t)kvh * C::DV;
+  // byte strides of one token's row in the caches and this KV head's column
+  const size_t tok_k = (size_t)a.hkv * C::D * C::EB, tok_v = (size_t)a.hkv * C::DV * C::EB;
+  const char* kcb = static_cast<const char*>(a.kc) + (size_t)kvh * C::D * C::EB;
+  const char* vcb = static_cast<const char*>(C::VSHARED ? a.kc : a.vc) + (size_t)kvh * C::DV * C::EB;
   const int* btb = a.block_table + (size_t)b * a.max_pages;
   const int kv_last = kv1 - 1;
-  const size_t tok_k = (size_t)a.hkv * C::D, tok_v = (size_t)a.hkv * C::DV;
-  const uint32_t kstride = (uint32_t)(tok_k * 2), vstride = (uint32_t)(tok_v * 2);
-  const uint32_t klane = T::k_lane_off(lane, kstride);
-  const uint32_t vlane = T::v_lane_off(lane, vstride);
-  const char* kcb = reinterpret_cast<const char*>(kc);
-  const char* vcb = reinterpret_cast<const char*>(vc);
+  // lane parts of the saddr-form DMA: bf16 tiles one offset each for K and V;
+  // FP8 tiles two (the swizzle depends on one bit of the 8-row group)
+  uint32_t klane = 0, vlane = 0, k8[2] = {0, 0};
+  if constexpr (C::FP8) {
+    k8[0] = T::lane_off8(lane, (uint32_t)tok_k, 0);
+    k8[1] = T::lane_off8(lane, (uint32_t)tok_k, 1);
+  } else {
+    klane = T::k_lane_off(lane, (uint32_t)tok_k);
+    vlane = T::v_lane_off(lane, (uint32_t)tok_v);
+  }
   auto issue = [&](char* st, int ti) {
     // A 16-row block of a tile lies on one page (pages are multiples of 16
     // rows and splits start on page boundaries). slot0 / slot1: cache slot
@@ -154,23 +109,39 @@ k_decode(DecodeArgs a) {
     const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
     const int rmax = kv_last - j0;
     if (rmax >= C::BN - 1) {
-      T::dma_tile_sv(
-          st,
-          [&](int rb, int colb) {
-            return typename T::Src{kcb + (rb ? slot1 : slot0) * (long)kstride + colb, klane};
-          },
-          [&](int rb, int sub, int colb) {
-            return typename T::Src{
-                vcb + (rb ? slot1 : slot0) * (long)vstride + sub * 8 * (long)vstride + colb, vlane};
-          },
-          wave);
+      if constexpr (C::FP8) {
+        auto kb = [&](int r8) {
+          return kcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok_k;
+        };
+        auto vb = [&](int r8) {
+          return vcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok_v;
+        };
+        T::dma_tile8_sv(st, kb, vb, k8[0], k8[1], k8[0], k8[1]);
+      } else {
+        T::dma_tile_sv(
+            st,
+            [&](int rb, int colb) {
+              return typename T::Src{kcb + (rb ? slot1 : slot0) * (long)tok_k + colb, klane};
+            },
+            [&](int rb, int sub, int colb) {
+              return typename T::Src{
+                  vcb + ((rb ? slot1 : slot0) + sub * 8) * (long)tok_v + colb, vlane};
+            },
+            wave);
+      }
     } else {
       // last tile of the split: rows past its last key re-read that key,
       // which is masked
       auto row = [&](int rr) { rr = min(rr, rmax); return (rr >> 4 ? slot1 : slot0) + (rr & 15); };
-      T::dma_tile(
-          st, [&](int rr) { return kc + row(rr) * tok_k; },
-          [&](int rr) { return vc + row(rr) * tok_v; }, wave, lane);
+      if constexpr (C::FP8)
+        T::dma_tile8(
+            st, [&](int rr) { return kcb + row(rr) * tok_k; },
+            [&](int rr) { return vcb + row(rr) * tok_v; }, lane);
+      else
+        T::dma_tile(
+            st, [&](int rr) { return reinterpret_cast<const bf16_t*>(kcb + row(rr) * tok_k); },
+            [&](int rr) { return reinterpret_cast<const bf16_t*>(vcb + row(rr) * tok_v); }, wave,
+            lane);
     }
   };
   const int first_t = (mt * C::ROWS) / grp;
@@ -182,13 +153,12 @@ k_decode(DecodeArgs a) {
     tile.qk(st, lane, sc);
     tile.exchange(xchg, wave, lane, sc);
     const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
-    const float m_use = tile.prep(sc, a.scale_log2, lane, need,
+    const float m_use = tile.prep(sc, cscale, lane, need,
                                   [&](int jr) { return j0 + jr <= hi_vis; });
     uint32_t pk[C::NSB * 2];
-    tile.probs(sc, a.scale_log2, m_use, pk);
+    tile.probs(sc, cscale, m_use, pk);
     tile.pv(st, lane, pk);
   });
-  }
 
   float lse;
   const float inv = tile.finish(false, 0.f, lse) * vscale;
