@@ -31,6 +31,7 @@ SEED_SPARSE_MLA = 1005
 SEED_CHUNKED_PREFILL = 1006
 SEED_PAGED_DECODE_FP8 = 1007
 SEED_SPARSE_PAGED = 1008
+SEED_VARLEN_PREFILL_FP8 = 1009
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -383,6 +384,72 @@ def paged_fp8(seed: int, lens, fmt: str = "e4m3", sq: int = 1, hq: int = 32, hkv
     v8 = _normal_fp8(rng, (pool, page, hkv, d), fmt, cmult((1.0 / vd).astype(np.float32)))
     return PagedFP8(q8, k8, v8, fmt, ds[0], ds[1], ds[2], table, lens.astype(np.int32), page,
                     1.0 / np.sqrt(d), causal)
+
+
+@dataclasses.dataclass
+class DenseFP8:
+    """Packed varlen problem with FP8 codes: q (Tq,Hq,D), k (Tk,Hkv,D),
+    v (Tk,Hkv,Dv) uint8 of format fmt; descales float32 (B, Hkv) or None."""
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    fmt: str
+    q_descale: np.ndarray | None
+    k_descale: np.ndarray | None
+    v_descale: np.ndarray | None
+    cu_seqlens_q: np.ndarray
+    cu_seqlens_k: np.ndarray
+    scale: float
+    causal: bool
+    window: tuple
+
+
+def varlen_fp8(seed: int, lens_q, lens_k=None, fmt: str = "e4m3", hq: int = 32, hkv: int = 8,
+               d: int = 128, causal: bool = True, window=(-1, -1),
+               descale: bool = True) -> DenseFP8:
+    """N(0,1) Q, K, V stored as FP8 codes of x / descale, descales per
+    (sequence, KV head) from U[0.25, 4] (or none). Draw order: descales, Q,
+    K, V."""
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = lens_q if lens_k is None else np.asarray(lens_k, dtype=np.int64)
+    b = len(lens_q)
+    ds = [rng.uniform(0.25, 4.0, size=(b, hkv)).astype(np.float32) if descale else None
+          for _ in range(3)]
+    one = np.ones((b, hkv), np.float32)
+    qd, kd, vd = (one if x is None else x for x in ds)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    seq_q = np.repeat(np.arange(b), lens_q)          # sequence of each packed row
+    seq_k = np.repeat(np.arange(b), lens_k)
+    grp = hq // hkv
+    qinv = np.repeat(1.0 / qd, grp, axis=1).astype(np.float32)   # (B, Hq)
+    kinv, vinv = (1.0 / kd).astype(np.float32), (1.0 / vd).astype(np.float32)
+
+    def rows_q(r0, r1):                    # rows of q are (token, head)
+        r = np.arange(r0, r1)
+        return qinv[seq_q[r // hq], r % hq]
+
+    def rows_kv(inv):
+        def f(r0, r1):
+            r = np.arange(r0, r1)
+            return inv[seq_k[r // hkv], r % hkv]
+        return f
+
+    q = _normal_fp8(rng, (int(lens_q.sum()), hq, d), fmt, rows_q)
+    k = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(kinv))
+    v = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(vinv))
+    return DenseFP8(q, k, v, fmt, ds[0], ds[1], ds[2], cu_q, cu_k, 1.0 / np.sqrt(d), causal,
+                    tuple(window))
+
+
+def varlen_prefill_fp8(seed: int = SEED_VARLEN_PREFILL_FP8) -> DenseFP8:
+    """The varlen causal GQA prefill shape (8 sequences U[512, 4096], Hq=32,
+    Hkv=8, D=128) with e4m3 Q/K/V codes and per-(sequence, KV head)
+    descales."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(512, 4096, endpoint=True, size=8)
+    return varlen_fp8(int(rng.integers(0, 2**63 - 1)), lens, fmt="e4m3")
 
 
 def paged_decode_fp8(seed: int = SEED_PAGED_DECODE_FP8, batch: int = 64, lo: int = 1024,

@@ -25,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from oracle.attention import _group, attend_rows, gather_paged, visible_band
+from oracle.attention import _group, attend_rows, attention_varlen, gather_paged, visible_band
 
 FORMATS = {"e4m3": (4, 3, 7), "e5m2": (5, 2, 15)}   # exponent bits, mantissa bits, bias
 
@@ -85,3 +85,33 @@ def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_
             o[b, :, h] = ob
             lse[b, h] = lb
     return o, lse
+
+
+def attention_varlen_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, cu_seqlens_q,
+                         cu_seqlens_k, scale, causal=False, window=(-1, -1), sinks=None,
+                         seqs=None):
+    """Packed varlen attention on FP8 codes.  [MATE FMHA FP8 dtype notes;
+    flash_attn_varlen_func]
+
+    q8 (Tq, Hq, D), k8 (Tk, Hkv, D), v8 (Tk, Hkv, Dv) uint8 codes of fmt;
+    descales float (B, Hkv) or None (= 1). The rows of sequence b are
+    decode(x8) * descale[b, kv head] (query head h: its KV head h // (Hq/Hkv));
+    then attention_varlen. Returns O (Tq, Hq, Dv), LSE (Hq, Tq)."""
+    tq, hq, _ = q8.shape
+    hkv = k8.shape[1]
+    g = _group(hq, hkv)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    bsz = len(cq) - 1
+    one = np.ones((bsz, hkv))
+    qd = one if q_descale is None else np.asarray(q_descale, np.float64)
+    kd = one if k_descale is None else np.asarray(k_descale, np.float64)
+    vd = one if v_descale is None else np.asarray(v_descale, np.float64)
+    q = decode(q8, fmt)
+    k = decode(k8, fmt)
+    v = decode(v8, fmt)
+    for b in range(bsz):
+        q[cq[b]:cq[b + 1]] *= np.repeat(qd[b], g)[None, :, None]
+        k[ck[b]:ck[b + 1]] *= kd[b][None, :, None]
+        v[ck[b]:ck[b + 1]] *= vd[b][None, :, None]
+    return attention_varlen(q, k, v, cq, ck, scale, causal, window, sinks, seqs)

@@ -469,6 +469,40 @@ def check_fp8_descale_identities():
     np.testing.assert_allclose(l1, l3, rtol=0, atol=1e-14)
 
 
+def check_fp8_varlen():
+    """Varlen FP8: brute force on values dequantized by torch's float8
+    conversion and the (sequence, h // (Hq/Hkv)) descales; unit descales are
+    plain varlen attention on the decoded codes."""
+    import torch
+    w = inputs.varlen_fp8(63, [3, 5], [4, 5], "e5m2", hq=4, hkv=2, d=4, causal=True)
+    o, lse = ofp8.attention_varlen_fp8(w.q, w.k, w.v, "e5m2", w.q_descale, w.k_descale,
+                                       w.v_descale, w.cu_seqlens_q, w.cu_seqlens_k, w.scale, True)
+    deq = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(
+        torch.float64).numpy()
+    cq, ck = w.cu_seqlens_q, w.cu_seqlens_k
+    for b in range(2):
+        nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+        for h in range(4):
+            g = h // 2
+            qs = [list(deq(w.q[cq[b] + t, h]) * float(w.q_descale[b, g])) for t in range(nq)]
+            ks = [list(deq(w.k[ck[b] + j, g]) * float(w.k_descale[b, g])) for j in range(nk)]
+            vs = [list(deq(w.v[ck[b] + j, g]) * float(w.v_descale[b, g])) for j in range(nk)]
+            ob, lb = brute.rows(qs, ks, vs, w.scale, visible=lambda t, j: j <= t + nk - nq)
+            for t in range(nq):
+                assert abs(lse[h, cq[b] + t] - lb[t]) <= 1e-12
+                np.testing.assert_allclose(o[cq[b] + t, h], ob[t], rtol=0, atol=1e-12)
+    o1, l1 = ofp8.attention_varlen_fp8(w.q, w.k, w.v, "e5m2", None, None, None, cq, ck,
+                                       w.scale, True)
+    o2, l2 = orc.attention_varlen(ofp8.decode(w.q, "e5m2"), ofp8.decode(w.k, "e5m2"),
+                                  ofp8.decode(w.v, "e5m2"), cq, ck, w.scale, True)
+    np.testing.assert_allclose(o1, o2, atol=0)
+    np.testing.assert_allclose(l1, l2, atol=0)
+
+
+def test_fp8_varlen():
+    check_fp8_varlen()
+
+
 def test_fp8_decode_library():
     check_fp8_decode_library()
 
@@ -486,7 +520,7 @@ def test_fp8_descale_identities():
 
 
 FP8_PINS = [check_fp8_decode_library, check_fp8_decode_values, check_fp8_attention_brute,
-            check_fp8_descale_identities]
+            check_fp8_descale_identities, check_fp8_varlen]
 
 
 def _fp8_mutants():
@@ -507,12 +541,20 @@ def _fp8_mutants():
     def v_descale_on_k(q8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, **kw):
         return base_attn(q8, k8, v8, fmt, q_descale, v_descale, k_descale, *rest, **kw)
 
+    base_varlen = ofp8.attention_varlen_fp8
+
+    def varlen_q_descale_by_query_head(q8, k8, v8, fmt, q_descale, k_descale, v_descale,
+                                       *rest, **kw):
+        qd = None if q_descale is None else np.asarray(q_descale)[:, ::-1]
+        return base_varlen(q8, k8, v8, fmt, qd, k_descale, v_descale, *rest, **kw)
+
     return [("decode", decode_bias_off), ("decode", decode_no_inf),
             ("attention_paged_fp8", q_descale_by_query_head),
-            ("attention_paged_fp8", v_descale_on_k)]
+            ("attention_paged_fp8", v_descale_on_k),
+            ("attention_varlen_fp8", varlen_q_descale_by_query_head)]
 
 
-@pytest.mark.parametrize("i", range(4))
+@pytest.mark.parametrize("i", range(5))
 def test_fp8_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _fp8_mutants()[i]
     monkeypatch.setattr(ofp8, name, fn)
