@@ -32,6 +32,8 @@ _SIGNATURES = {
     "attn_device_info": (_I, [_I, ctypes.POINTER(_I)]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P, _P, _P, _P]),
+    "attn_fwd_varlen_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
+                                 _F, _I, _I, _I, _P, _P, _P, _P]),
     "attn_fwd_varlen_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      _I, _I, _I, _F, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]),
     "attn_plan_words": (ctypes.c_size_t, [_I, _I]),
@@ -140,6 +142,36 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
                                   hq, hkv, d, dv, _dtype_code(q), float(scale), int(bool(causal)),
                                   int(window[0]), int(window[1]), _ptr(sinks), _ptr(out),
                                   _ptr(lse), _stream()))
+    return out, lse
+
+
+def attn_fwd_varlen_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
+                        fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
+                        causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
+                        return_lse=True):
+    """q (Tq,Hq,128), k (Tk,Hkv,128), v (Tk,Hkv,128) uint8 FP8 codes of fmt
+    ("e4m3" or "e5m2"); descales float32 (B,Hkv) or None; cu_seqlens int32
+    (B+1). Returns (out (Tq,Hq,128) bf16, lse (Hq,Tq) fp32 or None)."""
+    _dev(q, k, v, dtype=torch.uint8)
+    _dev(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    _dev(sinks, q_descale, k_descale, v_descale, dtype=torch.float32)
+    tq, hq, d = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    for t in (q_descale, k_descale, v_descale):
+        if t is not None and tuple(t.shape) != (batch, hkv):
+            raise ValueError("descales must be (batch, hkv)")
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_fwd_varlen_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dv, FP8_FORMATS[fmt], _ptr(q_descale),
+        _ptr(k_descale), _ptr(v_descale), float(scale), int(bool(causal)), int(window[0]),
+        int(window[1]), _ptr(sinks), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

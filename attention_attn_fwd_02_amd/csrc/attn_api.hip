@@ -115,6 +115,57 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   return hip_status(e, "attn_fwd_varlen launch");
 }
 
+int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t fp8_format,
+                            const float* q_descale, const float* k_descale,
+                            const float* v_descale, float scale, int32_t causal,
+                            int32_t window_left, int32_t window_right, const float* sinks,
+                            void* out, float* lse, void* stream) {
+  REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0, ATTN_EEMPTY,
+          "empty dimension (batch=%d max_seqlen_q=%d hq=%d hkv=%d d=%d dv=%d)", batch,
+          max_seqlen_q, hq, hkv, d, dv);
+  REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
+  REQUIRE(q && k && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL,
+          "null tensor pointer");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(fp8_format == ATTN_FP8_E4M3 || fp8_format == ATTN_FP8_E5M2, ATTN_EUNSUPPORTED,
+          "fp8_format %d (expected ATTN_FP8_E4M3 or ATTN_FP8_E5M2)", fp8_format);
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "FP8 varlen supports d = dv = 128 (got %d, %d)",
+          d, dv);
+  REQUIRE((long)hkv * d * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
+  attn::VarlenArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  const int rows = attn::varlen_bf16_rows(d);
+  a.nqt = (max_seqlen_q + rows - 1) / rows;
+  REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
+  return hip_status(attn::launch_varlen_fp8(a, fp8_format == ATTN_FP8_E4M3 ? 1 : 2,
+                                            as_stream(stream)),
+                    "attn_fwd_varlen_fp8 launch");
+}
+
 int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                 const void* k_cache, const void* v_cache,

@@ -68,10 +68,12 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 // MASK: an additive bf16 mask (mask_heads, Tq, mask_ld) is added to the scaled
 // scores; each wave streams its 32 rows x BN mask entries of every key tile
 // into the stage beside K and V (4 lanes per 64-byte row segment, coalesced).
-template <class C, bool KVC, bool MASK = false>
-__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES)
-k_varlen_bf16(VarlenArgs a) {
+// C::FP8: Q, K and V are FP8 codes; the descales of (sequence, KV head) scale
+// the scores (q and k) and the output (v).
+template <class C, bool KVC, bool MASK>
+__device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   using T = PrefillTile<C>;
+  static_assert(C::FP8 == 0 || (!KVC && !MASK), "FP8 tiles: current keys, no mask");
   constexpr int MASK_BAND = C::R * C::BN * 2;              // one wave's rows of a tile
   constexpr int STAGE = 2 * C::TILE_BYTES + (MASK ? C::NW * MASK_BAND : 0);
   constexpr int MASK_DMA = MASK ? C::BN / 16 : 0;          // mask instructions per wave
@@ -97,27 +99,31 @@ k_varlen_bf16(VarlenArgs a) {
   const bool row_ok = trow < lq;
   T t;
   t.init();
-  t.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + ((size_t)(q0 + trow) * a.hq + w.h) * C::D
-                  : nullptr,
-           lane);
+  const size_t qoff = ((size_t)(q0 + trow) * a.hq + w.h) * C::D;
+  if constexpr (C::FP8 != 0)
+    t.load_q8(row_ok ? static_cast<const uint8_t*>(a.q) + qoff : nullptr, lane);
+  else
+    t.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + qoff : nullptr, lane);
   // Q must be in registers before any LDS-DMA is in flight: the compiler
   // cannot count the DMA operations, so any vmcnt wait it placed for Q inside
   // the key loop would also drain the prefetch of the next tile.
   wait_vmcnt<0>();
 
-  const size_t kst = (size_t)a.hkv * C::D;
-  const bf16_t* kb = static_cast<const bf16_t*>(a.k) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
-  const bf16_t* vb = static_cast<const bf16_t*>(a.v) + (size_t)k0 * kst + (size_t)w.kvh * C::D;
+  // rows of this KV head, row_bytes apart (byte addresses)
+  const long row_bytes = (long)a.hkv * C::D * C::EB;
+  const size_t head = (size_t)w.kvh * C::D * C::EB;
+  const char* kb = static_cast<const char*>(a.k) + (size_t)k0 * row_bytes + head;
+  const char* vb = static_cast<const char*>(a.v) + (size_t)k0 * row_bytes + head;
   const int last = lk - 1;  // rows past the sequence re-read its last key (then masked)
   // STAGES-1 tiles are in flight while one is computed; a single barrier per
   // tile both publishes tile i and retires every wave's reads of tile i-1,
   // whose buffer then receives tile i+STAGES-1.
-  const long row_bytes = (long)kst * 2;
-  const uint32_t koff = T::template dma_lane_off<false>(lane, (uint32_t)row_bytes);
-  const uint32_t voff = T::template dma_lane_off<true>(lane, (uint32_t)row_bytes);
+  uint32_t koff[C::NOFF], voff[C::NOFF];
+  T::template dma_lane_offs<false>(lane, (uint32_t)row_bytes, wave, koff);
+  T::template dma_lane_offs<true>(lane, (uint32_t)row_bytes, wave, voff);
   // cache bases of this KV head (KVC only)
-  const char* kcb = KVC ? static_cast<const char*>(a.kc) + (size_t)w.kvh * C::D * 2 : nullptr;
-  const char* vcb = KVC ? static_cast<const char*>(a.vc) + (size_t)w.kvh * C::D * 2 : nullptr;
+  const char* kcb = KVC ? static_cast<const char*>(a.kc) + head : nullptr;
+  const char* vcb = KVC ? static_cast<const char*>(a.vc) + head : nullptr;
   const int* btb = KVC ? a.block_table + (size_t)w.b * a.max_pages : nullptr;
   // mask rows of this wave (rows past the sequence re-read its last row)
   const char* mbase = nullptr;
@@ -144,20 +150,18 @@ k_varlen_bf16(VarlenArgs a) {
     if (!KVC || j0 >= lc) {
       const int c0 = j0 - lc;  // current row of tile row 0
       if (j0 + C::BN - 1 <= last) {
-        T::template dma_tile_sv<false>(buf, reinterpret_cast<const char*>(kb) + c0 * row_bytes,
-                                       row_bytes, koff, wave);
-        T::template dma_tile_sv<true>(buf + C::TILE_BYTES,
-                                      reinterpret_cast<const char*>(vb) + c0 * row_bytes,
-                                      row_bytes, voff, wave);
+        T::template dma_tile_sv<false>(buf, kb + c0 * row_bytes, row_bytes, koff, wave);
+        T::template dma_tile_sv<true>(buf + C::TILE_BYTES, vb + c0 * row_bytes, row_bytes, voff,
+                                      wave);
       } else {
         // the cache variant holds more state across the key loop: its lane
         // constants are rebuilt here rather than kept live
         const int ln = KVC ? fresh_lane() : lane;
         T::template dma_tile<false>(
-            buf, [&](int r) { return kb + (size_t)(min(j0 + r, last) - lc) * kst; }, wave, ln);
+            buf, [&](int r) { return kb + (long)(min(j0 + r, last) - lc) * row_bytes; }, wave, ln);
         T::template dma_tile<true>(
-            buf + C::TILE_BYTES, [&](int r) { return vb + (size_t)(min(j0 + r, last) - lc) * kst; },
-            wave, ln);
+            buf + C::TILE_BYTES,
+            [&](int r) { return vb + (long)(min(j0 + r, last) - lc) * row_bytes; }, wave, ln);
       }
       return;
     }
@@ -190,12 +194,10 @@ k_varlen_bf16(VarlenArgs a) {
         // the tile straddles the end of the cache (or is the last tile):
         // per-lane rows, cached ones through the block slots above
         const int ln = fresh_lane();
-        auto row = [&](const char* cb, const bf16_t* cur, int r) -> const bf16_t* {
+        auto row = [&](const char* cb, const char* cur, int r) -> const char* {
           const int j = min(j0 + r, last);
-          if (j < lc)
-            return reinterpret_cast<const bf16_t*>(cb + slot((j - j0) >> 4) * row_bytes) +
-                   (size_t)((j - j0) & 15) * kst;
-          return cur + (size_t)(j - lc) * kst;
+          if (j < lc) return cb + (slot((j - j0) >> 4) + ((j - j0) & 15)) * row_bytes;
+          return cur + (long)(j - lc) * row_bytes;
         };
         T::template dma_tile<false>(buf, [&](int r) { return row(kcb, kb, r); }, wave, ln);
         T::template dma_tile<true>(buf + C::TILE_BYTES, [&](int r) { return row(vcb, vb, r); },
@@ -204,6 +206,14 @@ k_varlen_bf16(VarlenArgs a) {
     }
   };
   const int tdiag = trow + bd.delta;
+  float cscale = a.scale_log2;
+  float vscale = 1.f;
+  if constexpr (C::FP8 != 0) {
+    const int dsi = w.b * a.hkv + w.kvh;
+    if (a.q_descale) cscale *= a.q_descale[dsi];
+    if (a.k_descale) cscale *= a.k_descale[dsi];
+    if (a.v_descale) vscale = a.v_descale[dsi];
+  }
   const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
   auto stage = [&](int i) { return ring + i * STAGE; };  // i < STAGES
   constexpr int PER_TILE = 2 * C::DMA_PER_WAVE + MASK_DMA;  // DMA instructions per wave per tile
@@ -232,7 +242,7 @@ k_varlen_bf16(VarlenArgs a) {
                       (bd.wl >= 0 && j0 < wrow1 + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
-    float cs = a.scale_log2;
+    float cs = cscale;
     if constexpr (MASK) {
       T::add_mask(s, cur + 2 * C::TILE_BYTES + wave * MASK_BAND, cs, lane);
       cs = 1.f;  // the scores are scaled
@@ -257,11 +267,22 @@ k_varlen_bf16(VarlenArgs a) {
   }
 
   float lse;
-  const float inv = t.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse);
+  const float inv =
+      t.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse) * vscale;
   if (row_ok) {
     t.store(static_cast<bf16_t*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * C::DV, inv, lane);
     if (a.lse && lane < 32) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
   }
+}
+
+template <class C, bool KVC, bool MASK = false>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_bf16(VarlenArgs a) {
+  varlen_body<C, KVC, MASK>(a);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8(VarlenArgs a) {
+  varlen_body<C, false, false>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -382,6 +403,9 @@ __global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
 
 using CfgP64 = PrefillCfg<64, 4, 64>;
 using CfgP128 = PrefillCfg<128, 4, 32, 3>;
+template <int FMT>
+using CfgP8 = PrefillCfg<128, 4, 32, 3, 3, FMT>;
+static_assert(CfgP8<1>::ROWS == CfgP128::ROWS, "FP8 grid sized by varlen_bf16_rows(128)");
 
 }  // namespace
 
@@ -412,6 +436,15 @@ hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s)
   } else {
     hipLaunchKernelGGL((k_varlen_bf16<CfgP128, true>), dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_varlen_fp8<CfgP8<1>>, dim3(grid), dim3(CfgP8<1>::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_varlen_fp8<CfgP8<2>>, dim3(grid), dim3(CfgP8<2>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

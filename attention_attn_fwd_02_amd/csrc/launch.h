@@ -30,6 +30,10 @@ struct VarlenArgs {
   // scores; column = key position of the query's sequence
   const void* mask;
   int32_t mask_heads, mask_ld;
+  // FP8 inputs (attn_fwd_varlen_fp8): descales (batch, hkv) float32, NULL = 1
+  const float* q_descale;
+  const float* k_descale;
+  const float* v_descale;
 };
 
 struct DecodeArgs {
@@ -75,12 +79,13 @@ struct CombineArgs {
 };
 
 // rows per workgroup of each instance (sizes the grids)
-int varlen_bf16_rows(int d);
+int varlen_bf16_rows(int d);  // also the FP8 instance (d = 128)
 int varlen_f32_rows(int d);
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);  // mask: a.mask
+hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s);  // d = 128
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s);  // fmt 1 e4m3, 2 e5m2
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

@@ -1,4 +1,5 @@
-// bf16 prefill tile engine for gfx950 (32 query rows per wave, 32x32x16 MFMA).
+// Prefill tile engine for gfx950 (32 query rows per wave, 32x32 MFMA), for
+// bfloat16 inputs or FP8 codes (FP8 = 1 e4m3fn, 2 e5m2).
 //
 // Per workgroup: NW waves x 32 rows share one key sequence. Key tiles of BN
 // rows are copied HBM/L2 -> LDS by global_load_lds_dwordx4 (no register
@@ -20,6 +21,18 @@
 // 64-byte row segment (K: 16 rows x 64 B per instruction; V: 8 rows x 2
 // segments).
 // All MFMA operand addresses are a per-lane base plus a compile-time offset.
+//
+// FP8 tiles (D = 128: rows of 128 bytes, 8 units): unit u of row r is stored
+// at u ^ f(r) within the row, with
+//   K: f(r) = (r / 2) % 8            (16 rows of one A-operand read cycle)
+//   V: f(r) = 2 ((r / 2) % 2) + 4 ((r / 8) % 2)
+//      (the 32 lanes of a ds_read_b64_tr_b8 cycle: rows 0-3 and 8-11, or
+//      4-7 and 12-15, of a 16-key chunk, two units each)
+// which puts every read cycle in 64 distinct banks. A DMA instruction fills 8
+// rows, 8 lanes per 128-byte row (coalesced); f depends on the instruction
+// only through its parity. S^T = K Q^T runs on the FP8 MFMA (32x32x64,
+// products exact, fp32 sums); V widens to bfloat16 exactly after the
+// transposing read, and P.V is the bfloat16 path's.
 //
 // Softmax runs in the base-2 domain on unscaled scores s: p = 2^(s*c - m),
 // c = scale*log2(e). The reference m is only raised when a row max exceeds it
@@ -87,30 +100,37 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2, int STAGES_ = 3>
+template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2, int STAGES_ = 3, int FP8_ = 0>
 struct PrefillCfg {
   static constexpr int D = D_, DV = D_, NW = NW_, BN = BN_;
   static constexpr int MIN_WAVES = MIN_WAVES_;  // waves per SIMD the registers must allow
   static constexpr int STAGES = STAGES_;        // K+V tile buffers in the LDS ring
+  static constexpr int FP8 = FP8_;              // 0 bfloat16, 1 e4m3fn, 2 e5m2 codes
+  static constexpr int EB = FP8 ? 1 : 2;        // bytes per element
   static constexpr int R = 32;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW * R;
-  static constexpr int NCH = D / 8;                    // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * D * 2;        // one K (or V) tile
+  static constexpr int NCH = D * EB / 16;              // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * EB;       // one K (or V) tile
   static constexpr int DMA_PER_TILE = TILE_BYTES / 1024;
   static constexpr int DMA_PER_WAVE = DMA_PER_TILE / NW;  // per wave, per K or V tile
-  static constexpr int NQ = D / 16;                    // Q fragments per row
+  static constexpr int NOFF = FP8 ? DMA_PER_WAVE : 1;     // DMA lane offsets per wave
+  static constexpr int NQ = FP8 ? D / 64 : D / 16;     // Q fragments per row
   static constexpr int NSB = BN / 32;                  // S^T blocks per tile
   static constexpr int NPC = BN / 16;                  // P chunks per tile
   static constexpr int NOB = DV / 32;                  // O^T blocks
   static_assert(DMA_PER_TILE % NW == 0, "tile must split evenly over the waves");
   static_assert(BN % 32 == 0 && D % 64 == 0, "shape");
+  static_assert(FP8 == 0 || D == 128, "FP8 tiles: D = 128");
 };
 
 template <class C>
 struct PrefillTile {
   using M = Mfma<32>;
-  bf16x8 qf[C::NQ];
+  // bfloat16: fragment i = dims 16 i + 8 g .. + 7; FP8: fragment m = dims
+  // 64 m + 32 g .. + 31 (the B operand of one 32x32x64 FP8 MFMA)
+  using QFrag = std::conditional_t<(C::FP8 != 0), i32x8, bf16x8>;
+  QFrag qf[C::NQ];
   f32x16 o[C::NOB];
   float m_ref;  // reference max (base-2 scaled domain), -inf until a key is seen
   float m_use;  // exponent offset: m_ref, or 0 while m_ref is -inf
@@ -136,14 +156,49 @@ struct PrefillTile {
     }
   }
 
+  __device__ __forceinline__ void load_q8(const uint8_t* qrow, int lane) {
+    const int g = lane >> 5;
+#pragma unroll
+    for (int m = 0; m < C::NQ; ++m) {
+      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+      if (qrow) {
+        v0 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32);
+        v1 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32 + 16);
+      }
+      qf[m] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                    (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+    }
+  }
+
+  // FP8 unit swizzles (see the header comment)
+  __device__ __forceinline__ static constexpr int fk8(int r) { return (r >> 1) & 7; }
+  __device__ __forceinline__ static constexpr int fv8(int r) {
+    return ((r >> 1) & 1) * 2 + ((r >> 3) & 1) * 4;
+  }
+  __device__ __forceinline__ static i32x8 join8(u32x4 a, u32x4 b) {
+    return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3],
+                 (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+  __device__ __forceinline__ static f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
+    // operand formats: 0 = e4m3, 1 = e5m2; block scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, C::FP8 - 1, C::FP8 - 1, 0,
+                                                           127, 0, 127);
+  }
+
   // Issues this wave's share of the DMA for one K or V tile whose key rows
-  // start at row(0); row(r) returns the global row pointer of key r (always a
-  // valid address). V tiles use the chunk-pair layout.
+  // start at row(0); row(r) returns the global byte address of key r's row
+  // (always a valid address). V tiles use the V layout.
   template <bool VLAYOUT, class RowPtr>
   __device__ __forceinline__ static void dma_tile(char* buf, RowPtr row, int wave, int lane) {
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       const int inst = wave * C::DMA_PER_WAVE + n;
+      if constexpr (C::FP8 != 0) {
+        const int r = inst * 8 + (lane >> 3);
+        const int f = VLAYOUT ? fv8(r) : fk8(r);
+        lds_dma16(row(r) + ((lane & 7) ^ f) * 16, buf + inst * 1024);
+        continue;
+      }
       int r, c;
       if constexpr (!VLAYOUT) {
         // instruction -> (16-row block, 4 chunks); 4 lanes per row, the
@@ -158,7 +213,7 @@ struct PrefillTile {
         r = (blk / (C::NCH / 4)) * 8 + ((lane >> 4) & 1) * 4 + ((lane >> 2) & 3);
         c = (blk % (C::NCH / 4)) * 4 + (lane & 3);
       }
-      lds_dma16(row(r) + c * 8, buf + inst * 1024);
+      lds_dma16(row(r) + c * 16, buf + inst * 1024);
     }
   }
 
@@ -167,8 +222,14 @@ struct PrefillTile {
   // every instruction's uniform part (its row block and chunk group) goes
   // into the scalar base and the lane's part is lane_off, computed once by
   // dma_lane_off.
+  // FP8: the offset also depends on the parity of the instruction (par).
   template <bool VLAYOUT>
-  __device__ __forceinline__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes) {
+  __device__ __forceinline__ static uint32_t dma_lane_off(int lane, uint32_t row_bytes,
+                                                          int par = 0) {
+    if constexpr (C::FP8 != 0) {
+      const int f = VLAYOUT ? ((lane >> 4) & 1) * 2 + par * 4 : par * 4 + (lane >> 4);
+      return (uint32_t)(lane >> 3) * row_bytes + (uint32_t)((lane & 7) ^ f) * 16;
+    }
     if constexpr (!VLAYOUT)
       return (uint32_t)(lane >> 2) * row_bytes + ((lane & 3) ^ ((lane >> 4) & 3)) * 16;
     return (uint32_t)(((lane >> 4) & 1) * 4 + ((lane >> 2) & 3)) * row_bytes +
@@ -177,13 +238,27 @@ struct PrefillTile {
   // blk(rb): wave-uniform byte pointer of tile row 16 rb; rows of one
   // 16-row block are row_bytes apart (different blocks may lie on different
   // pages).
+  // Lane offsets of this wave's instructions, computed once.
+  template <bool VLAYOUT>
+  __device__ __forceinline__ static void dma_lane_offs(int lane, uint32_t row_bytes, int wave,
+                                                       uint32_t (&off)[C::NOFF]) {
+#pragma unroll
+    for (int n = 0; n < C::NOFF; ++n)
+      off[n] = dma_lane_off<VLAYOUT>(lane, row_bytes, (wave * C::DMA_PER_WAVE + n) & 1);
+  }
   template <bool VLAYOUT, class Blk>
   __device__ __forceinline__ static void dma_tile_blk(char* buf, Blk blk, long row_bytes,
-                                                      uint32_t lane_off, int wave) {
+                                                      const uint32_t (&lane_off)[C::NOFF],
+                                                      int wave) {
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       const int inst = wave * C::DMA_PER_WAVE + n;
       const char* src;
+      if constexpr (C::FP8 != 0) {
+        src = blk(inst >> 1) + (inst & 1) * 8 * row_bytes;  // rows 8 inst .. 8 inst + 7
+        lds_dma16_sv(src, lane_off[n], buf + inst * 1024);
+        continue;
+      }
       if constexpr (!VLAYOUT) {
         constexpr int IPB = C::NCH / 4;
         src = blk(inst / IPB) + (inst % IPB) * 64;
@@ -194,12 +269,13 @@ struct PrefillTile {
         const int q8 = (2 * inst) / BPR;
         src = blk(q8 >> 1) + (q8 & 1) * 8 * row_bytes + ((2 * inst) % BPR) * 64;
       }
-      lds_dma16_sv(src, lane_off, buf + inst * 1024);
+      lds_dma16_sv(src, lane_off[0], buf + inst * 1024);
     }
   }
   template <bool VLAYOUT>
   __device__ __forceinline__ static void dma_tile_sv(char* buf, const char* tile, long row_bytes,
-                                                     uint32_t lane_off, int wave) {
+                                                     const uint32_t (&lane_off)[C::NOFF],
+                                                     int wave) {
     dma_tile_blk<VLAYOUT>(
         buf, [&](int rb) { return tile + rb * 16 * row_bytes; }, row_bytes, lane_off, wave);
   }
@@ -209,6 +285,31 @@ struct PrefillTile {
   // (2 (dq % 2) + g) ^ ((k % 16) / 4); the two slot patterns of even and odd
   // dq give two per-lane bases.
   __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[C::NSB]) const {
+    if constexpr (C::FP8 != 0) {
+      // key k = lane % 32 of block sb: dims 64 m + 32 g .. + 31 are units
+      // 4 m + 2 g + t (t = 0, 1) of its row, stored at unit ^ fk8(k); A and B
+      // hold the same dims in the same registers, so any assignment of the
+      // 64 reduction indices to registers gives the same dot products
+      const int k = lane & 31, g = lane >> 5, f = fk8(k);
+      const char* base = kbuf + k * 128;
+      const char* kp[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) kp[m][t2] = base + ((4 * m + 2 * g + t2) ^ f) * 16;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        i32x8 kf[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          kf[m] = join8(*reinterpret_cast<const u32x4*>(kp[m][0] + sb * 32 * 128),
+                        *reinterpret_cast<const u32x4*>(kp[m][1] + sb * 32 * 128));
+        s[sb] = f32x16{};
+#pragma unroll
+        for (int m = 0; m < 2; ++m) s[sb] = mma8(kf[m], qf[m], s[sb]);
+      }
+      return;
+    } else {
     constexpr int IPB = C::NCH / 4;
     const int g = lane >> 5, r = lane & 15, sw = (r >> 2) & 3;
     const char* base = kbuf + ((lane >> 4) & 1) * IPB * 1024 + r * 64;
@@ -224,6 +325,7 @@ struct PrefillTile {
       s[sb] = f32x16{};
 #pragma unroll
       for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], qf[dq], s[sb]);
+    }
     }
   }
 
@@ -316,6 +418,27 @@ struct PrefillTile {
 
   // O^T += V^T P^T with V read transposed.
   __device__ __forceinline__ void pv(const char* vbuf, int lane, const uint32_t (&pk)[C::NSB * 8]) {
+    if constexpr (C::FP8 != 0) {
+      // P (B operand) of lane group g holds, for k-index j = 0..7 of chunk
+      // c, key 16 c + 8 (j / 4) + 4 g + j % 4. Lane i of each 16-lane block
+      // must receive V[key_j][dv] for dv = 32 ob + 16 hb + i: the
+      // transposing read gives it byte i % 8 of lane 2 j + i / 8, so lane m
+      // addresses row key_{m/2}, bytes 32 ob + 16 hb + 8 (m % 2) .. + 7.
+      const int g = lane >> 5, hb = (lane >> 4) & 1, i = lane & 15, jj = i >> 1;
+      const int row = (jj >> 2) * 8 + 4 * g + (jj & 3);
+      const int fh = fv8(row) >> 1;  // fv8 is even: it flips units in pairs
+      const char* vb = vbuf + row * 128 + hb * 16 + (i & 1) * 8;
+#pragma unroll
+      for (int c = 0; c < C::NPC; ++c) {
+        const u32x4 pv4 = {pk[c * 4], pk[c * 4 + 1], pk[c * 4 + 2], pk[c * 4 + 3]};
+        const bf16x8 b = as_bf16x8(pv4);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob)
+          o[ob] = M::mma(fp8x8_to_bf16<C::FP8>(lds_read_tr8(vb + c * 16 * 128 + (ob ^ fh) * 32)),
+                         b, o[ob]);
+      }
+      return;
+    }
     const int g = lane >> 5;
     const char* vb = vbuf + (g * 256 + ((lane & 15) >> 2) * 64 + ((lane >> 4) & 1) * 32 + (lane & 3) * 8);
 #pragma unroll

@@ -402,14 +402,15 @@ class DenseFP8:
     scale: float
     causal: bool
     window: tuple
+    sinks: np.ndarray | None = None
 
 
 def varlen_fp8(seed: int, lens_q, lens_k=None, fmt: str = "e4m3", hq: int = 32, hkv: int = 8,
                d: int = 128, causal: bool = True, window=(-1, -1),
-               descale: bool = True) -> DenseFP8:
+               descale: bool = True, with_sinks: bool = False) -> DenseFP8:
     """N(0,1) Q, K, V stored as FP8 codes of x / descale, descales per
-    (sequence, KV head) from U[0.25, 4] (or none). Draw order: descales, Q,
-    K, V."""
+    (sequence, KV head) from U[0.25, 4] (or none); sinks float32 N(0,1) per
+    query head. Draw order: descales, Q, K, V, sinks."""
     rng = np.random.default_rng(seed)
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_k = lens_q if lens_k is None else np.asarray(lens_k, dtype=np.int64)
@@ -439,8 +440,9 @@ def varlen_fp8(seed: int, lens_q, lens_k=None, fmt: str = "e4m3", hq: int = 32, 
     q = _normal_fp8(rng, (int(lens_q.sum()), hq, d), fmt, rows_q)
     k = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(kinv))
     v = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(vinv))
+    sinks = rng.standard_normal(hq).astype(np.float32) if with_sinks else None
     return DenseFP8(q, k, v, fmt, ds[0], ds[1], ds[2], cu_q, cu_k, 1.0 / np.sqrt(d), causal,
-                    tuple(window))
+                    tuple(window), sinks)
 
 
 def varlen_prefill_fp8(seed: int = SEED_VARLEN_PREFILL_FP8) -> DenseFP8:

@@ -33,6 +33,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD published spec)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD published spec)
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (AMD published spec)
+# FP8 prefill: Q.K^T (half the flops) runs on FP8 MFMA, P.V on bf16 MFMA
+PEAK_FP8_MIX_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 
 PREFILL_WORKLOAD = ("varlen causal GQA prefill: 8 sequences, lengths U[512,4096] packed with "
                     "cu_seqlens, Hq=32, Hkv=8, D=128, bf16 Q/K/V ~ N(0,1), scale 1/sqrt(128), "
@@ -142,6 +145,28 @@ def bench_prefill(steps, warmup):
     out_bytes = out_buf.numel() * 2 + lse_buf.numel() * 4
     return dict(ms=ms, ms_cold=ms_cold, tflops=tflops, flops=flops, lens=lens.tolist(), w=w,
                 bytes=in_bytes + out_bytes)
+
+
+def bench_prefill_fp8(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.varlen_prefill_fp8()
+    lens = np.diff(w.cu_seqlens_q)
+    t = dict(q=dev(w.q), k=dev(w.k), v=dev(w.v), cq=dev(w.cu_seqlens_q), ck=dev(w.cu_seqlens_k),
+             qd=dev(w.q_descale), kd=dev(w.k_descale), vd=dev(w.v_descale))
+    hq, d = w.q.shape[1], w.q.shape[2]
+    out = torch.empty((int(lens.sum()), hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, int(lens.sum())), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.attn_fwd_varlen_fp8(t["q"], t["k"], t["v"], t["cq"], t["ck"], int(lens.max()),
+                              int(lens.max()), w.scale, w.fmt, t["qd"], t["kd"], t["vd"],
+                              causal=True, out=out, lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    flops = prefill_flops(lens, hq, d)
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lens=lens.tolist())
 
 
 def bench_decode(steps, warmup):
@@ -450,8 +475,8 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
-                    default="prefill,decode,decode_fp8,mla,chunked,chunked_mask,sparse,"
-                            "sparse_paged")
+                    default="prefill,prefill_fp8,decode,decode_fp8,mla,chunked,chunked_mask,"
+                            "sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -493,6 +518,22 @@ def main():
     log(f"prefill {pre['ms']:.3f} ms  {pre['tflops']:.1f} TFLOP/s")
     traffic = measured_traffic()
     secondary = []
+    if "prefill_fp8" in only:
+        log("prefill fp8 ...")
+        p8 = bench_prefill_fp8(args.steps, args.warmup)
+        log(f"prefill_fp8 {p8['ms']:.3f} ms {p8['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "attention TFLOP/s (varlen prefill, FP8 e4m3 Q/K/V)", "value": p8["tflops"],
+            "unit": "TFLOP/s", "ms_per_step": p8["ms"],
+            "workload": "varlen causal GQA prefill: 8 sequences U[512,4096] (drawn "
+                        f"{p8['lens']}), Hq=32, Hkv=8, D=128, e4m3 codes with per-(sequence, KV "
+                        "head) descales, bf16 out (seed 1009)",
+            "roofline": {"bound": "mfma", "achieved": p8["tflops"], "peak": PEAK_FP8_MIX_TFLOPS,
+                         "unit": "TFLOP/s", "frac": p8["tflops"] / PEAK_FP8_MIX_TFLOPS,
+                         "traffic": None, "kernel": "k_varlen_fp8 (D=128)",
+                         "peak_note": "half the flops (Q.K^T) on FP8 MFMA (5033 TFLOP/s), "
+                                      "half (P.V) on bf16 MFMA (2517 TFLOP/s): the harmonic "
+                                      "mix"}})
     if "decode" in only:
         log("paged decode ...")
         dec = bench_decode(args.steps, args.warmup)

@@ -89,6 +89,33 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v,
                         const float* sinks, void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_fp8 - attn_fwd_varlen with FP8 Q, K and V.
+ * [MATE "Attention" page, FMHA forward dtype notes: float8_e4m3fn and
+ *  float8_e5m2 inputs of flash_attn_varlen_func; optional float32 q_descale,
+ *  k_descale, v_descale of shape (batch_size, num_heads_kv); FP8 inputs give
+ *  bfloat16 outputs]
+ *
+ *  q (Tq, hq, 128), k (Tk, hkv, 128), v (Tk, hkv, 128): 8-bit codes of
+ *  fp8_format (ATTN_FP8_E4M3 or ATTN_FP8_E5M2, as in attn_decode_paged_fp8).
+ *  q_descale, k_descale, v_descale: NULL (= 1) or float32 (batch, hkv); the
+ *  real value of a code of sequence b and KV head g is code * descale[b][g],
+ *  query head h using its KV head g = h / (hq / hkv). Descales must be
+ *  positive and finite (not checked).
+ *  out (Tq, hq, 128) bfloat16; lse NULL or float32 (hq, Tq). Sequences,
+ *  masks, sinks and errors are as in attn_fwd_varlen.
+ *  Supported: d = dv = 128. Scores are exact products of the codes summed in
+ *  float32; the probabilities and V are used as in the bfloat16 path.
+ */
+int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                            int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t fp8_format,
+                            const float* q_descale, const float* k_descale,
+                            const float* v_descale, float scale, int32_t causal,
+                            int32_t window_left, int32_t window_right, const float* sinks,
+                            void* out, float* lse, void* stream);
+
+/*
  * attn_fwd_varlen_kvcache - packed queries over a paged cache of earlier
  * tokens followed by the current K/V rows, without concatenating them
  * (chunked / append prefill).

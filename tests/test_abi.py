@@ -29,7 +29,7 @@ def lib():
 def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
-              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -154,6 +154,27 @@ def test_decode_fp8_host_checks(lib):
     assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
     assert b"fp8_format" in (call(fmt=7) and lib.attn_last_error())
+
+
+def test_varlen_fp8_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, cq=P, ck=P, batch=2, mq=100, mk=100, hq=8, hkv=2, d=128, dv=128,
+                 fmt=B.ATTN_FP8_E4M3, scale=0.1, causal=1, wl=-1, wr=-1, out=P)
+        a.update(kw)
+        return lib.attn_fwd_varlen_fp8(a["q"], a["k"], a["v"], a["cq"], a["ck"], a["batch"],
+                                       a["mq"], a["mk"], a["hq"], a["hkv"], a["d"], a["dv"],
+                                       a["fmt"], None, None, None, a["scale"], a["causal"],
+                                       a["wl"], a["wr"], None, a["out"], None, None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(mq=0) == B.ATTN_EEMPTY
+    assert call(k=None) == B.ATTN_EINVAL
+    assert call(hq=7) == B.ATTN_EINVAL
+    assert call(wl=-2) == B.ATTN_EINVAL
+    assert call(scale=0.0) == B.ATTN_EINVAL
+    assert call(scale=float("nan")) == B.ATTN_EINVAL
+    assert call(fmt=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
+    assert b"fp8_format" in (call(fmt=9) and lib.attn_last_error())
 
 
 def test_mla_and_sparse_host_checks(lib):
