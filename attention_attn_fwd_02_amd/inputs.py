@@ -247,6 +247,7 @@ class Paged:
     scale: float
     causal: bool
     sinks: np.ndarray | None = None
+    qv: np.ndarray | None = None     # (B,Sq,Hq,Dv) bits of the second query, or None
 
     @property
     def batch(self):
@@ -255,11 +256,16 @@ class Paged:
 
 def paged(seed: int, lens, sq: int = 1, hq: int = 32, hkv: int = 8, d: int = 128,
           dv: int | None = None, page: int = 64, shared_kv: bool = False,
-          causal: bool = False, scale: float | None = None, with_sinks: bool = False) -> Paged:
+          causal: bool = False, scale: float | None = None, with_sinks: bool = False,
+          with_qv: bool = False) -> Paged:
+    """Draw order: Q, K cache, V cache, page permutation, sinks, then qv."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
-    return _paged_draw(rng, lens, sq, hq, hkv, d, dv or d, page, shared_kv, causal,
-                       scale, with_sinks)
+    w = _paged_draw(rng, lens, sq, hq, hkv, d, dv or d, page, shared_kv, causal,
+                    scale, with_sinks)
+    if with_qv:
+        w.qv = _normal_bf16(rng, (len(lens), sq, hq, dv or d))
+    return w
 
 
 def _paged_draw(rng, lens, sq, hq, hkv, d, dv, page, shared_kv, causal, scale, with_sinks):
@@ -338,6 +344,7 @@ class PagedFP8:
     page_size: int
     scale: float
     causal: bool
+    qv: np.ndarray | None = None     # (B,Sq,Hq,Dv) codes of the second query, or None
 
     @property
     def batch(self):
@@ -346,11 +353,12 @@ class PagedFP8:
 
 def paged_fp8(seed: int, lens, fmt: str = "e4m3", sq: int = 1, hq: int = 32, hkv: int = 8,
               d: int = 128, page: int = 64, causal: bool = False, descale: bool = True,
-              spare_pages: int = 0) -> PagedFP8:
+              spare_pages: int = 0, with_qv: bool = False) -> PagedFP8:
     """N(0,1) Q, K, V stored as FP8 codes of x / descale, with descales drawn
     per (batch, KV head) from U[0.25, 4] (or none); a cache page is quantized
     with the descales of the sequence that owns it. Draw order: descales, Q,
-    page permutation, K cache, V cache."""
+    page permutation, K cache, V cache, then qv (quantized with the Q
+    descales)."""
     rng = np.random.default_rng(seed)
     lens = np.asarray(lens, dtype=np.int64)
     b = len(lens)
@@ -382,8 +390,9 @@ def paged_fp8(seed: int, lens, fmt: str = "e4m3", sq: int = 1, hq: int = 32, hkv
 
     k8 = _normal_fp8(rng, (pool, page, hkv, d), fmt, cmult((1.0 / kd).astype(np.float32)))
     v8 = _normal_fp8(rng, (pool, page, hkv, d), fmt, cmult((1.0 / vd).astype(np.float32)))
+    qv8 = _normal_fp8(rng, (b, sq, hq, d), fmt, qmult) if with_qv else None
     return PagedFP8(q8, k8, v8, fmt, ds[0], ds[1], ds[2], table, lens.astype(np.int32), page,
-                    1.0 / np.sqrt(d), causal)
+                    1.0 / np.sqrt(d), causal, qv8)
 
 
 @dataclasses.dataclass

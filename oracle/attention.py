@@ -188,7 +188,8 @@ def gather_paged(cache, block_table, b, n, page_size):
 
 
 def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale,
-                    causal=False, sinks=None, dv=None, batches=None, key_range=None):
+                    causal=False, sinks=None, dv=None, batches=None, key_range=None, qv=None,
+                    only_qv=False):
     """Decode against a paged cache.         [MATE flash_attn_with_kvcache / MLA]
 
     q (B, Sq, Hq, D); k_cache (P, page, Hkv, D); v_cache (P, page, Hkv, Dv), or
@@ -197,12 +198,22 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
     Sequence b sees keys 0..cache_seqlens[b]-1 (the cache already holds the
     current tokens). Causal is bottom-right: query token t sees j <= t + L - Sq.
 
+    qv (B, Sq, Hq, Dv): a second query scored against the value rows of the
+    same KV head [MATE FMHA notes: optional qv input; only_qv skips the QK
+    score path, q and k_cache may then be None]. The score of key j is
+    scale * (q . k_j + qv . v_j), or scale * (qv . v_j) with only_qv; it is
+    evaluated as one dot product of the concatenated rows [q | qv] and
+    [k_j | v_j].
+
     key_range: optional (b -> (start, end)) restricting the keys to
     [start, end) of the full sequence (split mode); masks stay relative to the
     full length. Returns O (B, Sq, Hq, Dv) and LSE (B, Hq, Sq).
     """
-    bsz, sq, hq, _ = q.shape
-    hkv = k_cache.shape[2]
+    if only_qv and qv is None:
+        raise ValueError("only_qv needs qv")
+    src = qv if only_qv else q
+    bsz, sq, hq, _ = src.shape
+    hkv = (v_cache if only_qv else k_cache).shape[2]
     g = _group(hq, hkv)
     if v_cache is None:
         dv = dv if dv is not None else k_cache.shape[3]
@@ -213,14 +224,23 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
     for b in (range(bsz) if batches is None else batches):
         lk = int(cache_seqlens[b])
         j0, j1 = (0, lk) if key_range is None else key_range(b)
-        kr = gather_paged(k_cache, block_table, b, lk, page_size)[j0:j1]
-        vr = kr[..., :dv] if v_cache is None else \
+        vr = None if v_cache is None else \
             gather_paged(v_cache, block_table, b, lk, page_size)[j0:j1]
+        kr = None if only_qv else gather_paged(k_cache, block_table, b, lk, page_size)[j0:j1]
+        if vr is None:
+            vr = kr[..., :dv]
         vis = visible_band(sq, lk, causal, k_pos=np.arange(j0, j1))
         for h in range(hq):
             kh = h // g
             sink = None if sinks is None else float(sinks[h])
-            ob, lb = attend_rows(q[b, :, h], kr[:, kh], vr[:, kh], scale, vis, sink)
+            if qv is None:
+                qh, kj = q[b, :, h], kr[:, kh]
+            elif only_qv:
+                qh, kj = qv[b, :, h], vr[:, kh]
+            else:
+                qh = np.concatenate([q[b, :, h], qv[b, :, h]], axis=-1)
+                kj = np.concatenate([kr[:, kh], vr[:, kh]], axis=-1)
+            ob, lb = attend_rows(qh, kj, vr[:, kh], scale, vis, sink)
             o[b, :, h] = ob
             lse[b, h] = lb
     return o, lse

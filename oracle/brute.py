@@ -17,16 +17,25 @@ def _dot(a, b):
     return math.fsum(float(x) * float(y) for x, y in zip(a, b))
 
 
-def rows(q, k, v, scale, visible=None, sink=None):
+def rows(q, k, v, scale, visible=None, sink=None, qv=None):
     """q: list of M rows, k/v: lists of N rows; visible(i, j) -> bool or None.
+    qv: None or M rows of a second query whose dot product with v_j is added
+    to q_i . k_j before the scale ([MATE] FMHA notes: optional qv input); q
+    may then be None (the QK term is skipped, only_qv).
     Returns (o, lse) as Python lists."""
     out, lses = [], []
     dv = len(v[0]) if len(v) else 0
-    for i, qi in enumerate(q):
+    m_rows = len(q) if q is not None else len(qv)
+    for i in range(m_rows):
         s = []
-        for j, kj in enumerate(k):
+        for j in range(len(v)):
             if visible is None or visible(i, j):
-                s.append((scale * _dot(qi, kj), j))
+                terms = []
+                if q is not None:
+                    terms.append(_dot(q[i], k[j]))
+                if qv is not None:
+                    terms.append(_dot(qv[i], v[j]))
+                s.append((scale * math.fsum(terms), j))
         if not s:
             out.append([0.0] * dv)
             lses.append(-math.inf)

@@ -51,7 +51,7 @@ def decode(bits, fmt):
 
 def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_table,
                         cache_seqlens, page_size, scale, causal=False, sinks=None,
-                        batches=None):
+                        batches=None, qv8=None, only_qv=False):
     """Decode against a paged FP8 cache.          [MATE FMHA FP8 dtype notes]
 
     q8 (B, Sq, Hq, D), k8 (P, page, Hkv, D), v8 (P, page, Hkv, Dv) uint8 codes
@@ -60,9 +60,16 @@ def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_
     then the paged decode of the plain definition (sequence b sees keys
     0..cache_seqlens[b]-1, bottom-right causal). Returns O (B, Sq, Hq, Dv)
     and LSE (B, Hq, Sq).
+
+    qv8 (B, Sq, Hq, Dv): FP8 codes of the second query; its real value uses
+    q_descale as q does (the notes: q_descale applies to both query tensors).
+    The score is scale * (q . k_j + qv . v_j) on the real values, or
+    scale * (qv . v_j) with only_qv (q8 and k8 may then be None).
     """
-    bsz, sq, hq, _ = q8.shape
-    hkv = k8.shape[2]
+    if only_qv and qv8 is None:
+        raise ValueError("only_qv needs qv8")
+    bsz, sq, hq, _ = (qv8 if only_qv else q8).shape
+    hkv = v8.shape[2]
     g = _group(hq, hkv)
     dv = v8.shape[3]
     one = np.ones((bsz, hkv))
@@ -73,15 +80,21 @@ def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_
     lse = np.full((bsz, hq, sq), np.nan)
     for b in (range(bsz) if batches is None else batches):
         lk = int(cache_seqlens[b])
-        kr = decode(gather_paged(k8, block_table, b, lk, page_size), fmt)
+        kr = None if only_qv else decode(gather_paged(k8, block_table, b, lk, page_size), fmt)
         vr = decode(gather_paged(v8, block_table, b, lk, page_size), fmt)
         vis = visible_band(sq, lk, causal)
         for h in range(hq):
             kh = h // g
-            qh = decode(q8[b, :, h], fmt) * qd[b, kh]
+            vh = vr[:, kh] * vd[b, kh]
+            if only_qv:
+                qh, kj = decode(qv8[b, :, h], fmt) * qd[b, kh], vh
+            else:
+                qh, kj = decode(q8[b, :, h], fmt) * qd[b, kh], kr[:, kh] * kd[b, kh]
+                if qv8 is not None:
+                    qh = np.concatenate([qh, decode(qv8[b, :, h], fmt) * qd[b, kh]], axis=-1)
+                    kj = np.concatenate([kj, vh], axis=-1)
             sink = None if sinks is None else float(sinks[h])
-            ob, lb = attend_rows(qh, kr[:, kh] * kd[b, kh], vr[:, kh] * vd[b, kh], scale, vis,
-                                 sink)
+            ob, lb = attend_rows(qh, kj, vh, scale, vis, sink)
             o[b, :, h] = ob
             lse[b, h] = lb
     return o, lse

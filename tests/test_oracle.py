@@ -499,6 +499,50 @@ def check_fp8_varlen():
     np.testing.assert_allclose(l1, l2, atol=0)
 
 
+def check_fp8_qv():
+    """FP8 qv: brute force on torch-dequantized codes (qv with the query
+    descale, scored against the descaled V rows), with and without the QK
+    path; unit descales equal the real-valued oracle on the decoded codes."""
+    import torch
+    w = inputs.paged_fp8(64, [6, 11], "e4m3", sq=2, hq=4, hkv=2, d=4, page=4, causal=True,
+                         with_qv=True)
+    deq = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e4m3fn).to(
+        torch.float64).numpy()
+    for only in (False, True):
+        o, lse = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, "e4m3", w.q_descale,
+                                          w.k_descale, w.v_descale, w.block_table,
+                                          w.cache_seqlens, w.page_size, w.scale, True,
+                                          qv8=w.qv, only_qv=only)
+        for b, lk in enumerate(w.cache_seqlens):
+            rows = [orc.gather_paged(c, w.block_table, b, int(lk), w.page_size)
+                    for c in (w.k_cache, w.v_cache)]
+            for h in range(4):
+                g = h // 2
+                qd, kd, vd = (float(x[b, g]) for x in (w.q_descale, w.k_descale, w.v_descale))
+                qs = [list(deq(w.q[b, t, h]) * qd) for t in range(2)]
+                qvs = [list(deq(w.qv[b, t, h]) * qd) for t in range(2)]
+                ks = [list(deq(r) * kd) for r in rows[0][:, g]]
+                vs = [list(deq(r) * vd) for r in rows[1][:, g]]
+                ob, lb = brute.rows(None if only else qs, ks, vs, w.scale,
+                                    visible=lambda t, j, lk=int(lk): j <= t + lk - 2, qv=qvs)
+                for t in range(2):
+                    assert abs(lse[b, h, t] - lb[t]) <= 1e-12
+                    np.testing.assert_allclose(o[b, t, h], ob[t], rtol=0, atol=1e-12)
+    # unit descales: the real-valued oracle on the decoded codes
+    dec = lambda x: ofp8.decode(x, "e4m3")
+    o1, l1 = ofp8.attention_paged_fp8(w.q, w.k_cache, w.v_cache, "e4m3", None, None, None,
+                                      w.block_table, w.cache_seqlens, w.page_size, w.scale, True,
+                                      qv8=w.qv)
+    o2, l2 = orc.attention_paged(dec(w.q), dec(w.k_cache), dec(w.v_cache), w.block_table,
+                                 w.cache_seqlens, w.page_size, w.scale, True, qv=dec(w.qv))
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_fp8_qv():
+    check_fp8_qv()
+
+
 def test_fp8_varlen():
     check_fp8_varlen()
 
@@ -520,7 +564,7 @@ def test_fp8_descale_identities():
 
 
 FP8_PINS = [check_fp8_decode_library, check_fp8_decode_values, check_fp8_attention_brute,
-            check_fp8_descale_identities, check_fp8_varlen]
+            check_fp8_descale_identities, check_fp8_varlen, check_fp8_qv]
 
 
 def _fp8_mutants():
@@ -548,13 +592,22 @@ def _fp8_mutants():
         qd = None if q_descale is None else np.asarray(q_descale)[:, ::-1]
         return base_varlen(q8, k8, v8, fmt, qd, k_descale, v_descale, *rest, **kw)
 
+    def qv_and_q_crossed(q8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, qv8=None,
+                         only_qv=False, **kw):
+        # q scored against V and qv against K
+        if qv8 is None or only_qv:
+            return base_attn(q8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, qv8=qv8,
+                             only_qv=only_qv, **kw)
+        return base_attn(qv8, k8, v8, fmt, q_descale, k_descale, v_descale, *rest, qv8=q8, **kw)
+
     return [("decode", decode_bias_off), ("decode", decode_no_inf),
             ("attention_paged_fp8", q_descale_by_query_head),
             ("attention_paged_fp8", v_descale_on_k),
-            ("attention_varlen_fp8", varlen_q_descale_by_query_head)]
+            ("attention_varlen_fp8", varlen_q_descale_by_query_head),
+            ("attention_paged_fp8", qv_and_q_crossed)]
 
 
-@pytest.mark.parametrize("i", range(5))
+@pytest.mark.parametrize("i", range(6))
 def test_fp8_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _fp8_mutants()[i]
     monkeypatch.setattr(ofp8, name, fn)
@@ -565,6 +618,55 @@ def test_fp8_pins_catch_planted_mistakes(monkeypatch, i):
         except (AssertionError, IndexError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"mutant {fn.__name__} of {name} passed every pin"
+
+
+def check_qv():
+    """qv ([MATE] FMHA notes; reading: a second query scored against the V
+    rows of the same KV head, added to q . k before the scale). Brute force
+    with and without the QK path (only_qv), and identities: qv = 0 is plain
+    decode; with V = K, only_qv is plain decode with q := qv and qv = a q
+    scales the scores by (1 + a); q = 0 equals only_qv."""
+    w = inputs.paged(65, [7, 13], sq=2, hq=4, hkv=2, d=4, page=4, causal=True, with_qv=True)
+    f = lambda x: inputs.bits_to_f32(x).astype(np.float64)
+    q, kc, vc, qv = f(w.q), f(w.k_cache), f(w.v_cache), f(w.qv)
+    args = (w.block_table, w.cache_seqlens, w.page_size, w.scale, True)
+    for only in (False, True):
+        o, lse = orc.attention_paged(None if only else q, None if only else kc, vc, *args,
+                                     qv=qv, only_qv=only)
+        for b, lk in enumerate(w.cache_seqlens):
+            ks = orc.gather_paged(kc, w.block_table, b, int(lk), w.page_size)
+            vs = orc.gather_paged(vc, w.block_table, b, int(lk), w.page_size)
+            for h in range(4):
+                g = h // 2
+                ob, lb = brute.rows(None if only else [list(r) for r in q[b, :, h]],
+                                    [list(r) for r in ks[:, g]], [list(r) for r in vs[:, g]],
+                                    w.scale, visible=lambda t, j, lk=int(lk): j <= t + lk - 2,
+                                    qv=[list(r) for r in qv[b, :, h]])
+                for t in range(2):
+                    assert abs(lse[b, h, t] - lb[t]) <= 1e-12
+                    np.testing.assert_allclose(o[b, t, h], ob[t], rtol=0, atol=1e-12)
+    o0, l0 = orc.attention_paged(q, kc, vc, *args)
+    o1, l1 = orc.attention_paged(q, kc, vc, *args, qv=np.zeros_like(qv))
+    np.testing.assert_allclose(o1, o0, atol=1e-13)
+    np.testing.assert_allclose(l1, l0, atol=1e-13)
+    o2, l2 = orc.attention_paged(None, None, kc, *args, qv=qv, only_qv=True)
+    o3, l3 = orc.attention_paged(qv, kc, kc, *args)
+    np.testing.assert_allclose(o2, o3, atol=1e-13)
+    np.testing.assert_allclose(l2, l3, atol=1e-13)
+    a = 0.75
+    o4, l4 = orc.attention_paged(q, kc, kc, *args, qv=a * q)
+    o5, l5 = orc.attention_paged(q, kc, kc, w.block_table, w.cache_seqlens, w.page_size,
+                                 w.scale * (1 + a), True)
+    np.testing.assert_allclose(o4, o5, atol=1e-12)
+    np.testing.assert_allclose(l4, l5, atol=1e-12)
+    o6, l6 = orc.attention_paged(np.zeros_like(q), kc, vc, *args, qv=qv)
+    o7, l7 = orc.attention_paged(None, None, vc, *args, qv=qv, only_qv=True)
+    np.testing.assert_allclose(o6, o7, atol=1e-13)
+    np.testing.assert_allclose(l6, l7, atol=1e-13)
+
+
+def test_qv():
+    check_qv()
 
 
 def test_mate_mla_example_shape():
@@ -845,7 +947,27 @@ def _mutants():
             keep &= keys <= t + (seqlen_k - seqlen_q)
         return keys[keep]
 
-    return [("sparse_block_keys", block_keys_unscaled), ("attend_rows", bias_scaled),
+    base_paged = orc.attention_paged
+
+    def qv_against_k(q, k_cache, v_cache, *rest, qv=None, only_qv=False, **kw):
+        # qv scored against the key rows: q . k + qv . k = (q + qv) . k
+        if qv is None:
+            return base_paged(q, k_cache, v_cache, *rest, **kw)
+        if only_qv:
+            return base_paged(qv, k_cache if k_cache is not None else v_cache, v_cache, *rest,
+                              **kw)
+        return base_paged(q + qv, k_cache, v_cache, *rest, **kw)
+
+    def qv_unscaled(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale, *rest,
+                    qv=None, only_qv=False, **kw):
+        # the softmax scale applied to q . k only
+        if qv is not None:
+            qv = np.asarray(qv, np.float64) / scale
+        return base_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale,
+                          *rest, qv=qv, only_qv=only_qv, **kw)
+
+    return [("attention_paged", qv_against_k), ("attention_paged", qv_unscaled),
+            ("sparse_block_keys", block_keys_unscaled), ("attend_rows", bias_scaled),
             ("attend_rows", no_scale), ("attend_rows", sink_dropped),
             ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
             ("visible_band", causal_top_left), ("visible_band", window_sides_swapped),
@@ -857,10 +979,10 @@ PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
         check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases,
-        check_sparse_paged, check_additive_mask]
+        check_sparse_paged, check_additive_mask, check_qv]
 
 
-@pytest.mark.parametrize("i", range(11))
+@pytest.mark.parametrize("i", range(13))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
