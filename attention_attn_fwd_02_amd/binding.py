@@ -42,6 +42,8 @@ _SIGNATURES = {
                                _P, _I, _P, _P, _P]),
     "attn_decode_paged_fp8": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                    _P, _P, _F, _I, _P, _I, _P, _P, _P]),
+    "attn_decode_paged_qv": (_I, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                  _P, _P, _P, _F, _I, _I, _P, _I, _P, _P, _P]),
     "attn_combine": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P]),
     "mla_decode_paged": (_I, [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _I, _P, _I, _P, _P, _P]),
     "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
@@ -288,6 +290,42 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan,
     return o_partial, lse_partial
 
 
+def attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
+                         scale, fmt=None, q_descale=None, k_descale=None, v_descale=None,
+                         causal=False, only_qv=False, o_partial=None, lse_partial=None):
+    """Decode with a second query qv (B,Sq,Hq,Dv) scored against the value
+    rows. fmt None: bf16 tensors; "e4m3" / "e5m2": uint8 FP8 codes with
+    optional float32 (B,Hkv) descales. only_qv: q and k_cache are not used
+    (may be None). Returns partials as attn_decode_paged."""
+    el = torch.bfloat16 if fmt is None else torch.uint8
+    _dev(q, qv, k_cache, v_cache, dtype=el)
+    _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
+    _dev(q_descale, k_descale, v_descale, dtype=torch.float32)
+    if qv is None or v_cache is None:
+        raise ValueError("qv and v_cache are required")
+    b, sq, hq, dv = qv.shape
+    page, hkv = v_cache.shape[1], v_cache.shape[2]
+    d = dv if only_qv or q is None else q.shape[3]
+    for t in (q_descale, k_descale, v_descale):
+        if t is not None and tuple(t.shape) != (b, hkv):
+            raise ValueError("descales must be (batch, hkv)")
+    if o_partial is None:
+        o_partial = torch.empty((b * max_splits, sq * hq, dv), dtype=torch.float32,
+                                device=qv.device)
+    if lse_partial is None:
+        lse_partial = torch.empty((b * max_splits, sq * hq), dtype=torch.float32,
+                                  device=qv.device)
+    _dev(o_partial, lse_partial, dtype=torch.float32)
+    code = ATTN_BF16 if fmt is None else FP8_FORMATS[fmt]
+    _check(load().attn_decode_paged_qv(
+        None if only_qv else _ptr(q), _ptr(qv), None if only_qv else _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), b, sq, hq,
+        hkv, d, dv, page, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), float(scale),
+        int(bool(causal)), int(bool(only_qv)), _ptr(plan), int(max_splits), _ptr(o_partial),
+        _ptr(lse_partial), _stream()))
+    return o_partial, lse_partial
+
+
 def attn_combine(o_partial, lse_partial, plan, batch, seqlen_q, hq, max_splits, sinks=None,
                  out_dtype=torch.bfloat16, out=None, lse=None, return_lse=True):
     _dev(o_partial, lse_partial, dtype=torch.float32)
@@ -435,6 +473,27 @@ def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale, fmt
     op, lp = attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan,
                                    max_splits, scale, fmt, q_descale, k_descale, v_descale,
                                    causal)
+    out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
+    return out, lse, plan
+
+
+def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale, fmt=None,
+                    q_descale=None, k_descale=None, v_descale=None, causal=False, only_qv=False,
+                    max_splits=16, waves=None, min_blocks=2, num_cu=None):
+    """plan -> attn_decode_paged_qv -> attn_combine (bfloat16 out). The plan
+    defaults follow the bytes per tile: those of paged_decode for bf16 K and
+    V tiles, twice the workgroups per CU (as paged_decode_fp8) for the
+    half-size tiles of FP8 or only_qv (measured on MI355X)."""
+    b, sq, hq, _ = qv.shape
+    hkv = v_cache.shape[2]
+    rows = sq * (hq // max(1, hkv))
+    upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
+    waves = waves or (8 if fmt is None and not only_qv else 16)
+    plan = attn_plan_splits(cache_seqlens, v_cache.shape[1], upb, num_cu or _num_cu(qv.device),
+                            waves, max_splits, min_blocks)
+    op, lp = attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, plan,
+                                  max_splits, scale, fmt, q_descale, k_descale, v_descale,
+                                  causal, only_qv)
     out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
     return out, lse, plan
 

@@ -348,6 +348,76 @@ int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_
                     "attn_decode_paged_fp8 launch");
 }
 
+int32_t attn_decode_paged_qv(const void* q, const void* qv, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* cache_seqlens,
+                             int32_t batch, int32_t seqlen_q, int32_t hq, int32_t hkv, int32_t d,
+                             int32_t dv, int32_t page_size, int32_t dtype,
+                             const float* q_descale, const float* k_descale,
+                             const float* v_descale, float scale, int32_t causal,
+                             int32_t only_qv, const int32_t* plan, int32_t max_splits,
+                             float* o_partial, float* lse_partial, void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
+              max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(qv && v_cache && block_table && cache_seqlens && plan && o_partial && lse_partial,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(only_qv || (q && k_cache), ATTN_EINVAL, "q and k_cache are required unless only_qv");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2,
+          ATTN_EUNSUPPORTED, "dtype %d (expected ATTN_BF16, ATTN_FP8_E4M3 or ATTN_FP8_E5M2)",
+          dtype);
+  const bool fp8 = dtype != ATTN_BF16;
+  REQUIRE(fp8 || (!q_descale && !k_descale && !v_descale), ATTN_EINVAL,
+          "descales apply to FP8 inputs only");
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
+          d, dv);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
+  attn::DecodeArgs a{};
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.page = page_size;
+  a.causal = causal ? 1 : 0;
+  a.max_splits = max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.q_descale = q_descale;
+  a.v_descale = v_descale;
+  if (only_qv) {
+    // scores qv . v_j alone: tiles of V only; the score scale takes the V
+    // descale where the QK path takes the K descale (q and K are not read)
+    a.q = qv;
+    a.qv = qv;
+    a.only_qv = 1;
+    a.kc = v_cache;
+    a.vc = v_cache;
+    a.k_descale = v_descale;
+  } else {
+    a.q = q;
+    a.qv = qv;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.k_descale = k_descale;
+  }
+  const hipError_t e =
+      fp8 ? attn::launch_decode_gqa_fp8(a, dtype == ATTN_FP8_E4M3 ? 1 : 2, as_stream(stream))
+          : attn::launch_decode_gqa(a, as_stream(stream));
+  return hip_status(e, "attn_decode_paged_qv launch");
+}
+
 int32_t attn_combine(const float* o_partial, const float* lse_partial, const int32_t* plan,
                      int32_t batch, int32_t seqlen_q, int32_t hq, int32_t dv, int32_t max_splits,
                      const float* sinks, int32_t out_dtype, void* out, float* lse,

@@ -52,19 +52,25 @@ struct DmaSrc {
 // as bytes (half the traffic) and every fragment is widened to bfloat16 as it
 // is read (exact), so the MFMAs, softmax and partial outputs are those of the
 // bfloat16 path; descales are applied to the scores and to O.
-template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1, int FP8_ = 0>
+//
+// QV = 1: a second query qv (Dv wide) is scored against the value rows of
+// the tile, S^T += V Qv^T, read in place from the V layout (no second copy).
+// QV = 2: only that score path; tiles hold V alone (no K bytes, no Q).
+template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1, int FP8_ = 0,
+          int QV_ = 0>
 struct StreamCfg {
   static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
   static constexpr bool VSHARED = VSHARED_;
   static constexpr int DSPLIT = DSPLIT_;
   static constexpr int FP8 = FP8_;
+  static constexpr int QV = QV_;
   static constexpr int EB = FP8 ? 1 : 2;  // bytes per element in memory and LDS
   static constexpr int BN = 32, R = 16;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW / DSPLIT * R;
   static constexpr int DMA_WAVES = NW / DSPLIT;
   static constexpr int NCH = D / 8;
-  static constexpr int K_BYTES = BN * D * EB;
+  static constexpr int K_BYTES = QV == 2 ? 0 : BN * D * EB;
   static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * EB;
   static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
   static constexpr int K_DMA = K_BYTES / 1024;
@@ -83,12 +89,14 @@ struct StreamCfg {
   static_assert(DMA_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
   static_assert(FP8 == 0 || (D == 128 && DV == 128 && !VSHARED && DSPLIT == 1),
                 "FP8 tiles: D = Dv = 128, separate V, whole head per wave");
+  static_assert(QV == 0 || (!VSHARED && DSPLIT == 1 && DV == D), "qv: separate V, Dv = D");
 };
 
 template <class C>
 struct StreamTile {
   using M = Mfma<16>;
   bf16x8 qf[C::NQ];
+  bf16x8 qvf[C::QV ? C::NQ : 1];  // qv fragments, chunks as those of Q
   f32x4 o[C::NOB];
   float m_ref;
   float l_run;
@@ -125,12 +133,34 @@ struct StreamTile {
 
   // FP8 Q: fragment dq holds chunk dq * 4 + g (8 codes), widened to bf16.
   __device__ __forceinline__ void load_q8(const uint8_t* qrow, int lane) {
+    load_frag8(qf, qrow, lane);
+  }
+  __device__ __forceinline__ static void load_frag8(bf16x8 (&f)[C::NQ], const uint8_t* row,
+                                                    int lane) {
     const int g = lane >> 4;
 #pragma unroll
     for (int i = 0; i < C::NQ; ++i) {
       u32x2 v = {0u, 0u};
-      if (qrow) v = *reinterpret_cast<const u32x2*>(qrow + (i * 4 + g) * 8);
-      qf[i] = fp8x8_to_bf16<C::FP8>(v);
+      if (row) v = *reinterpret_cast<const u32x2*>(row + (i * 4 + g) * 8);
+      f[i] = fp8x8_to_bf16<C::FP8>(v);
+    }
+  }
+  // qv row (bf16 or FP8 codes), in the fragments of Q
+  __device__ __forceinline__ void load_qv(const void* row, int lane) {
+    if constexpr (C::QV != 0) {
+      if constexpr (C::FP8 != 0) {
+        load_frag8(qvf, static_cast<const uint8_t*>(row), lane);
+      } else {
+        const int g = lane >> 4;
+#pragma unroll
+        for (int i = 0; i < C::NQ; ++i) {
+          u32x4 v = {0u, 0u, 0u, 0u};
+          if (row)
+            v = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(row) +
+                                                q_chunk(i, 0, g) * 8);
+          qvf[i] = as_bf16x8(v);
+        }
+      }
     }
   }
 
@@ -155,9 +185,11 @@ struct StreamTile {
   __device__ __forceinline__ static void dma_tile8_sv(char* stage, KB kbase, VB vbase,
                                                       uint32_t koff0, uint32_t koff1,
                                                       uint32_t voff0, uint32_t voff1) {
+    if constexpr (C::K_BYTES > 0) {
 #pragma unroll
-    for (int r8 = 0; r8 < 4; ++r8)
-      lds_dma16_sv(kbase(r8), (r8 & 1) ? koff1 : koff0, stage + r8 * 1024);
+      for (int r8 = 0; r8 < 4; ++r8)
+        lds_dma16_sv(kbase(r8), (r8 & 1) ? koff1 : koff0, stage + r8 * 1024);
+    }
 #pragma unroll
     for (int r8 = 0; r8 < 4; ++r8)
       lds_dma16_sv(vbase(r8), (r8 >> 1) ? voff1 : voff0, stage + C::K_BYTES + r8 * 1024);
@@ -168,7 +200,8 @@ struct StreamTile {
 #pragma unroll
     for (int r8 = 0; r8 < 4; ++r8) {
       const int r = r8 * 8 + (lane >> 3);
-      lds_dma16(krow(r) + ((lane & 7) ^ swz8_k(r)) * 16, stage + r8 * 1024);
+      if constexpr (C::K_BYTES > 0)
+        lds_dma16(krow(r) + ((lane & 7) ^ swz8_k(r)) * 16, stage + r8 * 1024);
       lds_dma16(vrow(r) + ((lane & 7) ^ swz8_v(r)) * 16, stage + C::K_BYTES + r8 * 1024);
     }
   }
@@ -254,7 +287,10 @@ struct StreamTile {
   // S^T for one tile.
   __device__ __forceinline__ void qk(const char* stage, int lane, f32x4 (&s)[C::NSB]) const {
     const int g = lane >> 4;
-    if constexpr (C::FP8) {
+    if constexpr (C::QV == 2) {  // no Q.K^T path: the scores start at zero
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) s[sb] = f32x4{};
+    } else if constexpr (C::FP8) {
       // key r = lane % 16 of block sb, chunk dq * 4 + g: unit 2 dq + g / 2,
       // half g % 2; stored at unit (2 dq) ^ (g / 2) ^ ((r / 2) % 8)
       const int r = lane & 15;
@@ -304,6 +340,46 @@ struct StreamTile {
           const u32x4 a =
               *reinterpret_cast<const u32x4*>(kb + (sb * IPB + (f >> 1) * 2) * 1024);
           s[sb] = M::mma(as_bf16x8(a), qf[dq], s[sb]);
+        }
+      }
+    }
+  }
+
+  // S^T += ratio * V Qv^T: lane (key r = lane % 16 of block sb, group g)
+  // reads the chunks of its value row that its Q fragments hold, from the V
+  // layout in place. bf16: chunk c of row r at block (r / 8, c / 2), row
+  // r % 8, half c % 2 (two rows per 32-byte line: 2-way bank conflicts,
+  // which the HBM-bound decode hides). FP8: 8 codes of unit
+  // (2 dq + g / 2) ^ swz8_v(r), half g % 2. ratio = v_descale / k_descale
+  // for FP8 (a second accumulator), 1 for bf16 (the same MFMA chain).
+  __device__ __forceinline__ void qv_scores(const char* stage, int lane, f32x4 (&s)[C::NSB],
+                                            float ratio) const {
+    if constexpr (C::QV != 0) {
+      const int g = lane >> 4, r = lane & 15;
+      const char* vbase = stage + C::K_BYTES;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+        const int row = sb * 16 + r;
+        if constexpr (C::FP8 != 0) {
+          const int fv = swz8_v(row);
+          const char* base = vbase + row * 128 + (g & 1) * 8;
+          f32x4 t = f32x4{};
+#pragma unroll
+          for (int dq = 0; dq < C::NQ; ++dq) {
+            const u32x2 w =
+                *reinterpret_cast<const u32x2*>(base + ((2 * dq + (g >> 1)) ^ fv) * 16);
+            t = M::mma(fp8x8_to_bf16<C::FP8>(w), qvf[dq], t);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[sb][e] = __builtin_fmaf(t[e], ratio, s[sb][e]);
+        } else {
+          const char* base = vbase + (row >> 3) * (C::NCH / 2) * 256 + (row & 7) * 32;
+#pragma unroll
+          for (int dq = 0; dq < C::NQ; ++dq) {
+            const int c = q_chunk(dq, 0, g);
+            const u32x4 a = *reinterpret_cast<const u32x4*>(base + (c >> 1) * 256 + (c & 1) * 16);
+            s[sb] = M::mma(as_bf16x8(a), qvf[dq], s[sb]);
+          }
         }
       }
     }

@@ -67,16 +67,26 @@ k_decode(DecodeArgs a) {
   T tile;
   tile.init(wave);
   const size_t qoff = (((size_t)b * a.sq + tq) * a.hq + h) * C::D;
-  if constexpr (C::FP8)
+  if constexpr (C::QV == 2) {
+    // only the qv path: no Q
+  } else if constexpr (C::FP8) {
     tile.load_q8(row_ok ? static_cast<const uint8_t*>(a.q) + qoff : nullptr, lane);
-  else
+  } else {
     tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + qoff : nullptr, lane);
-  // FP8: descales of (b, kvh) scale the scores and O (1 when not given)
-  float cscale = a.scale_log2, vscale = 1.f;
+  }
+  if constexpr (C::QV != 0) {
+    const size_t qvoff = (((size_t)b * a.sq + tq) * a.hq + h) * C::DV * C::EB;
+    tile.load_qv(row_ok ? static_cast<const char*>(a.qv) + qvoff : nullptr, lane);
+  }
+  // FP8: descales of (b, kvh) scale the scores and O (1 when not given); the
+  // qv . v scores carry v_descale where q . k carry k_descale
+  float cscale = a.scale_log2, vscale = 1.f, qv_ratio = 1.f;
   if constexpr (C::FP8) {
     const size_t di = (size_t)b * a.hkv + kvh;
-    cscale *= (a.q_descale ? a.q_descale[di] : 1.f) * (a.k_descale ? a.k_descale[di] : 1.f);
+    const float kd = a.k_descale ? a.k_descale[di] : 1.f;
+    cscale *= (a.q_descale ? a.q_descale[di] : 1.f) * kd;
     vscale = a.v_descale ? a.v_descale[di] : 1.f;
+    qv_ratio = vscale / kd;
   }
   wait_vmcnt<0>();  // Q in registers before any DMA is in flight
 
@@ -151,6 +161,7 @@ k_decode(DecodeArgs a) {
     const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
     f32x4 sc[C::NSB];
     tile.qk(st, lane, sc);
+    tile.qv_scores(st, lane, sc, qv_ratio);
     tile.exchange(xchg, wave, lane, sc);
     const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
     const float m_use = tile.prep(sc, cscale, lane, need,
@@ -368,20 +379,26 @@ k_sparse(SparseArgs a) {
   }
 }
 
-using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false>;
-template <int FMT>
-using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT>;
+template <int QV = 0>
+using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false, 1, 0, QV>;
+template <int FMT, int QV = 0>
+using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV>;
 using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
-  using C = CfgDecodeGqa;
+  using C = CfgDecodeGqa<>;
   const int nrows = a.sq * (a.hq / a.hkv);
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-  hipLaunchKernelGGL(k_decode<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  if (a.qv && a.only_qv)
+    hipLaunchKernelGGL(k_decode<CfgDecodeGqa<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  else if (a.qv)
+    hipLaunchKernelGGL(k_decode<CfgDecodeGqa<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_decode<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
@@ -390,10 +407,21 @@ hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s) {
   const int nrows = a.sq * (a.hq / a.hkv);
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-  if (fmt == 1)
+  if (a.qv && a.only_qv) {
+    if (fmt == 1)
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<1, 2>>), dim3(grid), dim3(C::THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<2, 2>>), dim3(grid), dim3(C::THREADS), 0, s, a);
+  } else if (a.qv) {
+    if (fmt == 1)
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<1, 1>>), dim3(grid), dim3(C::THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<2, 1>>), dim3(grid), dim3(C::THREADS), 0, s, a);
+  } else if (fmt == 1) {
     hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -51,6 +51,10 @@ struct DecodeArgs {
   const float* q_descale;
   const float* k_descale;
   const float* v_descale;
+  // second query (B, Sq, Hq, Dv) scored against the value rows, or NULL;
+  // only_qv: that score path alone (q and the K cache are not read)
+  const void* qv;
+  int32_t only_qv;
 };
 
 struct SparseArgs {

@@ -32,6 +32,7 @@ SEED_CHUNKED_PREFILL = 1006
 SEED_PAGED_DECODE_FP8 = 1007
 SEED_SPARSE_PAGED = 1008
 SEED_VARLEN_PREFILL_FP8 = 1009
+SEED_PAGED_DECODE_QV = 1010
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -482,6 +483,13 @@ def paged_decode(seed: int = SEED_PAGED_DECODE, batch: int = 64, lo: int = 1024,
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, endpoint=True, size=batch)
     return _paged_draw(rng, lens, 1, hq, hkv, d, d, page, False, False, None, False)
+
+
+def paged_decode_qv(w: Paged, seed: int = SEED_PAGED_DECODE_QV) -> np.ndarray:
+    """A bf16 N(0,1) qv (B, Sq, Hq, Dv) for a paged problem w, from its own
+    seed (w's draws stay those of its generator)."""
+    rng = np.random.default_rng(seed)
+    return _normal_bf16(rng, w.q.shape[:3] + (w.dv,))
 
 
 def mla_decode(seed: int = SEED_MLA_DECODE, batch: int = 64, sq: int = 2, hq: int = 128,

@@ -207,6 +207,48 @@ def bench_decode(steps, warmup):
                 splits=int(plan[0].item()))
 
 
+def bench_decode_qv(steps, warmup, only_qv=False):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.paged_decode()
+    qvh = inputs.paged_decode_qv(w)
+    q, qv, kc, vc = dev(w.q), dev(qvh), dev(w.k_cache), dev(w.v_cache)
+    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
+    ncu = B.attn_device_info(0)
+    b, sq, hq, d = w.q.shape
+    hkv = w.k_cache.shape[2]
+    # V-only tiles are half the bytes: twice the workgroups per CU
+    ms_, waves, mb = (16, 16, 2) if only_qv else (16, 8, 2)
+    upb = hkv * ((sq * hq // hkv + 15) // 16)
+    plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
+    op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
+    lp = torch.empty((b * ms_, sq * hq), dtype=torch.float32, device="cuda")
+    out = torch.empty((b, sq, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((b, hq, sq), dtype=torch.float32, device="cuda")
+    qq, kk = (None, None) if only_qv else (q, kc)
+
+    def decode_only():
+        B.attn_decode_paged_qv(qq, qv, kk, vc, bt, lens, plan, ms_, w.scale, None, causal=False,
+                               only_qv=only_qv, o_partial=op, lse_partial=lp)
+
+    def full():
+        B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb, plan=plan)
+        decode_only()
+        B.attn_combine(op, lp, plan, b, sq, hq, ms_, None, torch.bfloat16, out, lse)
+
+    ms_full = time_steps(full, steps, warmup)
+    ms_dec = time_steps(decode_only, steps, warmup)
+    total_len = int(w.cache_seqlens.astype(np.int64).sum())
+    nblk = int(((w.cache_seqlens + 63) // 64).sum())
+    kv_bytes = total_len * hkv * (128 if only_qv else 256) * 2   # V only with only_qv
+    alg_bytes = (kv_bytes + qvh.nbytes + (0 if only_qv else w.q.nbytes) + out.numel() * 2 +
+                 lse.numel() * 4 + nblk * 4)
+    return dict(ms=ms_full, ms_kernel=ms_dec, bytes=alg_bytes,
+                gbs=alg_bytes / (ms_full * 1e-3) / 1e9, gbs_kernel=alg_bytes / (ms_dec * 1e-3) / 1e9,
+                splits=int(plan[0].item()))
+
+
 FP8_DECODE_PLAN = (16, 16, 2)  # max_splits, waves, min_blocks for the FP8 decode
 
 
@@ -475,8 +517,8 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
-                    default="prefill,prefill_fp8,decode,decode_fp8,mla,chunked,chunked_mask,"
-                            "sparse,sparse_paged")
+                    default="prefill,prefill_fp8,decode,decode_fp8,decode_qv,decode_only_qv,"
+                            "mla,chunked,chunked_mask,sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -570,6 +612,25 @@ def main():
                          "traffic": None, "kernel": "k_decode (GQA, FP8)",
                          "kernel_ms": d8["ms_kernel"]},
             "frac_of_hbm_peak_whole_op": d8["gbs"] / PEAK_HBM_GBS})
+    for key, only_qv in (("decode_qv", False), ("decode_only_qv", True)):
+        if key not in only:
+            continue
+        log(f"{key} ...")
+        dq = bench_decode_qv(args.steps, args.warmup, only_qv)
+        log(f"{key} {dq['ms']:.3f} ms (kernel {dq['ms_kernel']:.3f}) {dq['gbs']:.0f} GB/s")
+        what = ("qv alone (only_qv: V read, K not)" if only_qv
+                else "q . k + qv . v scores (K and V read)")
+        secondary.append({
+            "metric": f"KV-read GB/s (paged decode, {'only_qv' if only_qv else 'qv'})",
+            "value": dq["gbs"], "unit": "GB/s", "ms_per_step": dq["ms"],
+            "workload": "the paged GQA decode workload (seed 1003) with a bf16 qv "
+                        f"(B,1,32,128) N(0,1) (seed 1010); {what}; plan + split decode + "
+                        f"combine; {dq['splits']} splits",
+            "roofline": {"bound": "hbm", "achieved": dq["gbs_kernel"], "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": dq["gbs_kernel"] / PEAK_HBM_GBS,
+                         "traffic": None, "kernel": "k_decode (GQA, qv)",
+                         "kernel_ms": dq["ms_kernel"]},
+            "frac_of_hbm_peak_whole_op": dq["gbs"] / PEAK_HBM_GBS})
     if "mla" in only:
         log("mla decode ...")
         mla = bench_mla(args.steps, args.warmup)

@@ -238,6 +238,37 @@ int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_
                               float* o_partial, float* lse_partial, void* stream);
 
 /*
+ * attn_decode_paged_qv - attn_decode_paged with a second query qv scored
+ * against the value rows (bf16 or FP8 inputs).
+ * [MATE "Attention" page, FMHA forward notes: optional qv input, also with
+ *  FP8 inputs (q_descale then applies to both query tensors);
+ *  flash_attn_with_kvcache(only_qv=True) skips the QK score path, q and
+ *  k_cache may then be None]
+ *
+ *  qv (B, Sq, Hq, dv), same element type as the caches. The score of key j
+ *  for query head h (KV head g = h / (Hq / Hkv)) is
+ *      scale * (q . k_j + qv . v_j)       (only_qv = 0)
+ *      scale * (qv . v_j)                 (only_qv != 0; q and k_cache are
+ *                                          then not read and may be NULL)
+ *  on the real values; softmax, output (the partials, then attn_combine) and
+ *  LSE are those of attn_decode_paged over these scores.
+ *  dtype: ATTN_BF16 (descales must be NULL), ATTN_FP8_E4M3 or ATTN_FP8_E5M2
+ *  (codes, descales as in attn_decode_paged_fp8; qv uses q_descale).
+ *  Everything else (block table, plan, partial layouts, causal, errors) is
+ *  as in attn_decode_paged. Supported: d = dv = 128, page_size a multiple of
+ *  16.
+ */
+int32_t attn_decode_paged_qv(const void* q, const void* qv, const void* k_cache,
+                             const void* v_cache, const int32_t* block_table,
+                             int32_t max_pages_per_seq, const int32_t* cache_seqlens,
+                             int32_t batch, int32_t seqlen_q, int32_t hq, int32_t hkv, int32_t d,
+                             int32_t dv, int32_t page_size, int32_t dtype,
+                             const float* q_descale, const float* k_descale,
+                             const float* v_descale, float scale, int32_t causal,
+                             int32_t only_qv, const int32_t* plan, int32_t max_splits,
+                             float* o_partial, float* lse_partial, void* stream);
+
+/*
  * attn_combine - LSE-weighted merge of split results.
  * [MATE FMHA: flash_attn_combine merges partial outputs and LSE buffers;
  *  CANN flash_attn: softmax_lse definition]

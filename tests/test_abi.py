@@ -29,7 +29,7 @@ def lib():
 def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
-              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "attn_decode_paged_qv", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -175,6 +175,31 @@ def test_varlen_fp8_host_checks(lib):
     assert call(fmt=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
     assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
     assert b"fp8_format" in (call(fmt=9) and lib.attn_last_error())
+
+
+def test_decode_qv_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, qv=P, kc=P, vc=P, bt=P, mp=4, lens=P, batch=2, sq=1, hq=32, hkv=8, d=128,
+                 dv=128, page=64, dtype=B.ATTN_BF16, qd=None, scale=0.1, causal=0, only=0,
+                 plan=P, ms=16, op=P, lp=P)
+        a.update(kw)
+        return lib.attn_decode_paged_qv(a["q"], a["qv"], a["kc"], a["vc"], a["bt"], a["mp"],
+                                        a["lens"], a["batch"], a["sq"], a["hq"], a["hkv"],
+                                        a["d"], a["dv"], a["page"], a["dtype"], a["qd"], None,
+                                        None, a["scale"], a["causal"], a["only"], a["plan"],
+                                        a["ms"], a["op"], a["lp"], None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(qv=None) == B.ATTN_EINVAL
+    assert call(q=None) == B.ATTN_EINVAL
+    assert call(kc=None) == B.ATTN_EINVAL
+    assert call(vc=None, only=1) == B.ATTN_EINVAL
+    assert call(hq=12) == B.ATTN_EINVAL
+    assert call(ms=17) == B.ATTN_EINVAL
+    assert call(scale=-1.0) == B.ATTN_EINVAL
+    assert call(qd=P) == B.ATTN_EINVAL          # descales with bf16 inputs
+    assert call(dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
+    assert call(page=24) == B.ATTN_EUNSUPPORTED
 
 
 def test_mla_and_sparse_host_checks(lib):
