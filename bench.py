@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD published spec)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (AMD published spec)
 PEAK_FP8_TFLOPS = 5033.2    # MI355X dense FP8 MFMA (AMD published spec)
+PEAK_CLOCK_GHZ = 2.4        # the engine clock those peaks assume
 # FP8 prefill: Q.K^T (half the flops) runs on FP8 MFMA, P.V on bf16 MFMA
 PEAK_FP8_MIX_TFLOPS = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
 
@@ -430,11 +431,9 @@ def prefill_source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per prefill launch from the committed counter profile of this
-    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the same counters read on a
-    plain copy of known size), or None when no such profile matches the
-    current prefill sources."""
+def prefill_record():
+    """The committed counter profile of the prefill kernel, or None when it
+    does not match the current prefill sources."""
     try:
         with open(TRAFFIC_PATH) as f:
             rec = json.load(f)
@@ -442,13 +441,55 @@ def measured_traffic():
         return None
     if rec.get("prefill_source_sha256_16") != prefill_source_digest():
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
-def write_traffic(fetch_dir, write_dir, command):
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed counter profile of this
+    kernel (FETCH_SIZE + WRITE_SIZE, scaled by the same counters read on a
+    plain copy of known size), or None when no such profile matches the
+    current prefill sources."""
+    rec = prefill_record()
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+N_XCD, N_SIMD = 8, 1024      # MI355X: GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def measured_clock(clock_dir):
+    """Engine clock and MFMA busy fraction during the timed prefill launches,
+    from a rocprofv3 --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES
+    --kernel-trace run of `bench.py --only prefill --no-secondary --no-cpu`:
+    per dispatch, GRBM_GUI_ACTIVE / 8 XCDs / duration, median over the last
+    20 dispatches (the timed steps come after the clock ramp and warm-up)."""
+    import csv
+    import glob
+    import statistics
+    d = {}
+    for fn in glob.glob(os.path.join(clock_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if "k_varlen_bf16" not in r["Kernel_Name"] or "PrefillCfg<128" not in r["Kernel_Name"]:
+                    continue
+                e = d.setdefault(int(r["Dispatch_Id"]), {})
+                e[r["Counter_Name"]] = float(r["Counter_Value"])
+                e["dur"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    ids = sorted(d)
+    if len(ids) < 29:
+        raise SystemExit(f"expected >= 29 prefill dispatches in {clock_dir}, got {len(ids)}")
+    # bench.py's order: ramp, 3 warm-up, 20 timed, then 9 cold-cache steps
+    timed = ids[-29:-9]
+    ghz = statistics.median(d[i]["GRBM_GUI_ACTIVE"] / N_XCD / d[i]["dur"] / 1e9 for i in timed)
+    busy = statistics.median(d[i]["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD /
+                             (d[i]["GRBM_GUI_ACTIVE"] / N_XCD) for i in timed)
+    return {"ghz_median": ghz, "mfma_busy_frac_median": busy, "dispatches": len(timed)}
+
+
+def write_traffic(fetch_dir, write_dir, command, clock_dir=None):
     """Builds the traffic record from two rocprofv3 --pmc runs of
     `bench.py --only prefill --no-secondary --no-cpu --copy-calibration`
-    (one with FETCH_SIZE, one with WRITE_SIZE; both in KiB per dispatch)."""
+    (one with FETCH_SIZE, one with WRITE_SIZE; both in KiB per dispatch),
+    and optionally the engine clock from a third (measured_clock)."""
     import csv
     import glob
 
@@ -483,6 +524,8 @@ def write_traffic(fetch_dir, write_dir, command):
         "prefill_source_sha256_16": prefill_source_digest(),
         "command": command,
     }
+    if clock_dir:
+        rec["clock"] = measured_clock(clock_dir)
     with open(TRAFFIC_PATH, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -524,15 +567,20 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy, so that a "
                          "counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--traffic-from", nargs="+", metavar="DIR",
                     help="no GPU work: write the prefill traffic record from two "
-                         "rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE)")
+                         "rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) and "
+                         "optionally a third (GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES "
+                         "with --kernel-trace) for the engine clock")
     ap.add_argument("--traffic-command", default="",
                     help="the profiling command, stored with the traffic record")
     args = ap.parse_args()
     RAMP_MS[0] = max(0.0, args.ramp_ms)
     if args.traffic_from:
-        write_traffic(args.traffic_from[0], args.traffic_from[1], args.traffic_command)
+        if len(args.traffic_from) not in (2, 3):
+            ap.error("--traffic-from takes FETCH_DIR WRITE_DIR [CLOCK_DIR]")
+        write_traffic(*args.traffic_from[:2], args.traffic_command,
+                      args.traffic_from[2] if len(args.traffic_from) == 3 else None)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -737,6 +785,19 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
     }
+    prec = prefill_record()
+    if prec and "clock" in prec:
+        # the same kernel's engine clock in the committed counter run: the peak
+        # scales with it (MFMA throughput per cycle is fixed)
+        ghz = prec["clock"]["ghz_median"]
+        peak_clk = PEAK_BF16_TFLOPS * ghz / PEAK_CLOCK_GHZ
+        rec["roofline"].update({
+            "clock_ghz_measured": ghz, "peak_at_measured_clock": peak_clk,
+            "frac_at_measured_clock": pre["tflops"] / peak_clk,
+            "mfma_busy_frac_measured": prec["clock"]["mfma_busy_frac_median"],
+            "clock_source": "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration over the timed "
+                            "launches of a rocprofv3 counter run (" +
+                            os.path.relpath(TRAFFIC_PATH, ROOT) + ")"})
     print(json.dumps(rec), flush=True)
 
 
