@@ -111,6 +111,7 @@ class Dense:
     causal: bool
     window: tuple
     sinks: np.ndarray | None = None
+    qv: np.ndarray | None = None     # (Tq,Hq,Dv) second query, same element type, or None
 
     @property
     def batch(self):
@@ -134,13 +135,20 @@ def tiny_dense(seed: int = SEED_TINY_DENSE, s: int = 128, h: int = 4, d: int = 6
 
 def varlen(seed: int, lens_q, lens_k=None, hq: int = 32, hkv: int = 8, d: int = 128,
            dv: int | None = None, dtype: str = "bf16", causal: bool = True,
-           window=(-1, -1), scale: float | None = None, with_sinks: bool = False) -> Dense:
-    """Packed varlen problem with explicit per-sequence lengths."""
+           window=(-1, -1), scale: float | None = None, with_sinks: bool = False,
+           with_qv: bool = False) -> Dense:
+    """Packed varlen problem with explicit per-sequence lengths (qv, when
+    asked for, drawn last)."""
     rng = np.random.default_rng(seed)
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_k = lens_q if lens_k is None else np.asarray(lens_k, dtype=np.int64)
-    return _varlen_draw(rng, lens_q, lens_k, hq, hkv, d, dv or d, dtype, causal,
-                        window, scale, with_sinks)
+    w = _varlen_draw(rng, lens_q, lens_k, hq, hkv, d, dv or d, dtype, causal,
+                     window, scale, with_sinks)
+    if with_qv:
+        shape = (int(lens_q.sum()), hq, dv or d)
+        w.qv = _normal_bf16(rng, shape) if dtype == "bf16" else \
+            rng.standard_normal(shape, dtype=np.float32)
+    return w
 
 
 def _varlen_draw(rng, lens_q, lens_k, hq, hkv, d, dv, dtype, causal, window, scale,
@@ -413,14 +421,17 @@ class DenseFP8:
     causal: bool
     window: tuple
     sinks: np.ndarray | None = None
+    qv: np.ndarray | None = None     # (Tq,Hq,Dv) codes of the second query, or None
 
 
 def varlen_fp8(seed: int, lens_q, lens_k=None, fmt: str = "e4m3", hq: int = 32, hkv: int = 8,
                d: int = 128, causal: bool = True, window=(-1, -1),
-               descale: bool = True, with_sinks: bool = False) -> DenseFP8:
+               descale: bool = True, with_sinks: bool = False,
+               with_qv: bool = False) -> DenseFP8:
     """N(0,1) Q, K, V stored as FP8 codes of x / descale, descales per
     (sequence, KV head) from U[0.25, 4] (or none); sinks float32 N(0,1) per
-    query head. Draw order: descales, Q, K, V, sinks."""
+    query head. Draw order: descales, Q, K, V, sinks, then qv (with the Q
+    descales)."""
     rng = np.random.default_rng(seed)
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_k = lens_q if lens_k is None else np.asarray(lens_k, dtype=np.int64)
@@ -451,8 +462,9 @@ def varlen_fp8(seed: int, lens_q, lens_k=None, fmt: str = "e4m3", hq: int = 32, 
     k = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(kinv))
     v = _normal_fp8(rng, (int(lens_k.sum()), hkv, d), fmt, rows_kv(vinv))
     sinks = rng.standard_normal(hq).astype(np.float32) if with_sinks else None
+    qv = _normal_fp8(rng, (int(lens_q.sum()), hq, d), fmt, rows_q) if with_qv else None
     return DenseFP8(q, k, v, fmt, ds[0], ds[1], ds[2], cu_q, cu_k, 1.0 / np.sqrt(d), causal,
-                    tuple(window), sinks)
+                    tuple(window), sinks, qv)
 
 
 def varlen_prefill_fp8(seed: int = SEED_VARLEN_PREFILL_FP8) -> DenseFP8:

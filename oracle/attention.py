@@ -124,7 +124,8 @@ def _group(hq, hkv):
 # Packed variable-length attention (prefill)
 # --------------------------------------------------------------------------
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
-                     window=(-1, -1), sinks=None, seqs=None, mask=None):
+                     window=(-1, -1), sinks=None, seqs=None, mask=None, qv=None,
+                     only_qv=False):
     """Packed varlen attention.                [MATE FMHA flash_attn_varlen_func]
 
     q (Tq, Hq, D), k (Tk, Hkv, D), v (Tk, Hkv, Dv); cu_seqlens_* (B+1) prefix
@@ -136,11 +137,17 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
     adds mask[h or 0, r, j] to its scaled score with key j of the sequence
     [MOJO flash_attention_split_kv input_mask_fn].
 
+    qv (Tq, Hq, Dv): a second query scored against the value rows, as in
+    attention_paged: score scale * (q . k_j + qv . v_j), or scale * qv . v_j
+    with only_qv (q and k may then be None) [MATE FMHA notes: optional qv].
+
     Returns O (Tq, Hq, Dv) float64 and LSE (Hq, Tq) float64 [CANN: TND LSE is
     (Q_N, Q_T)].
     """
-    tq, hq, _ = q.shape
-    hkv, dv = k.shape[1], v.shape[2]
+    if only_qv and qv is None:
+        raise ValueError("only_qv needs qv")
+    tq, hq, _ = (qv if only_qv else q).shape
+    hkv, dv = v.shape[1], v.shape[2]
     g = _group(hq, hkv)
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_k, dtype=np.int64)
@@ -155,8 +162,15 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
             kh = h // g
             sink = None if sinks is None else float(sinks[h])
             bias = None if mask is None else mask[h if mask.shape[0] > 1 else 0, q0:q1, :lk]
-            ob, lb = attend_rows(q[q0:q1, h], k[k0:k1, kh], v[k0:k1, kh], scale, vis, sink,
-                                 bias)
+            vj = v[k0:k1, kh]
+            if qv is None:
+                qh, kj = q[q0:q1, h], k[k0:k1, kh]
+            elif only_qv:
+                qh, kj = qv[q0:q1, h], vj
+            else:
+                qh = np.concatenate([q[q0:q1, h], qv[q0:q1, h]], axis=-1)
+                kj = np.concatenate([k[k0:k1, kh], vj], axis=-1)
+            ob, lb = attend_rows(qh, kj, vj, scale, vis, sink, bias)
             o[q0:q1, h] = ob
             lse[h, q0:q1] = lb
     return o, lse

@@ -102,16 +102,20 @@ def attention_paged_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, block_
 
 def attention_varlen_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, cu_seqlens_q,
                          cu_seqlens_k, scale, causal=False, window=(-1, -1), sinks=None,
-                         seqs=None):
+                         seqs=None, qv8=None, only_qv=False):
     """Packed varlen attention on FP8 codes.  [MATE FMHA FP8 dtype notes;
     flash_attn_varlen_func]
 
     q8 (Tq, Hq, D), k8 (Tk, Hkv, D), v8 (Tk, Hkv, Dv) uint8 codes of fmt;
     descales float (B, Hkv) or None (= 1). The rows of sequence b are
     decode(x8) * descale[b, kv head] (query head h: its KV head h // (Hq/Hkv));
-    then attention_varlen. Returns O (Tq, Hq, Dv), LSE (Hq, Tq)."""
-    tq, hq, _ = q8.shape
-    hkv = k8.shape[1]
+    then attention_varlen. qv8 (Tq, Hq, Dv): codes of the second query, with
+    the Q descales (only_qv: q8 and k8 may be None). Returns O (Tq, Hq, Dv),
+    LSE (Hq, Tq)."""
+    if only_qv and qv8 is None:
+        raise ValueError("only_qv needs qv8")
+    tq, hq, _ = (qv8 if only_qv else q8).shape
+    hkv = v8.shape[1]
     g = _group(hq, hkv)
     cq = np.asarray(cu_seqlens_q, dtype=np.int64)
     ck = np.asarray(cu_seqlens_k, dtype=np.int64)
@@ -120,11 +124,17 @@ def attention_varlen_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, cu_se
     qd = one if q_descale is None else np.asarray(q_descale, np.float64)
     kd = one if k_descale is None else np.asarray(k_descale, np.float64)
     vd = one if v_descale is None else np.asarray(v_descale, np.float64)
-    q = decode(q8, fmt)
-    k = decode(k8, fmt)
+    q = None if only_qv else decode(q8, fmt)
+    k = None if only_qv else decode(k8, fmt)
     v = decode(v8, fmt)
+    qv = None if qv8 is None else decode(qv8, fmt)
     for b in range(bsz):
-        q[cq[b]:cq[b + 1]] *= np.repeat(qd[b], g)[None, :, None]
-        k[ck[b]:ck[b + 1]] *= kd[b][None, :, None]
+        qrow = np.repeat(qd[b], g)[None, :, None]
+        if not only_qv:
+            q[cq[b]:cq[b + 1]] *= qrow
+            k[ck[b]:ck[b + 1]] *= kd[b][None, :, None]
+        if qv is not None:
+            qv[cq[b]:cq[b + 1]] *= qrow
         v[ck[b]:ck[b + 1]] *= vd[b][None, :, None]
-    return attention_varlen(q, k, v, cq, ck, scale, causal, window, sinks, seqs)
+    return attention_varlen(q, k, v, cq, ck, scale, causal, window, sinks, seqs, qv=qv,
+                            only_qv=only_qv)

@@ -669,6 +669,58 @@ def test_qv():
     check_qv()
 
 
+def check_qv_varlen():
+    """qv on packed varlen sequences (bottom-right causal, Lq != Lk): brute
+    force per sequence and head with and without the QK path; the FP8 form on
+    torch-dequantized codes (qv with the Q descale)."""
+    import torch
+    w = inputs.varlen(66, [3, 6], [5, 6], hq=4, hkv=2, d=4, causal=True, with_qv=True)
+    q, k, v, qv = (w.f32(n).astype(np.float64) for n in ("q", "k", "v", "qv"))
+    cq, ck = w.cu_seqlens_q, w.cu_seqlens_k
+    for only in (False, True):
+        o, lse = orc.attention_varlen(None if only else q, None if only else k, v, cq, ck,
+                                      w.scale, True, qv=qv, only_qv=only)
+        for b in range(2):
+            nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+            for h in range(4):
+                g = h // 2
+                ob, lb = brute.rows(None if only else [list(r) for r in q[cq[b]:cq[b + 1], h]],
+                                    [list(r) for r in k[ck[b]:ck[b + 1], g]],
+                                    [list(r) for r in v[ck[b]:ck[b + 1], g]], w.scale,
+                                    visible=lambda t, j: j <= t + nk - nq,
+                                    qv=[list(r) for r in qv[cq[b]:cq[b + 1], h]])
+                for t in range(nq):
+                    assert abs(lse[h, cq[b] + t] - lb[t]) <= 1e-12
+                    np.testing.assert_allclose(o[cq[b] + t, h], ob[t], rtol=0, atol=1e-12)
+    w8 = inputs.varlen_fp8(67, [3, 6], [5, 6], fmt="e5m2", hq=4, hkv=2, d=4, with_qv=True)
+    deq = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.float8_e5m2).to(
+        torch.float64).numpy()
+    cq, ck = w8.cu_seqlens_q, w8.cu_seqlens_k
+    for only in (False, True):
+        o, lse = ofp8.attention_varlen_fp8(None if only else w8.q, None if only else w8.k,
+                                           w8.v, "e5m2", w8.q_descale, w8.k_descale,
+                                           w8.v_descale, cq, ck, w8.scale, True, qv8=w8.qv,
+                                           only_qv=only)
+        for b in range(2):
+            nq, nk = cq[b + 1] - cq[b], ck[b + 1] - ck[b]
+            for h in range(4):
+                g = h // 2
+                qd, kd, vd = (float(x[b, g]) for x in (w8.q_descale, w8.k_descale, w8.v_descale))
+                ob, lb = brute.rows(
+                    None if only else [list(deq(r) * qd) for r in w8.q[cq[b]:cq[b + 1], h]],
+                    [list(deq(r) * kd) for r in w8.k[ck[b]:ck[b + 1], g]],
+                    [list(deq(r) * vd) for r in w8.v[ck[b]:ck[b + 1], g]], w8.scale,
+                    visible=lambda t, j: j <= t + nk - nq,
+                    qv=[list(deq(r) * qd) for r in w8.qv[cq[b]:cq[b + 1], h]])
+                for t in range(nq):
+                    assert abs(lse[h, cq[b] + t] - lb[t]) <= 1e-12
+                    np.testing.assert_allclose(o[cq[b] + t, h], ob[t], rtol=0, atol=1e-12)
+
+
+def test_qv_varlen():
+    check_qv_varlen()
+
+
 def test_mate_mla_example_shape():
     """MATE minimal MLA example: q (1,32,8,576), k_cache (4,16,2,576),
     block_table zeros (1,4), cache_seqlens [32], head_dim_v 512. Every logical
@@ -966,7 +1018,23 @@ def _mutants():
         return base_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale,
                           *rest, qv=qv, only_qv=only_qv, **kw)
 
-    return [("attention_paged", qv_against_k), ("attention_paged", qv_unscaled),
+    base_varlen = orc.attention_varlen
+
+    def varlen_qv_against_k(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal=False,
+                            window=(-1, -1), sinks=None, seqs=None, mask=None, qv=None,
+                            only_qv=False):
+        if qv is None:
+            return base_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, window,
+                               sinks, seqs, mask)
+        # qv scored against the key rows: q . k + qv . k = (q + qv) . k
+        if only_qv:
+            return base_varlen(qv, v if k is None else k, v, cu_seqlens_q, cu_seqlens_k, scale,
+                               causal, window, sinks, seqs, mask)
+        return base_varlen(q + qv, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, window,
+                           sinks, seqs, mask)
+
+    return [("attention_varlen", varlen_qv_against_k),
+            ("attention_paged", qv_against_k), ("attention_paged", qv_unscaled),
             ("sparse_block_keys", block_keys_unscaled), ("attend_rows", bias_scaled),
             ("attend_rows", no_scale), ("attend_rows", sink_dropped),
             ("attend_rows", lse_without_max), ("attend_rows", transposed_kv),
@@ -979,10 +1047,10 @@ PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
         check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases,
-        check_sparse_paged, check_additive_mask, check_qv]
+        check_sparse_paged, check_additive_mask, check_qv, check_qv_varlen]
 
 
-@pytest.mark.parametrize("i", range(13))
+@pytest.mark.parametrize("i", range(14))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
