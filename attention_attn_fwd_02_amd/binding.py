@@ -34,6 +34,8 @@ _SIGNATURES = {
                              _P, _P, _P, _P]),
     "attn_fwd_varlen_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                  _F, _I, _I, _I, _P, _P, _P, _P]),
+    "attn_fwd_varlen_qv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P,
+                                _P, _F, _I, _I, _I, _P, _I, _P, _P, _P]),
     "attn_fwd_varlen_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      _I, _I, _I, _F, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]),
     "attn_plan_words": (ctypes.c_size_t, [_I, _I]),
@@ -174,6 +176,43 @@ def attn_fwd_varlen_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
         int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dv, FP8_FORMATS[fmt], _ptr(q_descale),
         _ptr(k_descale), _ptr(v_descale), float(scale), int(bool(causal)), int(window[0]),
         int(window[1]), _ptr(sinks), _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def attn_fwd_varlen_qv(q, qv, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                       scale, fmt=None, q_descale=None, k_descale=None, v_descale=None,
+                       causal=False, window=(-1, -1), sinks=None, only_qv=False, out=None,
+                       lse=None, return_lse=True):
+    """Varlen attention with a second query qv (Tq,Hq,128) scored against the
+    value rows. fmt None: bf16 tensors; "e4m3" / "e5m2": uint8 FP8 codes with
+    optional float32 (B,Hkv) descales. only_qv: q and k are not used (may be
+    None). Returns (out (Tq,Hq,128) bf16, lse (Hq,Tq) fp32 or None)."""
+    el = torch.bfloat16 if fmt is None else torch.uint8
+    _dev(q, qv, k, v, dtype=el)
+    _dev(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    _dev(sinks, q_descale, k_descale, v_descale, dtype=torch.float32)
+    if qv is None or v is None:
+        raise ValueError("qv and v are required")
+    tq, hq, dv = qv.shape
+    hkv = v.shape[1]
+    d = dv if only_qv or q is None else q.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    for t in (q_descale, k_descale, v_descale):
+        if t is not None and tuple(t.shape) != (batch, hkv):
+            raise ValueError("descales must be (batch, hkv)")
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=torch.bfloat16, device=qv.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=qv.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    code = ATTN_BF16 if fmt is None else FP8_FORMATS[fmt]
+    _check(load().attn_fwd_varlen_qv(
+        None if only_qv else _ptr(q), _ptr(qv), None if only_qv else _ptr(k), _ptr(v),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), hq,
+        hkv, d, dv, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), float(scale),
+        int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), int(bool(only_qv)),
+        _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -166,6 +166,73 @@ int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,
                     "attn_fwd_varlen_fp8 launch");
 }
 
+int32_t attn_fwd_varlen_qv(const void* q, const void* qv, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                           int32_t hkv, int32_t d, int32_t dv, int32_t dtype,
+                           const float* q_descale, const float* k_descale,
+                           const float* v_descale, float scale, int32_t causal,
+                           int32_t window_left, int32_t window_right, const float* sinks,
+                           int32_t only_qv, void* out, float* lse, void* stream) {
+  REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0, ATTN_EEMPTY,
+          "empty dimension (batch=%d max_seqlen_q=%d hq=%d hkv=%d d=%d dv=%d)", batch,
+          max_seqlen_q, hq, hkv, d, dv);
+  REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
+  REQUIRE(qv && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(only_qv || (q && k), ATTN_EINVAL, "q and k are required unless only_qv");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2,
+          ATTN_EUNSUPPORTED, "dtype %d (expected ATTN_BF16, ATTN_FP8_E4M3 or ATTN_FP8_E5M2)",
+          dtype);
+  const int fmt = dtype == ATTN_BF16 ? 0 : (dtype == ATTN_FP8_E4M3 ? 1 : 2);
+  REQUIRE(fmt != 0 || (!q_descale && !k_descale && !v_descale), ATTN_EINVAL,
+          "descales apply to FP8 inputs only");
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "qv supports d = dv = 128 (got %d, %d)", d,
+          dv);
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
+  attn::VarlenArgs a{};
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  a.q_descale = q_descale;
+  a.v_descale = v_descale;
+  const int rows = attn::varlen_bf16_rows(d);
+  a.nqt = (max_seqlen_q + rows - 1) / rows;
+  REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
+  hipError_t e;
+  if (only_qv) {
+    // scores qv . v_j alone: the plain prefill with qv as its query and the
+    // value rows in the role of the keys (k_descale -> v_descale)
+    a.q = qv;
+    a.k = v;
+    a.v = v;
+    a.k_descale = v_descale;
+    e = fmt == 0 ? attn::launch_varlen_bf16(a, d, as_stream(stream))
+                 : attn::launch_varlen_fp8(a, fmt, as_stream(stream));
+  } else {
+    a.q = q;
+    a.qv = qv;
+    a.k = k;
+    a.v = v;
+    a.k_descale = k_descale;
+    e = attn::launch_varlen_qv(a, fmt, as_stream(stream));
+  }
+  return hip_status(e, "attn_fwd_varlen_qv launch");
+}
+
 int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                                 const void* k_cache, const void* v_cache,

@@ -70,12 +70,17 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 // into the stage beside K and V (4 lanes per 64-byte row segment, coalesced).
 // C::FP8: Q, K and V are FP8 codes; the descales of (sequence, KV head) scale
 // the scores (q and k) and the output (v).
-template <class C, bool KVC, bool MASK>
+// QV: a second query qv is scored against the V rows; each stage also holds
+// V in the K layout (a third DMA of the same rows) for that product.
+template <class C, bool KVC, bool MASK, bool QV = false>
 __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
-  using T = PrefillTile<C>;
+  using T = PrefillTile<C, QV>;
   static_assert(C::FP8 == 0 || (!KVC && !MASK), "FP8 tiles: current keys, no mask");
+  static_assert(!QV || (!KVC && !MASK), "qv: current keys, no mask");
   constexpr int MASK_BAND = C::R * C::BN * 2;              // one wave's rows of a tile
-  constexpr int STAGE = 2 * C::TILE_BYTES + (MASK ? C::NW * MASK_BAND : 0);
+  constexpr int VK_OFF = 2 * C::TILE_BYTES;                // V in the K layout (QV)
+  constexpr int MASK_OFF = VK_OFF + (QV ? C::TILE_BYTES : 0);
+  constexpr int STAGE = MASK_OFF + (MASK ? C::NW * MASK_BAND : 0);
   constexpr int MASK_DMA = MASK ? C::BN / 16 : 0;          // mask instructions per wave
   // ring of STAGES buffers, each one K tile, one V tile (and the mask tile)
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * STAGE];
@@ -99,11 +104,9 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   const bool row_ok = trow < lq;
   T t;
   t.init();
-  const size_t qoff = ((size_t)(q0 + trow) * a.hq + w.h) * C::D;
-  if constexpr (C::FP8 != 0)
-    t.load_q8(row_ok ? static_cast<const uint8_t*>(a.q) + qoff : nullptr, lane);
-  else
-    t.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + qoff : nullptr, lane);
+  const size_t qoff = ((size_t)(q0 + trow) * a.hq + w.h) * C::D * C::EB;  // bytes
+  t.load_q(row_ok ? static_cast<const char*>(a.q) + qoff : nullptr, lane);
+  if constexpr (QV) t.load_qv(row_ok ? static_cast<const char*>(a.qv) + qoff : nullptr, lane);
   // Q must be in registers before any LDS-DMA is in flight: the compiler
   // cannot count the DMA operations, so any vmcnt wait it placed for Q inside
   // the key loop would also drain the prefetch of the next tile.
@@ -145,7 +148,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
     if constexpr (MASK) {
 #pragma unroll
       for (int n = 0; n < MASK_DMA; ++n)
-        lds_dma16_sv(mbase + j0 * 2, moff[n], buf + 2 * C::TILE_BYTES + wave * MASK_BAND + n * 1024);
+        lds_dma16_sv(mbase + j0 * 2, moff[n], buf + MASK_OFF + wave * MASK_BAND + n * 1024);
     }
     if (!KVC || j0 >= lc) {
       const int c0 = j0 - lc;  // current row of tile row 0
@@ -153,6 +156,9 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
         T::template dma_tile_sv<false>(buf, kb + c0 * row_bytes, row_bytes, koff, wave);
         T::template dma_tile_sv<true>(buf + C::TILE_BYTES, vb + c0 * row_bytes, row_bytes, voff,
                                       wave);
+        if constexpr (QV)
+          T::template dma_tile_sv<false>(buf + VK_OFF, vb + c0 * row_bytes, row_bytes, koff,
+                                         wave);
       } else {
         // the cache variant holds more state across the key loop: its lane
         // constants are rebuilt here rather than kept live
@@ -162,6 +168,10 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
         T::template dma_tile<true>(
             buf + C::TILE_BYTES,
             [&](int r) { return vb + (long)(min(j0 + r, last) - lc) * row_bytes; }, wave, ln);
+        if constexpr (QV)
+          T::template dma_tile<false>(
+              buf + VK_OFF, [&](int r) { return vb + (long)(min(j0 + r, last) - lc) * row_bytes; },
+              wave, ln);
       }
       return;
     }
@@ -207,16 +217,19 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   };
   const int tdiag = trow + bd.delta;
   float cscale = a.scale_log2;
-  float vscale = 1.f;
+  float vscale = 1.f, qv_ratio = 1.f;
   if constexpr (C::FP8 != 0) {
     const int dsi = w.b * a.hkv + w.kvh;
+    const float kd = a.k_descale ? a.k_descale[dsi] : 1.f;
     if (a.q_descale) cscale *= a.q_descale[dsi];
-    if (a.k_descale) cscale *= a.k_descale[dsi];
+    cscale *= kd;
     if (a.v_descale) vscale = a.v_descale[dsi];
+    qv_ratio = vscale / kd;
   }
   const int ntiles = bd.hi > bd.lo ? (bd.hi - bd.lo + C::BN - 1) / C::BN : 0;
   auto stage = [&](int i) { return ring + i * STAGE; };  // i < STAGES
-  constexpr int PER_TILE = 2 * C::DMA_PER_WAVE + MASK_DMA;  // DMA instructions per wave per tile
+  // DMA instructions per wave per tile
+  constexpr int PER_TILE = (QV ? 3 : 2) * C::DMA_PER_WAVE + MASK_DMA;
   static_assert(PER_TILE * (C::STAGES - 1) < 64, "vmcnt range");
 #pragma unroll
   for (int i = 0; i < C::STAGES - 1; ++i)
@@ -242,9 +255,10 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
                       (bd.wl >= 0 && j0 < wrow1 + bd.delta - bd.wl);
     f32x16 s[C::NSB];
     t.qk(cur, lane, s);
+    t.qv_scores(cur + VK_OFF, lane, s, qv_ratio);
     float cs = cscale;
     if constexpr (MASK) {
-      T::add_mask(s, cur + 2 * C::TILE_BYTES + wave * MASK_BAND, cs, lane);
+      T::add_mask(s, cur + MASK_OFF + wave * MASK_BAND, cs, lane);
       cs = 1.f;  // the scores are scaled
     }
     if (need) {
@@ -283,6 +297,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_bf16(Varlen
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8(VarlenArgs a) {
   varlen_body<C, false, false>(a);
+}
+
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv(VarlenArgs a) {
+  varlen_body<C, false, false, true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -406,6 +425,10 @@ using CfgP128 = PrefillCfg<128, 4, 32, 3>;
 template <int FMT>
 using CfgP8 = PrefillCfg<128, 4, 32, 3, 3, FMT>;
 static_assert(CfgP8<1>::ROWS == CfgP128::ROWS, "FP8 grid sized by varlen_bf16_rows(128)");
+// qv: the second query's fragments take 2 waves per SIMD (bf16 or FP8 codes)
+template <int FMT>
+using CfgPQv = PrefillCfg<128, 4, 32, 2, 3, FMT>;
+static_assert(CfgPQv<0>::ROWS == CfgP128::ROWS, "qv grid sized by varlen_bf16_rows(128)");
 
 }  // namespace
 
@@ -445,6 +468,17 @@ hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s) {
     hipLaunchKernelGGL(k_varlen_fp8<CfgP8<1>>, dim3(grid), dim3(CfgP8<1>::THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(k_varlen_fp8<CfgP8<2>>, dim3(grid), dim3(CfgP8<2>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_qv(const VarlenArgs& a, int fmt, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_varlen_qv<CfgPQv<0>>, dim3(grid), dim3(CfgPQv<0>::THREADS), 0, s, a);
+  else if (fmt == 1)
+    hipLaunchKernelGGL(k_varlen_qv<CfgPQv<1>>, dim3(grid), dim3(CfgPQv<1>::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_varlen_qv<CfgPQv<2>>, dim3(grid), dim3(CfgPQv<2>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -34,6 +34,8 @@ struct VarlenArgs {
   const float* q_descale;
   const float* k_descale;
   const float* v_descale;
+  // second query (Tq, hq, dv) scored against the value rows (launch_varlen_qv)
+  const void* qv;
 };
 
 struct DecodeArgs {
@@ -90,6 +92,8 @@ hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);  // mask: a.mask
 hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s);  // d = 128
+// q.k + qv.v scores; fmt 0 bf16, 1 e4m3, 2 e5m2; d = dv = 128
+hipError_t launch_varlen_qv(const VarlenArgs& a, int fmt, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s);  // fmt 1 e4m3, 2 e5m2
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s);

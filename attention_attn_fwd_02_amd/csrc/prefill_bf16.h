@@ -124,13 +124,16 @@ struct PrefillCfg {
   static_assert(FP8 == 0 || D == 128, "FP8 tiles: D = 128");
 };
 
-template <class C>
+// QV: the tile also holds a second query qv (Dv = D wide), scored against
+// the V rows of each tile (a copy of V in the K layout) and added to Q.K^T.
+template <class C, bool QV = false>
 struct PrefillTile {
   using M = Mfma<32>;
   // bfloat16: fragment i = dims 16 i + 8 g .. + 7; FP8: fragment m = dims
   // 64 m + 32 g .. + 31 (the B operand of one 32x32x64 FP8 MFMA)
   using QFrag = std::conditional_t<(C::FP8 != 0), i32x8, bf16x8>;
   QFrag qf[C::NQ];
+  QFrag qvf[QV ? C::NQ : 1];
   f32x16 o[C::NOB];
   float m_ref;  // reference max (base-2 scaled domain), -inf until a key is seen
   float m_use;  // exponent offset: m_ref, or 0 while m_ref is -inf
@@ -146,28 +149,35 @@ struct PrefillTile {
     l_run = 0.f;
   }
 
-  __device__ __forceinline__ void load_q(const bf16_t* qrow, int lane) {
+  // One query row (bf16 elements or FP8 codes) into B-operand fragments.
+  __device__ __forceinline__ static void load_frags(QFrag (&f)[C::NQ], const void* row,
+                                                    int lane) {
     const int g = lane >> 5;
+    if constexpr (C::FP8 != 0) {
+      const uint8_t* qrow = static_cast<const uint8_t*>(row);
 #pragma unroll
-    for (int i = 0; i < C::NQ; ++i) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * 16 + g * 8);
-      qf[i] = as_bf16x8(v);
+      for (int m = 0; m < C::NQ; ++m) {
+        u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+        if (qrow) {
+          v0 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32);
+          v1 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32 + 16);
+        }
+        f[m] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
+                     (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
+      }
+    } else {
+      const bf16_t* qrow = static_cast<const bf16_t*>(row);
+#pragma unroll
+      for (int i = 0; i < C::NQ; ++i) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qrow) v = *reinterpret_cast<const u32x4*>(qrow + i * 16 + g * 8);
+        f[i] = as_bf16x8(v);
+      }
     }
   }
-
-  __device__ __forceinline__ void load_q8(const uint8_t* qrow, int lane) {
-    const int g = lane >> 5;
-#pragma unroll
-    for (int m = 0; m < C::NQ; ++m) {
-      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
-      if (qrow) {
-        v0 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32);
-        v1 = *reinterpret_cast<const u32x4*>(qrow + m * 64 + g * 32 + 16);
-      }
-      qf[m] = i32x8{(int)v0[0], (int)v0[1], (int)v0[2], (int)v0[3],
-                    (int)v1[0], (int)v1[1], (int)v1[2], (int)v1[3]};
-    }
+  __device__ __forceinline__ void load_q(const void* qrow, int lane) { load_frags(qf, qrow, lane); }
+  __device__ __forceinline__ void load_qv(const void* row, int lane) {
+    if constexpr (QV) load_frags(qvf, row, lane);
   }
 
   // FP8 unit swizzles (see the header comment)
@@ -285,6 +295,19 @@ struct PrefillTile {
   // (2 (dq % 2) + g) ^ ((k % 16) / 4); the two slot patterns of even and odd
   // dq give two per-lane bases.
   __device__ __forceinline__ void qk(const char* kbuf, int lane, f32x16 (&s)[C::NSB]) const {
+    qk_frags<false>(kbuf, qf, lane, s, 1.f);
+  }
+  // S^T += ratio * V Qv^T from the copy of V in the K layout at vkbuf (bf16:
+  // the same MFMA chain, ratio 1; FP8: a second accumulator, ratio =
+  // v_descale / k_descale, as the score scale carries k_descale).
+  __device__ __forceinline__ void qv_scores(const char* vkbuf, int lane, f32x16 (&s)[C::NSB],
+                                            float ratio) const {
+    if constexpr (QV) qk_frags<true>(vkbuf, qvf, lane, s, ratio);
+  }
+  // ACC = false: S^T = K F^T; ACC = true: S^T += ratio * K F^T.
+  template <bool ACC>
+  __device__ __forceinline__ void qk_frags(const char* kbuf, const QFrag (&fr)[C::NQ], int lane,
+                                           f32x16 (&s)[C::NSB], float ratio) const {
     if constexpr (C::FP8 != 0) {
       // key k = lane % 32 of block sb: dims 64 m + 32 g .. + 31 are units
       // 4 m + 2 g + t (t = 0, 1) of its row, stored at unit ^ fk8(k); A and B
@@ -304,9 +327,15 @@ struct PrefillTile {
         for (int m = 0; m < 2; ++m)
           kf[m] = join8(*reinterpret_cast<const u32x4*>(kp[m][0] + sb * 32 * 128),
                         *reinterpret_cast<const u32x4*>(kp[m][1] + sb * 32 * 128));
-        s[sb] = f32x16{};
+        f32x16 acc = f32x16{};
 #pragma unroll
-        for (int m = 0; m < 2; ++m) s[sb] = mma8(kf[m], qf[m], s[sb]);
+        for (int m = 0; m < 2; ++m) acc = mma8(kf[m], fr[m], acc);
+        if constexpr (ACC) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[sb][e] = __builtin_fmaf(acc[e], ratio, s[sb][e]);
+        } else {
+          s[sb] = acc;
+        }
       }
       return;
     } else {
@@ -322,9 +351,9 @@ struct PrefillTile {
       for (int dq = 0; dq < C::NQ; ++dq)
         kf[dq] = as_bf16x8(*reinterpret_cast<const u32x4*>((dq & 1 ? kb1 : kb0) +
                                                            (sb * 2 * IPB + dq / 2) * 1024));
-      s[sb] = f32x16{};
+      if constexpr (!ACC) s[sb] = f32x16{};
 #pragma unroll
-      for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], qf[dq], s[sb]);
+      for (int dq = 0; dq < C::NQ; ++dq) s[sb] = M::mma(kf[dq], fr[dq], s[sb]);
     }
     }
   }

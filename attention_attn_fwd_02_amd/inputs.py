@@ -33,6 +33,7 @@ SEED_PAGED_DECODE_FP8 = 1007
 SEED_SPARSE_PAGED = 1008
 SEED_VARLEN_PREFILL_FP8 = 1009
 SEED_PAGED_DECODE_QV = 1010
+SEED_VARLEN_PREFILL_QV = 1011
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -495,6 +496,12 @@ def paged_decode(seed: int = SEED_PAGED_DECODE, batch: int = 64, lo: int = 1024,
     rng = np.random.default_rng(seed)
     lens = rng.integers(lo, hi, endpoint=True, size=batch)
     return _paged_draw(rng, lens, 1, hq, hkv, d, d, page, False, False, None, False)
+
+
+def varlen_prefill_qv(w: Dense, seed: int = SEED_VARLEN_PREFILL_QV) -> np.ndarray:
+    """A bf16 N(0,1) qv (Tq, Hq, Dv) for a packed problem w, from its own seed."""
+    rng = np.random.default_rng(seed)
+    return _normal_bf16(rng, w.q.shape[:2] + (w.v.shape[2],))
 
 
 def paged_decode_qv(w: Paged, seed: int = SEED_PAGED_DECODE_QV) -> np.ndarray:

@@ -170,6 +170,29 @@ def bench_prefill_fp8(steps, warmup):
     return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lens=lens.tolist())
 
 
+def bench_prefill_qv(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.varlen_prefill()
+    qvh = inputs.varlen_prefill_qv(w)
+    lens = np.diff(w.cu_seqlens_q)
+    q, qv, k, v = dev(w.q), dev(qvh), dev(w.k), dev(w.v)
+    cq, ck = dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
+    hq, d = w.q.shape[1], w.q.shape[2]
+    out = torch.empty((int(lens.sum()), hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, int(lens.sum())), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.attn_fwd_varlen_qv(q, qv, k, v, cq, ck, int(lens.max()), int(lens.max()), w.scale,
+                             causal=True, out=out, lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    # q.k, qv.v and p.v: 6 D flop per visible (row, key) pair
+    flops = prefill_flops(lens, hq, d) * 6 / 4
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12)
+
+
 def bench_decode(steps, warmup):
     import torch
     from attention_attn_fwd_02_amd import binding as B
@@ -560,8 +583,8 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
-                    default="prefill,prefill_fp8,decode,decode_fp8,decode_qv,decode_only_qv,"
-                            "mla,chunked,chunked_mask,sparse,sparse_paged")
+                    default="prefill,prefill_fp8,prefill_qv,decode,decode_fp8,decode_qv,"
+                            "decode_only_qv,mla,chunked,chunked_mask,sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -624,6 +647,19 @@ def main():
                          "peak_note": "half the flops (Q.K^T) on FP8 MFMA (5033 TFLOP/s), "
                                       "half (P.V) on bf16 MFMA (2517 TFLOP/s): the harmonic "
                                       "mix"}})
+    if "prefill_qv" in only:
+        log("prefill qv ...")
+        pq = bench_prefill_qv(args.steps, args.warmup)
+        log(f"prefill_qv {pq['ms']:.3f} ms {pq['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "attention TFLOP/s (varlen prefill with qv)", "value": pq["tflops"],
+            "unit": "TFLOP/s", "ms_per_step": pq["ms"],
+            "workload": "the varlen causal GQA prefill workload (seed 1002) with a bf16 qv "
+                        "(T,32,128) N(0,1) (seed 1011); scores q.k + qv.v; 6 D flop per visible "
+                        "(row, key) pair",
+            "roofline": {"bound": "mfma", "achieved": pq["tflops"], "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": pq["tflops"] / PEAK_BF16_TFLOPS,
+                         "traffic": None, "kernel": "k_varlen_qv (D=128)"}})
     if "decode" in only:
         log("paged decode ...")
         dec = bench_decode(args.steps, args.warmup)

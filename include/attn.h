@@ -116,6 +116,35 @@ int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,
                             void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_qv - attn_fwd_varlen with a second query qv scored against
+ * the value rows (bf16 or FP8 inputs).
+ * [MATE "Attention" page, FMHA forward notes: optional qv input on the FMHA
+ *  forward path, also with FP8 inputs (q_descale then applies to both query
+ *  tensors); only_qv skips the QK score path]
+ *
+ *  q (Tq, hq, 128), qv (Tq, hq, 128), k (Tk, hkv, 128), v (Tk, hkv, 128),
+ *  sequences as in attn_fwd_varlen. The score of key j for query head h
+ *  (KV head g = h / (hq / hkv)) is
+ *      scale * (q . k_j + qv . v_j)     (only_qv = 0)
+ *      scale * (qv . v_j)               (only_qv != 0; q and k are then not
+ *                                        read and may be NULL)
+ *  on the real values; masks, sinks, output and LSE are those of
+ *  attn_fwd_varlen over these scores. out (Tq, hq, 128) bfloat16; lse NULL or
+ *  float32 (hq, Tq).
+ *  dtype: ATTN_BF16 (descales must be NULL), ATTN_FP8_E4M3 or ATTN_FP8_E5M2
+ *  (codes; descales as in attn_fwd_varlen_fp8, qv using q_descale).
+ *  Errors as in attn_fwd_varlen. Supported: d = dv = 128.
+ */
+int32_t attn_fwd_varlen_qv(const void* q, const void* qv, const void* k, const void* v,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                           int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                           int32_t hkv, int32_t d, int32_t dv, int32_t dtype,
+                           const float* q_descale, const float* k_descale,
+                           const float* v_descale, float scale, int32_t causal,
+                           int32_t window_left, int32_t window_right, const float* sinks,
+                           int32_t only_qv, void* out, float* lse, void* stream);
+
+/*
  * attn_fwd_varlen_kvcache - packed queries over a paged cache of earlier
  * tokens followed by the current K/V rows, without concatenating them
  * (chunked / append prefill).

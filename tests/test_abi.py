@@ -29,7 +29,7 @@ def lib():
 def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
-              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "attn_decode_paged_qv", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "attn_decode_paged_qv", "attn_fwd_varlen_qv", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -200,6 +200,30 @@ def test_decode_qv_host_checks(lib):
     assert call(dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
     assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
+
+
+def test_varlen_qv_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, qv=P, k=P, v=P, cq=P, ck=P, batch=2, mq=100, mk=100, hq=8, hkv=2, d=128,
+                 dv=128, dtype=B.ATTN_BF16, qd=None, scale=0.1, causal=1, wl=-1, wr=-1, only=0,
+                 out=P)
+        a.update(kw)
+        return lib.attn_fwd_varlen_qv(a["q"], a["qv"], a["k"], a["v"], a["cq"], a["ck"],
+                                      a["batch"], a["mq"], a["mk"], a["hq"], a["hkv"], a["d"],
+                                      a["dv"], a["dtype"], a["qd"], None, None, a["scale"],
+                                      a["causal"], a["wl"], a["wr"], None, a["only"], a["out"],
+                                      None, None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(qv=None) == B.ATTN_EINVAL
+    assert call(q=None) == B.ATTN_EINVAL
+    assert call(k=None) == B.ATTN_EINVAL
+    assert call(v=None, only=1) == B.ATTN_EINVAL
+    assert call(hq=7) == B.ATTN_EINVAL
+    assert call(wr=-3) == B.ATTN_EINVAL
+    assert call(scale=0.0) == B.ATTN_EINVAL
+    assert call(qd=P) == B.ATTN_EINVAL
+    assert call(dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
 
 
 def test_mla_and_sparse_host_checks(lib):
