@@ -96,6 +96,7 @@ template <class C>
 struct StreamTile {
   using M = Mfma<16>;
   bf16x8 qf[C::NQ];
+  i32x8 q8f;  // FP8: the Q row's codes as the B operand of the 16x16x128 FP8 MFMA
   bf16x8 qvf[C::QV ? C::NQ : 1];  // qv fragments, chunks as those of Q
   f32x4 o[C::NOB];
   float m_ref;
@@ -131,9 +132,16 @@ struct StreamTile {
     }
   }
 
-  // FP8 Q: fragment dq holds chunk dq * 4 + g (8 codes), widened to bf16.
+  // FP8 Q: lane group g holds codes 32 g .. 32 g + 31 of its row (the K
+  // fragments below hold the same dims, so the 128-deep products pair them).
   __device__ __forceinline__ void load_q8(const uint8_t* qrow, int lane) {
-    load_frag8(qf, qrow, lane);
+    const int g = lane >> 4;
+    u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+    if (qrow) {
+      v0 = *reinterpret_cast<const u32x4*>(qrow + g * 32);
+      v1 = *reinterpret_cast<const u32x4*>(qrow + g * 32 + 16);
+    }
+    q8f = join_i32x8(v0, v1);
   }
   __device__ __forceinline__ static void load_frag8(bf16x8 (&f)[C::NQ], const uint8_t* row,
                                                     int lane) {
@@ -291,20 +299,19 @@ struct StreamTile {
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) s[sb] = f32x4{};
     } else if constexpr (C::FP8) {
-      // key r = lane % 16 of block sb, chunk dq * 4 + g: unit 2 dq + g / 2,
-      // half g % 2; stored at unit (2 dq) ^ (g / 2) ^ ((r / 2) % 8)
-      const int r = lane & 15;
-      const int fl = (g >> 1) ^ swz8_k(r);
-      const char* base = stage + r * 128 + (g & 1) * 8;
+      // one 16x16x128 FP8 MFMA per 16-key block on the codes themselves
+      // (exact products, fp32 sums): key r = lane % 16 gives units 2 g and
+      // 2 g + 1 of its row (codes 32 g .. 32 g + 31, as Q), stored at
+      // unit ^ swz8_k(r)
+      const int r = lane & 15, sw = swz8_k(r);
+      const char* k0 = stage + r * 128 + ((2 * g) ^ sw) * 16;
+      const char* k1 = stage + r * 128 + ((2 * g + 1) ^ sw) * 16;
 #pragma unroll
       for (int sb = 0; sb < C::NSB; ++sb) {
-        s[sb] = f32x4{};
-#pragma unroll
-        for (int dq = 0; dq < C::NQ; ++dq) {
-          const u32x2 w =
-              *reinterpret_cast<const u32x2*>(base + sb * 16 * 128 + ((2 * dq) ^ fl) * 16);
-          s[sb] = M::mma(fp8x8_to_bf16<C::FP8>(w), qf[dq], s[sb]);
-        }
+        const i32x8 a = join_i32x8(*reinterpret_cast<const u32x4*>(k0 + sb * 16 * 128),
+                                   *reinterpret_cast<const u32x4*>(k1 + sb * 16 * 128));
+        s[sb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, q8f, f32x4{}, C::FP8 - 1,
+                                                                 C::FP8 - 1, 0, 127, 0, 127);
       }
     } else if constexpr (C::VSHARED) {
       // chunk parity p = f & 1; chunk c = (f >> 1) * 8 + 2g + p sits at

@@ -131,6 +131,12 @@ __device__ __forceinline__ s16x4 lds_read_tr(const bf16_t* p) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Two 16-byte halves as one 8-register MFMA operand (FP8 codes).
+__device__ __forceinline__ i32x8 join_i32x8(u32x4 a, u32x4 b) {
+  return i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2],
+               (int)b[3]};
+}
+
 // Transposing read of 8-bit elements (ds_read_b64_tr_b8). Within each block of
 // 16 lanes, lane m addresses 8 bytes; lane i receives byte i % 8 of the bytes
 // lane 2j + i/8 addressed, for j = 0..7 (so if lane m addresses row m/2,
