@@ -221,8 +221,8 @@ def varlen_kvcache(seed: int, lens_q, lens_new, lens_cache, hq: int = 32, hkv: i
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_new)]).astype(np.int32)
     return DenseKV(q, k, v, cu_q, cu_k, "bf16", scale if scale is not None else 1.0 / np.sqrt(d),
-                   causal, tuple(window), sinks, k_cache, v_cache, table,
-                   lens_cache.astype(np.int32), page)
+                   causal, tuple(window), sinks, k_cache=k_cache, v_cache=v_cache,
+                   block_table=table, cache_seqlens=lens_cache.astype(np.int32), page_size=page)
 
 
 def chunked_prefill(seed: int = SEED_CHUNKED_PREFILL, nseq: int = 8, chunk: int = 1024,
