@@ -56,8 +56,11 @@ struct DmaSrc {
 // QV = 1: a second query qv (Dv wide) is scored against the value rows of
 // the tile, S^T += V Qv^T, read in place from the V layout (no second copy).
 // QV = 2: only that score path; tiles hold V alone (no K bytes, no Q).
+//
+// BN: keys per tile, 32, or a multiple of 32 for FP8 tiles (whose rows are
+// half as wide, so 64 keys move the bytes of a 32-key bf16 tile).
 template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1, int FP8_ = 0,
-          int QV_ = 0>
+          int QV_ = 0, int BN_ = 32>
 struct StreamCfg {
   static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
   static constexpr bool VSHARED = VSHARED_;
@@ -65,7 +68,7 @@ struct StreamCfg {
   static constexpr int FP8 = FP8_;
   static constexpr int QV = QV_;
   static constexpr int EB = FP8 ? 1 : 2;  // bytes per element in memory and LDS
-  static constexpr int BN = 32, R = 16;
+  static constexpr int BN = BN_, R = 16;
   static constexpr int THREADS = NW * 64;
   static constexpr int ROWS = NW / DSPLIT * R;
   static constexpr int DMA_WAVES = NW / DSPLIT;
@@ -90,6 +93,8 @@ struct StreamCfg {
   static_assert(FP8 == 0 || (D == 128 && DV == 128 && !VSHARED && DSPLIT == 1),
                 "FP8 tiles: D = Dv = 128, separate V, whole head per wave");
   static_assert(QV == 0 || (!VSHARED && DSPLIT == 1 && DV == D), "qv: separate V, Dv = D");
+  static_assert(BN == 32 || (FP8 != 0 && BN % 32 == 0 && BN <= 64),
+                "tiles of 32 keys, or up to 64 with FP8 codes");
 };
 
 template <class C>
@@ -174,39 +179,43 @@ struct StreamTile {
 
   // FP8 LDS layouts: tile rows of 128 bytes; the 16-byte unit u of row r is
   // stored at unit u ^ f(r), with
-  //   K: f(r) = (r / 2) % 8              (16 consecutive rows of one block)
-  //   V: f(r) = (r / 2) % 4 + 4 (r / 16)  (rows 4g..4g+3 and 16+4g..16+4g+3)
+  //   K: f(r) = (r / 2) % 8                    (16 consecutive rows of one block)
+  //   V: f(r) = (r / 2) % 4 + 4 ((r / 16) % 2)  (rows 4g..4g+3 and 16+4g..16+4g+3
+  //                                             of a 32-key chunk)
   // so that the 32 lanes of each read cycle hit 64 distinct banks. A DMA
   // instruction fills 8 rows: lane l reads 16 bytes of row l / 8 (8 lanes
   // per 128-byte row, coalesced); its unit depends on the instruction's rows
   // through one bit, hence two lane offsets each for K and V.
   __device__ __forceinline__ static int swz8_k(int r) { return (r >> 1) & 7; }
-  __device__ __forceinline__ static int swz8_v(int r) { return ((r >> 1) & 3) | ((r >> 4) << 2); }
+  __device__ __forceinline__ static int swz8_v(int r) {
+    return ((r >> 1) & 3) | (((r >> 4) & 1) << 2);
+  }
   // lane offsets for instructions whose 8-row groups r8 have (r8 & 1) = hi
-  // (K) or (r8 >> 1) = hi (V); rows `stride` bytes apart
+  // (K) or ((r8 >> 1) & 1) = hi (V); rows `stride` bytes apart
   __device__ __forceinline__ static uint32_t lane_off8(int lane, uint32_t stride, int hi) {
     return (uint32_t)(lane >> 3) * stride + (uint32_t)((lane & 7) ^ (hi * 4 + (lane >> 4))) * 16;
   }
   // Saddr form: kbase(r8) / vbase(r8) give the wave-uniform pointer of tile
-  // row 8 r8 (r8 = 0..3; rows 8 r8 .. 8 r8 + 7 are `stride` bytes apart).
+  // row 8 r8 (r8 < BN / 8; rows 8 r8 .. 8 r8 + 7 are `stride` bytes apart).
   template <class KB, class VB>
   __device__ __forceinline__ static void dma_tile8_sv(char* stage, KB kbase, VB vbase,
                                                       uint32_t koff0, uint32_t koff1,
                                                       uint32_t voff0, uint32_t voff1) {
     if constexpr (C::K_BYTES > 0) {
 #pragma unroll
-      for (int r8 = 0; r8 < 4; ++r8)
+      for (int r8 = 0; r8 < C::BN / 8; ++r8)
         lds_dma16_sv(kbase(r8), (r8 & 1) ? koff1 : koff0, stage + r8 * 1024);
     }
 #pragma unroll
-    for (int r8 = 0; r8 < 4; ++r8)
-      lds_dma16_sv(vbase(r8), (r8 >> 1) ? voff1 : voff0, stage + C::K_BYTES + r8 * 1024);
+    for (int r8 = 0; r8 < C::BN / 8; ++r8)
+      lds_dma16_sv(vbase(r8), ((r8 >> 1) & 1) ? voff1 : voff0,
+                   stage + C::K_BYTES + r8 * 1024);
   }
   // Per-lane form: krow(r) / vrow(r) are the byte addresses of tile row r.
   template <class KRow, class VRow>
   __device__ __forceinline__ static void dma_tile8(char* stage, KRow krow, VRow vrow, int lane) {
 #pragma unroll
-    for (int r8 = 0; r8 < 4; ++r8) {
+    for (int r8 = 0; r8 < C::BN / 8; ++r8) {
       const int r = r8 * 8 + (lane >> 3);
       if constexpr (C::K_BYTES > 0)
         lds_dma16(krow(r) + ((lane & 7) ^ swz8_k(r)) * 16, stage + r8 * 1024);
@@ -463,18 +472,25 @@ struct StreamTile {
     const u32x4 pv4 = {pk[0], pk[1], pk[2], pk[3]};
     const bf16x8 b = as_bf16x8(pv4);
     if constexpr (C::FP8) {
-      // The B operand (P) of lane group g holds keys 4g..4g+3 and
-      // 16+4g..16+4g+3 (the S^T accumulator layout of the two 16-key
-      // blocks); the A operand must list the same keys: lane i of block g
-      // receives V[key k_j][dv ob*16 + i], k_j = (j % 4) + 4g + 16 (j / 4),
-      // by addressing row k_{i/2}, bytes ob*16 + 8 (i % 2) .. + 7.
+      // Per 32-key chunk c, the B operand (P) of lane group g holds keys
+      // 32c + 4g..4g+3 and 32c + 16+4g..16+4g+3 (the S^T accumulator layout
+      // of the chunk's two 16-key blocks); the A operand must list the same
+      // keys: lane i of block g receives V[key k_j][dv ob*16 + i],
+      // k_j = 32c + (j % 4) + 4g + 16 (j / 4), by addressing row k_{i/2},
+      // bytes ob*16 + 8 (i % 2) .. + 7 (swz8_v repeats every 32 rows).
       const int jj = i >> 1;
       const int row = (jj & 3) + 4 * g + 16 * (jj >> 2);
       const int fv = swz8_v(row);
       const char* vb = stage + C::K_BYTES + row * 128 + (i & 1) * 8;
 #pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob)
-        o[ob] = M::mma(fp8x8_to_bf16<C::FP8>(lds_read_tr8(vb + (ob ^ fv) * 16)), b, o[ob]);
+      for (int c = 0; c < C::BN / 32; ++c) {
+        const u32x4 pc = {pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]};
+        const bf16x8 bc = as_bf16x8(pc);
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob)
+          o[ob] = M::mma(fp8x8_to_bf16<C::FP8>(lds_read_tr8(vb + c * 32 * 128 + (ob ^ fv) * 16)),
+                         bc, o[ob]);
+      }
     } else if constexpr (C::VSHARED) {
       const int par = (i >> 1) & 1;
       const char* vb = stage + (par * 256 + ((g * 4 + (i >> 2)) ^ (par * 8)) * 16 + (i & 1) * 8) +

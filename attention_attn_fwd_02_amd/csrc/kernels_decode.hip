@@ -108,41 +108,48 @@ k_decode(DecodeArgs a) {
   }
   auto issue = [&](char* st, int ti) {
     // A 16-row block of a tile lies on one page (pages are multiples of 16
-    // rows and splits start on page boundaries). slot0 / slot1: cache slot
-    // of tile row 0 and of tile row 16 (clamped to the split's last key).
+    // rows and splits start on page boundaries). sl[b]: cache slot of tile
+    // row 16 b (clamped to the split's last key).
+    constexpr int NB = C::BN / 16;
     const int j0 = kv0 + ti * C::BN;
-    const int j1 = min(j0 + 16, kv_last);
-    const int lp0 = j0 / a.page, lp1 = j1 / a.page;
-    int p0, p1;
-    sload2_uniform(btb + lp0, btb + lp1, p0, p1);
-    const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
-    const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
+    long sl[NB];
+    static_for<NB / 2>([&](auto I) {
+      constexpr int bb = 2 * decltype(I)::value;
+      const int ja = min(j0 + 16 * bb, kv_last), jb = min(j0 + 16 * (bb + 1), kv_last);
+      const int la = ja / a.page, lb = jb / a.page;
+      int pa, pb;
+      sload2_uniform(btb + la, btb + lb, pa, pb);
+      sl[bb] = (long)pa * a.page + (ja - la * a.page);
+      sl[bb + 1] = (long)pb * a.page + (jb - lb * a.page);
+    });
     const int rmax = kv_last - j0;
     if (rmax >= C::BN - 1) {
       if constexpr (C::FP8) {
-        auto kb = [&](int r8) {
-          return kcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok_k;
-        };
-        auto vb = [&](int r8) {
-          return vcb + ((r8 >> 1 ? slot1 : slot0) + (r8 & 1) * 8) * (long)tok_v;
-        };
+        auto kb = [&](int r8) { return kcb + (sl[r8 >> 1] + (r8 & 1) * 8) * (long)tok_k; };
+        auto vb = [&](int r8) { return vcb + (sl[r8 >> 1] + (r8 & 1) * 8) * (long)tok_v; };
         T::dma_tile8_sv(st, kb, vb, k8[0], k8[1], k8[0], k8[1]);
       } else {
         T::dma_tile_sv(
             st,
             [&](int rb, int colb) {
-              return typename T::Src{kcb + (rb ? slot1 : slot0) * (long)tok_k + colb, klane};
+              return typename T::Src{kcb + sl[rb] * (long)tok_k + colb, klane};
             },
             [&](int rb, int sub, int colb) {
-              return typename T::Src{
-                  vcb + ((rb ? slot1 : slot0) + sub * 8) * (long)tok_v + colb, vlane};
+              return typename T::Src{vcb + (sl[rb] + sub * 8) * (long)tok_v + colb, vlane};
             },
             wave);
       }
     } else {
       // last tile of the split: rows past its last key re-read that key,
-      // which is masked
-      auto row = [&](int rr) { rr = min(rr, rmax); return (rr >> 4 ? slot1 : slot0) + (rr & 15); };
+      // which is masked; the lane's 16-row block selects its slot
+      auto row = [&](int rr) {
+        rr = min(rr, rmax);
+        long v = sl[0];
+        static_for<NB - 1>([&](auto I) {
+          if ((rr >> 4) == decltype(I)::value + 1) v = sl[decltype(I)::value + 1];
+        });
+        return v + (rr & 15);
+      };
       if constexpr (C::FP8)
         T::dma_tile8(
             st, [&](int rr) { return kcb + row(rr) * tok_k; },
@@ -381,8 +388,9 @@ k_sparse(SparseArgs a) {
 
 template <int QV = 0>
 using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false, 1, 0, QV>;
+// FP8 tiles of 64 keys: the bytes of a 32-key bf16 tile
 template <int FMT, int QV = 0>
-using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV>;
+using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 64>;
 using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
