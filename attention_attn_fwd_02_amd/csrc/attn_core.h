@@ -8,7 +8,7 @@
 //   O^T += V^T P^T (A = V read transposed from LDS, B = P from the S^T
 //   registers, which are already in B-operand order)
 //
-// Keys are consumed in tiles of BN = 32 rows. Each tile is copied global ->
+// Keys are consumed in tiles of BN rows (32; 64 for FP8). Each tile is copied global ->
 // LDS with global_load_lds_dwordx4 into a ring of STAGES buffers, so up to
 // STAGES-1 tiles are in flight per workgroup; the caller supplies the global
 // row address of every key of a tile (row(r), always a valid address) and,
@@ -49,9 +49,10 @@ struct DmaSrc {
 // fit on each SIMD and hide each other's LDS latency.
 //
 // FP8 = 1 (e4m3fn) or 2 (e5m2): Q, K and V hold 8-bit codes. Tiles reach LDS
-// as bytes (half the traffic) and every fragment is widened to bfloat16 as it
-// is read (exact), so the MFMAs, softmax and partial outputs are those of the
-// bfloat16 path; descales are applied to the scores and to O.
+// as bytes (half the traffic). Q.K^T runs on the FP8 MFMA over the codes
+// (exact products, fp32 sums); V fragments are widened to bfloat16 as they
+// are read (exact), so P.V, the softmax and the partial outputs are those of
+// the bfloat16 path; descales are applied to the scores and to O.
 //
 // QV = 1: a second query qv (Dv wide) is scored against the value rows of
 // the tile, S^T += V Qv^T, read in place from the V layout (no second copy).
@@ -466,7 +467,7 @@ struct StreamTile {
     l_run += lsum;
   }
 
-  // O^T += V^T P^T for one tile (one 32-key chunk).
+  // O^T += V^T P^T for one tile (one 32-key chunk; FP8 tiles loop over theirs).
   __device__ __forceinline__ void pv(const char* stage, int lane, const uint32_t (&pk)[C::NSB * 2]) {
     const int g = lane >> 4, i = lane & 15;
     const u32x4 pv4 = {pk[0], pk[1], pk[2], pk[3]};

@@ -29,9 +29,9 @@ inline int round_grid(long total, int grp) {
 // One workgroup = (sequence b, split s, KV head kvh, row tile mt). Rows of a
 // KV head are (query token t, query head of the group): row r -> t = r / G,
 // head kvh*G + r % G. Keys are the split's range [kv0, kv1) of the sequence.
-// A 32-key tile spans at most two cache pages (page sizes are multiples of
-// 16 and splits start on page boundaries); their physical page numbers are
-// wave-uniform and come from scalar loads of the block table.
+// Each 16-row block of a tile lies on one cache page (page sizes are
+// multiples of 16 and splits start on page boundaries); the blocks' physical
+// page numbers are wave-uniform and come from scalar loads of the block table.
 template <class C>
 __global__ void __launch_bounds__(C::THREADS)
 k_decode(DecodeArgs a) {
