@@ -3,6 +3,7 @@
 // before anything is enqueued; device tensor contents are never inspected.
 #include <hip/hip_runtime.h>
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 
@@ -32,6 +33,13 @@ int32_t hip_status(hipError_t e, const char* what) {
 }
 
 inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// The kernels move 16-byte vectors of every element tensor; NULL (an absent
+// optional tensor) passes.
+template <class... P>
+bool aligned16(const P*... p) {
+  return ((((uintptr_t)p & 15) == 0) && ...);
+}
 
 #define REQUIRE(cond, code, ...) \
   do {                           \
@@ -76,6 +84,8 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
   REQUIRE(q && k && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL,
           "null tensor pointer");
+  REQUIRE(aligned16(q, k, v, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
@@ -129,6 +139,8 @@ int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,
   REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
   REQUIRE(q && k && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL,
           "null tensor pointer");
+  REQUIRE(aligned16(q, k, v, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
@@ -179,6 +191,8 @@ int32_t attn_fwd_varlen_qv(const void* q, const void* qv, const void* k, const v
           max_seqlen_q, hq, hkv, d, dv);
   REQUIRE(max_seqlen_k >= 0, ATTN_EINVAL, "max_seqlen_k < 0");
   REQUIRE(qv && v && cu_seqlens_q && cu_seqlens_k && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, qv, k, v, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(only_qv || (q && k), ATTN_EINVAL, "q and k are required unless only_qv");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
@@ -250,6 +264,8 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
   REQUIRE(q && cu_seqlens_q && cu_seqlens_k && k_cache && v_cache && block_table &&
               cache_seqlens && out,
           ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, k, v, k_cache, v_cache, out, mask), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
@@ -331,6 +347,8 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(q && k_cache && v_cache && block_table && cache_seqlens && plan && o_partial &&
               lse_partial,
           ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, k_cache, v_cache, o_partial), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
@@ -377,6 +395,8 @@ int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_
   REQUIRE(q && k_cache && v_cache && block_table && cache_seqlens && plan && o_partial &&
               lse_partial,
           ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, k_cache, v_cache, o_partial), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
@@ -429,6 +449,8 @@ int32_t attn_decode_paged_qv(const void* q, const void* qv, const void* k_cache,
           ATTN_EEMPTY, "empty dimension");
   REQUIRE(qv && v_cache && block_table && cache_seqlens && plan && o_partial && lse_partial,
           ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, qv, k_cache, v_cache, o_partial), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(only_qv || (q && k_cache), ATTN_EINVAL, "q and k_cache are required unless only_qv");
   REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
@@ -491,6 +513,8 @@ int32_t attn_combine(const float* o_partial, const float* lse_partial, const int
                      void* stream) {
   REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && dv > 0, ATTN_EEMPTY, "empty dimension");
   REQUIRE(o_partial && lse_partial && plan && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(o_partial, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
   REQUIRE(out_dtype == ATTN_BF16 || out_dtype == ATTN_F32, ATTN_EUNSUPPORTED, "out_dtype %d",
@@ -521,6 +545,8 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
           ATTN_EEMPTY, "empty dimension");
   REQUIRE(q && kv_cache && block_table && cache_seqlens && plan && o_partial && lse_partial,
           ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, kv_cache, o_partial), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
           max_splits);
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
@@ -555,6 +581,8 @@ int32_t mla_sparse_fwd(const void* q, const void* kv, const int32_t* sparse_indi
   REQUIRE(batch > 0 && seqlen_q > 0 && seqlen_k > 0 && hq > 0 && topk > 0, ATTN_EEMPTY,
           "empty dimension");
   REQUIRE(q && kv && sparse_indices && out, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, kv, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
@@ -592,6 +620,8 @@ int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_bl
           ATTN_EEMPTY, "empty dimension");
   REQUIRE(q && kv_cache && block_table && seqlens_kv && sparse_indices && out, ATTN_EINVAL,
           "null tensor pointer");
+  REQUIRE(aligned16(q, kv_cache, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
@@ -633,6 +663,8 @@ int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,
                                 int32_t page_size, int32_t row_elems, int32_t max_rows, void* dst,
                                 void* stream) {
   REQUIRE(cache && block_table && cache_seqlens && dst, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(cache, dst), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
   REQUIRE(page_size > 0 && max_pages_per_seq > 0 && row_elems > 0 && b >= 0, ATTN_EEMPTY,
           "empty dimension");
   REQUIRE(row_elems % 8 == 0, ATTN_EUNSUPPORTED, "row_elems must be a multiple of 8");

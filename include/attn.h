@@ -11,7 +11,9 @@
  * Conventions shared by all calls
  *  - Tensor arguments are DEVICE pointers, allocated and owned by the caller,
  *    dense row-major in the shapes given. The library never allocates device
- *    memory and keeps no pointer after the call returns.
+ *    memory and keeps no pointer after the call returns. Element tensors
+ *    (Q, K, V, caches, masks, outputs, partials) must be 16-byte aligned
+ *    (ATTN_EINVAL otherwise): the kernels move 16-byte vectors.
  *  - Scalar arguments (sizes, flags, scale) are host values. scale must be
  *    positive and finite (ATTN_EINVAL otherwise): the kernels track the row
  *    maximum of the scaled scores through the maximum of the raw ones.

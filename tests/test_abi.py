@@ -226,6 +226,24 @@ def test_varlen_qv_host_checks(lib):
     assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
 
 
+def test_misaligned_tensors_rejected(lib):
+    """Element tensors must be 16-byte aligned: an 8-byte offset is EINVAL
+    before anything is enqueued."""
+    M = P + 8
+    assert lib.attn_fwd_varlen(P, M, P, P, P, 2, 100, 100, 8, 2, 128, 128, B.ATTN_BF16, 0.1, 1,
+                               -1, -1, None, P, None, None) == B.ATTN_EINVAL
+    assert b"aligned" in lib.attn_last_error()
+    assert lib.attn_fwd_varlen_fp8(P, P, P, P, P, 2, 100, 100, 8, 2, 128, 128,
+                                   B.ATTN_FP8_E4M3, None, None, None, 0.1, 1, -1, -1, None, M,
+                                   None, None) == B.ATTN_EINVAL
+    assert lib.attn_decode_paged(P, P, M, P, 4, P, 2, 1, 32, 8, 128, 128, 64, B.ATTN_BF16, 0.1,
+                                 0, P, 16, P, P, None) == B.ATTN_EINVAL
+    assert lib.attn_combine(M, P, P, 2, 1, 32, 128, 16, None, B.ATTN_BF16, P, None,
+                            None) == B.ATTN_EINVAL
+    assert lib.mla_sparse_fwd(P, M, P, 2048, 1, 4, 64, 64, 0.1, 3, None, P, None,
+                              None) == B.ATTN_EINVAL
+
+
 def test_mla_and_sparse_host_checks(lib):
     assert lib.mla_decode_paged(P, P, P, 4, P, 0, 1, 128, 64, 0.1, 0, P, 16, P, P,
                                 None) == B.ATTN_EEMPTY
