@@ -355,8 +355,8 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
-  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED, "decode supports d = dv = 128 (got %d, %d)",
-          d, dv);
+  REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
+          "decode supports d = dv in {64, 128} (got %d, %d)", d, dv);
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
@@ -378,7 +378,7 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = o_partial;
   a.lse_part = lse_partial;
-  return hip_status(attn::launch_decode_gqa(a, as_stream(stream)), "attn_decode_paged launch");
+  return hip_status(attn::launch_decode_gqa(a, d, as_stream(stream)), "attn_decode_paged launch");
 }
 
 int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
@@ -503,7 +503,7 @@ int32_t attn_decode_paged_qv(const void* q, const void* qv, const void* k_cache,
   }
   const hipError_t e =
       fp8 ? attn::launch_decode_gqa_fp8(a, dtype == ATTN_FP8_E4M3 ? 1 : 2, as_stream(stream))
-          : attn::launch_decode_gqa(a, as_stream(stream));
+          : attn::launch_decode_gqa(a, d, as_stream(stream));
   return hip_status(e, "attn_decode_paged_qv launch");
 }
 

@@ -386,8 +386,8 @@ k_sparse(SparseArgs a) {
   }
 }
 
-template <int QV = 0>
-using CfgDecodeGqa = StreamCfg<128, 128, 1, 3, false, 1, 0, QV>;
+template <int QV = 0, int D = 128>
+using CfgDecodeGqa = StreamCfg<D, D, 1, 3, false, 1, 0, QV>;
 // FP8 tiles of 64 keys: the bytes of a 32-key bf16 tile
 template <int FMT, int QV = 0>
 using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 64>;
@@ -396,12 +396,15 @@ using CfgSparseMla = StreamCfg<576, 512, 8, 3, true, 2>;
 
 }  // namespace
 
-hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t s) {
+hipError_t launch_decode_gqa(const DecodeArgs& a, int d, hipStream_t s) {
   using C = CfgDecodeGqa<>;
   const int nrows = a.sq * (a.hq / a.hkv);
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-  if (a.qv && a.only_qv)
+  static_assert(CfgDecodeGqa<0, 64>::ROWS == C::ROWS, "one grid for both head dims");
+  if (d == 64)
+    hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 64>>), dim3(grid), dim3(C::THREADS), 0, s, a);
+  else if (a.qv && a.only_qv)
     hipLaunchKernelGGL(k_decode<CfgDecodeGqa<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
   else if (a.qv)
     hipLaunchKernelGGL(k_decode<CfgDecodeGqa<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);

@@ -231,7 +231,7 @@ int32_t attn_plan_splits(const int32_t* cache_seqlens, int32_t batch, int32_t pa
  *  o_partial float32 (batch*max_splits, seqlen_q*hq, dv), lse_partial float32
  *  (batch*max_splits, seqlen_q*hq): split s of b writes slot b*max_splits+s,
  *  row t*hq+h, normalised within the split. Unused slots are untouched.
- *  Supported: BF16, d = dv = 128, page_size a multiple of 16.
+ *  Supported: BF16, d = dv in {64, 128}, page_size a multiple of 16.
  */
 int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int32_t max_pages_per_seq,

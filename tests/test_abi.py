@@ -132,7 +132,8 @@ def test_decode_host_checks(lib):
     assert call(plan=None) == B.ATTN_EINVAL
     assert call(ms=17) == B.ATTN_EINVAL
     assert call(hq=12) == B.ATTN_EINVAL
-    assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
+    assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=128) == B.ATTN_EUNSUPPORTED
     assert call(dtype=1) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
 

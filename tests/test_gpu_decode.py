@@ -73,6 +73,25 @@ DECODE_CASES = [
     ("gqa16_rows32", [333, 1000], 2, 16, 1, 64, True, False, 16, 8, 2),
 ]
 
+# head dim 64: name, lens, sq, hq, hkv, page, causal, max_splits, waves, min_blocks
+DECODE_D64_CASES = [
+    ("d64_ragged", [1, 63, 64, 65, 700, 2049], 1, 32, 8, 64, False, 16, 4, 4),
+    ("d64_causal_sq3_page16", [90, 400, 3], 3, 16, 4, 16, True, 8, 16, 1),
+    ("d64_many_splits", [5000, 130, 4097], 1, 8, 2, 16, False, 16, 64, 1),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_D64_CASES, ids=[c[0] for c in DECODE_D64_CASES])
+def test_decode_gqa_d64(case):
+    name, lens, sq, hq, hkv, page, causal, ms, waves, mb = case
+    log("case decode", name)
+    w = inputs.paged(6400 + len(name), lens, sq=sq, hq=hq, hkv=hkv, d=64, page=page,
+                     causal=causal)
+    o, lse, _ = run_decode(w, ms, waves, mb)
+    torch.cuda.synchronize()
+    ro, rl = oracle_decode(w)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
 
 @pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
 def test_decode_gqa(case):
