@@ -84,12 +84,13 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
 // LSE-weighted combine [MATE flash_attn_combine; CANN softmax_lse]. Each
 // thread owns four output columns of one row; rows are (b, t, h) with the
 // partial layout slot = b*max_splits + s, row t*hq + h. All of a row's split
-// LSEs and partial outputs are loaded before any is used (unrolled over the
-// largest split count, extra splits re-reading the last one with weight 0),
-// so a thread waits for one round trip to memory instead of one per split.
+// LSEs and partial outputs are loaded before any is used (unrolled over
+// kMaxSplits >= max_splits, the instance chosen at launch; extra splits
+// re-read the last one with weight 0), so a thread waits for one round trip
+// to memory instead of one per split.
 constexpr int kCombineThreads = 256;
-constexpr int kMaxSplits = 16;
 
+template <int kMaxSplits>
 __global__ void __launch_bounds__(kCombineThreads)
 k_combine(CombineArgs a) {
   const int per_row = a.dv / 4;
@@ -176,7 +177,13 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int rows_per_block = kCombineThreads / (a.dv / 4);
   const long rows = (long)a.batch * a.sq * a.hq;
   const long grid = (rows + rows_per_block - 1) / rows_per_block;
-  hipLaunchKernelGGL(k_combine, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+  // the smallest unrolled split count that covers the plan's maximum
+  if (a.max_splits <= 4)
+    hipLaunchKernelGGL(k_combine<4>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+  else if (a.max_splits <= 8)
+    hipLaunchKernelGGL(k_combine<8>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_combine<16>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 
