@@ -230,3 +230,30 @@ def test_mla_decode_full():
     mask[pick] = True
     compare("mla_decode_full", o, lse, ro, rl, TOL_O_BF16, mask=mask)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_decode_peaky_q():
+    """The paged-decode and MLA workloads with Q scaled by 4 (exact in bf16):
+    sharper softmax rows, so an output error cannot hide behind the small |O|
+    of rows averaging thousands of keys; four sequences of each compared
+    element by element."""
+    w = inputs.paged_decode()
+    w.q = inputs.bf16_bits(inputs.bits_to_f32(w.q) * 4)
+    log("case decode_peaky")
+    o, lse, _ = run_decode(w, 16, 8, 2)
+    torch.cuda.synchronize()
+    pick = [0, 21, 42, 63]
+    ro, rl = oracle_decode(w, batches=pick)
+    mask = np.zeros(ro.shape, bool)
+    mask[pick] = True
+    compare("decode_peaky", o, lse, ro, rl, TOL_O_BF16, mask=mask)
+    m = inputs.mla_decode()
+    m.q = inputs.bf16_bits(inputs.bits_to_f32(m.q) * 4)
+    log("case mla_peaky")
+    o, lse, _ = run_mla(m, 8, 3, 8)
+    torch.cuda.synchronize()
+    pick = [0, 31, 63]
+    ro, rl = oracle_mla(m, batches=pick)
+    mask = np.zeros(ro.shape, bool)
+    mask[pick] = True
+    compare("mla_peaky", o, lse, ro, rl, TOL_O_BF16, mask=mask)
