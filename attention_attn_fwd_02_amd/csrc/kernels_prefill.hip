@@ -306,18 +306,22 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv(VarlenAr
 
 // ---------------------------------------------------------------------------
 // float32 variant: VALU arithmetic in fp32 throughout (no bf16 rounding of
-// inputs or probabilities). LPR lanes share one query row, each holding 64 of
-// its head dimensions; K/V tiles of 32 keys are staged in LDS.
+// inputs or probabilities). LPR = D / 8 lanes share one query row, each
+// holding 8 of its head dimensions; a dot product is summed over those lanes
+// with log2(LPR) butterfly exchanges. K/V tiles of 32 keys are staged in LDS
+// by the whole workgroup with 16-byte loads.
 template <int D>
 struct F32Cfg {
-  static constexpr int LPR = D / 64;
-  static constexpr int THREADS = 64;
+  static constexpr int DPL = 8;           // head dimensions per lane
+  static constexpr int LPR = D / DPL;     // lanes per query row (8 or 16)
+  static constexpr int THREADS = 256;
   static constexpr int ROWS = THREADS / LPR;
   static constexpr int BN = 32;
+  static_assert(64 % LPR == 0, "a row's lanes stay within one wave");
 };
 
 template <int D>
-__global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
+__global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   using C = F32Cfg<D>;
   __shared__ __attribute__((aligned(16))) float ks[C::BN][D];
   __shared__ __attribute__((aligned(16))) float vs[C::BN][D];
@@ -339,64 +343,79 @@ __global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
   const float* q = static_cast<const float*>(a.q);
   const float* kg = static_cast<const float*>(a.k);
   const float* vg = static_cast<const float*>(a.v);
-  float qr[64], o[64];
+  float qr[C::DPL], o[C::DPL];
+  {
+    f32x4 q4[2] = {f32x4{}, f32x4{}};
+    if (row_ok) {
+      const f32x4* qp = reinterpret_cast<const f32x4*>(
+          q + ((size_t)(q0 + trow) * a.hq + w.h) * D + part * C::DPL);
+      q4[0] = qp[0];
+      q4[1] = qp[1];
+    }
 #pragma unroll
-  for (int d = 0; d < 64; ++d) {
-    qr[d] = row_ok ? q[((size_t)(q0 + trow) * a.hq + w.h) * D + part * 64 + d] : 0.f;
-    o[d] = 0.f;
+    for (int d = 0; d < C::DPL; ++d) {
+      qr[d] = q4[d / 4][d % 4];
+      o[d] = 0.f;
+    }
   }
   float m_run = kNegInf, l_run = 0.f;
   const int tdiag = trow + bd.delta;
   for (int j0 = bd.lo; j0 < bd.hi; j0 += C::BN) {
-    for (int e = tid; e < C::BN * D; e += 64) {
-      const int r = e / D, c = e % D;
+    for (int e = tid; e < C::BN * D / 4; e += C::THREADS) {
+      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
       const int j = j0 + r;
-      const bool ok = j < lk;
-      ks[r][c] = ok ? kg[((size_t)(k0 + j) * a.hkv + w.kvh) * D + c] : 0.f;
-      vs[r][c] = ok ? vg[((size_t)(k0 + j) * a.hkv + w.kvh) * D + c] : 0.f;
+      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
+      if (j < lk) {
+        const size_t off = ((size_t)(k0 + j) * a.hkv + w.kvh) * D + c;
+        kv = *reinterpret_cast<const f32x4*>(kg + off);
+        vv = *reinterpret_cast<const f32x4*>(vg + off);
+      }
+      *reinterpret_cast<f32x4*>(&ks[r][c]) = kv;
+      *reinterpret_cast<f32x4*>(&vs[r][c]) = vv;
     }
     __syncthreads();
     float s[C::BN];
     float mx = kNegInf;
-    for (int j = 0; j < C::BN; ++j) {
-      const f32x4* kr = reinterpret_cast<const f32x4*>(&ks[j][part * 64]);
-      float acc = 0.f;
 #pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const f32x4 kv = kr[d];
-        acc = fmaf(qr[4 * d], kv[0], acc);
-        acc = fmaf(qr[4 * d + 1], kv[1], acc);
-        acc = fmaf(qr[4 * d + 2], kv[2], acc);
-        acc = fmaf(qr[4 * d + 3], kv[3], acc);
-      }
-      if (C::LPR == 2) acc += __shfl_xor(acc, 1);
+    for (int j = 0; j < C::BN; ++j) {
+      const f32x4* kr = reinterpret_cast<const f32x4*>(&ks[j][part * C::DPL]);
+      const f32x4 ka = kr[0], kb = kr[1];
+      float acc = qr[0] * ka[0];
+      acc = fmaf(qr[1], ka[1], acc);
+      acc = fmaf(qr[2], ka[2], acc);
+      acc = fmaf(qr[3], ka[3], acc);
+      acc = fmaf(qr[4], kb[0], acc);
+      acc = fmaf(qr[5], kb[1], acc);
+      acc = fmaf(qr[6], kb[2], acc);
+      acc = fmaf(qr[7], kb[3], acc);
+#pragma unroll
+      for (int m = 1; m < C::LPR; m <<= 1) acc += __shfl_xor(acc, m);
       const int jj = j0 + j;
       const bool ok = jj < lk && (bd.wr < 0 || jj <= tdiag + bd.wr) && (bd.wl < 0 || jj >= tdiag - bd.wl);
       s[j] = ok ? acc * a.scale_log2 : kNegInf;
+      mx = fmaxf(mx, s[j]);
     }
-#pragma unroll
-    for (int j = 0; j < C::BN; ++j) mx = fmaxf(mx, s[j]);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == kNegInf ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
-    for (int d = 0; d < 64; ++d) o[d] *= alpha;
+    for (int d = 0; d < C::DPL; ++d) o[d] *= alpha;
 #pragma unroll
-    for (int j = 0; j < C::BN; ++j) s[j] = fast_exp2(s[j] - m_use);
     for (int j = 0; j < C::BN; ++j) {
-      const float p = s[j];
+      const float p = fast_exp2(s[j] - m_use);
       l_run += p;
-      const f32x4* vr = reinterpret_cast<const f32x4*>(&vs[j][part * 64]);
-#pragma unroll
-      for (int d = 0; d < 16; ++d) {
-        const f32x4 vv = vr[d];
-        o[4 * d] = fmaf(p, vv[0], o[4 * d]);
-        o[4 * d + 1] = fmaf(p, vv[1], o[4 * d + 1]);
-        o[4 * d + 2] = fmaf(p, vv[2], o[4 * d + 2]);
-        o[4 * d + 3] = fmaf(p, vv[3], o[4 * d + 3]);
-      }
+      const f32x4* vr = reinterpret_cast<const f32x4*>(&vs[j][part * C::DPL]);
+      const f32x4 va = vr[0], vb = vr[1];
+      o[0] = fmaf(p, va[0], o[0]);
+      o[1] = fmaf(p, va[1], o[1]);
+      o[2] = fmaf(p, va[2], o[2]);
+      o[3] = fmaf(p, va[3], o[3]);
+      o[4] = fmaf(p, vb[0], o[4]);
+      o[5] = fmaf(p, vb[1], o[5]);
+      o[6] = fmaf(p, vb[2], o[6]);
+      o[7] = fmaf(p, vb[3], o[7]);
     }
     __syncthreads();
   }
@@ -410,12 +429,11 @@ __global__ void __launch_bounds__(64) k_varlen_f32(VarlenArgs a) {
     inv = f / (l_run * f + fast_exp2(sink2 - ms));
   }
   if (row_ok) {
-    float* orow = static_cast<float*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * D + part * 64;
-#pragma unroll
-    for (int d = 0; d < 64; d += 4) {
-      const f32x4 v = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
-      *reinterpret_cast<f32x4*>(orow + d) = v;
-    }
+    f32x4* orow = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) +
+                                           ((size_t)(q0 + trow) * a.hq + w.h) * D +
+                                           part * C::DPL);
+    orow[0] = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    orow[1] = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
     if (a.lse && part == 0) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
   }
 }
@@ -485,9 +503,9 @@ hipError_t launch_varlen_qv(const VarlenArgs& a, int fmt, hipStream_t s) {
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s) {
   const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
   if (d == 64)
-    hipLaunchKernelGGL(k_varlen_f32<64>, dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_varlen_f32<64>, dim3(grid), dim3(F32Cfg<64>::THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL(k_varlen_f32<128>, dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_varlen_f32<128>, dim3(grid), dim3(F32Cfg<128>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -148,6 +148,23 @@ def bench_prefill(steps, warmup):
                 bytes=in_bytes + out_bytes)
 
 
+def bench_tiny(steps, warmup):
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.tiny_dense()
+    q, k, v = dev(w.q), dev(w.k), dev(w.v)
+    cq, ck = dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty((w.q.shape[1], w.q.shape[0]), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.attn_fwd_varlen(q, k, v, cq, ck, 128, 128, w.scale, False, out=out, lse=lse)
+
+    ms = time_steps(step, max(steps, 50), warmup)
+    return dict(ms=ms, us=ms * 1e3)
+
+
 def bench_prefill_fp8(steps, warmup):
     import torch
     from attention_attn_fwd_02_amd import binding as B
@@ -585,7 +602,7 @@ def main():
     ap.add_argument("--ramp-ms", type=float, default=200.0,
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
-                    default="prefill,prefill_fp8,prefill_qv,decode,decode_fp8,decode_qv,"
+                    default="prefill,tiny,prefill_fp8,prefill_qv,decode,decode_fp8,decode_qv,"
                             "decode_only_qv,mla,chunked,chunked_mask,sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
@@ -633,6 +650,17 @@ def main():
     log(f"prefill {pre['ms']:.3f} ms  {pre['tflops']:.1f} TFLOP/s")
     traffic = measured_traffic()
     secondary = []
+    if "tiny" in only:
+        log("tiny dense fp32 ...")
+        ti = bench_tiny(args.steps, args.warmup)
+        log(f"tiny {ti['us']:.1f} us per call")
+        secondary.append({
+            "metric": "latency of one call (tiny dense attention, fp32)", "value": ti["us"],
+            "unit": "us", "higher_is_better": False, "ms_per_step": ti["ms"],
+            "workload": "B=1, Sq=Sk=128, Hq=Hkv=4, D=64, fp32 Q/K/V ~ N(0,1), non-causal, scale "
+                        "1/8, O and LSE out (seed 1001); back-to-back calls on one stream",
+            "roofline": {"bound": "latency", "achieved": None, "peak": None, "unit": "us",
+                         "frac": None, "traffic": None, "kernel": "k_varlen_f32 (D=64)"}})
     if "prefill_fp8" in only:
         log("prefill fp8 ...")
         p8 = bench_prefill_fp8(args.steps, args.warmup)
