@@ -11,6 +11,7 @@ Function names are those of the C ABI.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import torch
@@ -97,6 +98,12 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _scale(scale, query):
+    """The softmax scale; None means 1/sqrt(D) of the query's head dimension
+    (the lite_boost flash_attention softmax_scale default)."""
+    return 1.0 / math.sqrt(query.shape[-1]) if scale is None else _scale(scale, q)
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -122,8 +129,8 @@ def _dtype_code(t):
 
 
 # ------------------------------------------------------------------- prefill
-def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
-                    causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    scale=None, causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
                     return_lse=True):
     """q (Tq,Hq,D), k (Tk,Hkv,D), v (Tk,Hkv,Dv) bf16 or fp32; cu_seqlens int32
     (B+1). Returns (out (Tq,Hq,Dv), lse (Hq,Tq) fp32 or None)."""
@@ -143,14 +150,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     _dev(lse, dtype=torch.float32)
     _check(load().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
                                   _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k),
-                                  hq, hkv, d, dv, _dtype_code(q), float(scale), int(bool(causal)),
-                                  int(window[0]), int(window[1]), _ptr(sinks), _ptr(out),
-                                  _ptr(lse), _stream()))
+                                  hq, hkv, d, dv, _dtype_code(q), _scale(scale, q),
+                                  int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks),
+                                  _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 
-def attn_fwd_varlen_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, scale,
-                        fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
+def attn_fwd_varlen_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                        scale=None, fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
                         causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
                         return_lse=True):
     """q (Tq,Hq,128), k (Tk,Hkv,128), v (Tk,Hkv,128) uint8 FP8 codes of fmt
@@ -174,15 +181,15 @@ def attn_fwd_varlen_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_s
     _check(load().attn_fwd_varlen_fp8(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
         int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dv, FP8_FORMATS[fmt], _ptr(q_descale),
-        _ptr(k_descale), _ptr(v_descale), float(scale), int(bool(causal)), int(window[0]),
+        _ptr(k_descale), _ptr(v_descale), _scale(scale, q), int(bool(causal)), int(window[0]),
         int(window[1]), _ptr(sinks), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 
 def attn_fwd_varlen_qv(q, qv, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                       scale, fmt=None, q_descale=None, k_descale=None, v_descale=None,
-                       causal=False, window=(-1, -1), sinks=None, only_qv=False, out=None,
-                       lse=None, return_lse=True):
+                       scale=None, fmt=None, q_descale=None, k_descale=None, v_descale=None,
+                       causal=False, window=(-1, -1), sinks=None, only_qv=False, out=None, lse=None,
+                       return_lse=True):
     """Varlen attention with a second query qv (Tq,Hq,128) scored against the
     value rows. fmt None: bf16 tensors; "e4m3" / "e5m2": uint8 FP8 codes with
     optional float32 (B,Hkv) descales. only_qv: q and k are not used (may be
@@ -210,7 +217,8 @@ def attn_fwd_varlen_qv(q, qv, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
     _check(load().attn_fwd_varlen_qv(
         None if only_qv else _ptr(q), _ptr(qv), None if only_qv else _ptr(k), _ptr(v),
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, int(max_seqlen_q), int(max_seqlen_k), hq,
-        hkv, d, dv, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), float(scale),
+        hkv, d, dv, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        _scale(scale, qv if only_qv or q is None else q),
         int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), int(bool(only_qv)),
         _ptr(out), _ptr(lse), _stream()))
     return out, lse
@@ -246,7 +254,7 @@ def attn_fwd_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cach
     _check(load().attn_fwd_varlen_kvcache(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(k_cache),
         _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
-        k_cache.shape[1], batch, int(max_seqlen_q), hq, hkv, d, dv, ATTN_BF16, float(scale),
+        k_cache.shape[1], batch, int(max_seqlen_q), hq, hkv, d, dv, ATTN_BF16, _scale(scale, q),
         int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(mask),
         0 if mask is None else mask.shape[0], 0 if mask is None else mask.shape[2], _ptr(out),
         _ptr(lse), _stream()))
@@ -279,8 +287,8 @@ def attn_device_info(device=0):
 
 
 # --------------------------------------------------------------------- decode
-def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits, scale,
-                      causal=False, o_partial=None, lse_partial=None):
+def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
+                      scale=None, causal=False, o_partial=None, lse_partial=None):
     """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) bf16. Returns partials
     (B*max_splits, Sq*Hq, Dv) and (B*max_splits, Sq*Hq) fp32."""
     _dev(q, k_cache, v_cache, dtype=torch.bfloat16)
@@ -295,14 +303,14 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max
     _dev(o_partial, lse_partial, dtype=torch.float32)
     _check(load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                     block_table.shape[1], _ptr(cache_seqlens), b, sq, hq, hkv, d,
-                                    dv, page, ATTN_BF16, float(scale), int(bool(causal)),
+                                    dv, page, ATTN_BF16, _scale(scale, q), int(bool(causal)),
                                     _ptr(plan), int(max_splits), _ptr(o_partial),
                                     _ptr(lse_partial), _stream()))
     return o_partial, lse_partial
 
 
 def attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
-                          scale, fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
+                          scale=None, fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
                           causal=False, o_partial=None, lse_partial=None):
     """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) uint8 FP8 codes of fmt ("e4m3" or
     "e5m2"); descales float32 (B,Hkv) or None. Returns partials as
@@ -324,13 +332,13 @@ def attn_decode_paged_fp8(q, k_cache, v_cache, block_table, cache_seqlens, plan,
     _check(load().attn_decode_paged_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
         _ptr(cache_seqlens), b, sq, hq, hkv, d, dv, page, FP8_FORMATS[fmt], _ptr(q_descale),
-        _ptr(k_descale), _ptr(v_descale), float(scale), int(bool(causal)), _ptr(plan),
+        _ptr(k_descale), _ptr(v_descale), _scale(scale, q), int(bool(causal)), _ptr(plan),
         int(max_splits), _ptr(o_partial), _ptr(lse_partial), _stream()))
     return o_partial, lse_partial
 
 
 def attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
-                         scale, fmt=None, q_descale=None, k_descale=None, v_descale=None,
+                         scale=None, fmt=None, q_descale=None, k_descale=None, v_descale=None,
                          causal=False, only_qv=False, o_partial=None, lse_partial=None):
     """Decode with a second query qv (B,Sq,Hq,Dv) scored against the value
     rows. fmt None: bf16 tensors; "e4m3" / "e5m2": uint8 FP8 codes with
@@ -359,7 +367,8 @@ def attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, pl
     _check(load().attn_decode_paged_qv(
         None if only_qv else _ptr(q), _ptr(qv), None if only_qv else _ptr(k_cache),
         _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), b, sq, hq,
-        hkv, d, dv, page, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), float(scale),
+        hkv, d, dv, page, code, _ptr(q_descale), _ptr(k_descale), _ptr(v_descale),
+        _scale(scale, qv if only_qv or q is None else q),
         int(bool(causal)), int(bool(only_qv)), _ptr(plan), int(max_splits), _ptr(o_partial),
         _ptr(lse_partial), _stream()))
     return o_partial, lse_partial
@@ -383,7 +392,7 @@ def attn_combine(o_partial, lse_partial, plan, batch, seqlen_q, hq, max_splits, 
     return out, lse
 
 
-def mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, scale,
+def mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, scale=None,
                      causal=False, o_partial=None, lse_partial=None):
     """q (B,Sq,Hq,576), kv_cache (P,page,1,576) bf16; partials with Dv = 512."""
     _dev(q, kv_cache, dtype=torch.bfloat16)
@@ -399,14 +408,14 @@ def mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, 
     _dev(o_partial, lse_partial, dtype=torch.float32)
     _check(load().mla_decode_paged(_ptr(q), _ptr(kv_cache), _ptr(block_table),
                                    block_table.shape[1], _ptr(cache_seqlens), b, sq, hq,
-                                   kv_cache.shape[1], float(scale), int(bool(causal)), _ptr(plan),
-                                   int(max_splits), _ptr(o_partial), _ptr(lse_partial),
+                                   kv_cache.shape[1], _scale(scale, q), int(bool(causal)),
+                                   _ptr(plan), int(max_splits), _ptr(o_partial), _ptr(lse_partial),
                                    _stream()))
     return o_partial, lse_partial
 
 
-def mla_sparse_fwd(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, out=None, lse=None,
-                   return_lse=True):
+def mla_sparse_fwd(q, kv, sparse_indices, scale=None, sparse_mode=3, sinks=None, out=None,
+                   lse=None, return_lse=True):
     """q (B,Sq,Hq,576), kv (B,Sk,1,576) bf16, indices (B,Sq,1,topk) int32."""
     _dev(q, kv, dtype=torch.bfloat16)
     _dev(sparse_indices, dtype=torch.int32)
@@ -423,12 +432,12 @@ def mla_sparse_fwd(q, kv, sparse_indices, scale, sparse_mode=3, sinks=None, out=
     _dev(out, dtype=torch.bfloat16)
     _dev(lse, dtype=torch.float32)
     _check(load().mla_sparse_fwd(_ptr(q), _ptr(kv), _ptr(sparse_indices), topk, b, sq, sk, hq,
-                                 float(scale), int(sparse_mode), _ptr(sinks), _ptr(out), _ptr(lse),
-                                 _stream()))
+                                 _scale(scale, q), int(sparse_mode), _ptr(sinks), _ptr(out),
+                                 _ptr(lse), _stream()))
     return out, lse
 
 
-def mla_sparse_paged_fwd(q, kv_cache, block_table, seqlens_kv, sparse_indices, scale,
+def mla_sparse_paged_fwd(q, kv_cache, block_table, seqlens_kv, sparse_indices, scale=None,
                          sparse_block_size=1, sparse_mode=3, sinks=None, out=None, lse=None,
                          return_lse=True):
     """q (B,Sq,Hq,576) bf16, kv_cache (P,page,1,576) bf16, block_table
@@ -448,8 +457,8 @@ def mla_sparse_paged_fwd(q, kv_cache, block_table, seqlens_kv, sparse_indices, s
     _check(load().mla_sparse_paged_fwd(
         _ptr(q), _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1], _ptr(block_table),
         block_table.shape[1], _ptr(seqlens_kv), _ptr(sparse_indices), sparse_indices.shape[-1],
-        int(sparse_block_size), b, sq, hq, float(scale), int(sparse_mode), _ptr(sinks), _ptr(out),
-        _ptr(lse), _stream()))
+        int(sparse_block_size), b, sq, hq, _scale(scale, q), int(sparse_mode), _ptr(sinks),
+        _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 
@@ -481,8 +490,9 @@ def _num_cu(device):
     return attn_device_info(device.index if device.index is not None else 0)
 
 
-def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=False, sinks=None,
-                 max_splits=16, waves=8, min_blocks=2, num_cu=None, out_dtype=torch.bfloat16):
+def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, causal=False,
+                 sinks=None, max_splits=16, waves=8, min_blocks=2, num_cu=None,
+                 out_dtype=torch.bfloat16):
     """plan -> attn_decode_paged -> attn_combine. Returns (out (B,Sq,Hq,Dv),
     lse (B,Hq,Sq), plan)."""
     b, sq, hq, _ = q.shape
@@ -497,9 +507,9 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale, causal=
     return out, lse, plan
 
 
-def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale, fmt="e4m3",
-                     q_descale=None, k_descale=None, v_descale=None, causal=False,
-                     max_splits=16, waves=16, min_blocks=2, num_cu=None):
+def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, fmt="e4m3",
+                     q_descale=None, k_descale=None, v_descale=None, causal=False, max_splits=16,
+                     waves=16, min_blocks=2, num_cu=None):
     """plan -> attn_decode_paged_fp8 -> attn_combine (bfloat16 out). FP8 tiles
     are half the bytes of bf16 ones, so the default plan aims at twice as
     many workgroups per CU as paged_decode's (measured on MI355X)."""
@@ -516,7 +526,7 @@ def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale, fmt
     return out, lse, plan
 
 
-def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale, fmt=None,
+def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale=None, fmt=None,
                     q_descale=None, k_descale=None, v_descale=None, causal=False, only_qv=False,
                     max_splits=16, waves=None, min_blocks=2, num_cu=None):
     """plan -> attn_decode_paged_qv -> attn_combine (bfloat16 out). The plan
@@ -537,7 +547,7 @@ def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale, 
     return out, lse, plan
 
 
-def mla_decode(q, kv_cache, block_table, cache_seqlens, scale, causal=False, max_splits=8,
+def mla_decode(q, kv_cache, block_table, cache_seqlens, scale=None, causal=False, max_splits=8,
                waves=3, min_blocks=8, num_cu=None):
     """plan -> mla_decode_paged -> attn_combine (dv = 512)."""
     b, sq, hq, _ = q.shape

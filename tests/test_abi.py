@@ -295,3 +295,14 @@ def test_combine_host_checks(lib):
 def test_gather_host_checks(lib):
     assert lib.attn_debug_gather_paged(P, P, 4, P, 0, 64, 12, 10, P, None) == B.ATTN_EUNSUPPORTED
     assert lib.attn_debug_gather_paged(None, P, 4, P, 0, 64, 16, 10, P, None) == B.ATTN_EINVAL
+
+
+def test_default_softmax_scale():
+    # An omitted scale means 1/sqrt(head dim of the query that is scored).
+    import math
+
+    import torch
+    q = torch.empty((3, 2, 128))
+    assert B._scale(None, q) == pytest.approx(1.0 / math.sqrt(128))
+    assert B._scale(0.25, q) == 0.25
+    assert B._scale(None, torch.empty((1, 1, 1, 576))) == pytest.approx(1.0 / 24.0)
