@@ -101,7 +101,7 @@ def _ptr(t):
 def _scale(scale, query):
     """The softmax scale; None means 1/sqrt(D) of the query's head dimension
     (the lite_boost flash_attention softmax_scale default)."""
-    return 1.0 / math.sqrt(query.shape[-1]) if scale is None else _scale(scale, q)
+    return 1.0 / math.sqrt(query.shape[-1]) if scale is None else float(scale)
 
 
 def _stream():
