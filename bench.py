@@ -625,7 +625,7 @@ def main():
                       args.traffic_from[2] if len(args.traffic_from) == 3 else None)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library runs on a single GPU "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     import torch
