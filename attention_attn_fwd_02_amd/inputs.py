@@ -34,6 +34,7 @@ SEED_SPARSE_PAGED = 1008
 SEED_VARLEN_PREFILL_FP8 = 1009
 SEED_PAGED_DECODE_QV = 1010
 SEED_VARLEN_PREFILL_QV = 1011
+SEED_CHUNKED_PREFILL_FP8 = 1012
 
 _CHUNK = 1 << 22  # elements per independently seeded block of a large tensor
 
@@ -475,6 +476,89 @@ def varlen_prefill_fp8(seed: int = SEED_VARLEN_PREFILL_FP8) -> DenseFP8:
     rng = np.random.default_rng(seed)
     lens = rng.integers(512, 4096, endpoint=True, size=8)
     return varlen_fp8(int(rng.integers(0, 2**63 - 1)), lens, fmt="e4m3")
+
+
+@dataclasses.dataclass
+class DenseKVFP8(DenseFP8):
+    """A DenseFP8 problem whose keys also have an earlier part in a paged FP8
+    cache: k_cache (P,page,Hkv,D), v_cache (P,page,Hkv,D) uint8 codes,
+    block_table (B, max_pages) int32 (-1 past a sequence's pages),
+    cache_seqlens (B)."""
+    k_cache: np.ndarray = None
+    v_cache: np.ndarray = None
+    block_table: np.ndarray = None
+    cache_seqlens: np.ndarray = None
+    page_size: int = 0
+
+
+def varlen_kvcache_fp8(seed: int, lens_q, lens_new, lens_cache, fmt: str = "e4m3",
+                       hq: int = 32, hkv: int = 8, d: int = 128, page: int = 64,
+                       causal: bool = True, window=(-1, -1), descale: bool = True,
+                       with_sinks: bool = False) -> DenseKVFP8:
+    """Chunked prefill on FP8 codes: per sequence lens_q queries and lens_new
+    current K/V rows after lens_cache rows in a paged cache. Every value is
+    N(0,1) stored as the FP8 code of x / descale, with the descales of its
+    sequence (per KV head, U[0.25, 4], or none); a cache page takes those of
+    the sequence that owns it (pages are not shared). Draw order: descales,
+    page permutation, Q, K, V, K cache, V cache, sinks."""
+    rng = np.random.default_rng(seed)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_new = np.asarray(lens_new, dtype=np.int64)
+    lens_cache = np.asarray(lens_cache, dtype=np.int64)
+    b = len(lens_q)
+    ds = [rng.uniform(0.25, 4.0, size=(b, hkv)).astype(np.float32) if descale else None
+          for _ in range(3)]
+    one = np.ones((b, hkv), np.float32)
+    qd, kd, vd = (one if x is None else x for x in ds)
+    table, pool = _paged_table(rng, lens_cache, page)
+    owner = np.zeros(max(1, pool), dtype=np.int64)
+    for s, row in enumerate(table):
+        owner[row[row >= 0]] = s
+    pool = max(1, pool)
+    seq_q = np.repeat(np.arange(b), lens_q)
+    seq_k = np.repeat(np.arange(b), lens_new)
+    qinv = np.repeat(1.0 / qd, hq // hkv, axis=1).astype(np.float32)   # (B, Hq)
+    kinv, vinv = (1.0 / kd).astype(np.float32), (1.0 / vd).astype(np.float32)
+
+    def rows_q(r0, r1):
+        r = np.arange(r0, r1)
+        return qinv[seq_q[r // hq], r % hq]
+
+    def rows_new(inv):
+        def f(r0, r1):
+            r = np.arange(r0, r1)
+            return inv[seq_k[r // hkv], r % hkv]
+        return f
+
+    def rows_cache(inv):                   # rows are (page, slot, head)
+        def f(r0, r1):
+            r = np.arange(r0, r1)
+            return inv[owner[r // (page * hkv)], r % hkv]
+        return f
+
+    tq, tk = int(lens_q.sum()), int(lens_new.sum())
+    q = _normal_fp8(rng, (tq, hq, d), fmt, rows_q)
+    k = _normal_fp8(rng, (tk, hkv, d), fmt, rows_new(kinv))
+    v = _normal_fp8(rng, (tk, hkv, d), fmt, rows_new(vinv))
+    k_cache = _normal_fp8(rng, (pool, page, hkv, d), fmt, rows_cache(kinv))
+    v_cache = _normal_fp8(rng, (pool, page, hkv, d), fmt, rows_cache(vinv))
+    sinks = rng.standard_normal(hq).astype(np.float32) if with_sinks else None
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_new)]).astype(np.int32)
+    return DenseKVFP8(q, k, v, fmt, ds[0], ds[1], ds[2], cu_q, cu_k, 1.0 / np.sqrt(d), causal,
+                      tuple(window), sinks, k_cache=k_cache, v_cache=v_cache, block_table=table,
+                      cache_seqlens=lens_cache.astype(np.int32), page_size=page)
+
+
+def chunked_prefill_fp8(seed: int = SEED_CHUNKED_PREFILL_FP8, nseq: int = 8, chunk: int = 1024,
+                        lo: int = 1024, hi: int = 8192, fmt: str = "e4m3") -> DenseKVFP8:
+    """The chunked causal GQA prefill shape (nseq chunks of `chunk` new tokens
+    after cached prefixes of U[lo, hi] tokens, Hq=32, Hkv=8, D=128, page 64) on
+    FP8 codes with per-(sequence, KV head) descales."""
+    rng = np.random.default_rng(seed)
+    lens_cache = rng.integers(lo, hi, endpoint=True, size=nseq)
+    lens = np.full(nseq, chunk)
+    return varlen_kvcache_fp8(int(rng.integers(0, 2**63 - 1)), lens, lens, lens_cache, fmt)
 
 
 def paged_decode_fp8(seed: int = SEED_PAGED_DECODE_FP8, batch: int = 64, lo: int = 1024,

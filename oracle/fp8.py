@@ -138,3 +138,43 @@ def attention_varlen_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale, cu_se
         v[ck[b]:ck[b + 1]] *= vd[b][None, :, None]
     return attention_varlen(q, k, v, cq, ck, scale, causal, window, sinks, seqs, qv=qv,
                             only_qv=only_qv)
+
+
+def attention_varlen_kvcache_fp8(q8, k8, v8, fmt, q_descale, k_descale, v_descale,
+                                 cu_seqlens_q, cu_seqlens_k, k8_cache, v8_cache, block_table,
+                                 cache_seqlens, page_size, scale, causal=False, window=(-1, -1),
+                                 sinks=None, seqs=None):
+    """Queries over a paged FP8 cache of earlier tokens plus the current FP8
+    K/V rows.           [MATE FMHA FP8 dtype notes; MOJO flash_attention_split_kv]
+
+    q8 (Tq, Hq, D), k8 / v8 (Tk, Hkv, D) current rows and k8_cache / v8_cache
+    (P, page, Hkv, D) uint8 codes of fmt; descales float (B, Hkv) or None (= 1).
+    The keys of sequence b are its cache_seqlens[b] cached rows (through
+    block_table) followed by its current rows; each of them, cached or
+    current, is decode(code) * descale[b, kv head] (the descale belongs to the
+    sequence, not to the page). Then attention_varlen over those keys.
+    Returns O (Tq, Hq, Dv), LSE (Hq, Tq)."""
+    tq, hq, _ = q8.shape
+    hkv = v8_cache.shape[2]
+    g = _group(hq, hkv)
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    bsz = len(cq) - 1
+    one = np.ones((bsz, hkv))
+    qd = one if q_descale is None else np.asarray(q_descale, np.float64)
+    kd = one if k_descale is None else np.asarray(k_descale, np.float64)
+    vd = one if v_descale is None else np.asarray(v_descale, np.float64)
+    q = decode(q8, fmt)
+    ks, vs, cu = [], [], [0]
+    for b in range(bsz):
+        q[cq[b]:cq[b + 1]] *= np.repeat(qd[b], g)[None, :, None]
+        lc = int(cache_seqlens[b])
+        kb = np.concatenate([decode(gather_paged(k8_cache, block_table, b, lc, page_size), fmt),
+                             decode(k8[ck[b]:ck[b + 1]], fmt)])
+        vb = np.concatenate([decode(gather_paged(v8_cache, block_table, b, lc, page_size), fmt),
+                             decode(v8[ck[b]:ck[b + 1]], fmt)])
+        ks.append(kb * kd[b][None, :, None])
+        vs.append(vb * vd[b][None, :, None])
+        cu.append(cu[-1] + len(kb))
+    return attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cq,
+                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs)

@@ -1061,3 +1061,42 @@ def test_pins_catch_planted_mistakes(monkeypatch, i):
         except (AssertionError, IndexError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"mutant {fn.__name__} of {name} passed every pin"
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_kvcache_is_fp8_varlen_over_the_concatenation(fmt):
+    # Cache-plus-current attention on FP8 codes is the FP8 varlen attention
+    # over the keys [cached rows of b in page-table order ; current rows of b],
+    # with the descales of sequence b on both parts. The concatenation is
+    # written here by explicit page/slot indexing; distinct per-sequence
+    # descales and a permuted page table catch a descale taken per page or a
+    # swapped cache/current order.
+    from attention_attn_fwd_02_amd import inputs as I
+    from oracle import fp8 as F
+    w = I.varlen_kvcache_fp8(77, [20, 45, 9], [20, 45, 0], [70, 0, 33], fmt, hq=4, hkv=2,
+                             d=128, page=16, causal=True, with_sinks=True)
+    kc, vc, cu = [], [], [0]
+    for b in range(3):
+        rows_k, rows_v = [], []
+        for j in range(int(w.cache_seqlens[b])):
+            pg = w.block_table[b, j // w.page_size]
+            rows_k.append(w.k_cache[pg, j % w.page_size])
+            rows_v.append(w.v_cache[pg, j % w.page_size])
+        for j in range(w.cu_seqlens_k[b], w.cu_seqlens_k[b + 1]):
+            rows_k.append(w.k[j])
+            rows_v.append(w.v[j])
+        kc += rows_k
+        vc += rows_v
+        cu.append(cu[-1] + len(rows_k))
+    k8, v8 = np.stack(kc), np.stack(vc)
+    o1, l1 = F.attention_varlen_kvcache_fp8(
+        w.q, w.k, w.v, fmt, w.q_descale, w.k_descale, w.v_descale, w.cu_seqlens_q,
+        w.cu_seqlens_k, w.k_cache, w.v_cache, w.block_table, w.cache_seqlens, w.page_size,
+        w.scale, True, sinks=w.sinks)
+    o2, l2 = F.attention_varlen_fp8(w.q, k8, v8, fmt, w.q_descale, w.k_descale, w.v_descale,
+                                    w.cu_seqlens_q, np.asarray(cu), w.scale, True,
+                                    sinks=w.sinks)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12, equal_nan=True)
+    assert np.allclose(l1, l2, rtol=0, atol=1e-12, equal_nan=True)
+    assert np.isfinite(l1[:, :w.cu_seqlens_q[2]]).all()
+    assert len(np.unique(w.k_descale)) == w.k_descale.size
