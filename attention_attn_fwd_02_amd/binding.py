@@ -39,6 +39,9 @@ _SIGNATURES = {
                                 _P, _F, _I, _I, _I, _P, _I, _P, _P, _P]),
     "attn_fwd_varlen_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      _I, _I, _I, _F, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]),
+    "attn_fwd_varlen_kvcache_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I,
+                                         _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _I, _P, _P, _P,
+                                         _P]),
     "attn_plan_words": (ctypes.c_size_t, [_I, _I]),
     "attn_plan_splits": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -258,6 +261,45 @@ def attn_fwd_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cach
         int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(mask),
         0 if mask is None else mask.shape[0], 0 if mask is None else mask.shape[2], _ptr(out),
         _ptr(lse), _stream()))
+    return out, lse
+
+
+def attn_fwd_varlen_kvcache_fp8(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
+                                block_table, cache_seqlens, max_seqlen_q, scale=None,
+                                fmt="e4m3", q_descale=None, k_descale=None, v_descale=None,
+                                causal=False, window=(-1, -1), sinks=None, out=None, lse=None,
+                                return_lse=True):
+    """attn_fwd_varlen_kvcache on FP8 codes: q (Tq,Hq,128), k, v (Tk,Hkv,128)
+    and k_cache, v_cache (P,page,Hkv,128) uint8 codes of fmt ("e4m3" or
+    "e5m2"); descales float32 (B,Hkv) or None, one per (sequence, KV head) for
+    its cached and current rows. Returns (out (Tq,Hq,128) bf16, lse (Hq,Tq)
+    fp32 or None)."""
+    _dev(q, k, v, k_cache, v_cache, dtype=torch.uint8)
+    _dev(cu_seqlens_q, cu_seqlens_k, block_table, cache_seqlens, dtype=torch.int32)
+    _dev(sinks, q_descale, k_descale, v_descale, dtype=torch.float32)
+    tq, hq, d = q.shape
+    hkv, dv = k_cache.shape[2], v_cache.shape[3]
+    batch = cu_seqlens_q.numel() - 1
+    if k_cache.shape[3] != d or (k is not None and k.shape[1:] != (hkv, d)) or \
+            (v is not None and v.shape[1:] != (hkv, dv)):
+        raise ValueError("cache heads or widths differ from q, k, v")
+    if block_table.dim() != 2 or block_table.shape[0] != batch or cache_seqlens.numel() != batch:
+        raise ValueError("block_table must be (batch, max_pages) and cache_seqlens (batch)")
+    for t in (q_descale, k_descale, v_descale):
+        if t is not None and tuple(t.shape) != (batch, hkv):
+            raise ValueError("descales must be (batch, hkv)")
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_fwd_varlen_kvcache_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens),
+        k_cache.shape[1], batch, int(max_seqlen_q), hq, hkv, d, dv, FP8_FORMATS[fmt],
+        _ptr(q_descale), _ptr(k_descale), _ptr(v_descale), _scale(scale, q), int(bool(causal)),
+        int(window[0]), int(window[1]), _ptr(sinks), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

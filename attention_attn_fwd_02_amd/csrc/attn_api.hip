@@ -315,6 +315,70 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                     "attn_fwd_varlen_kvcache launch");
 }
 
+int32_t attn_fwd_varlen_kvcache_fp8(const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* cache_seqlens, int32_t page_size,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t hq, int32_t hkv,
+                                    int32_t d, int32_t dv, int32_t fp8_format,
+                                    const float* q_descale, const float* k_descale,
+                                    const float* v_descale, float scale, int32_t causal,
+                                    int32_t window_left, int32_t window_right,
+                                    const float* sinks, void* out, float* lse, void* stream) {
+  REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 &&
+              page_size > 0 && max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  // k and v may be NULL when no sequence has current rows (they are then never read)
+  REQUIRE(q && cu_seqlens_q && cu_seqlens_k && k_cache && v_cache && block_table &&
+              cache_seqlens && out,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(q, k, v, k_cache, v_cache, out), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(window_left >= -1 && window_right >= -1, ATTN_EINVAL, "window bounds must be >= -1");
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(fp8_format == ATTN_FP8_E4M3 || fp8_format == ATTN_FP8_E5M2, ATTN_EUNSUPPORTED,
+          "fp8_format %d (expected ATTN_FP8_E4M3 or ATTN_FP8_E5M2)", fp8_format);
+  REQUIRE(d == 128 && dv == 128, ATTN_EUNSUPPORTED,
+          "FP8 cache + current supports d = dv = 128 (got %d, %d)", d, dv);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 key rows are 32-bit)");
+  attn::VarlenArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.sinks = sinks;
+  a.out = out;
+  a.lse = lse;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.cache_lens = cache_seqlens;
+  a.max_pages = max_pages_per_seq;
+  a.page = page_size;
+  const int rows = attn::varlen_bf16_rows(d);
+  a.nqt = (max_seqlen_q + rows - 1) / rows;
+  REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
+  return hip_status(attn::launch_varlen_kvcache_fp8(a, fp8_format == ATTN_FP8_E4M3 ? 1 : 2,
+                                                    as_stream(stream)),
+                    "attn_fwd_varlen_kvcache_fp8 launch");
+}
+
 size_t attn_plan_words(int32_t batch, int32_t max_splits) {
   if (batch <= 0 || max_splits <= 0) return 0;
   return 3 + (size_t)batch + 3 * (size_t)batch * max_splits;

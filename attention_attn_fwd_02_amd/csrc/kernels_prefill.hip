@@ -75,7 +75,7 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 template <class C, bool KVC, bool MASK, bool QV = false>
 __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   using T = PrefillTile<C, QV>;
-  static_assert(C::FP8 == 0 || (!KVC && !MASK), "FP8 tiles: current keys, no mask");
+  static_assert(C::FP8 == 0 || !MASK, "FP8 tiles: no mask");
   static_assert(!QV || (!KVC && !MASK), "qv: current keys, no mask");
   constexpr int MASK_BAND = C::R * C::BN * 2;              // one wave's rows of a tile
   constexpr int VK_OFF = 2 * C::TILE_BYTES;                // V in the K layout (QV)
@@ -300,6 +300,11 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8(VarlenA
 }
 
 template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8_kvc(VarlenArgs a) {
+  varlen_body<C, true, false>(a);
+}
+
+template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv(VarlenArgs a) {
   varlen_body<C, false, false, true>(a);
 }
@@ -443,6 +448,9 @@ using CfgP128 = PrefillCfg<128, 4, 32, 3>;
 template <int FMT>
 using CfgP8 = PrefillCfg<128, 4, 32, 3, 3, FMT>;
 static_assert(CfgP8<1>::ROWS == CfgP128::ROWS, "FP8 grid sized by varlen_bf16_rows(128)");
+// FP8 keys over a paged cache (the same tile, with the cache slots)
+template <int FMT>
+using CfgP8Kv = PrefillCfg<128, 4, 32, 3, 3, FMT>;
 // qv: the second query's fragments take 2 waves per SIMD (bf16 or FP8 codes)
 template <int FMT>
 using CfgPQv = PrefillCfg<128, 4, 32, 2, 3, FMT>;
@@ -486,6 +494,17 @@ hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s) {
     hipLaunchKernelGGL(k_varlen_fp8<CfgP8<1>>, dim3(grid), dim3(CfgP8<1>::THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(k_varlen_fp8<CfgP8<2>>, dim3(grid), dim3(CfgP8<2>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_kvcache_fp8(const VarlenArgs& a, int fmt, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_varlen_fp8_kvc<CfgP8Kv<1>>, dim3(grid), dim3(CfgP8Kv<1>::THREADS), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL(k_varlen_fp8_kvc<CfgP8Kv<2>>, dim3(grid), dim3(CfgP8Kv<2>::THREADS), 0, s,
+                       a);
   return hipGetLastError();
 }
 

@@ -423,6 +423,30 @@ def bench_chunked(steps, warmup, with_mask=False):
     return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lc=lc.tolist())
 
 
+def bench_chunked_fp8(steps, warmup):
+    import torch
+    from attention_attn_fwd_02_amd import binding as B
+    from attention_attn_fwd_02_amd import inputs
+    w = inputs.chunked_prefill_fp8()
+    lq = np.diff(w.cu_seqlens_q)
+    lc = w.cache_seqlens.astype(np.int64)
+    t = [dev(x) for x in (w.q, w.k, w.v, w.cu_seqlens_q, w.cu_seqlens_k, w.k_cache, w.v_cache,
+                          w.block_table, w.cache_seqlens)]
+    ds = [dev(x) for x in (w.q_descale, w.k_descale, w.v_descale)]
+    hq, d = w.q.shape[1], w.q.shape[2]
+    out = torch.empty((int(lq.sum()), hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((hq, int(lq.sum())), dtype=torch.float32, device="cuda")
+
+    def step():
+        B.attn_fwd_varlen_kvcache_fp8(*t, int(lq.max()), w.scale, w.fmt, *ds, causal=True,
+                                      out=out, lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    flops = sum(4.0 * d * hq * (int(n) * int(c) + int(n) * (int(n) + 1) / 2)
+                for n, c in zip(lq, lc))
+    return dict(ms=ms, flops=flops, tflops=flops / (ms * 1e-3) / 1e12, lc=lc.tolist())
+
+
 def bench_sparse_paged(steps, warmup):
     import torch
     from attention_attn_fwd_02_amd import binding as B
@@ -603,7 +627,7 @@ def main():
                     help="untimed back-to-back steps before the warmup of each workload")
     ap.add_argument("--only",
                     default="prefill,tiny,prefill_fp8,prefill_qv,decode,decode_fp8,decode_qv,"
-                            "decode_only_qv,mla,chunked,chunked_mask,sparse,sparse_paged")
+                            "decode_only_qv,mla,chunked,chunked_mask,chunked_fp8,sparse,sparse_paged")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -787,6 +811,21 @@ def main():
             "roofline": {"bound": "mfma", "achieved": cm["tflops"], "peak": PEAK_BF16_TFLOPS,
                          "unit": "TFLOP/s", "frac": cm["tflops"] / PEAK_BF16_TFLOPS,
                          "traffic": None, "kernel": "k_varlen_bf16 (cache + current, mask)"}})
+    if "chunked_fp8" in only:
+        log("chunked prefill fp8 ...")
+        c8 = bench_chunked_fp8(args.steps, args.warmup)
+        log(f"chunked_fp8 {c8['ms']:.3f} ms {c8['tflops']:.1f} TFLOP/s")
+        secondary.append({
+            "metric": "chunked prefill TFLOP/s (cache + new K/V, FP8 e4m3 Q/K/V)",
+            "value": c8["tflops"], "unit": "TFLOP/s", "ms_per_step": c8["ms"],
+            "workload": "the chunked-prefill shape (8 sequences, 1024 new tokens each after a "
+                        f"paged cache of U[1024,8192] tokens (drawn {c8['lc']}), page 64, Hq=32, "
+                        "Hkv=8, D=128) on e4m3 codes with per-(sequence, KV head) descales, bf16 "
+                        "out; attn_fwd_varlen_kvcache_fp8 (seed 1012)",
+            "roofline": {"bound": "mfma", "achieved": c8["tflops"], "peak": PEAK_FP8_MIX_TFLOPS,
+                         "unit": "TFLOP/s", "frac": c8["tflops"] / PEAK_FP8_MIX_TFLOPS,
+                         "traffic": None, "kernel": "k_varlen_fp8_kvc (D=128)",
+                         "peak_note": "Q.K^T on FP8 MFMA, P.V on bf16 MFMA: the harmonic mix"}})
     if "sparse" in only:
         log("sparse mla ...")
         sp = bench_sparse(args.steps, args.warmup)

@@ -192,6 +192,37 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_kvcache_fp8 - attn_fwd_varlen_kvcache with FP8 Q, K, V and
+ * caches (chunked / append prefill on FP8 inputs).
+ * [MATE "Attention" page, FMHA forward dtype notes: the varlen and KV-cache
+ *  forward paths take float8_e4m3fn / float8_e5m2 with optional float32
+ *  q/k/v_descale of shape (batch, num_heads_kv), bf16 output; Modular
+ *  flash_attention_split_kv: cache and current K/V as separate inputs]
+ *
+ *  Arguments as attn_fwd_varlen_kvcache, with q, k, v, k_cache and v_cache
+ *  uint8 codes of fp8_format (ATTN_FP8_E4M3 or ATTN_FP8_E5M2) and no mask.
+ *  q_descale, k_descale, v_descale: NULL (= 1) or float32 (batch, hkv). The
+ *  real value of an element of sequence b is its FP8 value times the descale
+ *  of (b, its KV head), for cached and current rows alike (the descale belongs
+ *  to the sequence, not to the page); a query head uses its KV head's
+ *  q_descale. out (Tq, hq, 128) bf16; lse NULL or float32 (hq, Tq).
+ *  Supported: d = dv = 128, page_size a multiple of 16. Device values are not
+ *  checked (as attn_fwd_varlen_kvcache); host arguments are checked before
+ *  anything is enqueued (EEMPTY, EINVAL, EUNSUPPORTED).
+ */
+int32_t attn_fwd_varlen_kvcache_fp8(const void* q, const void* k, const void* v,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_table, int32_t max_pages_per_seq,
+                                    const int32_t* cache_seqlens, int32_t page_size,
+                                    int32_t batch, int32_t max_seqlen_q, int32_t hq, int32_t hkv,
+                                    int32_t d, int32_t dv, int32_t fp8_format,
+                                    const float* q_descale, const float* k_descale,
+                                    const float* v_descale, float scale, int32_t causal,
+                                    int32_t window_left, int32_t window_right,
+                                    const float* sinks, void* out, float* lse, void* stream);
+
+/*
  * Split-KV plan for paged decode.
  * [MATE: get_scheduler_metadata / get_mla_metadata precompute the work split;
  *  CANN flash_attn_metadata does the same before the main call. The rule

@@ -306,3 +306,25 @@ def test_default_softmax_scale():
     assert B._scale(None, q) == pytest.approx(1.0 / math.sqrt(128))
     assert B._scale(0.25, q) == 0.25
     assert B._scale(None, torch.empty((1, 1, 1, 576))) == pytest.approx(1.0 / 24.0)
+
+
+def test_varlen_kvcache_fp8_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, kc=P, vc=P, bt=P, mp=4, lens=P, page=64, batch=2, mq=100, hq=8,
+                 hkv=2, d=128, dv=128, fmt=B.ATTN_FP8_E4M3, scale=0.1, wl=-1, wr=-1, out=P)
+        a.update(kw)
+        return lib.attn_fwd_varlen_kvcache_fp8(
+            a["q"], a["k"], a["v"], P, P, a["kc"], a["vc"], a["bt"], a["mp"], a["lens"],
+            a["page"], a["batch"], a["mq"], a["hq"], a["hkv"], a["d"], a["dv"], a["fmt"], None,
+            None, None, a["scale"], 1, a["wl"], a["wr"], None, a["out"], None, None)
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(page=0) == B.ATTN_EEMPTY
+    assert call(kc=None) == B.ATTN_EINVAL
+    assert call(bt=None) == B.ATTN_EINVAL
+    assert call(hq=7) == B.ATTN_EINVAL
+    assert call(wr=-3) == B.ATTN_EINVAL
+    assert call(scale=-1.0) == B.ATTN_EINVAL
+    assert call(fmt=B.ATTN_BF16) == B.ATTN_EUNSUPPORTED
+    assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
+    assert call(page=24) == B.ATTN_EUNSUPPORTED
+    assert call(q=P + 8) == B.ATTN_EINVAL
