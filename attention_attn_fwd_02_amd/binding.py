@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_HERE, "libattn_mi355.so")
 
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EEMPTY, ATTN_EHIP = range(5)
 ATTN_BF16, ATTN_F32, ATTN_FP8_E4M3, ATTN_FP8_E5M2 = 0, 1, 2, 3
+ATTN_GATHER_DECODE, ATTN_GATHER_MLA = 0, 1
 FP8_FORMATS = {"e4m3": ATTN_FP8_E4M3, "e5m2": ATTN_FP8_E5M2}
 
 _P = ctypes.c_void_p
@@ -55,7 +56,12 @@ _SIGNATURES = {
     "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "mla_sparse_paged_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                   _P, _P, _P, _P]),
-    "attn_debug_gather_paged": (_I, [_P, _P, _I, _P, _I, _I, _I, _I, _P, _P]),
+    "attn_debug_gather_paged": (_I, [_I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _I, _I, _P,
+                                     _P, _P]),
+    "attn_debug_gather_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                       _I, _P, _P, _P]),
+    "attn_debug_gather_sparse": (_I, [_P, _I, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _P,
+                                      _P]),
 }
 
 _lib = None
@@ -332,11 +338,13 @@ def attn_device_info(device=0):
 def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
                       scale=None, causal=False, o_partial=None, lse_partial=None):
     """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) bf16. Returns partials
-    (B*max_splits, Sq*Hq, Dv) and (B*max_splits, Sq*Hq) fp32."""
+    (B*max_splits, Sq*Hq, Dv) and (B*max_splits, Sq*Hq) fp32. With D = 576
+    (MLA rows) v_cache is None and Dv = 512, the first entries of each row."""
     _dev(q, k_cache, v_cache, dtype=torch.bfloat16)
     _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
     b, sq, hq, d = q.shape
-    page, hkv, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    page, hkv = k_cache.shape[1], k_cache.shape[2]
+    dv = 512 if v_cache is None and d == 576 else v_cache.shape[3]
     if o_partial is None:
         o_partial = torch.empty((b * max_splits, sq * hq, dv), dtype=torch.float32,
                                 device=q.device)
@@ -504,26 +512,79 @@ def mla_sparse_paged_fwd(q, kv_cache, block_table, seqlens_kv, sparse_indices, s
     return out, lse
 
 
-def attn_debug_gather_paged(cache, block_table, cache_seqlens, b, max_rows):
-    """Logical rows of sequence b from a paged cache (P, page, ...) of 16-bit
-    elements, copied by the kernels' own page-address computation."""
-    _dev(cache)
-    _dev(block_table, cache_seqlens, dtype=torch.int32)
-    if cache.element_size() != 2:
-        raise ValueError("16-bit cache expected")
-    row_elems = cache[0, 0].numel()
-    dst = torch.zeros((max_rows, row_elems), dtype=cache.dtype, device=cache.device)
-    _check(load().attn_debug_gather_paged(_ptr(cache), _ptr(block_table), block_table.shape[1],
-                                          _ptr(cache_seqlens), int(b), cache.shape[1], row_elems,
-                                          int(max_rows), _ptr(dst), _stream()))
+def _cache_dtype(t, fmt):
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype != torch.uint8:
+        raise ValueError("caches must be bfloat16 or uint8 FP8 codes")
+    return FP8_FORMATS[fmt]
+
+
+def attn_debug_gather_paged(kernel, k_cache, v_cache, block_table, cache_seqlens, plan,
+                            max_splits, dump_rows, fmt="e4m3"):
+    """Rows staged in LDS by the decode kernel's own gather (test only):
+    returns (k_rows, v_rows), each (B, dump_rows, Hkv, D) of the cache type
+    (v_rows is None for the MLA kernel); rows past a sequence's length stay
+    zero. kernel: ATTN_GATHER_DECODE or ATTN_GATHER_MLA."""
+    _dev(k_cache, v_cache)
+    _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
+    b = cache_seqlens.shape[0]
+    _, page, hkv, d = k_cache.shape
+    kd = torch.zeros((b, int(dump_rows), hkv, d), dtype=k_cache.dtype, device=k_cache.device)
+    vd = None if kernel == ATTN_GATHER_MLA else torch.zeros_like(kd)
+    _check(load().attn_debug_gather_paged(
+        int(kernel), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), b, hkv, d, page, _cache_dtype(k_cache, fmt), _ptr(plan),
+        int(max_splits), int(dump_rows), _ptr(kd), _ptr(vd), _stream()))
+    return kd, vd
+
+
+def attn_debug_gather_kvcache(k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache, block_table,
+                              cache_seqlens, dump_rows, fmt="e4m3"):
+    """Keys (cache rows, then current rows) staged by the cache-plus-current
+    prefill's own gather (test only): (k_rows, v_rows), each (B, dump_rows,
+    Hkv, D)."""
+    _dev(k, v, k_cache, v_cache)
+    _dev(cu_seqlens_q, cu_seqlens_k, block_table, cache_seqlens, dtype=torch.int32)
+    b = cache_seqlens.shape[0]
+    _, page, hkv, d = k_cache.shape
+    kd = torch.zeros((b, int(dump_rows), hkv, d), dtype=k_cache.dtype, device=k_cache.device)
+    vd = torch.zeros_like(kd)
+    _check(load().attn_debug_gather_kvcache(
+        _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(k_cache), _ptr(v_cache),
+        _ptr(block_table), block_table.shape[1], _ptr(cache_seqlens), page, b, hkv, d,
+        _cache_dtype(k_cache, fmt), int(dump_rows), _ptr(kd), _ptr(vd), _stream()))
+    return kd, vd
+
+
+def attn_debug_gather_sparse(kv, sparse_indices, sparse_mode=3, block_table=None,
+                             seqlens_kv=None, sparse_block_size=1):
+    """Expanded key lists staged by the sparse MLA kernel's own gather (test
+    only): (B, Sq, topk * sparse_block_size, 576) bf16; skipped keys hold row
+    0 of the sequence (dense kv (B, Sk, 1, 576)) or of the pool (paged)."""
+    _dev(kv, dtype=torch.bfloat16)
+    _dev(sparse_indices, block_table, seqlens_kv, dtype=torch.int32)
+    b, sq, _, topk = sparse_indices.shape
+    rows = topk * int(sparse_block_size)
+    dst = torch.zeros((b, sq, rows, kv.shape[-1]), dtype=kv.dtype, device=kv.device)
+    paged = block_table is not None
+    _check(load().attn_debug_gather_sparse(
+        _ptr(kv), 0 if paged else kv.shape[1], _ptr(block_table),
+        block_table.shape[1] if paged else 0, _ptr(seqlens_kv), kv.shape[1] if paged else 0,
+        _ptr(sparse_indices), topk, int(sparse_block_size), b, sq, int(sparse_mode), rows,
+        _ptr(dst), _stream()))
     return dst
 
 
 # ------------------------------------------------------- composed decode calls
 # The split planner sizes splits so that the decode grid holds about
-# num_cu * waves workgroups; the defaults below were tuned on MI355X for the
-# two decode shapes (GQA: 8 per CU; MLA: 3 per CU, at most 8 splits, at
-# least 8 pages per split).
+# num_cu * waves workgroups. Plans as (max_splits, waves, min_blocks), tuned
+# on MI355X for each decode shape; the composed calls below default to them,
+# and the benchmark and the full-size parity tests use the same tuples.
+GQA_DECODE_PLAN = (16, 8, 2)       # bf16 K and V tiles: 8 workgroups per CU
+FP8_DECODE_PLAN = (16, 16, 2)      # half-size FP8 tiles: twice as many
+ONLY_QV_DECODE_PLAN = (16, 16, 2)  # V-only tiles: half the bytes, as FP8
+MLA_DECODE_PLAN = (8, 3, 8)        # 128-row MLA tiles: 3 per CU, >= 8 pages per split
 GQA_ROWS_PER_WG = 16
 MLA_ROWS_PER_WG = 128
 
@@ -533,8 +594,8 @@ def _num_cu(device):
 
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, causal=False,
-                 sinks=None, max_splits=16, waves=8, min_blocks=2, num_cu=None,
-                 out_dtype=torch.bfloat16):
+                 sinks=None, max_splits=GQA_DECODE_PLAN[0], waves=GQA_DECODE_PLAN[1],
+                 min_blocks=GQA_DECODE_PLAN[2], num_cu=None, out_dtype=torch.bfloat16):
     """plan -> attn_decode_paged -> attn_combine. Returns (out (B,Sq,Hq,Dv),
     lse (B,Hq,Sq), plan)."""
     b, sq, hq, _ = q.shape
@@ -550,8 +611,9 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, ca
 
 
 def paged_decode_fp8(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, fmt="e4m3",
-                     q_descale=None, k_descale=None, v_descale=None, causal=False, max_splits=16,
-                     waves=16, min_blocks=2, num_cu=None):
+                     q_descale=None, k_descale=None, v_descale=None, causal=False,
+                     max_splits=FP8_DECODE_PLAN[0], waves=FP8_DECODE_PLAN[1],
+                     min_blocks=FP8_DECODE_PLAN[2], num_cu=None):
     """plan -> attn_decode_paged_fp8 -> attn_combine (bfloat16 out). FP8 tiles
     are half the bytes of bf16 ones, so the default plan aims at twice as
     many workgroups per CU as paged_decode's (measured on MI355X)."""
@@ -579,7 +641,7 @@ def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale=N
     hkv = v_cache.shape[2]
     rows = sq * (hq // max(1, hkv))
     upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
-    waves = waves or (8 if fmt is None and not only_qv else 16)
+    waves = waves or (GQA_DECODE_PLAN[1] if fmt is None and not only_qv else FP8_DECODE_PLAN[1])
     plan = attn_plan_splits(cache_seqlens, v_cache.shape[1], upb, num_cu or _num_cu(qv.device),
                             waves, max_splits, min_blocks)
     op, lp = attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, plan,
@@ -589,14 +651,23 @@ def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale=N
     return out, lse, plan
 
 
-def mla_decode(q, kv_cache, block_table, cache_seqlens, scale=None, causal=False, max_splits=8,
-               waves=3, min_blocks=8, num_cu=None):
-    """plan -> mla_decode_paged -> attn_combine (dv = 512)."""
+def mla_decode(q, kv_cache, block_table, cache_seqlens, scale=None, causal=False,
+               max_splits=MLA_DECODE_PLAN[0], waves=MLA_DECODE_PLAN[1],
+               min_blocks=MLA_DECODE_PLAN[2], num_cu=None):
+    """plan -> MLA decode -> attn_combine (dv = 512). kv_cache (P, page, Hkv,
+    576): Hkv = 1 runs mla_decode_paged, Hkv > 1 attn_decode_paged with
+    d = 576, dv = 512 (the same kernel)."""
     b, sq, hq, _ = q.shape
-    upb = (sq * hq + MLA_ROWS_PER_WG - 1) // MLA_ROWS_PER_WG
+    hkv = kv_cache.shape[2]
+    rows = sq * (hq // hkv)
+    upb = hkv * ((rows + MLA_ROWS_PER_WG - 1) // MLA_ROWS_PER_WG)
     plan = attn_plan_splits(cache_seqlens, kv_cache.shape[1], upb, num_cu or _num_cu(q.device),
                             waves, max_splits, min_blocks)
-    op, lp = mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits, scale,
-                              causal)
+    if hkv == 1:
+        op, lp = mla_decode_paged(q, kv_cache, block_table, cache_seqlens, plan, max_splits,
+                                  scale, causal)
+    else:
+        op, lp = attn_decode_paged(q, kv_cache, None, block_table, cache_seqlens, plan,
+                                   max_splits, scale, causal)
     out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
     return out, lse, plan

@@ -408,7 +408,9 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
               max_pages_per_seq > 0,
           ATTN_EEMPTY, "empty dimension");
-  REQUIRE(q && k_cache && v_cache && block_table && cache_seqlens && plan && o_partial &&
+  // d = 576, dv = 512: the MLA-absorbed row (value = its first 512 entries)
+  const bool mla = d == 576 && dv == 512;
+  REQUIRE(q && k_cache && (v_cache || mla) && block_table && cache_seqlens && plan && o_partial &&
               lse_partial,
           ATTN_EINVAL, "null tensor pointer");
   REQUIRE(aligned16(q, k_cache, v_cache, o_partial), ATTN_EINVAL,
@@ -419,8 +421,10 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
-  REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
-          "decode supports d = dv in {64, 128} (got %d, %d)", d, dv);
+  REQUIRE((d == dv && (d == 64 || d == 128)) || mla, ATTN_EUNSUPPORTED,
+          "decode supports d = dv in {64, 128} and d = 576, dv = 512 (got %d, %d)", d, dv);
+  REQUIRE(!mla || v_cache == nullptr || v_cache == k_cache, ATTN_EUNSUPPORTED,
+          "d = 576, dv = 512 reads the values from the key rows: v_cache must be NULL or k_cache");
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
           "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
@@ -442,6 +446,10 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   a.scale_log2 = scale * 1.4426950408889634f;
   a.o_part = o_partial;
   a.lse_part = lse_partial;
+  if (mla) {
+    a.vc = nullptr;
+    return hip_status(attn::launch_decode_mla(a, as_stream(stream)), "attn_decode_paged launch");
+  }
   return hip_status(attn::launch_decode_gqa(a, d, as_stream(stream)), "attn_decode_paged launch");
 }
 
@@ -615,7 +623,6 @@ int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* blo
           max_splits);
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
-  REQUIRE(hq % 16 == 0, ATTN_EUNSUPPORTED, "hq must be a multiple of 16");
   REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
   attn::DecodeArgs a{};
   a.q = q;
@@ -722,20 +729,140 @@ int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_bl
   return hip_status(attn::launch_sparse_mla(a, as_stream(stream)), "mla_sparse_paged_fwd launch");
 }
 
-int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,
-                                int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t b,
-                                int32_t page_size, int32_t row_elems, int32_t max_rows, void* dst,
+int32_t attn_debug_gather_paged(int32_t kernel, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* cache_seqlens, int32_t batch, int32_t hkv, int32_t d,
+                                int32_t page_size, int32_t dtype, const int32_t* plan,
+                                int32_t max_splits, int32_t dump_rows, void* k_dst, void* v_dst,
                                 void* stream) {
-  REQUIRE(cache && block_table && cache_seqlens && dst, ATTN_EINVAL, "null tensor pointer");
-  REQUIRE(aligned16(cache, dst), ATTN_EINVAL,
+  REQUIRE(batch > 0 && hkv > 0 && d > 0 && page_size > 0 && max_pages_per_seq > 0 &&
+              dump_rows > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(kernel == ATTN_GATHER_DECODE || kernel == ATTN_GATHER_MLA, ATTN_EINVAL,
+          "kernel %d (expected ATTN_GATHER_DECODE or ATTN_GATHER_MLA)", kernel);
+  const bool mla = kernel == ATTN_GATHER_MLA;
+  REQUIRE(k_cache && (v_cache || mla) && block_table && cache_seqlens && plan && k_dst &&
+              (v_dst || mla),
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(k_cache, v_cache, k_dst, v_dst), ATTN_EINVAL,
           "tensor pointers must be 16-byte aligned");
-  REQUIRE(page_size > 0 && max_pages_per_seq > 0 && row_elems > 0 && b >= 0, ATTN_EEMPTY,
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  int fmt = 0;
+  if (mla) {
+    REQUIRE(d == 576 && dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "MLA rows are 576 bf16");
+  } else {
+    REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2,
+            ATTN_EUNSUPPORTED, "dtype %d", dtype);
+    fmt = dtype == ATTN_BF16 ? 0 : (dtype == ATTN_FP8_E4M3 ? 1 : 2);
+    REQUIRE(fmt == 0 ? (d == 64 || d == 128) : d == 128, ATTN_EUNSUPPORTED,
+            "head dim %d not supported by the decode kernel for dtype %d", d, dtype);
+  }
+  attn::DecodeArgs a{};
+  a.kc = k_cache;
+  a.vc = mla ? nullptr : v_cache;
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = 1;
+  a.hq = hkv;  // one row tile per (split, KV head)
+  a.hkv = hkv;
+  a.page = page_size;
+  a.max_splits = max_splits;
+  a.dump_k = k_dst;
+  a.dump_v = v_dst;
+  a.dump_rows = dump_rows;
+  const hipError_t e = mla ? attn::launch_dump_mla(a, as_stream(stream))
+                           : attn::launch_dump_decode(a, d, fmt, as_stream(stream));
+  return hip_status(e, "attn_debug_gather_paged launch");
+}
+
+int32_t attn_debug_gather_kvcache(const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  int32_t max_pages_per_seq, const int32_t* cache_seqlens,
+                                  int32_t page_size, int32_t batch, int32_t hkv, int32_t d,
+                                  int32_t dtype, int32_t dump_rows, void* k_dst, void* v_dst,
+                                  void* stream) {
+  REQUIRE(batch > 0 && hkv > 0 && d > 0 && page_size > 0 && max_pages_per_seq > 0 &&
+              dump_rows > 0,
+          ATTN_EEMPTY, "empty dimension");
+  REQUIRE(cu_seqlens_q && cu_seqlens_k && k_cache && v_cache && block_table && cache_seqlens &&
+              k_dst && v_dst,
+          ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(k, v, k_cache, v_cache, k_dst, v_dst), ATTN_EINVAL,
+          "tensor pointers must be 16-byte aligned");
+  REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_FP8_E4M3 || dtype == ATTN_FP8_E5M2,
+          ATTN_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(d == 128, ATTN_EUNSUPPORTED, "the cache-plus-current gather test covers d = 128");
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  attn::VarlenArgs a{};
+  a.k = k;
+  a.v = v;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.batch = batch;
+  a.hq = hkv;  // one query head per KV head: every (sequence, KV head) dumps once
+  a.hkv = hkv;
+  a.nqt = 1;   // query tile 0 only
+  a.causal = 0;
+  a.wl = -1;
+  a.wr = -1;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.cache_lens = cache_seqlens;
+  a.max_pages = max_pages_per_seq;
+  a.page = page_size;
+  a.dump_k = k_dst;
+  a.dump_v = v_dst;
+  a.dump_rows = dump_rows;
+  const int fmt = dtype == ATTN_BF16 ? 0 : (dtype == ATTN_FP8_E4M3 ? 1 : 2);
+  return hip_status(attn::launch_dump_kvcache(a, fmt, as_stream(stream)),
+                    "attn_debug_gather_kvcache launch");
+}
+
+int32_t attn_debug_gather_sparse(const void* kv, int32_t seqlen_k, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seqlens_kv,
+                                 int32_t page_size, const int32_t* sparse_indices, int32_t topk,
+                                 int32_t sparse_block_size, int32_t batch, int32_t seqlen_q,
+                                 int32_t sparse_mode, int32_t dump_rows, void* dst, void* stream) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && topk > 0 && dump_rows > 0, ATTN_EEMPTY,
           "empty dimension");
-  REQUIRE(row_elems % 8 == 0, ATTN_EUNSUPPORTED, "row_elems must be a multiple of 8");
-  REQUIRE(max_rows >= 0, ATTN_EINVAL, "max_rows < 0");
-  return hip_status(attn::launch_gather(cache, block_table, max_pages_per_seq, cache_seqlens, b,
-                                        page_size, row_elems, max_rows, dst, as_stream(stream)),
-                    "attn_debug_gather_paged launch");
+  REQUIRE(kv && sparse_indices && dst, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(!block_table || (seqlens_kv && page_size > 0 && max_pages_per_seq > 0), ATTN_EINVAL,
+          "a paged pool needs seqlens_kv, page_size and max_pages_per_seq");
+  REQUIRE(block_table || seqlen_k > 0, ATTN_EEMPTY, "seqlen_k is 0");
+  REQUIRE(aligned16(kv, dst), ATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  REQUIRE(sparse_mode == 0 || sparse_mode == 3, ATTN_EINVAL, "sparse_mode must be 0 or 3");
+  int ls = 0;
+  while (ls < 8 && (1 << ls) < sparse_block_size) ++ls;
+  REQUIRE(sparse_block_size >= 1 && sparse_block_size <= 128 && (1 << ls) == sparse_block_size,
+          ATTN_EINVAL, "sparse_block_size %d is not a power of two in [1, 128]",
+          sparse_block_size);
+  REQUIRE((long)topk * sparse_block_size <= dump_rows, ATTN_EINVAL,
+          "dump_rows must hold topk * sparse_block_size keys");
+  attn::SparseArgs a{};
+  a.kv = kv;
+  a.idx = sparse_indices;
+  a.block_table = block_table;
+  a.seqlens = seqlens_kv;
+  a.max_pages = max_pages_per_seq;
+  a.page = page_size;
+  a.ls = ls;
+  a.topk = topk;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.sk = block_table ? 0 : seqlen_k;
+  a.hq = 16;  // one head tile per token
+  a.mode = sparse_mode;
+  a.dump_k = dst;
+  a.dump_rows = dump_rows;
+  return hip_status(attn::launch_dump_sparse(a, as_stream(stream)),
+                    "attn_debug_gather_sparse launch");
 }
 
 }  // extern "C"

@@ -257,6 +257,24 @@ struct StreamTile {
 
   using Src = DmaSrc;
 
+  // Byte offset within a stage of the 16-byte unit u of tile row r (K rows,
+  // or V rows when is_v): the inverse of the DMA placement (FP8: units of 16
+  // codes; bf16: chunks of 8 elements). Used by the DUMP instances that copy
+  // staged tiles out for the gather test.
+  __device__ __forceinline__ static int lds_unit(bool is_v, int r, int u) {
+    if constexpr (C::FP8 != 0) {
+      return is_v ? C::K_BYTES + r * 128 + ((u ^ swz8_v(r)) * 16) : r * 128 + ((u ^ swz8_k(r)) * 16);
+    } else if constexpr (C::VSHARED) {
+      return (r >> 4) * C::NCH * 256 + u * 256 + ((r & 15) ^ ((u & 1) * 8)) * 16;
+    } else {
+      if (is_v)
+        return C::K_BYTES + (r >> 3) * (C::NCH / 2) * 256 + (u >> 1) * 256 + (r & 7) * 32 +
+               (u & 1) * 16;
+      return (r >> 4) * (C::NCH / 4) * 1024 + (u >> 2) * 1024 + (r & 15) * 64 +
+             ((u & 3) ^ ((r & 15) >> 2)) * 16;
+    }
+  }
+
   // Lane parts of the saddr form (tile-independent): the byte offset of this
   // lane's 16 bytes from the first row of a 16-row block whose rows are
   // kstride / vstride bytes apart, for the K and the (separate) V DMA.
@@ -571,6 +589,21 @@ __device__ __forceinline__ void stream_tiles(char* ring, int ntiles, Issue issue
     if (i + C::STAGES - 1 < ntiles) issue(stage(i + C::STAGES - 1), i + C::STAGES - 1);
     compute(i, stage(i));
   }
+}
+
+// DUMP instances (gather test): copies rows [0, nrows) of a staged tile out
+// of LDS, un-swizzled: unit u (16 bytes) of row r is read at stage +
+// off(r, u) and written to dst(r) + 16 u. Every thread of the workgroup takes
+// part; the stores are waited for before returning, so that the vmcnt waits
+// of the tile loop count only the DMA.
+template <int UNITS, class Off, class Dst>
+__device__ __forceinline__ void dump_rows(const char* stage, int nrows, Off off, Dst dst, int tid,
+                                          int nthreads) {
+  for (int e = tid; e < nrows * UNITS; e += nthreads) {
+    const int r = e / UNITS, u = e % UNITS;
+    *reinterpret_cast<u32x4*>(dst(r) + u * 16) = *reinterpret_cast<const u32x4*>(stage + off(r, u));
+  }
+  wait_vmcnt<0>();
 }
 
 }  // namespace attn

@@ -95,6 +95,12 @@ struct WideTile {
     }
   }
 
+  // Byte offset of 16-byte unit u (chunk u of 8 elements) of tile row r in a
+  // stage: the layout above (used by the DUMP instance of the gather test).
+  __device__ __forceinline__ static int lds_unit(int r, int u) {
+    return (r >> 4) * C::NCH * 256 + u * 256 + ((r & 15) ^ sw(u)) * 16;
+  }
+
   // DMA of one tile. Instruction inst covers the 16-row block inst / (NCH/4)
   // and chunks 4 (inst % (NCH/4)) .. +3; lane -> chunk +(lane >> 4), row
   // (lane & 15) ^ sw(lane >> 4) of the block, landing at 16 * lane of the

@@ -31,8 +31,12 @@ inline int round_grid(long total, int grp) {
 // head kvh*G + r % G. Keys are the split's range [kv0, kv1) of the sequence.
 // Each 16-row block of a tile lies on one cache page (page sizes are
 // multiples of 16 and splits start on page boundaries); the blocks' physical
-// page numbers are wave-uniform and come from scalar loads of the block table.
-template <class C>
+// page numbers are wave-uniform and come from scalar loads of the block table
+// (paged_block_slots).
+// DUMP: the gather-test instance; the same work items and tile issue, but each
+// staged tile is copied out (rows of the split's keys, un-swizzled) instead of
+// being computed on.
+template <class C, bool DUMP = false>
 __global__ void __launch_bounds__(C::THREADS)
 k_decode(DecodeArgs a) {
   using T = StreamTile<C>;
@@ -67,14 +71,14 @@ k_decode(DecodeArgs a) {
   T tile;
   tile.init(wave);
   const size_t qoff = (((size_t)b * a.sq + tq) * a.hq + h) * C::D;
-  if constexpr (C::QV == 2) {
-    // only the qv path: no Q
+  if constexpr (C::QV == 2 || DUMP) {
+    // only the qv path (or the gather test): no Q
   } else if constexpr (C::FP8) {
     tile.load_q8(row_ok ? static_cast<const uint8_t*>(a.q) + qoff : nullptr, lane);
   } else {
     tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + qoff : nullptr, lane);
   }
-  if constexpr (C::QV != 0) {
+  if constexpr (C::QV != 0 && !DUMP) {
     const size_t qvoff = (((size_t)b * a.sq + tq) * a.hq + h) * C::DV * C::EB;
     tile.load_qv(row_ok ? static_cast<const char*>(a.qv) + qvoff : nullptr, lane);
   }
@@ -108,20 +112,12 @@ k_decode(DecodeArgs a) {
   }
   auto issue = [&](char* st, int ti) {
     // A 16-row block of a tile lies on one page (pages are multiples of 16
-    // rows and splits start on page boundaries). sl[b]: cache slot of tile
-    // row 16 b (clamped to the split's last key).
+    // rows and splits start on page boundaries). sl[k]: cache slot of tile
+    // row 16 k (clamped to the split's last key).
     constexpr int NB = C::BN / 16;
     const int j0 = kv0 + ti * C::BN;
     long sl[NB];
-    static_for<NB / 2>([&](auto I) {
-      constexpr int bb = 2 * decltype(I)::value;
-      const int ja = min(j0 + 16 * bb, kv_last), jb = min(j0 + 16 * (bb + 1), kv_last);
-      const int la = ja / a.page, lb = jb / a.page;
-      int pa, pb;
-      sload2_uniform(btb + la, btb + lb, pa, pb);
-      sl[bb] = (long)pa * a.page + (ja - la * a.page);
-      sl[bb + 1] = (long)pb * a.page + (jb - lb * a.page);
-    });
+    paged_block_slots<NB>(btb, a.page, j0, kv_last, sl);
     const int rmax = kv_last - j0;
     if (rmax >= C::BN - 1) {
       if constexpr (C::FP8) {
@@ -144,11 +140,7 @@ k_decode(DecodeArgs a) {
       // which is masked; the lane's 16-row block selects its slot
       auto row = [&](int rr) {
         rr = min(rr, rmax);
-        long v = sl[0];
-        static_for<NB - 1>([&](auto I) {
-          if ((rr >> 4) == decltype(I)::value + 1) v = sl[decltype(I)::value + 1];
-        });
-        return v + (rr & 15);
+        return block_slot(sl, rr >> 4) + (rr & 15);
       };
       if constexpr (C::FP8)
         T::dma_tile8(
@@ -163,6 +155,26 @@ k_decode(DecodeArgs a) {
   };
   const int first_t = (mt * C::ROWS) / grp;
   const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
+  if constexpr (DUMP) {
+    // the tile rows of the split's keys, to dump_k / dump_v rows
+    // (b * dump_rows + key) * hkv + kvh, row tile 0 only
+    constexpr int UNITS = C::D * C::EB / 16;
+    auto dst = [&](void* base, int j) {
+      return static_cast<char*>(base) + (((size_t)b * a.dump_rows + j) * a.hkv + kvh) * (UNITS * 16);
+    };
+    stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+      if (mt != 0) return;
+      const int j0 = kv0 + ti * C::BN, n = min(C::BN, kv1 - j0);
+      dump_rows<UNITS>(
+          st, n, [](int r, int u) { return T::lds_unit(false, r, u); },
+          [&](int r) { return dst(a.dump_k, j0 + r); }, threadIdx.x, C::THREADS);
+      if constexpr (!C::VSHARED)
+        dump_rows<UNITS>(
+            st, n, [](int r, int u) { return T::lds_unit(true, r, u); },
+            [&](int r) { return dst(a.dump_v, j0 + r); }, threadIdx.x, C::THREADS);
+    });
+    return;
+  }
   stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
     const int j0 = kv0 + ti * C::BN;
     const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
@@ -188,23 +200,26 @@ k_decode(DecodeArgs a) {
   }
 }
 
-// MLA-absorbed decode on the wide tile: one workgroup = (split, row tile mt)
-// of 128 rows (query token, head) of the single latent KV head; the rest as in
-// k_decode.
-template <class C>
+// MLA-absorbed decode on the wide tile: one workgroup = (split, KV head kvh,
+// row tile mt) of 128 rows (query token, query head of kvh's group) of a
+// 576-wide latent KV head whose first 512 entries are the value row; the rest
+// as in k_decode (Hkv = 1 for the MLA workload; the MATE example has Hkv = 2).
+template <class C, bool DUMP = false>
 __global__ void __launch_bounds__(C::THREADS)
 k_decode_wide(DecodeArgs a) {
   using T = WideTile<C>;
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) char xchg[C::XCHG_BYTES];
   __shared__ __attribute__((aligned(16))) char qlds[C::QLDS_BYTES > 0 ? C::QLDS_BYTES : 16];
-  const int nrows = a.sq * a.hq;
+  const int grp = a.hq / a.hkv;
+  const int nrows = a.sq * grp;  // rows of one KV head
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
   const int logical = xcd_group(blockIdx.x, mtiles);
   const int total = a.plan[0];
-  if (logical >= total * mtiles) return;
+  if (logical >= total * a.hkv * mtiles) return;
   const int mt = logical % mtiles;
-  const int split = logical / mtiles;
+  const int kvh = (logical / mtiles) % a.hkv;
+  const int split = logical / (mtiles * a.hkv);
   const int* tri = a.plan + 3 + a.batch + 3 * split;
   const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
   const int s = split - a.plan[2 + b];
@@ -215,40 +230,37 @@ k_decode_wide(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = mt * C::ROWS + (wave >> 1) * C::R + (lane & 31);
   const bool row_ok = r < nrows;
-  const int tq = row_ok ? r / a.hq : 0;
-  const int h = row_ok ? r % a.hq : 0;
+  const int tq = row_ok ? r / grp : 0;
+  const int h = kvh * grp + (row_ok ? r % grp : 0);
   T tile;
   tile.init(wave);
-  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
-                     : nullptr,
-              qlds, wave, lane);
+  if constexpr (!DUMP)
+    tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + tq) * a.hq + h) * C::D
+                       : nullptr,
+                qlds, wave, lane);
   wait_vmcnt<0>();  // Q in registers before any DMA is in flight
 
   const int* btb = a.block_table + (size_t)b * a.max_pages;
   const int kv_last = kv1 - 1;
-  const uint32_t kstride = (uint32_t)(C::D * 2);
-  const char* kcb = static_cast<const char*>(a.kc);
+  const uint32_t kstride = (uint32_t)(a.hkv * C::D * 2);  // bytes of one token's row
+  const char* kcb = static_cast<const char*>(a.kc) + (size_t)kvh * C::D * 2;
   auto issue = [&](char* st, int ti) {
     // 16-row blocks lie on one page each (see k_decode)
     const int j0 = kv0 + ti * C::BN;
-    const int j1 = min(j0 + 16, kv_last);
-    const int lp0 = j0 / a.page, lp1 = j1 / a.page;
-    int p0, p1;
-    sload2_uniform(btb + lp0, btb + lp1, p0, p1);
-    const long slot0 = (long)p0 * a.page + (j0 - lp0 * a.page);
-    const long slot1 = (long)p1 * a.page + (j1 - lp1 * a.page);
+    long sl[2];
+    paged_block_slots<2>(btb, a.page, j0, kv_last, sl);
     const int rmax = kv_last - j0;
     if (rmax >= C::BN - 1) {
       const uint32_t klane = T::dma_lane_off(fresh_lane(), kstride);
       T::dma_tile_sv(
           st,
           [&](int rb, int colb) {
-            return DmaSrc{kcb + (rb ? slot1 : slot0) * (long)kstride + colb, klane};
+            return DmaSrc{kcb + (rb ? sl[1] : sl[0]) * (long)kstride + colb, klane};
           },
           wave);
     } else {
       const int lane = fresh_lane();
-      // last tile of the split: slot1 is tile row min(16, rmax); lane rows
+      // last tile of the split: sl[1] is tile row min(16, rmax); lane rows
       // past the split's last key re-read that key (masked), so the lane's
       // row offset from its block's first row is clamped to lim
       const int lim0 = min(rmax, 15), lim1 = max(rmax - 16, 0);
@@ -256,14 +268,31 @@ k_decode_wide(DecodeArgs a) {
           st,
           [&](int rb, int colb) {
             const uint32_t lr = min(T::dma_lane_row(lane), (uint32_t)(rb ? lim1 : lim0));
-            return DmaSrc{kcb + (rb ? slot1 : slot0) * (long)kstride + colb,
+            return DmaSrc{kcb + (rb ? sl[1] : sl[0]) * (long)kstride + colb,
                           lr * kstride + (lane >> 4) * 16};
           },
           wave);
     }
   };
-  const int first_t = (mt * C::ROWS) / a.hq;
+  const int first_t = (mt * C::ROWS) / grp;
   const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
+  if constexpr (DUMP) {
+    // the tile rows of the split's keys, to dump_k rows (b * dump_rows + key)
+    // * hkv + kvh, row tile 0 only
+    constexpr int UNITS = C::D / 8;
+    stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+      if (mt != 0) return;
+      const int j0 = kv0 + ti * C::BN, n = min(C::BN, kv1 - j0);
+      dump_rows<UNITS>(
+          st, n, [](int rr, int u) { return T::lds_unit(rr, u); },
+          [&](int rr) {
+            return static_cast<char*>(a.dump_k) +
+                   (((size_t)b * a.dump_rows + j0 + rr) * a.hkv + kvh) * (UNITS * 16);
+          },
+          threadIdx.x, C::THREADS);
+    });
+    return;
+  }
   stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
     const int j0 = kv0 + ti * C::BN;
     const bool need = j0 + C::BN > kv1 || (a.causal && j0 + C::BN - 1 > first_t + delta);
@@ -273,7 +302,7 @@ k_decode_wide(DecodeArgs a) {
     const float m_use = tile.prep(sc, a.scale_log2, need, [&](int jr) {
       // row of this lane, recomputed here rather than kept across the loop
       const int rr = mt * C::ROWS + (wave >> 1) * C::R + (fresh_lane() & 31);
-      const int hi_vis = a.causal ? min(kv1 - 1, rr / a.hq + delta) : kv1 - 1;
+      const int hi_vis = a.causal ? min(kv1 - 1, rr / grp + delta) : kv1 - 1;
       return j0 + jr <= hi_vis;
     });
     uint32_t pk[8];
@@ -285,7 +314,7 @@ k_decode_wide(DecodeArgs a) {
   const float inv = tile.finish(false, 0.f, lse);
   if (row_ok) {
     const size_t slot_id = (size_t)b * a.max_splits + s;
-    const size_t row = slot_id * nrows + (size_t)tq * a.hq + h;
+    const size_t row = slot_id * nrows * a.hkv + (size_t)tq * a.hq + h;
     tile.store(a.o_part + row * C::DV, inv, lane);
     if (lane < 32 && tile.half == 0) a.lse_part[row] = lse;
   }
@@ -299,7 +328,10 @@ k_decode_wide(DecodeArgs a) {
 // row 0 of the base (a valid address) and masked; the chunk is then streamed.
 constexpr int kMaxTopk = 4096;
 
-template <class C, bool PAGED>
+// DUMP: the gather-test instance (see k_decode); the staged rows of token
+// (b, t) go to dump_k rows (b * sq + t) * dump_rows + key, key = position in
+// the token's expanded key list (skipped keys hold the base's row 0).
+template <class C, bool PAGED, bool DUMP = false>
 __global__ void __launch_bounds__(C::THREADS)
 k_sparse(SparseArgs a) {
   using T = StreamTile<C>;
@@ -323,9 +355,10 @@ k_sparse(SparseArgs a) {
   const int nkeys = a.topk << a.ls;
   T tile;
   tile.init(wave);
-  tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + t) * a.hq + h) * C::D
-                     : nullptr,
-              lane);
+  if constexpr (!DUMP)
+    tile.load_q(row_ok ? static_cast<const bf16_t*>(a.q) + (((size_t)b * a.sq + t) * a.hq + h) * C::D
+                       : nullptr,
+                lane);
   wait_vmcnt<0>();
 
   // K rows are gathered: the uniform base is the sequence's first row (the
@@ -357,12 +390,27 @@ k_sparse(SparseArgs a) {
         const int id = ix[key >> a.ls];
         if (id >= 0 && id <= (limit >> a.ls)) {
           const int j = (id << a.ls) + (key & bmask);
-          if (j <= limit) row = PAGED ? btb[j / a.page] * a.page + j % a.page : j;
+          if (j <= limit) row = PAGED ? (int)paged_slot(btb, j, a.page) : j;
         }
       }
       sidx[k] = row;
     }
     __syncthreads();
+    if constexpr (DUMP) {
+      constexpr int UNITS = C::D / 8;
+      stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
+        if (mt != 0) return;
+        const int k0 = ti * C::BN;
+        dump_rows<UNITS>(
+            st, min(C::BN, n - k0), [](int r, int u) { return T::lds_unit(false, r, u); },
+            [&](int r) {
+              return static_cast<char*>(a.dump_k) +
+                     (((size_t)b * a.sq + t) * a.dump_rows + c0 + k0 + r) * (UNITS * 16);
+            },
+            threadIdx.x, C::THREADS);
+      });
+      continue;
+    }
     stream_tiles<C>(ring, ntiles, issue, [&](int ti, const char* st) {
       const int* tix = sidx + ti * C::BN;
       f32x4 sc[C::NSB];
@@ -376,6 +424,7 @@ k_sparse(SparseArgs a) {
     });
   }
 
+  if constexpr (DUMP) return;
   float lse;
   const float sink2 = (a.sinks && row_ok) ? a.sinks[h] * kLog2e : 0.f;
   const float inv = tile.finish(a.sinks != nullptr, sink2, lse);
@@ -436,12 +485,46 @@ hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s) {
   return hipGetLastError();
 }
 
+namespace {
+int mla_grid(const DecodeArgs& a) {
+  using C = CfgDecodeMla;
+  const int nrows = a.sq * (a.hq / a.hkv);
+  const int mt = (nrows + C::ROWS - 1) / C::ROWS;
+  return round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
+}
+int gqa_grid(const DecodeArgs& a, int rows) {
+  const int nrows = a.sq * (a.hq / a.hkv);
+  const int mt = (nrows + rows - 1) / rows;
+  return round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
+}
+}  // namespace
+
 hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t s) {
   using C = CfgDecodeMla;
-  const int nrows = a.sq * a.hq;
-  const int mt = (nrows + C::ROWS - 1) / C::ROWS;
-  const int grid = round_grid((long)a.batch * a.max_splits * mt, mt);
-  hipLaunchKernelGGL(k_decode_wide<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  hipLaunchKernelGGL(k_decode_wide<C>, dim3(mla_grid(a)), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dump_mla(const DecodeArgs& a, hipStream_t s) {
+  using C = CfgDecodeMla;
+  hipLaunchKernelGGL((k_decode_wide<C, true>), dim3(mla_grid(a)), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dump_decode(const DecodeArgs& a, int d, int fmt, hipStream_t s) {
+  if (fmt == 0 && d == 64) {
+    using C = CfgDecodeGqa<0, 64>;
+    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
+  } else if (fmt == 0) {
+    using C = CfgDecodeGqa<>;
+    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
+  } else if (fmt == 1) {
+    using C = CfgDecodeGqa8<1>;
+    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
+  } else {
+    using C = CfgDecodeGqa8<2>;
+    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -453,6 +536,17 @@ hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((k_sparse<C, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
   else
     hipLaunchKernelGGL((k_sparse<C, false>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dump_sparse(const SparseArgs& a, hipStream_t s) {
+  using C = CfgSparseMla;
+  const int mt = (a.hq + C::ROWS - 1) / C::ROWS;
+  const long grid = (long)a.batch * a.sq * mt;
+  if (a.block_table)
+    hipLaunchKernelGGL((k_sparse<C, true, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_sparse<C, false, true>), dim3((unsigned)grid), dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

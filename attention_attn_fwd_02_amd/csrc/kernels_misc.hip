@@ -1,7 +1,6 @@
-// Split planner, LSE-weighted combine and the paged-gather test kernel.
+// Split planner and LSE-weighted combine.
 #include "device_common.h"
 #include "launch.h"
-#include "paged.h"
 
 namespace attn {
 
@@ -149,21 +148,6 @@ k_combine(CombineArgs a) {
   if (a.lse && col == 0) a.lse[((size_t)b * a.hq + h) * a.sq + t] = lse;
 }
 
-// Copies logical rows [0, min(len_b, max_rows)) of sequence b out of a paged
-// cache through paged_row_offset(), 16 bytes per thread.
-__global__ void k_gather(const bf16_t* __restrict__ cache, const int32_t* __restrict__ bt,
-                         int max_pages, const int32_t* __restrict__ lens, int b, int page,
-                         int row_elems, int max_rows, bf16_t* __restrict__ dst) {
-  const int n = min(lens[b], max_rows);
-  const int chunks = row_elems / 8;
-  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long)n * chunks) return;
-  const int j = (int)(i / chunks), c = (int)(i % chunks);
-  const bf16_t* src = cache + paged_row_offset(bt, max_pages, b, j, page, 1, 0, row_elems);
-  *reinterpret_cast<u32x4*>(dst + (size_t)j * row_elems + c * 8) =
-      *reinterpret_cast<const u32x4*>(src + c * 8);
-}
-
 }  // namespace
 
 hipError_t launch_plan(const int32_t* lens, int batch, int page, int upb, int num_cu, int waves,
@@ -184,18 +168,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(k_combine<8>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
   else
     hipLaunchKernelGGL(k_combine<16>, dim3((unsigned)grid), dim3(kCombineThreads), 0, s, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_gather(const void* cache, const int32_t* block_table, int max_pages,
-                         const int32_t* lens, int b, int page, int row_elems, int max_rows,
-                         void* dst, hipStream_t s) {
-  const long total = (long)max_rows * (row_elems / 8);
-  const long grid = (total + 255) / 256;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather, dim3((unsigned)grid), dim3(256), 0, s,
-                     static_cast<const bf16_t*>(cache), block_table, max_pages, lens, b, page,
-                     row_elems, max_rows, static_cast<bf16_t*>(dst));
   return hipGetLastError();
 }
 

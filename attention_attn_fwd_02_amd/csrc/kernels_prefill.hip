@@ -2,7 +2,9 @@
 // [MATE "Attention" page, FMHA: flash_attn_varlen_func; CANN flash_attn:
 //  cu_seqlens_q / cu_seqlens_kv; lite_boost flash_attention: causal and
 //  window_size]
+#include "attn_core.h"  // dump_rows
 #include "launch.h"
+#include "paged.h"
 #include "prefill_bf16.h"
 
 namespace attn {
@@ -72,7 +74,12 @@ __device__ __forceinline__ Band make_band(int row0, int row_last, int lq, int lk
 // the scores (q and k) and the output (v).
 // QV: a second query qv is scored against the V rows; each stage also holds
 // V in the K layout (a third DMA of the same rows) for that product.
-template <class C, bool KVC, bool MASK, bool QV = false>
+// DUMP: the gather-test instance; the same work items and tile issue, but
+// query tile 0 of the first query head of each KV head copies every staged
+// K and V tile out (rows of the sequence's keys, cache rows first,
+// un-swizzled) instead of computing on it (launched without causal mask or
+// window, so that this tile visits every key).
+template <class C, bool KVC, bool MASK, bool QV = false, bool DUMP = false>
 __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   using T = PrefillTile<C, QV>;
   static_assert(C::FP8 == 0 || !MASK, "FP8 tiles: no mask");
@@ -105,7 +112,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   T t;
   t.init();
   const size_t qoff = ((size_t)(q0 + trow) * a.hq + w.h) * C::D * C::EB;  // bytes
-  t.load_q(row_ok ? static_cast<const char*>(a.q) + qoff : nullptr, lane);
+  if constexpr (!DUMP) t.load_q(row_ok ? static_cast<const char*>(a.q) + qoff : nullptr, lane);
   if constexpr (QV) t.load_qv(row_ok ? static_cast<const char*>(a.qv) + qoff : nullptr, lane);
   // Q must be in registers before any LDS-DMA is in flight: the compiler
   // cannot count the DMA operations, so any vmcnt wait it placed for Q inside
@@ -180,21 +187,8 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
       // past the cache clamp to its last row and are not used)
       constexpr int NB = C::BN / 16;
       long sl[NB];
-      static_for<NB / 2>([&](auto I) {
-        constexpr int b = 2 * decltype(I)::value;
-        const int ja = min(j0 + 16 * b, lc - 1), jb = min(j0 + 16 * (b + 1), lc - 1);
-        int pa, pb;
-        sload2_uniform(btb + ja / a.page, btb + jb / a.page, pa, pb);
-        sl[b] = (long)pa * a.page + ja % a.page;
-        sl[b + 1] = (long)pb * a.page + jb % a.page;
-      });
-      auto slot = [&](int rb) {
-        long v = sl[0];
-        static_for<NB - 1>([&](auto I) {
-          if (rb == decltype(I)::value + 1) v = sl[decltype(I)::value + 1];
-        });
-        return v;
-      };
+      paged_block_slots<NB>(btb, a.page, j0, lc - 1, sl);
+      auto slot = [&](int rb) { return block_slot(sl, rb); };
       if (j0 + C::BN - 1 < lc) {
         auto kblk = [&](int rb) { return kcb + slot(rb) * row_bytes; };
         auto vblk = [&](int rb) { return vcb + slot(rb) * row_bytes; };
@@ -244,6 +238,23 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
     barrier_no_fence();
     if (i + C::STAGES - 1 < ntiles) issue(refill, i + C::STAGES - 1);
     const int j0 = bd.lo + i * C::BN;
+    if constexpr (DUMP) {
+      if (w.qt == 0 && w.h % (a.hq / a.hkv) == 0) {
+        constexpr int UNITS = C::D * C::EB / 16;
+        auto dst = [&](void* base, int r) {
+          return static_cast<char*>(base) +
+                 (((size_t)w.b * a.dump_rows + j0 + r) * a.hkv + w.kvh) * (UNITS * 16);
+        };
+        const int n = min(C::BN, lk - j0);
+        dump_rows<UNITS>(
+            cur, n, [](int r, int u) { return T::template lds_unit<false>(r, u); },
+            [&](int r) { return dst(a.dump_k, r); }, threadIdx.x, C::THREADS);
+        dump_rows<UNITS>(
+            cur + C::TILE_BYTES, n, [](int r, int u) { return T::template lds_unit<true>(r, u); },
+            [&](int r) { return dst(a.dump_v, r); }, threadIdx.x, C::THREADS);
+      }
+      return;
+    }
     // per wave: skip a tile none of its rows sees (on the causal diagonal or
     // past a window, or rows past the sequence); mask only where some of its
     // rows see part of the tile
@@ -280,6 +291,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
         process(i + k, ring + k * STAGE, ring + ((k + C::STAGES - 1) % C::STAGES) * STAGE);
   }
 
+  if constexpr (DUMP) return;
   float lse;
   const float inv =
       t.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse) * vscale;
@@ -307,6 +319,12 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8_kvc(Var
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv(VarlenArgs a) {
   varlen_body<C, false, false, true>(a);
+}
+
+// gather test: the cache-plus-current tile issue with the tiles copied out
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_kvc_dump(VarlenArgs a) {
+  varlen_body<C, true, false, false, true>(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -504,6 +522,19 @@ hipError_t launch_varlen_kvcache_fp8(const VarlenArgs& a, int fmt, hipStream_t s
                        a);
   else
     hipLaunchKernelGGL(k_varlen_fp8_kvc<CfgP8Kv<2>>, dim3(grid), dim3(CfgP8Kv<2>::THREADS), 0, s,
+                       a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dump_kvcache(const VarlenArgs& a, int fmt, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (fmt == 0)
+    hipLaunchKernelGGL(k_varlen_kvc_dump<CfgP128>, dim3(grid), dim3(CfgP128::THREADS), 0, s, a);
+  else if (fmt == 1)
+    hipLaunchKernelGGL(k_varlen_kvc_dump<CfgP8Kv<1>>, dim3(grid), dim3(CfgP8Kv<1>::THREADS), 0, s,
+                       a);
+  else
+    hipLaunchKernelGGL(k_varlen_kvc_dump<CfgP8Kv<2>>, dim3(grid), dim3(CfgP8Kv<2>::THREADS), 0, s,
                        a);
   return hipGetLastError();
 }

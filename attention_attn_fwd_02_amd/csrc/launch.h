@@ -36,6 +36,11 @@ struct VarlenArgs {
   const float* v_descale;
   // second query (Tq, hq, dv) scored against the value rows (launch_varlen_qv)
   const void* qv;
+  // gather test: the DUMP instances copy every staged tile to dump_k / dump_v
+  // (key rows of sequence b at row b * dump_rows + key, heads interleaved)
+  void* dump_k;
+  void* dump_v;
+  int32_t dump_rows;
 };
 
 struct DecodeArgs {
@@ -57,6 +62,11 @@ struct DecodeArgs {
   // only_qv: that score path alone (q and the K cache are not read)
   const void* qv;
   int32_t only_qv;
+  // gather test: the DUMP instances copy every staged tile to dump_k / dump_v
+  // (key rows of sequence b at row b * dump_rows + key, heads interleaved)
+  void* dump_k;
+  void* dump_v;
+  int32_t dump_rows;
 };
 
 struct SparseArgs {
@@ -72,6 +82,11 @@ struct SparseArgs {
   const float* sinks;
   void* out;
   float* lse;
+  // gather test: the DUMP instances copy every staged tile to dump_k / dump_v
+  // (key rows of sequence b at row b * dump_rows + key, heads interleaved)
+  void* dump_k;
+  void* dump_v;
+  int32_t dump_rows;
 };
 
 struct CombineArgs {
@@ -102,8 +117,11 @@ hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_plan(const int32_t* lens, int batch, int page, int upb, int num_cu, int waves,
                        int max_splits, int min_blocks, int32_t* plan, hipStream_t s);
-hipError_t launch_gather(const void* cache, const int32_t* block_table, int max_pages,
-                         const int32_t* lens, int b, int page, int row_elems, int max_rows,
-                         void* dst, hipStream_t s);
+// DUMP instances of the paged kernels (gather test): the same grids and
+// tile issue as the kernels above, with the staged tiles copied out.
+hipError_t launch_dump_decode(const DecodeArgs& a, int d, int fmt, hipStream_t s);  // fmt 0 bf16
+hipError_t launch_dump_mla(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dump_sparse(const SparseArgs& a, hipStream_t s);
+hipError_t launch_dump_kvcache(const VarlenArgs& a, int fmt, hipStream_t s);  // d = 128
 
 }  // namespace attn

@@ -195,6 +195,20 @@ struct PrefillTile {
                                                            127, 0, 127);
   }
 
+  // Byte offset within a K (VLAYOUT = false) or V tile buffer of the 16-byte
+  // unit u of tile row r: the inverse of the DMA placement below (bf16: chunk
+  // u of 8 elements; FP8: unit u of 16 codes). Used by the DUMP instance that
+  // copies staged tiles out for the gather test.
+  template <bool VLAYOUT>
+  __device__ __forceinline__ static int lds_unit(int r, int u) {
+    if constexpr (C::FP8 != 0) return r * 128 + ((u ^ (VLAYOUT ? fv8(r) : fk8(r))) * 16);
+    if constexpr (!VLAYOUT)
+      return (r >> 4) * (C::NCH / 4) * 1024 + (u >> 2) * 1024 + (r & 15) * 64 +
+             ((u & 3) ^ ((r & 15) >> 2)) * 16;
+    return (r >> 3) * (C::NCH / 4) * 512 + (u >> 2) * 512 + ((r >> 2) & 1) * 256 + (r & 3) * 64 +
+           (u & 3) * 16;
+  }
+
   // Issues this wave's share of the DMA for one K or V tile whose key rows
   // start at row(0); row(r) returns the global byte address of key r's row
   // (always a valid address). V tiles use the V layout.

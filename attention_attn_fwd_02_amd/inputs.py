@@ -605,6 +605,18 @@ def mla_decode(seed: int = SEED_MLA_DECODE, batch: int = 64, sq: int = 2, hq: in
     return _paged_draw(rng, lens, sq, hq, 1, d, dv, page, True, False, None, False)
 
 
+def mla_mate_example(seed: int = 1013) -> Paged:
+    """The shapes of the MATE minimal MLA example: q (1, 32, 8, 576) and
+    k_cache (4, 16, 2, 576) N(0,1) bf16, block_table zeros (1, 4) (every
+    logical page is physical page 0), page 16, cache_seqlens [32], value = the
+    first 512 entries of a row, scale 1/sqrt(576). Draw order: Q, cache."""
+    rng = np.random.default_rng(seed)
+    q = _normal_bf16(rng, (1, 32, 8, 576))
+    k_cache = _normal_bf16(rng, (4, 16, 2, 576))
+    return Paged(q, k_cache, None, np.zeros((1, 4), np.int32), np.array([32], np.int32), 16, 512,
+                 1.0 / np.sqrt(576), False)
+
+
 @dataclasses.dataclass
 class Sparse:
     """Top-k sparse MLA: q (B,Sq,Hq,D) bits, kv (B,Sk,1,D) bits, indices

@@ -220,7 +220,7 @@ def bench_decode(steps, warmup):
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
     hkv = w.k_cache.shape[2]
-    ms_, waves, mb = 16, 8, 2
+    ms_, waves, mb = B.GQA_DECODE_PLAN
     upb = hkv * ((sq * hq // hkv + 15) // 16)
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
@@ -260,7 +260,7 @@ def bench_decode_qv(steps, warmup, only_qv=False):
     b, sq, hq, d = w.q.shape
     hkv = w.k_cache.shape[2]
     # V-only tiles are half the bytes: twice the workgroups per CU
-    ms_, waves, mb = (16, 16, 2) if only_qv else (16, 8, 2)
+    ms_, waves, mb = B.ONLY_QV_DECODE_PLAN if only_qv else B.GQA_DECODE_PLAN
     upb = hkv * ((sq * hq // hkv + 15) // 16)
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
@@ -290,10 +290,7 @@ def bench_decode_qv(steps, warmup, only_qv=False):
                 splits=int(plan[0].item()))
 
 
-FP8_DECODE_PLAN = (16, 16, 2)  # max_splits, waves, min_blocks for the FP8 decode
-
-
-def bench_decode_fp8(steps, warmup, plan_args=FP8_DECODE_PLAN):
+def bench_decode_fp8(steps, warmup):
     import torch
     from attention_attn_fwd_02_amd import binding as B
     from attention_attn_fwd_02_amd import inputs
@@ -304,7 +301,7 @@ def bench_decode_fp8(steps, warmup, plan_args=FP8_DECODE_PLAN):
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
     hkv = w.k_cache.shape[2]
-    ms_, waves, mb = plan_args
+    ms_, waves, mb = B.FP8_DECODE_PLAN
     upb = hkv * ((sq * hq // hkv + 15) // 16)
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 128), dtype=torch.float32, device="cuda")
@@ -343,7 +340,7 @@ def bench_mla(steps, warmup):
     bt, lens = dev(w.block_table), dev(w.cache_seqlens)
     ncu = B.attn_device_info(0)
     b, sq, hq, d = w.q.shape
-    ms_, waves, mb = 8, 3, 8
+    ms_, waves, mb = B.MLA_DECODE_PLAN
     upb = (sq * hq + B.MLA_ROWS_PER_WG - 1) // B.MLA_ROWS_PER_WG
     plan = B.attn_plan_splits(lens, 64, upb, ncu, waves, ms_, mb)
     op = torch.empty((b * ms_, sq * hq, 512), dtype=torch.float32, device="cuda")

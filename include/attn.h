@@ -53,6 +53,9 @@ typedef enum {
 
 typedef enum { ATTN_BF16 = 0, ATTN_F32 = 1, ATTN_FP8_E4M3 = 2, ATTN_FP8_E5M2 = 3 } attn_dtype;
 
+/* kernels whose page gather attn_debug_gather_paged runs (test only) */
+typedef enum { ATTN_GATHER_DECODE = 0, ATTN_GATHER_MLA = 1 } attn_gather_kernel;
+
 /* Human-readable name of a status code. Never NULL. */
 const char* attn_status_string(int32_t status);
 
@@ -262,7 +265,10 @@ int32_t attn_plan_splits(const int32_t* cache_seqlens, int32_t batch, int32_t pa
  *  o_partial float32 (batch*max_splits, seqlen_q*hq, dv), lse_partial float32
  *  (batch*max_splits, seqlen_q*hq): split s of b writes slot b*max_splits+s,
  *  row t*hq+h, normalised within the split. Unused slots are untouched.
- *  Supported: BF16, d = dv in {64, 128}, page_size a multiple of 16.
+ *  Supported: BF16, d = dv in {64, 128}, page_size a multiple of 16; and the
+ *  MLA-absorbed row d = 576, dv = 512 for any hkv (the MATE MLA example has
+ *  Hkv = 2): the key is the whole cached row, the value its first 512
+ *  entries, and v_cache must then be NULL or equal to k_cache.
  */
 int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                           const int32_t* block_table, int32_t max_pages_per_seq,
@@ -355,8 +361,8 @@ int32_t attn_combine(const float* o_partial, const float* lse_partial, const int
  *  MLA-absorb concat of nope and rope along D; CANN flash_attn: shared KV]
  *  q (batch, seqlen_q, hq, 576) bf16; kv_cache (P, page_size, 1, 576) bf16;
  *  other arguments and the partial layout (dv = 512) as attn_decode_paged;
- *  follow with attn_combine(dv = 512). hq must be a multiple of 16 and
- *  page_size a multiple of 16.
+ *  follow with attn_combine(dv = 512). page_size must be a multiple of 16.
+ *  This is attn_decode_paged with hkv = 1, d = 576, dv = 512.
  */
 int32_t mla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
                          int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t batch,
@@ -412,16 +418,61 @@ int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_bl
                              void* out, float* lse, void* stream);
 
 /*
- * attn_debug_gather_paged - copies logical rows [0, cache_seqlens[b]) of one
- * sequence out of a paged cache (P, page_size, row_elems) of 16-bit elements
- * into dst (len, row_elems), using the same page-address computation as the
- * decode kernels. For bit-exact tests of the gather. row_elems must be a
- * multiple of 8.
+ * Test-only gather checks. Each runs a DUMP instance of a kernel that reads
+ * a paged (or index-gathered) cache: the kernel's own work split, page-slot
+ * computation, tile DMA and LDS ring, with every staged tile copied back out
+ * of LDS (un-swizzled) instead of being computed on. A test compares the
+ * copies bit for bit with the rows the page table names.
+ * [MATE "Attention" page, FMHA: k_cache (num_blocks, page_block_size, Hkv, D)
+ *  addressed through block_table and cache_seqlens]
+ *
+ * attn_debug_gather_paged - the decode kernels. kernel = ATTN_GATHER_DECODE
+ *  (the GQA decode of attn_decode_paged / attn_decode_paged_fp8: dtype
+ *  ATTN_BF16 with d in {64, 128}, or ATTN_FP8_E4M3 / ATTN_FP8_E5M2 with
+ *  d = 128) or ATTN_GATHER_MLA (the wide MLA tile of mla_decode_paged: bf16
+ *  rows of d = 576, v_cache and v_dst unused). Caches and block table as in
+ *  attn_decode_paged; plan from attn_plan_splits(max_splits) over the same
+ *  cache_seqlens. k_dst / v_dst (batch, dump_rows, hkv, d) elements of the
+ *  cache type: key j < cache_seqlens[b] of KV head g is written to row
+ *  (b, j, g); other rows are untouched. dump_rows >= max cache_seqlens.
+ *
+ * attn_debug_gather_kvcache - the cache-plus-current prefill of
+ *  attn_fwd_varlen_kvcache (dtype ATTN_BF16) and attn_fwd_varlen_kvcache_fp8
+ *  (ATTN_FP8_E4M3 / ATTN_FP8_E5M2), d = 128. Arguments as those calls (k, v
+ *  the current rows, cu_seqlens_q the query rows per sequence: a sequence
+ *  with no query row is not gathered). k_dst / v_dst (batch, dump_rows, hkv,
+ *  d): key j of sequence b (its cache rows first, then its current rows) is
+ *  written to row (b, j, g). dump_rows >= the longest key sequence.
+ *
+ * attn_debug_gather_sparse - the key gather of mla_sparse_fwd (block_table
+ *  NULL: kv (batch, seqlen_k, 1, 576)) or mla_sparse_paged_fwd (kv the page
+ *  pool, block_table, seqlens_kv, page_size). dst (batch, seqlen_q,
+ *  dump_rows, 576) bf16: the expanded key list of token (b, t) (index i of
+ *  a block size s names keys i*s .. i*s + s - 1), in order; a skipped key
+ *  (negative index, past the length, or past the causal limit in mode 3)
+ *  holds row 0 of the sequence (dense) or of the pool (paged), which the
+ *  kernel fetches and masks. dump_rows >= topk * sparse_block_size.
+ *
+ *  Host checks as the calls they mirror; device contents are not checked.
  */
-int32_t attn_debug_gather_paged(const void* cache, const int32_t* block_table,
-                                int32_t max_pages_per_seq, const int32_t* cache_seqlens, int32_t b,
-                                int32_t page_size, int32_t row_elems, int32_t max_rows, void* dst,
+int32_t attn_debug_gather_paged(int32_t kernel, const void* k_cache, const void* v_cache,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* cache_seqlens, int32_t batch, int32_t hkv, int32_t d,
+                                int32_t page_size, int32_t dtype, const int32_t* plan,
+                                int32_t max_splits, int32_t dump_rows, void* k_dst, void* v_dst,
                                 void* stream);
+int32_t attn_debug_gather_kvcache(const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                  const int32_t* cu_seqlens_k, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table,
+                                  int32_t max_pages_per_seq, const int32_t* cache_seqlens,
+                                  int32_t page_size, int32_t batch, int32_t hkv, int32_t d,
+                                  int32_t dtype, int32_t dump_rows, void* k_dst, void* v_dst,
+                                  void* stream);
+int32_t attn_debug_gather_sparse(const void* kv, int32_t seqlen_k, const int32_t* block_table,
+                                 int32_t max_pages_per_seq, const int32_t* seqlens_kv,
+                                 int32_t page_size, const int32_t* sparse_indices, int32_t topk,
+                                 int32_t sparse_block_size, int32_t batch, int32_t seqlen_q,
+                                 int32_t sparse_mode, int32_t dump_rows, void* dst, void* stream);
 
 #ifdef __cplusplus
 }

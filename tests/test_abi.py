@@ -30,6 +30,7 @@ def test_header_lists_the_abi():
     names = declared()
     for n in ["attn_fwd_varlen", "attn_plan_words", "attn_plan_splits", "attn_decode_paged",
               "attn_combine", "mla_decode_paged", "attn_fwd_varlen_kvcache", "attn_decode_paged_fp8", "attn_fwd_varlen_fp8", "attn_decode_paged_qv", "attn_fwd_varlen_qv", "mla_sparse_paged_fwd", "mla_sparse_fwd", "attn_debug_gather_paged",
+              "attn_debug_gather_kvcache", "attn_debug_gather_sparse",
               "attn_status_string", "attn_last_error", "attn_device_info"]:
         assert n in names
 
@@ -72,7 +73,7 @@ def test_varlen_host_checks(lib):
     assert varlen(lib, d=96, dv=96) == B.ATTN_EUNSUPPORTED
     assert varlen(lib, d=128, dv=64) == B.ATTN_EUNSUPPORTED
     assert varlen(lib, dtype=7) == B.ATTN_EUNSUPPORTED
-    assert b"hkv" in lib.attn_last_error() or True
+    assert b"dtype 7" in lib.attn_last_error()
 
 
 def test_error_message_set(lib):
@@ -136,6 +137,11 @@ def test_decode_host_checks(lib):
     assert call(d=64, dv=128) == B.ATTN_EUNSUPPORTED
     assert call(dtype=1) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
+    # the MLA row (576 / 512) reads V from the key rows: v_cache NULL or k_cache
+    assert call(d=576, dv=512, vc=P + 4096) == B.ATTN_EUNSUPPORTED
+    assert b"v_cache" in lib.attn_last_error()
+    assert call(d=576, dv=256, vc=None) == B.ATTN_EINVAL   # not the MLA shape: V required
+    assert call(d=576, dv=512, vc=None, bt=None) == B.ATTN_EINVAL
 
 
 def test_decode_fp8_host_checks(lib):
@@ -248,8 +254,8 @@ def test_misaligned_tensors_rejected(lib):
 def test_mla_and_sparse_host_checks(lib):
     assert lib.mla_decode_paged(P, P, P, 4, P, 0, 1, 128, 64, 0.1, 0, P, 16, P, P,
                                 None) == B.ATTN_EEMPTY
-    assert lib.mla_decode_paged(P, P, P, 4, P, 2, 1, 120, 64, 0.1, 0, P, 16, P, P,
-                                None) == B.ATTN_EUNSUPPORTED
+    assert lib.mla_decode_paged(P, P, P, 4, P, 2, 1, 120, 24, 0.1, 0, P, 16, P, P,
+                                None) == B.ATTN_EUNSUPPORTED   # page not a multiple of 16
     assert lib.mla_decode_paged(P, P, P, 4, P, 2, 1, 128, 64, 0.1, 0, P, 0, P, P,
                                 None) == B.ATTN_EINVAL
     assert lib.mla_sparse_fwd(P, P, P, 2048, 1, 1, 10, 64, 0.1, 1, None, P, None,
@@ -293,8 +299,51 @@ def test_combine_host_checks(lib):
 
 
 def test_gather_host_checks(lib):
-    assert lib.attn_debug_gather_paged(P, P, 4, P, 0, 64, 12, 10, P, None) == B.ATTN_EUNSUPPORTED
-    assert lib.attn_debug_gather_paged(None, P, 4, P, 0, 64, 16, 10, P, None) == B.ATTN_EINVAL
+    def paged(**kw):
+        a = dict(kernel=B.ATTN_GATHER_DECODE, kc=P, vc=P, bt=P, mp=4, lens=P, batch=2, hkv=2,
+                 d=128, page=64, dtype=B.ATTN_BF16, plan=P, ms=16, rows=100, kd=P, vd=P)
+        a.update(kw)
+        return lib.attn_debug_gather_paged(a["kernel"], a["kc"], a["vc"], a["bt"], a["mp"],
+                                           a["lens"], a["batch"], a["hkv"], a["d"], a["page"],
+                                           a["dtype"], a["plan"], a["ms"], a["rows"], a["kd"],
+                                           a["vd"], None)
+    assert paged(kernel=5) == B.ATTN_EINVAL
+    assert paged(batch=0) == B.ATTN_EEMPTY
+    assert paged(rows=0) == B.ATTN_EEMPTY
+    assert paged(vd=None) == B.ATTN_EINVAL
+    assert paged(kernel=B.ATTN_GATHER_MLA, vc=None, vd=None) == B.ATTN_EUNSUPPORTED   # d != 576
+    assert paged(d=96) == B.ATTN_EUNSUPPORTED
+    assert paged(d=64, dtype=B.ATTN_FP8_E4M3) == B.ATTN_EUNSUPPORTED
+    assert paged(page=24) == B.ATTN_EUNSUPPORTED
+    assert paged(ms=17) == B.ATTN_EINVAL
+    assert paged(kd=P + 8) == B.ATTN_EINVAL
+
+    def kvc(**kw):
+        a = dict(k=P, v=P, cq=P, ck=P, kc=P, vc=P, bt=P, mp=4, lens=P, page=64, batch=2, hkv=2,
+                 d=128, dtype=B.ATTN_BF16, rows=100, kd=P, vd=P)
+        a.update(kw)
+        return lib.attn_debug_gather_kvcache(a["k"], a["v"], a["cq"], a["ck"], a["kc"], a["vc"],
+                                             a["bt"], a["mp"], a["lens"], a["page"], a["batch"],
+                                             a["hkv"], a["d"], a["dtype"], a["rows"], a["kd"],
+                                             a["vd"], None)
+    assert kvc(batch=0) == B.ATTN_EEMPTY
+    assert kvc(bt=None) == B.ATTN_EINVAL
+    assert kvc(d=64) == B.ATTN_EUNSUPPORTED
+    assert kvc(dtype=B.ATTN_F32) == B.ATTN_EUNSUPPORTED
+
+    def sparse(**kw):
+        a = dict(kv=P, sk=1000, bt=None, mp=0, lens=None, page=0, idx=P, topk=64, bs=1, batch=2,
+                 sq=4, mode=3, rows=64, dst=P)
+        a.update(kw)
+        return lib.attn_debug_gather_sparse(a["kv"], a["sk"], a["bt"], a["mp"], a["lens"],
+                                            a["page"], a["idx"], a["topk"], a["bs"], a["batch"],
+                                            a["sq"], a["mode"], a["rows"], a["dst"], None)
+    assert sparse(topk=0) == B.ATTN_EEMPTY
+    assert sparse(sk=0) == B.ATTN_EEMPTY
+    assert sparse(bt=P) == B.ATTN_EINVAL          # paged pool without lengths and page size
+    assert sparse(mode=1) == B.ATTN_EINVAL
+    assert sparse(bs=3) == B.ATTN_EINVAL
+    assert sparse(bs=2) == B.ATTN_EINVAL          # 128 keys do not fit 64 rows
 
 
 def test_default_softmax_scale():

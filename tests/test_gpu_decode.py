@@ -37,18 +37,6 @@ def test_plan_bit_exact(case):
     assert np.array_equal(got[:n], ref[:n]), f"plan mismatch at {np.nonzero(got[:n] != ref[:n])[0][:8]}"
 
 
-# -------------------------------------------------------------------- gather
-def test_gather_bit_exact():
-    w = inputs.paged(77, [1000, 64, 3, 130], sq=1, hq=4, hkv=2, d=64, page=16)
-    cache = dev(w.k_cache)
-    bt, lens = dev(w.block_table), dev(w.cache_seqlens)
-    for b, n in enumerate(w.cache_seqlens):
-        got = B.attn_debug_gather_paged(cache, bt, lens, b, int(n))
-        torch.cuda.synchronize()
-        ref = orc.gather_paged(w.k_cache, w.block_table, b, int(n), 16).reshape(int(n), -1)
-        assert np.array_equal(got.view(torch.int16).cpu().numpy().view(np.uint16), ref)
-
-
 # ---------------------------------------------------------------------- GQA
 def run_decode(w, max_splits=16, waves=4, min_blocks=4):
     return B.paged_decode(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
@@ -145,24 +133,17 @@ def test_decode_gqa_unreferenced_pages_poisoned():
 
 def test_decode_gqa_full():
     """Full workload: batch 64, lengths U[1024, 32768], page 64, Hq=32, Hkv=8,
-    D=128, up to 16 splits. Eight sequences are checked element by element
-    (the shortest, the longest and six seeded picks); every row of every
-    sequence must be finite with max S <= LSE-like bounds checked by the
-    oracle rows."""
+    D=128, with the plan the benchmark times (binding.GQA_DECODE_PLAN); every
+    sequence compared element by element, and the plan bit for bit."""
     w = inputs.paged_decode()
-    log("case decode_gqa_full seed", inputs.SEED_PAGED_DECODE)
-    o, lse, plan = run_decode(w)
+    log("case decode_gqa_full seed", inputs.SEED_PAGED_DECODE, "plan", B.GQA_DECODE_PLAN)
+    o, lse, plan = run_decode(w, *B.GQA_DECODE_PLAN)
     torch.cuda.synchronize()
-    lens = w.cache_seqlens
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
-                   *np.random.default_rng(7).choice(len(lens), 6, replace=False).tolist()})
-    ro, rl = oracle_decode(w, batches=pick)
-    mask = np.zeros(ro.shape, bool)
-    mask[pick] = True
-    compare("decode_gqa_full", o, lse, ro, rl, TOL_O_BF16, mask=mask)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    ref_plan = orc.plan_splits(lens, 64, 8, B.attn_device_info(0), 4, 16, 4)
-    n = 3 + len(lens) + 3 * int(ref_plan[0])
+    ro, rl = oracle_decode(w)
+    compare("decode_gqa_full", o, lse, ro, rl, TOL_O_BF16)
+    ms, waves, mb = B.GQA_DECODE_PLAN
+    ref_plan = orc.plan_splits(w.cache_seqlens, 64, 8, B.attn_device_info(0), waves, ms, mb)
+    n = 3 + len(w.cache_seqlens) + 3 * int(ref_plan[0])
     assert np.array_equal(host(plan)[:n], ref_plan[:n])
 
 
@@ -216,20 +197,60 @@ def test_mla_decode_poisoned():
 
 def test_mla_decode_full():
     """Full workload: batch 64, 2 query tokens, Hq=128, one 576-wide KV head,
-    V = first 512 entries, page 64, lengths U[2048, 16384]; six sequences
-    checked element by element."""
+    V = first 512 entries, page 64, lengths U[2048, 16384], with the plan the
+    benchmark times (binding.MLA_DECODE_PLAN); every sequence compared element
+    by element, and the plan bit for bit."""
     w = inputs.mla_decode()
-    log("case mla_decode_full seed", inputs.SEED_MLA_DECODE)
-    o, lse, _ = run_mla(w)
+    log("case mla_decode_full seed", inputs.SEED_MLA_DECODE, "plan", B.MLA_DECODE_PLAN)
+    o, lse, plan = run_mla(w, *B.MLA_DECODE_PLAN)
     torch.cuda.synchronize()
-    lens = w.cache_seqlens
-    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
-                   *np.random.default_rng(8).choice(len(lens), 4, replace=False).tolist()})
-    ro, rl = oracle_mla(w, batches=pick)
-    mask = np.zeros(ro.shape, bool)
-    mask[pick] = True
-    compare("mla_decode_full", o, lse, ro, rl, TOL_O_BF16, mask=mask)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    ro, rl = oracle_mla(w)
+    compare("mla_decode_full", o, lse, ro, rl, TOL_O_BF16)
+    ms, waves, mb = B.MLA_DECODE_PLAN
+    ref_plan = orc.plan_splits(w.cache_seqlens, 64, 2, B.attn_device_info(0), waves, ms, mb)
+    n = 3 + len(w.cache_seqlens) + 3 * int(ref_plan[0])
+    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+
+
+def test_mla_mate_example():
+    """The MATE minimal MLA example on the GPU: q (1, 32, 8, 576), k_cache
+    (4, 16, 2, 576) (two KV heads, four query heads each), block_table zeros
+    (1, 4), page 16, cache_seqlens [32], head_dim_v 512. Every logical page
+    is physical page 0, so keys 16..31 repeat keys 0..15: besides matching the
+    oracle, O equals attention over page 0's 16 keys and LSE is theirs + ln 2."""
+    w = inputs.mla_mate_example()
+    log("case mla_mate_example")
+    o, lse, _ = run_mla(w, 16, 8, 1)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mla(w)
+    compare("mla_mate_example", o, lse, ro, rl, TOL_O_BF16)
+    q, kc = inputs.bits_to_f32(w.q), inputs.bits_to_f32(w.k_cache)
+    k16 = kc[0][None]
+    o16, l16 = orc.attention_dense(q, k16, k16[..., :512], w.scale)
+    compare("mla_mate_example_16_keys", o, lse, o16, l16 + np.log(2.0), TOL_O_BF16)
+
+
+# MLA rows with several KV heads (attn_decode_paged, d = 576, dv = 512) and
+# head counts that are not multiples of 16
+MLA_GQA_CASES = [
+    # name, lens, sq, hq, hkv, page, causal, max_splits, waves, min_blocks
+    ("hkv2_hq8_sq32", [32, 300], 32, 8, 2, 16, False, 16, 8, 1),
+    ("hkv4_hq20_sq3_causal", [50, 1000, 7], 3, 20, 4, 32, True, 8, 16, 1),
+    ("hkv1_hq24_sq2", [100, 513], 2, 24, 1, 64, False, 16, 4, 2),
+    ("hkv2_hq256_sq1", [2000, 64], 1, 256, 2, 64, False, 8, 3, 2),
+]
+
+
+@pytest.mark.parametrize("case", MLA_GQA_CASES, ids=[c[0] for c in MLA_GQA_CASES])
+def test_mla_decode_hkv(case):
+    name, lens, sq, hq, hkv, page, causal, ms, waves, mb = case
+    log("case", name)
+    w = inputs.paged(6200 + len(name), lens, sq=sq, hq=hq, hkv=hkv, d=576, dv=512, page=page,
+                     shared_kv=True, causal=causal)
+    o, lse, _ = run_mla(w, ms, waves, mb)
+    torch.cuda.synchronize()
+    ro, rl = oracle_mla(w)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
 
 
 def test_decode_peaky_q():
@@ -240,7 +261,7 @@ def test_decode_peaky_q():
     w = inputs.paged_decode()
     w.q = inputs.bf16_bits(inputs.bits_to_f32(w.q) * 4)
     log("case decode_peaky")
-    o, lse, _ = run_decode(w, 16, 8, 2)
+    o, lse, _ = run_decode(w, *B.GQA_DECODE_PLAN)
     torch.cuda.synchronize()
     pick = [0, 21, 42, 63]
     ro, rl = oracle_decode(w, batches=pick)
@@ -250,7 +271,7 @@ def test_decode_peaky_q():
     m = inputs.mla_decode()
     m.q = inputs.bf16_bits(inputs.bits_to_f32(m.q) * 4)
     log("case mla_peaky")
-    o, lse, _ = run_mla(m, 8, 3, 8)
+    o, lse, _ = run_mla(m, *B.MLA_DECODE_PLAN)
     torch.cuda.synchronize()
     pick = [0, 31, 63]
     ro, rl = oracle_mla(m, batches=pick)

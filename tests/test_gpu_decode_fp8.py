@@ -114,11 +114,15 @@ def test_decode_fp8_poisoned_pool():
 def test_decode_fp8_workload():
     """The benchmarked FP8 decode workload (seed 1007: 64 sequences with cache
     lengths U[1024, 32768], page 64, Hq=32, Hkv=8, D=128, e4m3 with descales),
-    in the launch configuration bench.py times; sequences 0, 17 and 63
-    compared element by element."""
+    with the plan the benchmark times (binding.FP8_DECODE_PLAN); every
+    sequence compared element by element."""
     w = inputs.paged_decode_fp8()
-    log("case decode_fp8_workload")
-    o, lse, _ = run_fp8(w, 16, 8, 2)
+    log("case decode_fp8_workload plan", B.FP8_DECODE_PLAN)
+    o, lse, plan = run_fp8(w, *B.FP8_DECODE_PLAN)
     torch.cuda.synchronize()
-    ro, rl = oracle_fp8(w, batches=[0, 17, 63])
+    ro, rl = oracle_fp8(w)
     compare("decode_fp8_workload", o, lse, ro, rl, tol(w))
+    ms, waves, mb = B.FP8_DECODE_PLAN
+    ref_plan = orc.plan_splits(w.cache_seqlens, 64, 8, B.attn_device_info(0), waves, ms, mb)
+    n = 3 + len(w.cache_seqlens) + 3 * int(ref_plan[0])
+    assert np.array_equal(host(plan)[:n], ref_plan[:n])

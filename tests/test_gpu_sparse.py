@@ -61,14 +61,15 @@ def test_sparse_extreme_sinks():
 def test_sparse_full():
     """Full workload: 4 x 4096 query tokens, 32768 keys, Hq=64, D=576
     (V = first 512), 2048 indices per token from its bottom-right causal
-    prefix, per-head sinks; 16 tokens (all 64 heads each) element by element."""
+    prefix, per-head sinks; 72 tokens (all 64 heads each) element by element:
+    the first and last token of every sequence and 64 seeded picks."""
     s = inputs.sparse_mla()
     log("case sparse_full seed", inputs.SEED_SPARSE_MLA)
     o, lse = run_sparse(s)
     torch.cuda.synchronize()
     rng = np.random.default_rng(9)
-    toks = [(int(b), int(t)) for b, t in zip(rng.integers(0, 4, 14), rng.integers(0, 4096, 14))]
-    toks += [(0, 0), (3, 4095)]
+    toks = [(int(b), int(t)) for b, t in zip(rng.integers(0, 4, 64), rng.integers(0, 4096, 64))]
+    toks += [(b, t) for b in range(4) for t in (0, 4095)]
     ro, rl = oracle_sparse(s, toks)
     go = torch.stack([o[b, t] for b, t in toks])             # (n, Hq, 512)
     gl = torch.stack([lse[b, :, t] for b, t in toks])        # (n, Hq)
