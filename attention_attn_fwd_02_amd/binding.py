@@ -56,6 +56,9 @@ _SIGNATURES = {
     "mla_sparse_fwd": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P]),
     "mla_sparse_paged_fwd": (_I, [_P, _P, _I, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _F, _I,
                                   _P, _P, _P, _P]),
+    "attn_decode_paged_noalloc_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                       _F, _I, _P, _I, _I, _I, _I, _P, _P, _P]),
     "attn_debug_gather_paged": (_I, [_I, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _P, _I, _I, _P,
                                      _P, _P]),
     "attn_debug_gather_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
@@ -649,6 +652,33 @@ def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale=N
                                   causal, only_qv)
     out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits)
     return out, lse, plan
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, cache_seqlens, scale=None,
+                              causal=False, sinks=None, max_splits=GQA_DECODE_PLAN[0],
+                              waves=GQA_DECODE_PLAN[1], min_blocks=GQA_DECODE_PLAN[2],
+                              num_cu=None, out=None, lse=None):
+    """Plan, split decode and combine in one call with the plan and partials
+    in the library's fixed scratch array (no allocation by the library; out
+    and lse are allocated here only when not given). Returns (out (B,Sq,Hq,Dv)
+    bf16, lse (B,Hq,Sq) fp32). v_cache is None for the MLA row (D = 576)."""
+    _dev(q, k_cache, v_cache, dtype=torch.bfloat16)
+    _dev(block_table, cache_seqlens, dtype=torch.int32)
+    b, sq, hq, d = q.shape
+    page, hkv = k_cache.shape[1], k_cache.shape[2]
+    dv = 512 if v_cache is None and d == 576 else v_cache.shape[3]
+    if out is None:
+        out = torch.empty((b, sq, hq, dv), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((b, hq, sq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, sinks, dtype=torch.float32)
+    _check(load().attn_decode_paged_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), b, sq, hq, hkv, d, dv, page, ATTN_BF16, _scale(scale, q),
+        int(bool(causal)), _ptr(sinks), int(num_cu or _num_cu(q.device)), int(waves),
+        int(max_splits), int(min_blocks), _ptr(out), _ptr(lse), _stream()))
+    return out, lse
 
 
 def mla_decode(q, kv_cache, block_table, cache_seqlens, scale=None, causal=False,

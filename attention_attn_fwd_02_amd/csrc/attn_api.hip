@@ -48,6 +48,43 @@ bool aligned16(const P*... p) {
 
 }  // namespace
 
+namespace attn {
+
+int32_t set_error(int32_t code, const char* msg) { return fail(code, "%s", msg); }
+
+// Host checks of attn_decode_paged apart from its plan and partial buffers
+// (shared with attn_decode_paged_noalloc, which supplies those itself).
+int32_t check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                          int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                          int32_t dtype, float scale, int32_t max_splits) {
+  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
+              max_pages_per_seq > 0,
+          ATTN_EEMPTY, "empty dimension");
+  // d = 576, dv = 512: the MLA-absorbed row (value = its first 512 entries)
+  const bool mla = d == 576 && dv == 512;
+  REQUIRE(q && k_cache && (v_cache || mla) && block_table && cache_seqlens, ATTN_EINVAL,
+          "null tensor pointer");
+  REQUIRE(aligned16(q, k_cache, v_cache), ATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
+  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
+          max_splits);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
+          "scale must be positive and finite");
+  REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
+  REQUIRE((d == dv && (d == 64 || d == 128)) || mla, ATTN_EUNSUPPORTED,
+          "decode supports d = dv in {64, 128} and d = 576, dv = 512 (got %d, %d)", d, dv);
+  REQUIRE(!mla || v_cache == nullptr || v_cache == k_cache, ATTN_EUNSUPPORTED,
+          "d = 576, dv = 512 reads the values from the key rows: v_cache must be NULL or k_cache");
+  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
+  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
+          "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
 extern "C" {
 
 const char* attn_status_string(int32_t status) {
@@ -405,29 +442,13 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           int32_t dtype, float scale, int32_t causal, const int32_t* plan,
                           int32_t max_splits, float* o_partial, float* lse_partial,
                           void* stream) {
-  REQUIRE(batch > 0 && seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0 && page_size > 0 &&
-              max_pages_per_seq > 0,
-          ATTN_EEMPTY, "empty dimension");
-  // d = 576, dv = 512: the MLA-absorbed row (value = its first 512 entries)
+  const int32_t st = attn::check_decode_args(q, k_cache, v_cache, block_table,
+                                             max_pages_per_seq, cache_seqlens, batch, seqlen_q,
+                                             hq, hkv, d, dv, page_size, dtype, scale, max_splits);
+  if (st != ATTN_OK) return st;
   const bool mla = d == 576 && dv == 512;
-  REQUIRE(q && k_cache && (v_cache || mla) && block_table && cache_seqlens && plan && o_partial &&
-              lse_partial,
-          ATTN_EINVAL, "null tensor pointer");
-  REQUIRE(aligned16(q, k_cache, v_cache, o_partial), ATTN_EINVAL,
-          "tensor pointers must be 16-byte aligned");
-  REQUIRE(hq % hkv == 0, ATTN_EINVAL, "hq (%d) is not a multiple of hkv (%d)", hq, hkv);
-  REQUIRE(max_splits >= 1 && max_splits <= 16, ATTN_EINVAL, "max_splits %d not in [1, 16]",
-          max_splits);
-  REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
-          "scale must be positive and finite");
-  REQUIRE(dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "decode supports bf16 only");
-  REQUIRE((d == dv && (d == 64 || d == 128)) || mla, ATTN_EUNSUPPORTED,
-          "decode supports d = dv in {64, 128} and d = 576, dv = 512 (got %d, %d)", d, dv);
-  REQUIRE(!mla || v_cache == nullptr || v_cache == k_cache, ATTN_EUNSUPPORTED,
-          "d = 576, dv = 512 reads the values from the key rows: v_cache must be NULL or k_cache");
-  REQUIRE(page_size % 16 == 0, ATTN_EUNSUPPORTED, "page_size must be a multiple of 16");
-  REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
-          "hkv * d too large (byte offsets within 16 cache rows are 32-bit)");
+  REQUIRE(plan && o_partial && lse_partial, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(o_partial), ATTN_EINVAL, "tensor pointers must be 16-byte aligned");
   attn::DecodeArgs a{};
   a.q = q;
   a.kc = k_cache;

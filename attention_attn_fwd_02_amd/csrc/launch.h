@@ -99,6 +99,16 @@ struct CombineArgs {
   float* lse;
 };
 
+// Host-side helpers of the C ABI (attn_api.hip): sets the message that
+// attn_last_error() returns and passes the status through; the host checks
+// of attn_decode_paged other than its plan and partial buffers.
+int32_t set_error(int32_t code, const char* msg);
+int32_t check_decode_args(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_pages_per_seq,
+                          const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                          int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                          int32_t dtype, float scale, int32_t max_splits);
+
 // rows per workgroup of each instance (sizes the grids)
 int varlen_bf16_rows(int d);  // also the FP8 instance (d = 128)
 int varlen_f32_rows(int d);

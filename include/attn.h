@@ -418,6 +418,40 @@ int32_t mla_sparse_paged_fwd(const void* q, const void* kv_cache, int32_t num_bl
                              void* out, float* lse, void* stream);
 
 /*
+ * attn_decode_paged_noalloc - plan + attn_decode_paged + attn_combine in one
+ * call that allocates nothing and takes no workspace: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).
+ *
+ *  Arguments as attn_decode_paged (incl. the MLA row d = 576, dv = 512),
+ *  with the planner arguments of attn_plan_splits (num_cu, waves,
+ *  max_splits, min_blocks; units per block are derived from the shape) and
+ *  the outputs of attn_combine: sinks NULL or float32 (hq); out (batch,
+ *  seqlen_q, hq, dv) bf16; lse NULL or float32 (batch, hq, seqlen_q). The
+ *  result equals that of the three calls made with the same arguments.
+ *  The plan and the per-split partial results live in a device array of the
+ *  library of ATTN_NOALLOC_SCRATCH_BYTES bytes, one per GPU the library runs
+ *  on, held until the process ends; attn_decode_paged_noalloc_bytes gives a
+ *  call's need, and a call that needs more returns ATTN_EINVAL before any
+ *  device work. Every call on one GPU uses that GPU's array: calls whose
+ *  work overlaps on one GPU (other streams, other threads) race and must be
+ *  serialised by the caller. The array keeps the last call's contents;
+ *  nothing in it has to start at zero (the plan kernel writes every word the
+ *  decode and the combine read). The current device must be the stream's.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+size_t attn_decode_paged_noalloc_bytes(int32_t batch, int32_t seqlen_q, int32_t hq, int32_t dv,
+                                       int32_t max_splits);
+int32_t attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_pages_per_seq,
+                                  const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                                  int32_t hq, int32_t hkv, int32_t d, int32_t dv,
+                                  int32_t page_size, int32_t dtype, float scale, int32_t causal,
+                                  const float* sinks, int32_t num_cu, int32_t waves,
+                                  int32_t max_splits, int32_t min_blocks, void* out, float* lse,
+                                  void* stream);
+
+/*
  * Test-only gather checks. Each runs a DUMP instance of a kernel that reads
  * a paged (or index-gathered) cache: the kernel's own work split, page-slot
  * computation, tile DMA and LDS ring, with every staged tile copied back out

@@ -377,3 +377,26 @@ def test_varlen_kvcache_fp8_host_checks(lib):
     assert call(d=64, dv=64) == B.ATTN_EUNSUPPORTED
     assert call(page=24) == B.ATTN_EUNSUPPORTED
     assert call(q=P + 8) == B.ATTN_EINVAL
+
+
+def test_noalloc_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, bt=P, mp=4, lens=P, batch=2, sq=1, hq=32, hkv=8, d=128, dv=128,
+                 page=64, dtype=0, scale=0.1, ncu=256, waves=8, ms=16, mb=2, out=P)
+        a.update(kw)
+        return lib.attn_decode_paged_noalloc(
+            a["q"], a["kc"], a["vc"], a["bt"], a["mp"], a["lens"], a["batch"], a["sq"], a["hq"],
+            a["hkv"], a["d"], a["dv"], a["page"], a["dtype"], a["scale"], 0, None, a["ncu"],
+            a["waves"], a["ms"], a["mb"], a["out"], None, None)
+    need = lib.attn_decode_paged_noalloc_bytes(64, 1, 32, 128, 16)
+    assert 16 << 20 < need < 18 << 20          # the paged-decode workload fits
+    assert lib.attn_decode_paged_noalloc_bytes(0, 1, 32, 128, 16) == 0
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(hq=12) == B.ATTN_EINVAL
+    assert call(out=None) == B.ATTN_EINVAL
+    assert call(waves=0) == B.ATTN_EINVAL
+    assert call(ms=17) == B.ATTN_EINVAL
+    assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
+    # 4096 x 16 splits x 32 rows x 128 floats: far above the fixed scratch
+    assert call(batch=4096) == B.ATTN_EINVAL
+    assert b"scratch" in lib.attn_last_error()
