@@ -3,8 +3,8 @@
 // v_mfma_f32_16x16x32_bf16, keys streamed through an LDS ring.
 //
 //   S^T = K Q^T   (A = K tile from LDS, B = this wave's Q rows in registers)
-//   online softmax per row in the base-2 domain with a lazily raised
-//   reference max (see prefill_bf16.h)
+//   online softmax per row in the base-2 domain with a reference max
+//   checked after the exponentials (see prefill_bf16.h)
 //   O^T += V^T P^T (A = V read transposed from LDS, B = P from the S^T
 //   registers, which are already in B-operand order)
 //
@@ -29,7 +29,7 @@
 //      pair) cover 256 contiguous bytes.
 #pragma once
 #include "device_common.h"
-#include "prefill_bf16.h"  // lds_dma16, wait_vmcnt, barrier_no_fence, kRescaleSlack
+#include "prefill_bf16.h"  // lds_dma16, wait_vmcnt, barrier_no_fence, kSumLimit
 
 namespace attn {
 
@@ -437,52 +437,60 @@ struct StreamTile {
     }
   }
 
-  // Masking (vis(j) for tile-relative key j, only when need_mask), row max,
-  // lazy update of the reference; returns the exponent offset.
+  // Masks the scores of tile-relative keys j with !vis(j).
   template <class Vis>
-  __device__ __forceinline__ float prep(f32x4 (&s)[C::NSB], float cscale, int lane, bool need_mask,
-                                        Vis vis) {
+  __device__ __forceinline__ static void mask(f32x4 (&s)[C::NSB], int lane, Vis vis) {
     const int g = lane >> 4;
-    if (need_mask) {
-#pragma unroll
-      for (int sb = 0; sb < C::NSB; ++sb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (!vis(sb * 16 + g * 4 + r)) s[sb][r] = kNegInf;
-      }
-    }
-    float mx = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[sb][r]);
+      for (int r = 0; r < 4; ++r)
+        if (!vis(sb * 16 + g * 4 + r)) s[sb][r] = kNegInf;
     }
-    mx = M::group_max(mx) * cscale;
-    const bool raise = mx > m_ref + kRescaleSlack;
-    if (__ballot(raise) != 0) {
-      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;
-      m_ref = raise ? mx : m_ref;
-      l_run *= alpha;
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
-    }
-    return m_ref == kNegInf ? 0.f : m_ref;
   }
 
-  __device__ __forceinline__ void probs(const f32x4 (&s)[C::NSB], float cscale, float m_use,
-                                        uint32_t (&pk)[C::NSB * 2]) {
-    float lsum = 0.f;
+  // p = 2^(s*c - m) packed to bf16 pairs, l += sum p (float32), with the
+  // reference checked after the exponentials (see PrefillTile::softmax): a
+  // lane whose probabilities sum to more than kSumLimit, or whose row has no
+  // reference yet, sends the wave down the rare path that forms the row
+  // maximum across the row's lanes, raises the reference to it (rescaling O
+  // and l) and recomputes the tile.
+  __device__ __forceinline__ void exps(const f32x4 (&s)[C::NSB], float cscale,
+                                       uint32_t (&pk)[C::NSB * 2], float& l) const {
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
         const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use));
         const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use));
-        lsum += p0 + p1;
+        l = (sb == 0 && r == 0) ? p0 + p1 : l + (p0 + p1);
         pk[sb * 2 + r / 2] = pack_bf16x2(p0, p1);
       }
     }
-    l_run += lsum;
+  }
+  __device__ __forceinline__ void softmax(const f32x4 (&s)[C::NSB], float cscale,
+                                          uint32_t (&pk)[C::NSB * 2]) {
+    float l;
+    exps(s, cscale, pk, l);
+    if (__ballot(l > kSumLimit || m_ref == kNegInf) != 0) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[sb][r]);
+      }
+      const float rmx = M::group_max(mx) * cscale;
+      if (rmx > m_ref) {
+        const float alpha = fast_exp2(m_ref - rmx);  // m_ref = -inf -> 0
+        m_ref = rmx;
+        l_run *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+      }
+      exps(s, cscale, pk, l);
+    }
+    l_run += l;
   }
 
   // O^T += V^T P^T for one tile (one 32-key chunk; FP8 tiles loop over theirs).

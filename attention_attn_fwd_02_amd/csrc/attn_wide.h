@@ -202,43 +202,51 @@ struct WideTile {
     }
   }
 
-  // Masking (vis(j) for tile-relative key j, only when need_mask), row max
-  // and the lazy update of the reference; returns the exponent offset.
+  // Masks the scores of tile-relative keys j with !vis(j).
   template <class Vis>
-  __device__ __forceinline__ float prep(f32x16& s, float cscale, bool need_mask, Vis vis) {
+  __device__ __forceinline__ static void mask(f32x16& s, Vis vis) {
     const int g = fresh_lane() >> 5;
-    if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (!vis(M::mrow(g, r))) s[r] = kNegInf;
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    mx = M::group_max(mx) * cscale;
-    const bool raise = mx > m_ref + kRescaleSlack;
-    if (__ballot(raise) != 0) {
-      const float alpha = raise ? fast_exp2(m_ref - mx) : 1.f;
-      m_ref = raise ? mx : m_ref;
-      l_run *= alpha;
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
-    }
-    return m_ref == kNegInf ? 0.f : m_ref;
+    for (int r = 0; r < 16; ++r)
+      if (!vis(M::mrow(g, r))) s[r] = kNegInf;
   }
 
   // p = 2^(s*c - m) packed to bf16 pairs: pk[4c .. 4c+3] is the B operand of
-  // the P.V instruction over keys 16c .. 16c+15 (in the S^T register order).
-  __device__ __forceinline__ void probs(const f32x16& s, float cscale, float m_use, uint32_t (&pk)[8]) {
-    float lsum = 0.f;
+  // the P.V instruction over keys 16c .. 16c+15 (in the S^T register order);
+  // l += sum p in float32. The reference is checked after the exponentials
+  // (see PrefillTile::softmax): a lane whose probabilities sum to more than
+  // kSumLimit, or whose row has no reference yet, sends the wave down the
+  // rare path that raises the reference to the row maximum (rescaling O and
+  // l) and recomputes the tile.
+  __device__ __forceinline__ void exps(const f32x16& s, float cscale, uint32_t (&pk)[8],
+                                       float& l) const {
+    const float m_use = m_ref == kNegInf ? 0.f : m_ref;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
       const float p0 = fast_exp2(__builtin_fmaf(s[r], cscale, -m_use));
       const float p1 = fast_exp2(__builtin_fmaf(s[r + 1], cscale, -m_use));
-      lsum += p0 + p1;
+      l = r == 0 ? p0 + p1 : l + (p0 + p1);
       pk[r / 2] = pack_bf16x2(p0, p1);
     }
-    l_run += lsum;
+  }
+  __device__ __forceinline__ void softmax(const f32x16& s, float cscale, uint32_t (&pk)[8]) {
+    float l;
+    exps(s, cscale, pk, l);
+    if (__ballot(l > kSumLimit || m_ref == kNegInf) != 0) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      const float rmx = M::group_max(mx) * cscale;
+      if (rmx > m_ref) {
+        const float alpha = fast_exp2(m_ref - rmx);  // m_ref = -inf -> 0
+        m_ref = rmx;
+        l_run *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+      }
+      exps(s, cscale, pk, l);
+    }
+    l_run += l;
   }
 
   // O^T += V^T P^T. Lane l (16-lane block b = l >> 4, i = l & 15, group

@@ -183,10 +183,9 @@ k_decode(DecodeArgs a) {
     tile.qv_scores(st, lane, sc, qv_ratio);
     tile.exchange(xchg, wave, lane, sc);
     const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
-    const float m_use = tile.prep(sc, cscale, lane, need,
-                                  [&](int jr) { return j0 + jr <= hi_vis; });
+    if (need) T::mask(sc, lane, [&](int jr) { return j0 + jr <= hi_vis; });
     uint32_t pk[C::NSB * 2];
-    tile.probs(sc, cscale, m_use, pk);
+    tile.softmax(sc, cscale, pk);
     tile.pv(st, lane, pk);
   });
 
@@ -299,14 +298,15 @@ k_decode_wide(DecodeArgs a) {
     f32x16 sc;
     tile.qk(st, qlds, wave, sc);
     tile.exchange(xchg, wave, sc);
-    const float m_use = tile.prep(sc, a.scale_log2, need, [&](int jr) {
-      // row of this lane, recomputed here rather than kept across the loop
-      const int rr = mt * C::ROWS + (wave >> 1) * C::R + (fresh_lane() & 31);
-      const int hi_vis = a.causal ? min(kv1 - 1, rr / grp + delta) : kv1 - 1;
-      return j0 + jr <= hi_vis;
-    });
+    if (need)
+      T::mask(sc, [&](int jr) {
+        // row of this lane, recomputed here rather than kept across the loop
+        const int rr = mt * C::ROWS + (wave >> 1) * C::R + (fresh_lane() & 31);
+        const int hi_vis = a.causal ? min(kv1 - 1, rr / grp + delta) : kv1 - 1;
+        return j0 + jr <= hi_vis;
+      });
     uint32_t pk[8];
-    tile.probs(sc, a.scale_log2, m_use, pk);
+    tile.softmax(sc, a.scale_log2, pk);
     tile.pv(st, pk);
   });
 
@@ -416,10 +416,9 @@ k_sparse(SparseArgs a) {
       f32x4 sc[C::NSB];
       tile.qk(st, lane, sc);
       tile.exchange(xchg, wave, lane, sc);
-      const float m_use =
-          tile.prep(sc, a.scale_log2, lane, true, [&](int jr) { return tix[jr] >= 0; });
+      T::mask(sc, lane, [&](int jr) { return tix[jr] >= 0; });
       uint32_t pk[C::NSB * 2];
-      tile.probs(sc, a.scale_log2, m_use, pk);
+      tile.softmax(sc, a.scale_log2, pk);
       tile.pv(st, lane, pk);
     });
   }

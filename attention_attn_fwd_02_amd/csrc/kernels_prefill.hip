@@ -278,9 +278,8 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
       if (bd.wl < 0) T::template mask<false>(s, lane, 0, hi);
       else T::template mask<true>(s, lane, tdiag - bd.wl - j0, hi);
     }
-    const float m_use = t.prep(s, cs);
     uint32_t pk[C::NSB * 8];
-    t.probs(s, cs, m_use, pk);
+    t.softmax(s, cs, pk);
     t.pv(cur + C::TILE_BYTES, lane, pk);
   };
   // unrolled by STAGES so that every buffer address is a constant

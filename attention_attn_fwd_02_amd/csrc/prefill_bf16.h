@@ -35,10 +35,10 @@
 // transposing read, and P.V is the bfloat16 path's.
 //
 // Softmax runs in the base-2 domain on unscaled scores s: p = 2^(s*c - m),
-// c = scale*log2(e). The reference m is only raised when a row max exceeds it
-// by more than kRescaleSlack, so the O/l rescale is rare (p <= 2^slack keeps
-// fp32 and bf16 far from overflow); the final O = acc / l and
-// LSE = (m + log2 l) ln 2 are exact for any reference m.
+// c = scale*log2(e). The reference m is checked after the exponentials, from
+// the sums of p each lane forms anyway (see PrefillTile::softmax), so no row
+// maximum is formed on the common path and the O/l rescale is rare; the
+// final O = acc / l and LSE = (m + log2 l) ln 2 are exact for any reference m.
 #pragma once
 #include "device_common.h"
 
@@ -98,7 +98,10 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
-constexpr float kRescaleSlack = 8.0f;
+// Bound on one lane's sum of p over a tile before the reference is raised:
+// a sum above it means some p > kSumLimit / 16 = 2^8 (and p < 2^12 always,
+// far from float32 and bfloat16 overflow).
+constexpr float kSumLimit = 4096.0f;
 
 template <int D_, int NW_, int BN_, int MIN_WAVES_ = 2, int STAGES_ = 3, int FP8_ = 0>
 struct PrefillCfg {
@@ -137,7 +140,6 @@ struct PrefillTile {
   f32x16 o[C::NOB];
   float m_ref;  // reference max (base-2 scaled domain), -inf until a key is seen
   float m_use;  // exponent offset: m_ref, or 0 while m_ref is -inf
-  float thr;    // raw score above which the reference may have to rise
   float l_run;  // this lane's share of sum 2^(s*c - m_ref)
 
   __device__ __forceinline__ void init() {
@@ -145,7 +147,6 @@ struct PrefillTile {
     for (int i = 0; i < C::NOB; ++i) o[i] = f32x16{};
     m_ref = kNegInf;
     m_use = 0.f;
-    thr = kNegInf;
     l_run = 0.f;
   }
 
@@ -414,47 +415,52 @@ struct PrefillTile {
     }
   }
 
-  // Lazy update of the reference max: each lane compares the max of its own
-  // scores with the raw threshold thr = (m_ref + slack) / c (c > 0); only
-  // when some lane exceeds it is the row max formed across the lane pair and
-  // the reference raised (O and l rescaled). Returns the exponent offset.
-  __device__ __forceinline__ float prep(const f32x16 (&s)[C::NSB], float cscale) {
-    float mx = kNegInf;
-#pragma unroll
-    for (int sb = 0; sb < C::NSB; ++sb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-    }
-    if (__ballot(mx > thr) != 0) {
-      const float rmx = M::group_max(mx) * cscale;
-      const bool raise = rmx > m_ref + kRescaleSlack;
-      const float alpha = raise ? fast_exp2(m_ref - rmx) : 1.f;  // m_ref = -inf -> 0
-      m_ref = raise ? rmx : m_ref;
-      l_run *= alpha;
-#pragma unroll
-      for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
-      m_use = m_ref == kNegInf ? 0.f : m_ref;
-      thr = (m_ref + kRescaleSlack) / cscale;
-    }
-    return m_use;
-  }
-
-  // p = 2^(s*c - m), packed to bf16 pairs in B-operand order; l += sum p in
-  // float32 (summing the bf16-rounded p instead would move LSE by up to 2^-9
-  // on rows with few keys).
-  __device__ __forceinline__ void probs(const f32x16 (&s)[C::NSB], float cscale, float m_use_,
-                                        uint32_t (&pk)[C::NSB * 8]) {
-    float l0 = 0.f, l1 = 0.f;
+  // p = 2^(s*c - m) for one tile, packed to bf16 pairs in B-operand order,
+  // and l += sum p in float32 (summing the bf16-rounded p instead would move
+  // LSE by up to 2^-8 on rows with few keys).
+  //
+  // The reference m is checked after the exponentials rather than before,
+  // so no row maximum is formed on the common path: a lane whose 16
+  // probabilities sum to more than kSumLimit (so one of them exceeds 2^8),
+  // or whose row has no reference yet, sends the wave down the rare path,
+  // which forms the row maximum across the lane pair, raises the reference
+  // to it (rescaling O and l) and recomputes the tile. The final
+  // O = acc / l and LSE = m + log2 l are exact for any reference.
+  __device__ __forceinline__ void exps(const f32x16 (&s)[C::NSB], float cscale,
+                                       uint32_t (&pk)[C::NSB * 8], float& l0, float& l1) const {
 #pragma unroll
     for (int sb = 0; sb < C::NSB; ++sb) {
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use_));
-        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use_));
+        const float p0 = fast_exp2(__builtin_fmaf(s[sb][r], cscale, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], cscale, -m_use));
         pk[sb * 8 + r / 2] = pack_bf16x2(p0, p1);
-        if ((r >> 1) & 1) l1 += p0 + p1;
-        else l0 += p0 + p1;
+        float& l = ((r >> 1) & 1) ? l1 : l0;
+        l = (sb == 0 && r < 4) ? p0 + p1 : l + (p0 + p1);
       }
+    }
+  }
+  __device__ __forceinline__ void softmax(const f32x16 (&s)[C::NSB], float cscale,
+                                          uint32_t (&pk)[C::NSB * 8]) {
+    float l0, l1;
+    exps(s, cscale, pk, l0, l1);
+    if (__ballot(l0 + l1 > kSumLimit || m_ref == kNegInf) != 0) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int sb = 0; sb < C::NSB; ++sb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      }
+      const float rmx = M::group_max(mx) * cscale;
+      if (rmx > m_ref) {
+        const float alpha = fast_exp2(m_ref - rmx);  // m_ref = -inf -> 0
+        m_ref = rmx;
+        m_use = rmx;
+        l_run *= alpha;
+#pragma unroll
+        for (int ob = 0; ob < C::NOB; ++ob) o[ob] *= alpha;
+      }
+      exps(s, cscale, pk, l0, l1);
     }
     l_run += l0 + l1;
   }

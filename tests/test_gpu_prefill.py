@@ -50,7 +50,24 @@ VARLEN_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", VARLEN_CASES, ids=[c[0] for c in VARLEN_CASES])
+# Shapes served by the two-block kernel (bf16, D = 128, Hq a multiple of
+# 4 Hkv, no window): 64-row query tiles, so lengths around multiples of 64
+PP_CASES = [
+    ("pp_tile_edges", [1, 63, 64, 65, 127, 128, 129, 200], None, 8, 2, 128, True, (-1, -1),
+     False),
+    ("pp_noncausal", [5, 64, 129, 257], None, 4, 1, 128, False, (-1, -1), False),
+    ("pp_bottom_right_q_lt_k", [7, 100, 33, 64], [50, 300, 33, 200], 8, 2, 128, True, (-1, -1),
+     False),
+    ("pp_q_gt_k_empty_rows", [90, 10, 130], [40, 10, 3], 8, 2, 128, True, (-1, -1), False),
+    ("pp_empty_sequence", [30, 0, 70, 0], None, 4, 1, 128, True, (-1, -1), False),
+    ("pp_sinks", [150, 3, 96], None, 8, 2, 128, True, (-1, -1), True),
+    ("pp_gqa8", [100, 260], None, 16, 2, 128, True, (-1, -1), False),
+    ("pp_noncausal_lk_gt_lq", [40, 70], [500, 33], 8, 2, 128, False, (-1, -1), True),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES + PP_CASES,
+                         ids=[c[0] for c in VARLEN_CASES + PP_CASES])
 def test_varlen_bf16(case):
     name, lq, lk, hq, hkv, d, causal, window, sinks = case
     log("case", name)
