@@ -13,7 +13,7 @@ Inputs are seeded synthetic tensors already resident in HBM when timing
 starts. Protocol per workload (time_steps): its step runs untimed for
 --ramp-ms milliseconds (from idle the GPU takes about 40 ms of continuous
 work to leave its low clocks), then W warm-up steps, then K timed steps,
-each after an untimed 512 MiB write that evicts the Infinity Cache; every
+each after an untimed 512 MiB read that evicts the Infinity Cache; every
 step has its own pair of HIP events on the stream the kernels run on, and
 `value` is the median. The same K steps run back to back without eviction
 give the `warm` side figures.
@@ -86,19 +86,28 @@ def ramp(fn, ms):
         n += 4
 
 
-def _evict_buffer():
+def _evictor():
+    """A callable that reads a 512 MiB buffer (one reduction kernel writing 64
+    floats). Reading it leaves the Infinity Cache full of the buffer's clean
+    lines: the next step finds none of its inputs there, and the dirty lines
+    of the step before (its outputs) are written back during this untimed
+    read, not during the next step. A write of the buffer would leave up to
+    256 MB of dirty lines whose write-back fell inside the next timed step."""
     import torch
     if not _EVICT:
-        _EVICT.append(torch.empty(EVICT_BYTES // 4, dtype=torch.float32, device="cuda"))
+        buf = torch.ones(EVICT_BYTES // 4, dtype=torch.float32, device="cuda").view(64, -1)
+        out = torch.empty(64, dtype=torch.float32, device="cuda")
+        _EVICT.append(lambda: torch.sum(buf, dim=1, out=out))
     return _EVICT[0]
 
 
 def time_steps(fn, steps, warmup):
     """The timing protocol of every workload. Ramps the clocks (ramp), runs fn
     `warmup` times untimed, then times `steps` steps, each preceded on the same
-    stream by an untimed 512 MiB write that evicts the Infinity Cache, so no
-    step finds its inputs there from the step before. The evictions and the
-    steps are enqueued back to back (one synchronisation before and after),
+    stream by an untimed 512 MiB read that evicts the Infinity Cache (see
+    _evictor), so no step finds its inputs there from the step before. The
+    evictions and the steps are enqueued back to back (one synchronisation
+    before and after),
     so the GPU never idles between steps and its clocks stay where a
     continuous workload holds them. Each step is bracketed by its own pair of
     HIP events on the current stream (the stream every call is launched on).
@@ -111,12 +120,12 @@ def time_steps(fn, steps, warmup):
     ramp(fn, RAMP_MS[0])
     for _ in range(warmup):
         fn()
-    buf = _evict_buffer()
+    evict = _evictor()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(steps)]
-    for i, (a, b) in enumerate(evs):
-        buf.fill_(float(i))
+    for a, b in evs:
+        evict()
         a.record()
         fn()
         b.record()
@@ -616,7 +625,7 @@ def counter_record(key):
 
 def base_name(full):
     """k_decode from 'void attn::(anonymous namespace)::k_decode<...>(...)'."""
-    head = full.split("<")[0].split("(")[0]
+    head = full.replace("(anonymous namespace)::", "").split("<")[0].split("(")[0]
     return head.split("::")[-1].split(" ")[-1]
 
 
@@ -710,7 +719,7 @@ def profile_summary(key, trace_dir, bench_json, command):
            "Command (from the repository root on the MI355X box):", "", "    " + command, "",
            "Kernels are grouped by their full instance name (exact match). bench.py runs, per "
            "workload, 200 ms of untimed steps to raise the clocks, the warm-up steps, the timed "
-           "steps (each after an untimed 512 MiB Infinity-Cache eviction write) and as many "
+           "steps (each after an untimed 512 MiB Infinity-Cache eviction read) and as many "
            "back to back; the profiler averages every launch.", "",
            "| Kernel | Calls | Avg (us) | Median (us) | Min (us) | Max (us) |",
            "|---|---|---|---|---|---|"]
@@ -726,6 +735,55 @@ def profile_summary(key, trace_dir, bench_json, command):
                 f"{rf.get('kernel_ms', ent['ms_per_step']):.4f} ms = {rf['achieved']:.1f} "
                 f"{rf['unit']} ({100 * rf['frac']:.1f} % of {rf['peak']:.0f})."]
     path = os.path.join(ROOT, "profiles", WORKLOADS[key][6] + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(path)
+
+
+def counters_summary(key, dirs, command):
+    """Writes profiles/<stem>_counters.md: per-dispatch medians of every counter
+    in rocprofv3 --pmc folders of `bench.py --only KEY --no-secondary --no-cpu`
+    runs (one counter set per folder), for the workload's main kernel (exact
+    base name; the later half of its dispatches, after the clock ramp), with
+    the fractions they imply. SQ cycle counters share one unit, so their
+    ratios need no scaling; GRBM_GUI_ACTIVE sums the 8 XCDs' engine cycles."""
+    kernel = WORKLOADS[key][5]
+    vals = {}
+    for d in dirs:
+        disp = _kernel_dispatches(d, kernel)
+        ids = sorted(disp)
+        for i in ids[len(ids) // 2:]:
+            for c, v in disp[i].items():
+                if c != "dur":
+                    vals.setdefault(c, []).append(v)
+    med = {c: statistics.median(v) for c, v in vals.items()}
+    n = {c: len(v) for c, v in vals.items()}
+    rows = [f"| {c} | {med[c]:.4g} | {n[c]} |" for c in sorted(med)]
+    derived = []
+    if "GRBM_GUI_ACTIVE" in med:
+        cyc = med["GRBM_GUI_ACTIVE"] / N_XCD
+        derived.append(f"engine cycles per dispatch: {cyc:.4g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            derived.append(f"MFMA busy per SIMD: {100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / N_SIMD / cyc:.1f} %")
+    wc = med.get("SQ_WAVE_CYCLES")
+    if wc:
+        for c, what in (("SQ_WAIT_INST_ANY", "waiting on a counter (vmcnt/lgkmcnt)"),
+                        ("SQ_WAIT_INST_LDS", "waiting on LDS"),
+                        ("SQ_ACTIVE_INST_VALU", "issuing VALU (MFMA included)"),
+                        ("SQ_ACTIVE_INST_LDS", "issuing LDS instructions"),
+                        ("SQ_WAIT_ANY", "waiting (any)")):
+            if c in med:
+                derived.append(f"{what}: {100 * med[c] / wc:.1f} % of wave cycles ({c})")
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in med:
+        derived.append(f"bf16 MFMA flops per dispatch: {med['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g}")
+    out = [f"# rocprofv3 counters: {kernel} ({key})", "",
+           "Commands (from the repository root on the MI355X box; one counter set per run):", "",
+           "    " + command, "",
+           f"Medians per dispatch of {kernel} (exact base name), the later half of its "
+           "dispatches in each run:", "",
+           "| Counter | Median per dispatch | Dispatches |", "|---|---|---|", *rows, "",
+           "Derived:", "", *[f"- {x}" for x in derived]]
+    path = os.path.join(ROOT, "profiles", WORKLOADS[key][6] + "_counters.md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
     print(path)
@@ -833,6 +891,9 @@ def main():
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="no GPU work: write profiles/<kernel>_<workload>.md from a rocprofv3 "
                          "--kernel-trace folder and --bench-json (the line of the same run)")
+    ap.add_argument("--counters-summary", nargs="+", metavar="DIR",
+                    help="no GPU work: write profiles/<kernel>_<workload>_counters.md from "
+                         "rocprofv3 --pmc folders of the workload")
     ap.add_argument("--bench-json", default="")
     ap.add_argument("--command", default="", help="the profiling command, stored with a record")
     args = ap.parse_args()
@@ -845,6 +906,9 @@ def main():
         return
     if args.profile_summary:
         profile_summary(args.workload, args.profile_summary, args.bench_json, args.command)
+        return
+    if args.counters_summary:
+        counters_summary(args.workload, args.counters_summary, args.command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library runs on a single GPU "
@@ -897,7 +961,7 @@ def main():
         "warmup": args.warmup,
         "clock_ramp_ms": RAMP_MS[0],
         "ms_per_step": head["ms_per_step"],
-        "timing": "median over the timed steps, each after an untimed 512 MiB write that evicts "
+        "timing": "median over the timed steps, each after an untimed 512 MiB read that evicts "
                   "the Infinity Cache (steps and evictions enqueued back to back); `warm` = the "
                   "same number of steps back to back without eviction",
         "warm": head["warm"],
