@@ -730,10 +730,14 @@ def profile_summary(key, trace_dir, bench_json, command):
         out.append(f"| `{short}`{mark} | {len(d)} | {np.mean(d):.1f} | {np.median(d):.1f} | "
                    f"{min(d):.1f} | {max(d):.1f} |")
     rf = ent["roofline"]
-    out += ["", f"bench.py, same run: {ent['ms_per_step']:.4f} ms per step (median, evicted "
-                f"cache) = {ent['value']:.1f} {ent['unit']}; main kernel "
-                f"{rf.get('kernel_ms', ent['ms_per_step']):.4f} ms = {rf['achieved']:.1f} "
-                f"{rf['unit']} ({100 * rf['frac']:.1f} % of {rf['peak']:.0f})."]
+    if rf["achieved"] is None:     # latency workload
+        out += ["", f"bench.py, same run: {ent['value']:.1f} us per call (median, evicted "
+                    f"cache); {ent['warm']['value']:.1f} us back to back."]
+    else:
+        out += ["", f"bench.py, same run: {ent['ms_per_step']:.4f} ms per step (median, evicted "
+                    f"cache) = {ent['value']:.1f} {ent['unit']}; main kernel "
+                    f"{rf.get('kernel_ms', ent['ms_per_step']):.4f} ms = {rf['achieved']:.1f} "
+                    f"{rf['unit']} ({100 * rf['frac']:.1f} % of {rf['peak']:.0f})."]
     path = os.path.join(ROOT, "profiles", WORKLOADS[key][6] + ".md")
     with open(path, "w") as f:
         f.write("\n".join(out) + "\n")
@@ -965,16 +969,17 @@ def main():
                   "the Infinity Cache (steps and evictions enqueued back to back); `warm` = the "
                   "same number of steps back to back without eviction",
         "warm": head["warm"],
-        "higher_is_better": True,
+        "higher_is_better": head.get("higher_is_better", True),
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if head_key != "tiny" else "f32",
         "data": "synthetic",
         "key": head_key,
-        "config": {"workload": head["workload"], "global_batch": 8,
-                   "seq_len": f"U[512,4096] (drawn {runs[head_key].extra.get('lens')})",
-                   "heads_q": 32, "heads_kv": 8, "head_dim": 128, "causal": True,
-                   "parallelism": "none (1 GPU)"},
+        "config": ({"workload": head["workload"], "global_batch": 8,
+                    "seq_len": f"U[512,4096] (drawn {runs[head_key].extra.get('lens')})",
+                    "heads_q": 32, "heads_kv": 8, "head_dim": 128, "causal": True,
+                    "parallelism": "none (1 GPU)"} if head_key == "prefill" else
+                   {"workload": head["workload"], "parallelism": "none (1 GPU)"}),
         "roofline": rf,
         "cpu_baseline": cpu,
         "secondary": [lines[k] for k in lines if k != head_key],
