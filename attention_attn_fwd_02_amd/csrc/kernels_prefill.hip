@@ -330,14 +330,20 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_kvc_dump(Va
 // float32 variant: VALU arithmetic in fp32 throughout (no bf16 rounding of
 // inputs or probabilities). LPR = D / 8 lanes share one query row, each
 // holding 8 of its head dimensions; a dot product is summed over those lanes
-// with log2(LPR) butterfly exchanges. K/V tiles of 32 keys are staged in LDS
-// by the whole workgroup with 16-byte loads.
+// with log2(LPR) butterfly exchanges. One wave covers 64 / LPR rows, and the
+// four waves of a workgroup take the same rows and every fourth 32-key tile
+// of their key range each (a split of the keys inside the workgroup, so a
+// short problem still spreads over many SIMDs). Each wave stages its own
+// tiles in its part of LDS with 16-byte loads; at the end the waves' running
+// (max, sum, O) are merged through LDS by wave 0, the merge of [MATE]'s
+// combine with weights 2^(m_w - M).
 template <int D>
 struct F32Cfg {
   static constexpr int DPL = 8;           // head dimensions per lane
   static constexpr int LPR = D / DPL;     // lanes per query row (8 or 16)
-  static constexpr int THREADS = 256;
-  static constexpr int ROWS = THREADS / LPR;
+  static constexpr int NW = 4;            // waves, one key share each
+  static constexpr int THREADS = NW * 64;
+  static constexpr int ROWS = 64 / LPR;   // query rows of the workgroup (and of each wave)
   static constexpr int BN = 32;
   static_assert(64 % LPR == 0, "a row's lanes stay within one wave");
 };
@@ -345,8 +351,10 @@ struct F32Cfg {
 template <int D>
 __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   using C = F32Cfg<D>;
-  __shared__ __attribute__((aligned(16))) float ks[C::BN][D];
-  __shared__ __attribute__((aligned(16))) float vs[C::BN][D];
+  __shared__ __attribute__((aligned(16))) float ks[C::NW][C::BN][D];
+  __shared__ __attribute__((aligned(16))) float vs[C::NW][C::BN][D];
+  __shared__ __attribute__((aligned(16))) float mo[C::NW - 1][64][C::DPL];
+  __shared__ float ml[C::NW - 1][64][2];
   PrefillWork w;
   if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
   const int q0 = a.cu_q[w.b];
@@ -358,9 +366,10 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   const int row_last = min(lq, row0 + C::ROWS) - 1;
   const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
 
-  const int tid = threadIdx.x;
-  const int part = tid % C::LPR;
-  const int trow = row0 + tid / C::LPR;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = lane % C::LPR;
+  const int trow = row0 + lane / C::LPR;
   const bool row_ok = trow < lq;
   const float* q = static_cast<const float*>(a.q);
   const float* kg = static_cast<const float*>(a.k);
@@ -382,8 +391,12 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   }
   float m_run = kNegInf, l_run = 0.f;
   const int tdiag = trow + bd.delta;
-  for (int j0 = bd.lo; j0 < bd.hi; j0 += C::BN) {
-    for (int e = tid; e < C::BN * D / 4; e += C::THREADS) {
+  float (*kw)[D] = ks[wave];
+  float (*vw)[D] = vs[wave];
+  for (int j0 = bd.lo + wave * C::BN; j0 < bd.hi; j0 += C::NW * C::BN) {
+    // this wave's tile; only this wave reads it, so the wave's own ordering
+    // of LDS operations (and the compiler barrier) is the only sync needed
+    for (int e = lane; e < C::BN * D / 4; e += 64) {
       const int r = e / (D / 4), c = (e % (D / 4)) * 4;
       const int j = j0 + r;
       f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
@@ -392,15 +405,17 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
         kv = *reinterpret_cast<const f32x4*>(kg + off);
         vv = *reinterpret_cast<const f32x4*>(vg + off);
       }
-      *reinterpret_cast<f32x4*>(&ks[r][c]) = kv;
-      *reinterpret_cast<f32x4*>(&vs[r][c]) = vv;
+      *reinterpret_cast<f32x4*>(&kw[r][c]) = kv;
+      *reinterpret_cast<f32x4*>(&vw[r][c]) = vv;
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     float s[C::BN];
     float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < C::BN; ++j) {
-      const f32x4* kr = reinterpret_cast<const f32x4*>(&ks[j][part * C::DPL]);
+      const f32x4* kr = reinterpret_cast<const f32x4*>(&kw[j][part * C::DPL]);
       const f32x4 ka = kr[0], kb = kr[1];
       float acc = qr[0] * ka[0];
       acc = fmaf(qr[1], ka[1], acc);
@@ -428,7 +443,7 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
     for (int j = 0; j < C::BN; ++j) {
       const float p = fast_exp2(s[j] - m_use);
       l_run += p;
-      const f32x4* vr = reinterpret_cast<const f32x4*>(&vs[j][part * C::DPL]);
+      const f32x4* vr = reinterpret_cast<const f32x4*>(&vw[j][part * C::DPL]);
       const f32x4 va = vr[0], vb = vr[1];
       o[0] = fmaf(p, va[0], o[0]);
       o[1] = fmaf(p, va[1], o[1]);
@@ -439,16 +454,52 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
       o[6] = fmaf(p, vb[2], o[6]);
       o[7] = fmaf(p, vb[3], o[7]);
     }
-    __syncthreads();
+    // the next tile's stores must not pass this tile's reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const bool empty = !(l_run > 0.f);
-  const float lse = empty ? kNegInf : (m_run + fast_log2(l_run)) * kLn2;
-  float inv = empty ? 0.f : 1.f / l_run;
+  // merge: waves 1..NW-1 hand their (m, l, O) to wave 0
+  if (wave > 0) {
+#pragma unroll
+    for (int d = 0; d < C::DPL; ++d) mo[wave - 1][lane][d] = o[d];
+    ml[wave - 1][lane][0] = m_run;
+    ml[wave - 1][lane][1] = l_run;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  float mw[C::NW], lw[C::NW];
+  mw[0] = m_run;
+  lw[0] = l_run;
+  float mm = m_run;
+#pragma unroll
+  for (int v = 1; v < C::NW; ++v) {
+    mw[v] = ml[v - 1][lane][0];
+    lw[v] = ml[v - 1][lane][1];
+    mm = fmaxf(mm, mw[v]);
+  }
+  const float m_ref = mm == kNegInf ? 0.f : mm;
+  float l_sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < C::NW; ++v) {
+    const float f = fast_exp2(mw[v] - m_ref);  // 0 for a wave that saw no key
+    l_sum += lw[v] * f;
+    if (v == 0) {
+#pragma unroll
+      for (int d = 0; d < C::DPL; ++d) o[d] *= f;
+    } else {
+#pragma unroll
+      for (int d = 0; d < C::DPL; ++d) o[d] = fmaf(mo[v - 1][lane][d], f, o[d]);
+    }
+  }
+  const bool empty = !(l_sum > 0.f);
+  const float lse = empty ? kNegInf : (m_ref + fast_log2(l_sum)) * kLn2;
+  float inv = empty ? 0.f : 1.f / l_sum;
   if (a.sinks && !empty) {
     const float sink2 = a.sinks[w.h] * kLog2e;
-    const float ms = fmaxf(m_run, sink2);
-    const float f = fast_exp2(m_run - ms);
-    inv = f / (l_run * f + fast_exp2(sink2 - ms));
+    const float ms = fmaxf(m_ref, sink2);
+    const float f = fast_exp2(m_ref - ms);
+    inv = f / (l_sum * f + fast_exp2(sink2 - ms));
   }
   if (row_ok) {
     f32x4* orow = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) +

@@ -91,6 +91,32 @@ def test_varlen_fp32(d, causal):
     compare(f"varlen_fp32_d{d}_c{int(causal)}", o, lse, ro, rl, TOL_O_F32)
 
 
+F32_CASES = [
+    # name, lens_q, lens_k, d, causal, window, sinks
+    ("f32_q_lt_k", [7, 100, 33], [50, 300, 33], 64, True, (-1, -1), False),
+    ("f32_q_gt_k_empty_rows", [90, 10], [40, 10], 128, True, (-1, -1), True),
+    ("f32_window_left", [300, 77], None, 64, True, (40, -1), False),
+    ("f32_window_both", [260], None, 128, False, (31, 9), False),
+    ("f32_empty_sequence", [30, 0, 70], None, 64, True, (-1, -1), False),
+    ("f32_long_keys", [9, 700], [1000, 700], 128, True, (-1, -1), True),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=[c[0] for c in F32_CASES])
+def test_varlen_fp32_shapes(case):
+    """The fp32 kernel splits each workgroup's keys over its four waves and
+    merges them: ragged tails, rows and waves with no visible key, windows and
+    key ranges of several rounds of the four waves."""
+    name, lq, lk, d, causal, window, sinks = case
+    log("case", name)
+    w = inputs.varlen(3100 + len(name), lq, lk, hq=4, hkv=2, d=d, dtype="f32", causal=causal,
+                      window=window, with_sinks=sinks)
+    o, lse = run_varlen(w)
+    torch.cuda.synchronize()
+    ro, rl = oracle_varlen(w)
+    compare(name, o, lse, ro, rl, TOL_O_F32)
+
+
 def test_varlen_prefill_full():
     """Full workload: 8 sequences U[512, 4096], Hq=32, Hkv=8, D=128, causal;
     every output element against the oracle, plus a 4x-peakier Q run on two
