@@ -34,6 +34,10 @@ _SIGNATURES = {
     "attn_device_info": (_I, [_I, ctypes.POINTER(_I)]),
     "attn_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
                              _P, _P, _P, _P]),
+    # q, k, v, cu_q, cu_k, batch, max_q, max_k, hq, hkv, d, dv, scale, causal, wl, wr, sinks,
+    # mask, mask_heads, mask_ld, out, lse, stream
+    "attn_fwd_varlen_mask": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _I,
+                                  _P, _P, _I, _I, _P, _P, _P]),
     "attn_fwd_varlen_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P,
                                  _F, _I, _I, _I, _P, _P, _P, _P]),
     "attn_fwd_varlen_qv": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P,
@@ -233,6 +237,34 @@ def attn_fwd_varlen_qv(q, qv, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, ma
         _scale(scale, qv if only_qv or q is None else q),
         int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), int(bool(only_qv)),
         _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def attn_fwd_varlen_mask(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, mask,
+                         scale=None, causal=False, window=(-1, -1), sinks=None, out=None,
+                         lse=None, return_lse=True):
+    """attn_fwd_varlen (bf16) with an additive bf16 mask (1 or Hq, Tq, ld),
+    ld a multiple of 64 and >= max_seqlen_k. Returns (out (Tq,Hq,Dv),
+    lse (Hq,Tq) fp32 or None)."""
+    _dev(q, k, v, mask, dtype=torch.bfloat16)
+    _dev(cu_seqlens_q, cu_seqlens_k, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    tq, hq, d = q.shape
+    hkv, dv = k.shape[1], v.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if mask.dim() != 3 or mask.shape[1] != tq:
+        raise ValueError("mask must be (1 or Hq, Tq, ld)")
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=q.dtype, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=q.device)
+    _dev(out, dtype=q.dtype)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_fwd_varlen_mask(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch,
+        int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, dv, _scale(scale, q),
+        int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(mask), mask.shape[0],
+        mask.shape[2], _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -109,12 +109,16 @@ int32_t attn_device_info(int32_t device, int32_t* num_cu) {
   return ok();
 }
 
-int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
-                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
-                        int32_t max_seqlen_k, int32_t hq, int32_t hkv, int32_t d, int32_t dv,
-                        int32_t dtype, float scale, int32_t causal, int32_t window_left,
-                        int32_t window_right, const float* sinks, void* out, float* lse,
-                        void* stream) {
+// attn_fwd_varlen and attn_fwd_varlen_mask: host checks, then the launch
+// (mask NULL: the plain kernel).
+static int32_t varlen_launch(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                             int32_t hkv, int32_t d, int32_t dv, int32_t dtype, float scale,
+                             int32_t causal, int32_t window_left, int32_t window_right,
+                             const float* sinks, const void* mask, int32_t mask_heads,
+                             int32_t mask_ld, void* out, float* lse, void* stream,
+                             const char* what) {
   REQUIRE(batch > 0 && max_seqlen_q > 0 && hq > 0 && hkv > 0 && d > 0 && dv > 0, ATTN_EEMPTY,
           "empty dimension (batch=%d max_seqlen_q=%d hq=%d hkv=%d d=%d dv=%d)", batch,
           max_seqlen_q, hq, hkv, d, dv);
@@ -128,6 +132,7 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   REQUIRE(std::isfinite(scale) && scale > 0.f, ATTN_EINVAL,
           "scale must be positive and finite");
   REQUIRE(dtype == ATTN_BF16 || dtype == ATTN_F32, ATTN_EUNSUPPORTED, "dtype %d", dtype);
+  REQUIRE(!mask || dtype == ATTN_BF16, ATTN_EUNSUPPORTED, "the additive mask needs bf16 inputs");
   REQUIRE(d == dv && (d == 64 || d == 128), ATTN_EUNSUPPORTED,
           "head dims d=%d dv=%d not supported (d == dv in {64, 128})", d, dv);
   REQUIRE((long)hkv * d * 2 * 16 < (1L << 32), ATTN_EUNSUPPORTED,
@@ -148,6 +153,9 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   a.sinks = sinks;
   a.out = out;
   a.lse = lse;
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  a.mask_ld = mask_ld;
   a.kc = nullptr;
   a.vc = nullptr;
   a.block_table = nullptr;
@@ -159,7 +167,39 @@ int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32
   REQUIRE((long)a.nqt * batch * hq < (1L << 31), ATTN_EUNSUPPORTED, "grid too large");
   hipError_t e = dtype == ATTN_BF16 ? attn::launch_varlen_bf16(a, d, as_stream(stream))
                                     : attn::launch_varlen_f32(a, d, as_stream(stream));
-  return hip_status(e, "attn_fwd_varlen launch");
+  return hip_status(e, what);
+}
+
+int32_t attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int32_t batch, int32_t max_seqlen_q,
+                        int32_t max_seqlen_k, int32_t hq, int32_t hkv, int32_t d, int32_t dv,
+                        int32_t dtype, float scale, int32_t causal, int32_t window_left,
+                        int32_t window_right, const float* sinks, void* out, float* lse,
+                        void* stream) {
+  return varlen_launch(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                       hq, hkv, d, dv, dtype, scale, causal, window_left, window_right, sinks,
+                       nullptr, 0, 0, out, lse, stream, "attn_fwd_varlen launch");
+}
+
+int32_t attn_fwd_varlen_mask(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                             int32_t hkv, int32_t d, int32_t dv, float scale, int32_t causal,
+                             int32_t window_left, int32_t window_right, const float* sinks,
+                             const void* mask, int32_t mask_heads, int32_t mask_ld, void* out,
+                             float* lse, void* stream) {
+  REQUIRE(mask, ATTN_EINVAL, "null mask (attn_fwd_varlen computes the unmasked case)");
+  REQUIRE(mask_heads == 1 || mask_heads == hq, ATTN_EINVAL,
+          "mask_heads must be 1 or hq (got %d)", mask_heads);
+  REQUIRE(mask_ld > 0 && mask_ld % 64 == 0, ATTN_EINVAL,
+          "mask_ld must be a positive multiple of 64 (got %d)", mask_ld);
+  REQUIRE((long)mask_ld * 2 * 32 < (1L << 32), ATTN_EUNSUPPORTED, "mask_ld too large");
+  REQUIRE(max_seqlen_k <= mask_ld, ATTN_EINVAL,
+          "mask_ld (%d) is below max_seqlen_k (%d)", mask_ld, max_seqlen_k);
+  REQUIRE(aligned16(mask), ATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  return varlen_launch(q, k, v, cu_seqlens_q, cu_seqlens_k, batch, max_seqlen_q, max_seqlen_k,
+                       hq, hkv, d, dv, ATTN_BF16, scale, causal, window_left, window_right, sinks,
+                       mask, mask_heads, mask_ld, out, lse, stream, "attn_fwd_varlen_mask launch");
 }
 
 int32_t attn_fwd_varlen_fp8(const void* q, const void* k, const void* v,

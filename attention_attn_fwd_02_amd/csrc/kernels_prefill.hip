@@ -531,6 +531,15 @@ int varlen_f32_rows(int d) { return d == 64 ? F32Cfg<64>::ROWS : F32Cfg<128>::RO
 
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s) {
   const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  if (a.mask) {
+    if (d == 64)
+      hipLaunchKernelGGL((k_varlen_bf16<CfgP64, false, true>), dim3(grid), dim3(CfgP64::THREADS),
+                         0, s, a);
+    else
+      hipLaunchKernelGGL((k_varlen_bf16<CfgP128, false, true>), dim3(grid),
+                         dim3(CfgP128::THREADS), 0, s, a);
+    return hipGetLastError();
+  }
   if (d == 64)
     hipLaunchKernelGGL((k_varlen_bf16<CfgP64, false>), dim3(grid), dim3(CfgP64::THREADS), 0, s, a);
   else

@@ -150,6 +150,32 @@ int32_t attn_fwd_varlen_qv(const void* q, const void* qv, const void* k, const v
                            int32_t only_qv, void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_mask - attn_fwd_varlen (bfloat16) with an additive mask.
+ * [Modular flash_attention_split_kv: input_mask_fn loads additive mask
+ *  values; CANN flash_attn: attn_mask (its tables are garbled, so only the
+ *  additive form is taken)]
+ *
+ *  Arguments as attn_fwd_varlen with dtype ATTN_BF16, plus
+ *  mask: bf16 (mask_heads, Tq, mask_ld), 16-byte aligned: query row r
+ *      (packed index) of head h adds mask[h or 0][r][j] to its scaled score
+ *      with key j of its sequence (0 <= j < Lk); -inf removes the key, and a
+ *      row with every key removed is empty (O = 0, LSE = -inf). It is added
+ *      after the causal and window masks.
+ *  mask_heads: 1 (shared by all heads) or hq.
+ *  mask_ld: a multiple of 64, at least max_seqlen_k (columns up to every
+ *      sequence's Lk rounded up to 32 are read).
+ *  Errors: EINVAL for a NULL mask or the mask arguments above, the rest as
+ *  attn_fwd_varlen; supported d = dv in {64, 128}.
+ */
+int32_t attn_fwd_varlen_mask(const void* q, const void* k, const void* v,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                             int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t hq,
+                             int32_t hkv, int32_t d, int32_t dv, float scale, int32_t causal,
+                             int32_t window_left, int32_t window_right, const float* sinks,
+                             const void* mask, int32_t mask_heads, int32_t mask_ld, void* out,
+                             float* lse, void* stream);
+
+/*
  * attn_fwd_varlen_kvcache - packed queries over a paged cache of earlier
  * tokens followed by the current K/V rows, without concatenating them
  * (chunked / append prefill).

@@ -76,6 +76,25 @@ def test_varlen_host_checks(lib):
     assert b"dtype 7" in lib.attn_last_error()
 
 
+def test_varlen_mask_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, cq=P, ck=P, batch=2, mq=8, mk=100, hq=4, hkv=2, d=128, dv=128,
+                 scale=0.1, causal=1, wl=-1, wr=-1, mask=P, mh=1, mld=128)
+        a.update(kw)
+        return lib.attn_fwd_varlen_mask(
+            a["q"], a["k"], a["v"], a["cq"], a["ck"], a["batch"], a["mq"], a["mk"], a["hq"],
+            a["hkv"], a["d"], a["dv"], a["scale"], a["causal"], a["wl"], a["wr"], None,
+            a["mask"], a["mh"], a["mld"], P, None, None)
+    assert call(mask=None) == B.ATTN_EINVAL
+    assert call(mh=3) == B.ATTN_EINVAL
+    assert call(mld=100) == B.ATTN_EINVAL
+    assert call(mk=200) == B.ATTN_EINVAL
+    assert b"max_seqlen_k" in lib.attn_last_error()
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(hq=6, hkv=4) == B.ATTN_EINVAL
+    assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
+
+
 def test_error_message_set(lib):
     assert varlen(lib, hq=6, hkv=4) == B.ATTN_EINVAL
     assert b"multiple" in lib.attn_last_error()

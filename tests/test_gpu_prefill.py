@@ -91,6 +91,40 @@ def test_varlen_fp32(d, causal):
     compare(f"varlen_fp32_d{d}_c{int(causal)}", o, lse, ro, rl, TOL_O_F32)
 
 
+MASK_CASES = [
+    # name, lens_q, lens_k, hq, hkv, d, causal, window, sinks, mask_heads, neg_inf_fraction
+    ("mask_heads_d128", [37, 200, 64], None, 8, 2, 128, True, (-1, -1), False, 8, 0.0),
+    ("mask_shared_neginf_q_lt_k", [150, 3], [300, 40], 8, 2, 128, True, (-1, -1), True, 1, 0.2),
+    ("mask_d64_noncausal_window", [50, 130], [77, 250], 8, 1, 64, False, (40, 9), False, 8, 0.1),
+    ("mask_empty_sequence", [30, 0, 70], None, 4, 2, 128, True, (-1, -1), False, 1, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", MASK_CASES, ids=[c[0] for c in MASK_CASES])
+def test_varlen_additive_mask(case):
+    """attn_fwd_varlen_mask: an additive bf16 mask on the scaled scores,
+    N(0, 2^2) values with a share of -inf entries, per head or shared."""
+    name, lq, lk, hq, hkv, d, causal, window, sinks, mh, frac = case
+    log("case", name)
+    w = inputs.varlen(4100 + len(name), lq, lk, hq=hq, hkv=hkv, d=d, causal=causal,
+                      window=window, with_sinks=sinks)
+    lks = lq if lk is None else lk
+    tq = int(sum(lq))
+    ld = ((max(lks) + 63) // 64) * 64 + 64
+    rng = np.random.default_rng(4200 + len(name))
+    m = (2.0 * rng.standard_normal((mh, tq, ld))).astype(np.float32)
+    m[rng.random(m.shape) < frac] = -np.inf
+    mbits = inputs.bf16_bits(m)
+    o, lse = B.attn_fwd_varlen_mask(dev(w.q), dev(w.k), dev(w.v), dev(w.cu_seqlens_q),
+                                    dev(w.cu_seqlens_k), max(lq), max(lks), dev(mbits), w.scale,
+                                    causal, window, None if w.sinks is None else dev(w.sinks))
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_varlen(w.f32("q"), w.f32("k"), w.f32("v"), w.cu_seqlens_q,
+                                  w.cu_seqlens_k, w.scale, causal, window, w.sinks,
+                                  mask=inputs.bits_to_f32(mbits).astype(np.float64))
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
 F32_CASES = [
     # name, lens_q, lens_k, d, causal, window, sinks
     ("f32_q_lt_k", [7, 100, 33], [50, 300, 33], 64, True, (-1, -1), False),
