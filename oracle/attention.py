@@ -203,7 +203,7 @@ def gather_paged(cache, block_table, b, n, page_size):
 
 def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale,
                     causal=False, sinks=None, dv=None, batches=None, key_range=None, qv=None,
-                    only_qv=False):
+                    only_qv=False, mask=None):
     """Decode against a paged cache.         [MATE flash_attn_with_kvcache / MLA]
 
     q (B, Sq, Hq, D); k_cache (P, page, Hkv, D); v_cache (P, page, Hkv, Dv), or
@@ -221,7 +221,13 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
 
     key_range: optional (b -> (start, end)) restricting the keys to
     [start, end) of the full sequence (split mode); masks stay relative to the
-    full length. Returns O (B, Sq, Hq, Dv) and LSE (B, Hq, Sq).
+    full length.
+
+    mask: optional additive mask (B, Hm, Sq, L), Hm = 1 (all heads) or Hq, L
+    at least every cache_seqlens[b]: query token t of sequence b and head h
+    adds mask[b, h or 0, t, j] to its scaled score with key j
+    [MOJO flash_attention_split_kv input_mask_fn: additive mask values];
+    -inf removes the key. Returns O (B, Sq, Hq, Dv) and LSE (B, Hq, Sq).
     """
     if only_qv and qv is None:
         raise ValueError("only_qv needs qv")
@@ -254,7 +260,9 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
             else:
                 qh = np.concatenate([q[b, :, h], qv[b, :, h]], axis=-1)
                 kj = np.concatenate([kr[:, kh], vr[:, kh]], axis=-1)
-            ob, lb = attend_rows(qh, kj, vr[:, kh], scale, vis, sink)
+            bias = None if mask is None else \
+                np.asarray(mask[b, h if mask.shape[1] > 1 else 0, :, j0:j1], np.float64)
+            ob, lb = attend_rows(qh, kj, vr[:, kh], scale, vis, sink, bias)
             o[b, :, h] = ob
             lse[b, h] = lb
     return o, lse
@@ -358,13 +366,14 @@ def plan_unpack(plan, batch):
 
 
 def attention_paged_split(q, k_cache, v_cache, block_table, cache_seqlens, page_size, scale,
-                          plan, max_splits, causal=False, dv=None):
+                          plan, max_splits, causal=False, dv=None, mask=None):
     """Per-split partial results [MATE: partial outputs and LSE buffers].
 
     Split s of sequence b is plain attention restricted to its key range; its
     output is normalised within the split. Returns o_partial
     (B*max_splits, Sq*Hq, Dv) and lse_partial (B*max_splits, Sq*Hq), slot
-    b*max_splits + s, row t*Hq + h. Unused slots are NaN.
+    b*max_splits + s, row t*Hq + h. Unused slots are NaN. mask: as in
+    attention_paged (columns are key positions of the whole sequence).
     """
     bsz, sq, hq, _ = q.shape
     ptr, tri = plan_unpack(plan, bsz)
@@ -377,7 +386,8 @@ def attention_paged_split(q, k_cache, v_cache, block_table, cache_seqlens, page_
             assert tb == b
             o, lse = attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size,
                                      scale, causal, None, dv, batches=[b],
-                                     key_range=lambda _b, a=int(j0), e=int(j1): (a, e))
+                                     key_range=lambda _b, a=int(j0), e=int(j1): (a, e),
+                                     mask=mask)
             op[b * max_splits + s] = o[b].reshape(sq * hq, dv)
             lp[b * max_splits + s] = lse[b].transpose(1, 0).reshape(sq * hq)
     return op, lp

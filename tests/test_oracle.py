@@ -381,6 +381,71 @@ def test_additive_mask():
     check_additive_mask()
 
 
+def check_paged_mask():
+    """Additive mask on the paged decode [MOJO input_mask_fn]: zeros change
+    nothing; a constant c per (sequence, head) leaves O and adds c to LSE; a
+    shared plane equals the same plane repeated per head; a random mask with
+    -inf entries agrees with brute force over the rows gathered by explicit
+    page/slot loops; and split partials combined equal the unsplit result."""
+    p = inputs.paged(46, [13, 40, 1], sq=3, hq=4, hkv=2, d=8, page=8, causal=True)
+    q, kc, vc = (inputs.bits_to_f32(x) for x in (p.q, p.k_cache, p.v_cache))
+    bsz, sq, hq = q.shape[0], q.shape[1], q.shape[2]
+    ld = 48
+    args = (q, kc, vc, p.block_table, p.cache_seqlens, 8, p.scale, True)
+    base = orc.attention_paged(*args)
+    z = orc.attention_paged(*args, mask=np.zeros((bsz, 1, sq, ld)))
+    np.testing.assert_allclose(z[0], base[0], atol=0)
+    np.testing.assert_allclose(z[1], base[1], atol=0)
+    c = np.linspace(-1.25, 2.0, bsz * hq).reshape(bsz, hq)
+    sh = orc.attention_paged(*args, mask=c[:, :, None, None] * np.ones((bsz, hq, sq, ld)))
+    np.testing.assert_allclose(sh[0], base[0], atol=1e-13)
+    fin = np.isfinite(base[1])
+    np.testing.assert_allclose(sh[1][fin], (base[1] + c[:, :, None])[fin], atol=1e-13)
+    rng = _rng(47)
+    one = rng.standard_normal((bsz, 1, sq, ld))
+    a1 = orc.attention_paged(*args, mask=one)
+    a2 = orc.attention_paged(*args, mask=np.repeat(one, hq, axis=1))
+    np.testing.assert_allclose(a1[0], a2[0], atol=0)
+    np.testing.assert_allclose(a1[1], a2[1], atol=0)
+    m = rng.standard_normal((bsz, hq, sq, ld))
+    m[rng.random(m.shape) < 0.2] = -np.inf
+    o, lse = orc.attention_paged(*args, mask=m)
+    grp = hq // kc.shape[2]
+    for b in range(bsz):
+        n = int(p.cache_seqlens[b])
+        for h in range(hq):
+            g = h // grp
+            # Python floats throughout (float32 scalars would keep float32 products)
+            keys = [kc[p.block_table[b, j // 8], j % 8, g].tolist() for j in range(n)]
+            vals = [vc[p.block_table[b, j // 8], j % 8, g].tolist() for j in range(n)]
+            for t in range(sq):
+                qt = q[b, t, h].tolist()
+                w = [math.exp(p.scale * math.fsum(x * y for x, y in zip(qt, keys[j]))
+                              + m[b, h, t, j])
+                     if j <= t + n - sq and np.isfinite(m[b, h, t, j]) else 0.0
+                     for j in range(n)]
+                tot = math.fsum(w)
+                if tot == 0.0:
+                    assert np.isneginf(lse[b, h, t])
+                    continue
+                assert abs(lse[b, h, t] - math.log(tot)) <= 1e-12
+                ref = [math.fsum(w[j] * vals[j][e] for j in range(n)) / tot
+                       for e in range(vc.shape[3])]
+                np.testing.assert_allclose(o[b, t, h], ref, rtol=0, atol=1e-12)
+    # split partials combined equal the unsplit masked decode
+    plan = orc.plan_splits(p.cache_seqlens, 8, 2, 4, 8, 4, 1)
+    op, lp = orc.attention_paged_split(q, kc, vc, p.block_table, p.cache_seqlens, 8, p.scale,
+                                       plan, 4, True, mask=m)
+    ptr, _ = orc.plan_unpack(plan, bsz)
+    oc, lc = orc.combine(op, lp, ptr, bsz, sq, hq, 4)
+    np.testing.assert_allclose(oc, o, atol=1e-12)
+    np.testing.assert_allclose(lc, lse, atol=1e-12)
+
+
+def test_paged_mask():
+    check_paged_mask()
+
+
 def test_kvcache_brute_force():
     check_kvcache_brute_force()
 
@@ -1001,6 +1066,12 @@ def _mutants():
 
     base_paged = orc.attention_paged
 
+    def paged_mask_shifted(*args, mask=None, **kw):
+        # the decode mask read one key column late
+        if mask is not None:
+            mask = np.roll(np.asarray(mask, np.float64), -1, axis=3)
+        return base_paged(*args, mask=mask, **kw)
+
     def qv_against_k(q, k_cache, v_cache, *rest, qv=None, only_qv=False, **kw):
         # qv scored against the key rows: q . k + qv . k = (q + qv) . k
         if qv is None:
@@ -1033,7 +1104,7 @@ def _mutants():
         return base_varlen(q + qv, k, v, cu_seqlens_q, cu_seqlens_k, scale, causal, window,
                            sinks, seqs, mask)
 
-    return [("attention_varlen", varlen_qv_against_k),
+    return [("attention_paged", paged_mask_shifted), ("attention_varlen", varlen_qv_against_k),
             ("attention_paged", qv_against_k), ("attention_paged", qv_unscaled),
             ("sparse_block_keys", block_keys_unscaled), ("attend_rows", bias_scaled),
             ("attend_rows", no_scale), ("attend_rows", sink_dropped),
@@ -1047,10 +1118,10 @@ PINS = [check_golden, check_rows_sum_to_one, check_lse_identity, check_identical
         check_single_key, check_sink, check_split_combine, check_gqa_equals_mha,
         check_varlen_equals_dense, check_paged_equals_contiguous, check_gather, check_sparse,
         check_brute_force, check_kvcache_brute_force, check_kvcache_special_cases,
-        check_sparse_paged, check_additive_mask, check_qv, check_qv_varlen]
+        check_sparse_paged, check_additive_mask, check_qv, check_qv_varlen, check_paged_mask]
 
 
-@pytest.mark.parametrize("i", range(14))
+@pytest.mark.parametrize("i", range(15))
 def test_pins_catch_planted_mistakes(monkeypatch, i):
     name, fn = _mutants()[i]
     monkeypatch.setattr(orc, name, fn)
