@@ -51,6 +51,10 @@ _SIGNATURES = {
     "attn_plan_splits": (_I, [_P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                                _P, _I, _P, _P, _P]),
+    # q, k_cache, v_cache, block_table, max_pages, lens, batch, sq, hq, hkv, d, dv, page, scale,
+    # causal, mask, mask_heads, mask_ld, plan, max_splits, o_part, lse_part, stream
+    "attn_decode_paged_mask": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                                    _P, _I, _I, _P, _I, _P, _P, _P]),
     "attn_decode_paged_fp8": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                    _P, _P, _F, _I, _P, _I, _P, _P, _P]),
     "attn_decode_paged_qv": (_I, [_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _I,
@@ -371,11 +375,13 @@ def attn_device_info(device=0):
 
 # --------------------------------------------------------------------- decode
 def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
-                      scale=None, causal=False, o_partial=None, lse_partial=None):
+                      scale=None, causal=False, o_partial=None, lse_partial=None, mask=None):
     """q (B,Sq,Hq,D), caches (P,page,Hkv,D|Dv) bf16. Returns partials
     (B*max_splits, Sq*Hq, Dv) and (B*max_splits, Sq*Hq) fp32. With D = 576
-    (MLA rows) v_cache is None and Dv = 512, the first entries of each row."""
-    _dev(q, k_cache, v_cache, dtype=torch.bfloat16)
+    (MLA rows) v_cache is None and Dv = 512, the first entries of each row.
+    mask: None or an additive bf16 mask (B, 1 or Hq, Sq, ld), ld a multiple
+    of 64 and >= every cache length (attn_decode_paged_mask)."""
+    _dev(q, k_cache, v_cache, mask, dtype=torch.bfloat16)
     _dev(block_table, cache_seqlens, plan, dtype=torch.int32)
     b, sq, hq, d = q.shape
     page, hkv = k_cache.shape[1], k_cache.shape[2]
@@ -386,6 +392,15 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max
     if lse_partial is None:
         lse_partial = torch.empty((b * max_splits, sq * hq), dtype=torch.float32, device=q.device)
     _dev(o_partial, lse_partial, dtype=torch.float32)
+    if mask is not None:
+        if mask.dim() != 4 or mask.shape[0] != b or mask.shape[2] != sq:
+            raise ValueError("mask must be (B, 1 or Hq, Sq, ld)")
+        _check(load().attn_decode_paged_mask(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+            _ptr(cache_seqlens), b, sq, hq, hkv, d, dv, page, _scale(scale, q),
+            int(bool(causal)), _ptr(mask), mask.shape[1], mask.shape[3], _ptr(plan),
+            int(max_splits), _ptr(o_partial), _ptr(lse_partial), _stream()))
+        return o_partial, lse_partial
     _check(load().attn_decode_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                     block_table.shape[1], _ptr(cache_seqlens), b, sq, hq, hkv, d,
                                     dv, page, ATTN_BF16, _scale(scale, q), int(bool(causal)),
@@ -630,9 +645,10 @@ def _num_cu(device):
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, causal=False,
                  sinks=None, max_splits=GQA_DECODE_PLAN[0], waves=GQA_DECODE_PLAN[1],
-                 min_blocks=GQA_DECODE_PLAN[2], num_cu=None, out_dtype=torch.bfloat16):
-    """plan -> attn_decode_paged -> attn_combine. Returns (out (B,Sq,Hq,Dv),
-    lse (B,Hq,Sq), plan)."""
+                 min_blocks=GQA_DECODE_PLAN[2], num_cu=None, out_dtype=torch.bfloat16,
+                 mask=None):
+    """plan -> attn_decode_paged (or attn_decode_paged_mask) -> attn_combine.
+    Returns (out (B,Sq,Hq,Dv), lse (B,Hq,Sq), plan)."""
     b, sq, hq, _ = q.shape
     hkv = k_cache.shape[2]
     rows = sq * (hq // max(1, hkv))
@@ -640,7 +656,7 @@ def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, ca
     plan = attn_plan_splits(cache_seqlens, k_cache.shape[1], upb, num_cu or _num_cu(q.device),
                             waves, max_splits, min_blocks)
     op, lp = attn_decode_paged(q, k_cache, v_cache, block_table, cache_seqlens, plan, max_splits,
-                               scale, causal)
+                               scale, causal, mask=mask)
     out, lse = attn_combine(op, lp, plan, b, sq, hq, max_splits, sinks, out_dtype)
     return out, lse, plan
 

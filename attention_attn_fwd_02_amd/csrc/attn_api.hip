@@ -514,6 +514,51 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
   return hip_status(attn::launch_decode_gqa(a, d, as_stream(stream)), "attn_decode_paged launch");
 }
 
+int32_t attn_decode_paged_mask(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                               int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                               float scale, int32_t causal, const void* mask, int32_t mask_heads,
+                               int32_t mask_ld, const int32_t* plan, int32_t max_splits,
+                               float* o_partial, float* lse_partial, void* stream) {
+  const int32_t st = attn::check_decode_args(q, k_cache, v_cache, block_table,
+                                             max_pages_per_seq, cache_seqlens, batch, seqlen_q,
+                                             hq, hkv, d, dv, page_size, ATTN_BF16, scale,
+                                             max_splits);
+  if (st != ATTN_OK) return st;
+  REQUIRE(d == dv && (d == 64 || d == 128) && v_cache, ATTN_EUNSUPPORTED,
+          "the decode mask supports d == dv in {64, 128} with a separate V cache");
+  REQUIRE(plan && o_partial && lse_partial && mask, ATTN_EINVAL, "null tensor pointer");
+  REQUIRE(aligned16(o_partial, mask), ATTN_EINVAL, "tensor pointers must be 16-byte aligned");
+  REQUIRE(mask_heads == 1 || mask_heads == hq, ATTN_EINVAL,
+          "mask_heads must be 1 or hq (got %d)", mask_heads);
+  REQUIRE(mask_ld > 0 && mask_ld % 64 == 0, ATTN_EINVAL,
+          "mask_ld must be a positive multiple of 64 (got %d)", mask_ld);
+  attn::DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.block_table = block_table;
+  a.lens = cache_seqlens;
+  a.plan = plan;
+  a.max_pages = max_pages_per_seq;
+  a.batch = batch;
+  a.sq = seqlen_q;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.page = page_size;
+  a.causal = causal ? 1 : 0;
+  a.max_splits = max_splits;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.o_part = o_partial;
+  a.lse_part = lse_partial;
+  a.mask = mask;
+  a.mask_heads = mask_heads;
+  a.mask_ld = mask_ld;
+  return hip_status(attn::launch_decode_gqa(a, d, as_stream(stream)),
+                    "attn_decode_paged_mask launch");
+}
+
 int32_t attn_decode_paged_fp8(const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_table, int32_t max_pages_per_seq,
                               const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,

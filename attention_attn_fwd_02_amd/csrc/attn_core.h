@@ -60,14 +60,19 @@ struct DmaSrc {
 //
 // BN: keys per tile, 32, or a multiple of 32 for FP8 tiles (whose rows are
 // half as wide, so 64 keys move the bytes of a 32-key bf16 tile).
+//
+// MASK: an additive bf16 mask tile (16 rows x BN keys, row-major) follows K
+// and V in each stage, brought in by one more DMA instruction per tile; it is
+// added to the scaled scores before the softmax (one wave, bf16 only).
 template <int D_, int DV_, int NW_, int STAGES_, bool VSHARED_, int DSPLIT_ = 1, int FP8_ = 0,
-          int QV_ = 0, int BN_ = 32>
+          int QV_ = 0, int BN_ = 32, bool MASK_ = false>
 struct StreamCfg {
   static constexpr int D = D_, DV = DV_, NW = NW_, STAGES = STAGES_;
   static constexpr bool VSHARED = VSHARED_;
   static constexpr int DSPLIT = DSPLIT_;
   static constexpr int FP8 = FP8_;
   static constexpr int QV = QV_;
+  static constexpr bool MASK = MASK_;
   static constexpr int EB = FP8 ? 1 : 2;  // bytes per element in memory and LDS
   static constexpr int BN = BN_, R = 16;
   static constexpr int THREADS = NW * 64;
@@ -76,10 +81,13 @@ struct StreamCfg {
   static constexpr int NCH = D / 8;
   static constexpr int K_BYTES = QV == 2 ? 0 : BN * D * EB;
   static constexpr int V_BYTES = VSHARED ? 0 : BN * DV * EB;
-  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES;
+  static constexpr int MASK_BYTES = MASK ? R * BN * 2 : 0;
+  static constexpr int STAGE_BYTES = K_BYTES + V_BYTES + MASK_BYTES;
   static constexpr int K_DMA = K_BYTES / 1024;
   static constexpr int V_DMA = V_BYTES / 1024;
   static constexpr int DMA_PER_WAVE = (K_DMA + V_DMA) / DMA_WAVES;
+  // vector-memory instructions per wave per tile (the tile loop's vmcnt waits)
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE + (MASK ? 1 : 0);
   static constexpr int NQ = D / 32 / DSPLIT;    // Q fragments held per wave
   static constexpr int NSB = BN / 16;           // S^T blocks per tile
   static constexpr int NOB = DV / 16 / DSPLIT;  // O^T blocks held per wave
@@ -90,7 +98,9 @@ struct StreamCfg {
   static_assert((K_DMA + V_DMA) % DMA_WAVES == 0, "tile DMA must split evenly over the waves");
   static_assert(VSHARED || (NCH / 2) % 4 == 0, "V layout needs whole instructions per row block");
   static_assert(VSHARED ? DV <= D : DV == D, "value width");
-  static_assert(DMA_PER_WAVE * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(VM_PER_TILE * (STAGES - 1) < 64, "vmcnt range");
+  static_assert(!MASK || (NW == 1 && FP8 == 0 && QV == 0 && BN == 32 && !VSHARED),
+                "decode mask: one wave, bf16 K and V, 32-key tiles");
   static_assert(FP8 == 0 || (D == 128 && DV == 128 && !VSHARED && DSPLIT == 1),
                 "FP8 tiles: D = Dv = 128, separate V, whole head per wave");
   static_assert(QV == 0 || (!VSHARED && DSPLIT == 1 && DV == D), "qv: separate V, Dv = D");
@@ -437,6 +447,23 @@ struct StreamTile {
     }
   }
 
+  // MASK: s = s * cscale + mask * log2(e) from the stage's mask tile, whose
+  // row r (this lane's row, lane % 16) holds the tile's keys 0..BN-1; the
+  // scores are then in the scaled domain (softmax with cscale = 1).
+  __device__ __forceinline__ static void add_mask(f32x4 (&s)[C::NSB], const char* mbuf,
+                                                  float cscale, int lane) {
+    const char* mrow = mbuf + (lane & 15) * (C::BN * 2) + (lane >> 4) * 8;
+#pragma unroll
+    for (int sb = 0; sb < C::NSB; ++sb) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(mrow + sb * 32);  // keys 16 sb + 4 g ..
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+        s[sb][e] = __builtin_fmaf(s[sb][e], cscale, __builtin_bit_cast(float, bits) * kLog2e);
+      }
+    }
+  }
+
   // Masks the scores of tile-relative keys j with !vis(j).
   template <class Vis>
   __device__ __forceinline__ static void mask(f32x4 (&s)[C::NSB], int lane, Vis vis) {
@@ -571,7 +598,7 @@ struct StreamTile {
 
 // Streams tiles [0, ntiles) through the LDS ring `ring` (STAGES buffers of
 // STAGE_BYTES). issue(stage_ptr, t) enqueues the DMA of tile t; compute(t,
-// stage_ptr) consumes it. Exactly DMA_PER_WAVE DMA instructions per wave per
+// stage_ptr) consumes it. Exactly VM_PER_TILE DMA instructions per wave per
 // tile must be issued by issue(). Waits only for the tile about to be read.
 template <class C, class Issue, class Compute>
 __device__ __forceinline__ void stream_tiles(char* ring, int ntiles, Issue issue, Compute compute) {
@@ -583,11 +610,11 @@ __device__ __forceinline__ void stream_tiles(char* ring, int ntiles, Issue issue
     // tiles issued after tile i: min(ntiles-1-i, STAGES-2)
     const int after = min(ntiles - 1 - i, C::STAGES - 2);
     if constexpr (C::STAGES >= 4) {
-      if (after >= 2) wait_vmcnt<2 * C::DMA_PER_WAVE>();
-      else if (after == 1) wait_vmcnt<C::DMA_PER_WAVE>();
+      if (after >= 2) wait_vmcnt<2 * C::VM_PER_TILE>();
+      else if (after == 1) wait_vmcnt<C::VM_PER_TILE>();
       else wait_vmcnt<0>();
     } else if constexpr (C::STAGES == 3) {
-      if (after >= 1) wait_vmcnt<C::DMA_PER_WAVE>();
+      if (after >= 1) wait_vmcnt<C::VM_PER_TILE>();
       else wait_vmcnt<0>();
     } else {
       wait_vmcnt<0>();

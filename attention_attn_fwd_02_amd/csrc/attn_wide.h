@@ -40,6 +40,7 @@ struct WideCfg {
   static constexpr int K_DMA = K_BYTES / 1024;
   static constexpr int DMA_WAVES = NW / DSPLIT;
   static constexpr int DMA_PER_WAVE = K_DMA / DMA_WAVES;
+  static constexpr int VM_PER_TILE = DMA_PER_WAVE;  // vector-memory instructions per tile
   static constexpr int NQ = D / 16 / DSPLIT;    // Q fragments (16 head dims each) per wave
   static constexpr int NOB = DV / 32 / DSPLIT;  // 32-column O^T blocks per wave
   static constexpr int XCHG_BYTES = NW * 4 * 64 * 16;  // [wave][quarter][lane] x f32x4

@@ -110,6 +110,16 @@ k_decode(DecodeArgs a) {
     klane = T::k_lane_off(lane, (uint32_t)tok_k);
     vlane = T::v_lane_off(lane, (uint32_t)tok_v);
   }
+  // MASK: the DMA lane's mask row (tile row lane / 4, rows past the tile's
+  // last real row re-read that row); the lane reads keys 8 (lane % 4) .. +7
+  // of the tile
+  const char* mrow = nullptr;
+  if constexpr (C::MASK) {
+    const int rr = min(mt * C::ROWS + (lane >> 2), nrows - 1);
+    const int hm = a.mask_heads > 1 ? kvh * grp + rr % grp : 0;
+    mrow = static_cast<const char*>(a.mask) +
+           (((size_t)b * a.mask_heads + hm) * a.sq + rr / grp) * a.mask_ld * 2;
+  }
   auto issue = [&](char* st, int ti) {
     // A 16-row block of a tile lies on one page (pages are multiples of 16
     // rows and splits start on page boundaries). sl[k]: cache slot of tile
@@ -152,6 +162,15 @@ k_decode(DecodeArgs a) {
             [&](int rr) { return reinterpret_cast<const bf16_t*>(vcb + row(rr) * tok_v); }, wave,
             lane);
     }
+    // mask columns j0 .. j0 + BN - 1. Tiles start at multiples of 16, so a
+    // segment of the last tile can start at mask_ld (>= the sequence's
+    // length, a multiple of 64) or later; such a segment holds keys past the
+    // length only and re-reads the row's last segment instead (its values
+    // are masked out).
+    if constexpr (C::MASK) {
+      const int col = min(j0 + 8 * (fresh_lane() & 3), a.mask_ld - 8);
+      lds_dma16(mrow + (size_t)col * 2, st + C::K_BYTES + C::V_BYTES);
+    }
   };
   const int first_t = (mt * C::ROWS) / grp;
   const int ntiles = (kv1 - kv0 + C::BN - 1) / C::BN;
@@ -182,10 +201,15 @@ k_decode(DecodeArgs a) {
     tile.qk(st, lane, sc);
     tile.qv_scores(st, lane, sc, qv_ratio);
     tile.exchange(xchg, wave, lane, sc);
+    float cs = cscale;
+    if constexpr (C::MASK) {
+      T::add_mask(sc, st + C::K_BYTES + C::V_BYTES, cscale, lane);
+      cs = 1.f;  // the scores are scaled
+    }
     const int hi_vis = a.causal ? min(kv1 - 1, tq + delta) : kv1 - 1;
     if (need) T::mask(sc, lane, [&](int jr) { return j0 + jr <= hi_vis; });
     uint32_t pk[C::NSB * 2];
-    tile.softmax(sc, cscale, pk);
+    tile.softmax(sc, cs, pk);
     tile.pv(st, lane, pk);
   });
 
@@ -434,8 +458,8 @@ k_sparse(SparseArgs a) {
   }
 }
 
-template <int QV = 0, int D = 128>
-using CfgDecodeGqa = StreamCfg<D, D, 1, 3, false, 1, 0, QV>;
+template <int QV = 0, int D = 128, bool MASK = false>
+using CfgDecodeGqa = StreamCfg<D, D, 1, 3, false, 1, 0, QV, 32, MASK>;
 // FP8 tiles of 64 keys: the bytes of a 32-key bf16 tile
 template <int FMT, int QV = 0>
 using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 64>;
@@ -450,7 +474,14 @@ hipError_t launch_decode_gqa(const DecodeArgs& a, int d, hipStream_t s) {
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
   const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
   static_assert(CfgDecodeGqa<0, 64>::ROWS == C::ROWS, "one grid for both head dims");
-  if (d == 64)
+  if (a.mask) {
+    if (d == 64)
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 64, true>>), dim3(grid), dim3(C::THREADS), 0, s,
+                         a);
+    else
+      hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 128, true>>), dim3(grid), dim3(C::THREADS), 0,
+                         s, a);
+  } else if (d == 64)
     hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 64>>), dim3(grid), dim3(C::THREADS), 0, s, a);
   else if (a.qv && a.only_qv)
     hipLaunchKernelGGL(k_decode<CfgDecodeGqa<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);

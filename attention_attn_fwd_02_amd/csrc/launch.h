@@ -62,6 +62,10 @@ struct DecodeArgs {
   // only_qv: that score path alone (q and the K cache are not read)
   const void* qv;
   int32_t only_qv;
+  // additive bf16 mask (batch, mask_heads, sq, mask_ld) over the cache keys,
+  // or NULL
+  const void* mask;
+  int32_t mask_heads, mask_ld;
   // gather test: the DUMP instances copy every staged tile to dump_k / dump_v
   // (key rows of sequence b at row b * dump_rows + key, heads interleaved)
   void* dump_k;

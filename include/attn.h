@@ -305,6 +305,33 @@ int32_t attn_decode_paged(const void* q, const void* k_cache, const void* v_cach
                           void* stream);
 
 /*
+ * attn_decode_paged_mask - attn_decode_paged (bfloat16, GQA) with an
+ * additive mask on the scores.
+ * [Modular flash_attention_split_kv: input_mask_fn loads additive mask
+ *  values; MATE flash_attn_with_kvcache: paged k_cache / v_cache]
+ *
+ *  Arguments as attn_decode_paged with dtype bfloat16, plus
+ *  mask: bf16 (batch, mask_heads, seqlen_q, mask_ld), 16-byte aligned: query
+ *      token t of sequence b and head h add mask[b][h or 0][t][j] to the
+ *      scaled score with cached key j (0 <= j < cache_seqlens[b]); -inf
+ *      removes the key. Added after the causal mask; partials and the
+ *      combine as attn_decode_paged.
+ *  mask_heads: 1 (shared by all heads) or hq.
+ *  mask_ld: a multiple of 64; the caller keeps it >= every cache_seqlens[b]
+ *      (columns up to cache_seqlens[b] rounded up to 32 are read; device
+ *      values are not checked).
+ *  Supported: d = dv in {64, 128}, separate V cache. Errors: EINVAL for a
+ *  NULL mask or the mask arguments above, the rest as attn_decode_paged.
+ */
+int32_t attn_decode_paged_mask(const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* cache_seqlens, int32_t batch, int32_t seqlen_q,
+                               int32_t hq, int32_t hkv, int32_t d, int32_t dv, int32_t page_size,
+                               float scale, int32_t causal, const void* mask, int32_t mask_heads,
+                               int32_t mask_ld, const int32_t* plan, int32_t max_splits,
+                               float* o_partial, float* lse_partial, void* stream);
+
+/*
  * attn_decode_paged_fp8 - attn_decode_paged with FP8 query and cache.
  * [MATE "Attention" page, FMHA forward dtype notes: float8_e4m3fn and
  *  float8_e5m2 inputs of flash_attn_with_kvcache; optional float32 q_descale,

@@ -163,6 +163,25 @@ def test_decode_host_checks(lib):
     assert call(d=576, dv=512, vc=None, bt=None) == B.ATTN_EINVAL
 
 
+def test_decode_mask_host_checks(lib):
+    def call(**kw):
+        a = dict(q=P, kc=P, vc=P, bt=P, mp=4, lens=P, batch=2, sq=1, hq=8, hkv=2, d=128, dv=128,
+                 page=64, scale=0.1, causal=0, mask=P, mh=1, mld=128, plan=P, ms=4)
+        a.update(kw)
+        return lib.attn_decode_paged_mask(
+            a["q"], a["kc"], a["vc"], a["bt"], a["mp"], a["lens"], a["batch"], a["sq"], a["hq"],
+            a["hkv"], a["d"], a["dv"], a["page"], a["scale"], a["causal"], a["mask"], a["mh"],
+            a["mld"], a["plan"], a["ms"], P, P, None)
+    assert call(mask=None) == B.ATTN_EINVAL
+    assert call(mh=3) == B.ATTN_EINVAL
+    assert call(mld=96) == B.ATTN_EINVAL
+    assert call(plan=None) == B.ATTN_EINVAL
+    assert call(batch=0) == B.ATTN_EEMPTY
+    assert call(d=576, dv=512, vc=None) == B.ATTN_EUNSUPPORTED
+    assert b"decode mask" in lib.attn_last_error()
+    assert call(d=96, dv=96) == B.ATTN_EUNSUPPORTED
+
+
 def test_decode_fp8_host_checks(lib):
     def call(**kw):
         a = dict(q=P, kc=P, vc=P, bt=P, mp=4, lens=P, batch=2, sq=1, hq=32, hkv=8, d=128, dv=128,

@@ -97,6 +97,39 @@ def test_decode_gqa(case):
     assert np.array_equal(host(plan)[:n], ref_plan[:n])
 
 
+DECODE_MASK_CASES = [
+    # name, lens, sq, hq, hkv, d, page, causal, mask_heads, neg_inf_fraction, plan
+    ("mask_heads_d128", [1, 63, 700, 2049], 1, 32, 8, 128, 64, False, 32, 0.0, (16, 4, 4)),
+    ("mask_shared_neginf_causal_sq3", [90, 400, 3], 3, 16, 4, 128, 16, True, 1, 0.2, (8, 16, 1)),
+    ("mask_d64_gqa8_many_splits", [5000, 130, 17], 2, 16, 2, 64, 32, True, 16, 0.1,
+     (16, 64, 1)),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_MASK_CASES, ids=[c[0] for c in DECODE_MASK_CASES])
+def test_decode_additive_mask(case):
+    """attn_decode_paged_mask through plan, split decode and combine: an
+    additive bf16 mask (N(0, 2^2) with a share of -inf entries) per head or
+    shared, with ragged lengths, page sizes and plans of many short splits."""
+    name, lens, sq, hq, hkv, d, page, causal, mh, frac, (ms, waves, mb) = case
+    log("case decode_mask", name)
+    w = inputs.paged(5300 + len(name), lens, sq=sq, hq=hq, hkv=hkv, d=d, page=page,
+                     causal=causal)
+    ld = ((max(lens) + 63) // 64) * 64
+    rng = np.random.default_rng(5400 + len(name))
+    m = (2.0 * rng.standard_normal((len(lens), mh, sq, ld))).astype(np.float32)
+    m[rng.random(m.shape) < frac] = -np.inf
+    mbits = inputs.bf16_bits(m)
+    o, lse, _ = B.paged_decode(dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_table),
+                               dev(w.cache_seqlens), w.scale, w.causal, None, max_splits=ms,
+                               waves=waves, min_blocks=mb, mask=dev(mbits))
+    torch.cuda.synchronize()
+    q, kc, vc = (inputs.bits_to_f32(x) for x in (w.q, w.k_cache, w.v_cache))
+    ro, rl = orc.attention_paged(q, kc, vc, w.block_table, w.cache_seqlens, w.page_size, w.scale,
+                                 w.causal, mask=inputs.bits_to_f32(mbits).astype(np.float64))
+    compare(name, o, lse, ro, rl, TOL_O_BF16)
+
+
 NAN_BF16 = np.uint16(0x7FC0)
 
 
