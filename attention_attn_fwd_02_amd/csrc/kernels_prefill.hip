@@ -395,18 +395,30 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   float (*vw)[D] = vs[wave];
   for (int j0 = bd.lo + wave * C::BN; j0 < bd.hi; j0 += C::NW * C::BN) {
     // this wave's tile; only this wave reads it, so the wave's own ordering
-    // of LDS operations (and the compiler barrier) is the only sync needed
-    for (int e = lane; e < C::BN * D / 4; e += 64) {
+    // of LDS operations (and the compiler barrier) is the only sync needed.
+    // All of a lane's loads are issued before its first store, so the tile
+    // costs one memory latency, not one per 16-byte element.
+    constexpr int PER_LANE = C::BN * D / 4 / 64;
+    f32x4 kv[PER_LANE], vv[PER_LANE];
+#pragma unroll
+    for (int n = 0; n < PER_LANE; ++n) {
+      const int e = lane + 64 * n;
       const int r = e / (D / 4), c = (e % (D / 4)) * 4;
       const int j = j0 + r;
-      f32x4 kv = {0.f, 0.f, 0.f, 0.f}, vv = kv;
+      kv[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      vv[n] = kv[n];
       if (j < lk) {
         const size_t off = ((size_t)(k0 + j) * a.hkv + w.kvh) * D + c;
-        kv = *reinterpret_cast<const f32x4*>(kg + off);
-        vv = *reinterpret_cast<const f32x4*>(vg + off);
+        kv[n] = *reinterpret_cast<const f32x4*>(kg + off);
+        vv[n] = *reinterpret_cast<const f32x4*>(vg + off);
       }
-      *reinterpret_cast<f32x4*>(&kw[r][c]) = kv;
-      *reinterpret_cast<f32x4*>(&vw[r][c]) = vv;
+    }
+#pragma unroll
+    for (int n = 0; n < PER_LANE; ++n) {
+      const int e = lane + 64 * n;
+      const int r = e / (D / 4), c = (e % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(&kw[r][c]) = kv[n];
+      *reinterpret_cast<f32x4*>(&vw[r][c]) = vv[n];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
