@@ -302,10 +302,16 @@ def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cac
                             np.asarray(cu, np.int64), scale, causal, window, sinks, seqs, mask)
 
 
+# Plans of at most this many splits carry a longest-first work order; larger
+# ones keep the splits in batch order.
+PLAN_SORT_MAX = 4096
+
+
 def plan_words(batch, max_splits):
-    """int32 words of a plan buffer: header (2), split_ptr (B+1) and up to
-    B*max_splits (batch, kv_start, kv_end) triples."""
-    return 3 + batch + 3 * batch * max_splits
+    """int32 words of a plan buffer: header (2), split_ptr (B+1), up to
+    B*max_splits (batch, kv_start, kv_end) triples, then B*max_splits words of
+    work order."""
+    return 3 + batch + 4 * batch * max_splits
 
 
 def _cdiv(a, b):
@@ -326,10 +332,16 @@ def plan_splits(cache_seqlens, page_size, units_per_block, num_cu, waves, max_sp
       pps_b  = ceil(nblk_b / ns_b);  ns_b = ceil(nblk_b / pps_b)
       split s of b covers tokens [s*pps_b*page, min((s+1)*pps_b*page, len_b))
     Empty sequences get no split.
+    Work order (the order in which decode workgroups take the splits): by
+    length kv_end - kv_start, longest first, ties in split order (the
+    longest-processing-time rule of list scheduling); the identity when
+    there are more than PLAN_SORT_MAX splits.
 
     Returns the int32 plan: [total_splits, bps, split_ptr[0..B],
-    (batch, kv_start, kv_end) per split in batch order]; the buffer is
-    plan_words(B, max_splits) long and words past the last triple are 0.
+    (batch, kv_start, kv_end) per split in batch order, padded to
+    B*max_splits triples, then the work order (split indices) padded to
+    B*max_splits words]; the buffer is plan_words(B, max_splits) long and
+    padding words are 0.
     """
     lens = [max(0, int(x)) for x in cache_seqlens]
     bsz = len(lens)
@@ -353,7 +365,20 @@ def plan_splits(cache_seqlens, page_size, units_per_block, num_cu, waves, max_sp
     plan[2:3 + bsz] = ptr
     if triples:
         plan[3 + bsz:3 + bsz + 3 * len(triples)] = np.asarray(triples, dtype=np.int32).ravel()
+    n = len(triples)
+    if n <= PLAN_SORT_MAX:
+        order = sorted(range(n), key=lambda i: (-(triples[i][2] - triples[i][1]), i))
+    else:
+        order = list(range(n))
+    base = 3 + bsz + 3 * bsz * max_splits
+    plan[base:base + n] = order
     return plan
+
+
+def plan_order(plan, batch, max_splits):
+    """The work order (split indices, length total_splits) of a plan buffer."""
+    base = 3 + batch + 3 * batch * max_splits
+    return np.asarray(plan[base:base + int(plan[0])])
 
 
 def plan_unpack(plan, batch):

@@ -945,6 +945,18 @@ def _check_plan(plan, lens, page, max_splits):
     bsz = len(lens)
     ptr, tri = orc.plan_unpack(plan, bsz)
     assert ptr[0] == 0 and ptr[-1] == plan[0] == len(tri)
+    assert len(plan) == 3 + bsz + 4 * bsz * max_splits
+    # work order: a permutation of the splits, lengths non-increasing, ties
+    # in split order (identity above PLAN_SORT_MAX splits)
+    order = orc.plan_order(plan, bsz, max_splits)
+    assert sorted(order.tolist()) == list(range(len(tri)))
+    if len(tri) <= orc.PLAN_SORT_MAX:
+        ln = tri[order, 2] - tri[order, 1]
+        assert (ln[:-1] >= ln[1:]).all()
+        eq = ln[:-1] == ln[1:]
+        assert (order[:-1][eq] < order[1:][eq]).all()
+    else:
+        assert (order == np.arange(len(tri))).all()
     for b, n in enumerate(lens):
         ns = ptr[b + 1] - ptr[b]
         assert 0 <= ns <= max_splits
@@ -979,6 +991,28 @@ def test_planner_rule_example():
     plan = orc.plan_splits([1000, 64, 0], 64, 2, 4, 1, 3, 2)
     assert plan[:2 + 4 + 9].tolist() == [3, 9, 0, 2, 3, 3,
                                               0, 0, 512, 0, 512, 1000, 1, 0, 64]
+    assert orc.plan_order(plan, 3, 3).tolist() == [0, 1, 2]   # lengths 512, 488, 64
+
+
+def test_planner_order_example():
+    """Hand-worked work order: lens [70, 1000], page 64, units_per_block 2,
+    4 CUs x 1 wave, max 3 splits, min 2 blocks: nblk = [2, 16], total = 36,
+    bps = 9; sequence 0: one split [0,70); sequence 1: ns = 2, pps = 8,
+    splits [0,512) [512,1000). Split lengths 70, 512, 488 in plan order, so
+    the longest-first order is 1, 2, 0; the order section starts after the
+    3 * 2 * 3 triple words."""
+    plan = orc.plan_splits([70, 1000], 64, 2, 4, 1, 3, 2)
+    assert plan[:2 + 3 + 9].tolist() == [3, 9, 0, 1, 3, 0, 0, 70, 1, 0, 512, 1, 512, 1000]
+    assert plan[3 + 2 + 18:3 + 2 + 18 + 3].tolist() == [1, 2, 0]
+    assert (plan[3 + 2 + 18 + 3:] == 0).all() and len(plan) == 3 + 2 + 24
+
+
+def test_planner_order_identity_above_limit():
+    """More than PLAN_SORT_MAX splits: the work order is the plan order."""
+    lens = [1000 + 64 * (i % 7) for i in range(300)]
+    plan = orc.plan_splits(lens, 16, 1, 100000, 1, 16, 1)   # 14-16 splits per sequence
+    assert int(plan[0]) > orc.PLAN_SORT_MAX
+    _check_plan(plan, lens, 16, 16)
 
 
 # --------------------------------------------------------------- mutation test
