@@ -36,6 +36,57 @@ __device__ __forceinline__ bool decode_prefill_work(int p, int batch, int hq, in
   return true;
 }
 
+// Work order of the cache-plus-current kernels: sequences by their number of
+// keys (cache plus current rows, largest first), each sequence's query tiles
+// last to first, then its KV heads. Cache lengths vary widely between
+// sequences, so the qt-major order above would leave the longest items for
+// the end; taking them first is the longest-processing-time rule of list
+// scheduling (a list-schedule simulation of the chunked-prefill workload
+// over 768 workgroup slots: makespan 414 tiles against 482). The ranks are
+// computed by every workgroup from the lengths (batch <= kSortBatch; beyond
+// that the sequences keep their order). All threads take part (barriers).
+constexpr int kSortBatch = 256;
+
+struct SortScratch {
+  int key[kSortBatch];
+  int perm[kSortBatch];
+};
+
+__device__ __forceinline__ void sort_sequences(const VarlenArgs& a, SortScratch& ss, int tid,
+                                               int nthreads) {
+  const bool sorted = a.batch <= kSortBatch;
+  for (int b = tid; b < a.batch && sorted; b += nthreads)
+    ss.key[b] = a.cache_lens[b] + (a.cu_k[b + 1] - a.cu_k[b]);
+  __syncthreads();
+  for (int b = tid; b < a.batch && sorted; b += nthreads) {
+    const int kb = ss.key[b];
+    int r = 0;
+    for (int c = 0; c < a.batch; ++c) {
+      const int kc = ss.key[c];
+      r += (kc > kb || (kc == kb && c < b)) ? 1 : 0;
+    }
+    ss.perm[r] = b;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool decode_prefill_work_kvc(int p, const VarlenArgs& a,
+                                                        const SortScratch& ss, PrefillWork& w) {
+  const int grp = a.hq / a.hkv;
+  const int rest = (p / (8 * grp)) * 8 + (p & 7);
+  const int hg = (p >> 3) % grp;
+  const int logical = rest * grp + hg;
+  if (logical >= a.nqt * a.batch * a.hq) return false;
+  int t = logical / grp;
+  w.kvh = t % a.hkv;
+  t /= a.hkv;
+  w.qt = a.nqt - 1 - t % a.nqt;
+  const int r = t / a.nqt;
+  w.b = a.batch <= kSortBatch ? ss.perm[r] : r;
+  w.h = w.kvh * grp + hg;
+  return true;
+}
+
 int prefill_grid(int batch, int hq, int hkv, int nqt) {
   const int unit = 8 * (hq / hkv);
   const long total = (long)nqt * batch * hq;
@@ -92,7 +143,13 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   // ring of STAGES buffers, each one K tile, one V tile (and the mask tile)
   __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * STAGE];
   PrefillWork w;
-  if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
+  if constexpr (KVC && !DUMP) {
+    __shared__ SortScratch ss;
+    sort_sequences(a, ss, threadIdx.x, C::THREADS);
+    if (!decode_prefill_work_kvc(blockIdx.x, a, ss, w)) return;
+  } else {
+    if (!decode_prefill_work(blockIdx.x, a.batch, a.hq, a.hkv, a.nqt, w)) return;
+  }
   const int q0 = a.cu_q[w.b];
   const int lq = a.cu_q[w.b + 1] - q0;
   const int row0 = w.qt * C::ROWS;
