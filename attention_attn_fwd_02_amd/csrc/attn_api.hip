@@ -458,7 +458,7 @@ int32_t attn_fwd_varlen_kvcache_fp8(const void* q, const void* k, const void* v,
 
 size_t attn_plan_words(int32_t batch, int32_t max_splits) {
   if (batch <= 0 || max_splits <= 0) return 0;
-  return 3 + (size_t)batch + 3 * (size_t)batch * max_splits;
+  return 3 + (size_t)batch + 4 * (size_t)batch * max_splits;
 }
 
 int32_t attn_plan_splits(const int32_t* cache_seqlens, int32_t batch, int32_t page_size,

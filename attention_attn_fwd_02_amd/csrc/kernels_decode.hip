@@ -46,16 +46,18 @@ k_decode(DecodeArgs a) {
   const int grp = a.hq / a.hkv;
   const int nrows = a.sq * grp;
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
-  // Work items follow the plan's split list (batch-major, total = plan[0]):
-  // item = (split, kv head, row tile). Real items come first, so they spread
-  // over all XCDs; the row tiles of one (split, kv head) read the same keys
-  // and are placed on one XCD.
+  // Work items follow the plan's work order (splits longest first, total =
+  // plan[0]): item = (split, kv head, row tile). Real items come first, so
+  // they spread over all XCDs; the row tiles of one (split, kv head) read
+  // the same keys and are placed on one XCD.
   const int logical = xcd_group(blockIdx.x, mtiles);
   const int total = a.plan[0];
   if (logical >= total * a.hkv * mtiles) return;
   const int mt = logical % mtiles;
   const int kvh = (logical / mtiles) % a.hkv;
-  const int split = logical / (mtiles * a.hkv);
+  // the plan's work order: longest splits first
+  const int split =
+      a.plan[3 + a.batch + 3 * a.batch * a.max_splits + logical / (mtiles * a.hkv)];
   const int* tri = a.plan + 3 + a.batch + 3 * split;
   const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
   const int s = split - a.plan[2 + b];
@@ -242,7 +244,9 @@ k_decode_wide(DecodeArgs a) {
   if (logical >= total * a.hkv * mtiles) return;
   const int mt = logical % mtiles;
   const int kvh = (logical / mtiles) % a.hkv;
-  const int split = logical / (mtiles * a.hkv);
+  // the plan's work order: longest splits first
+  const int split =
+      a.plan[3 + a.batch + 3 * a.batch * a.max_splits + logical / (mtiles * a.hkv)];
   const int* tri = a.plan + 3 + a.batch + 3 * split;
   const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
   const int s = split - a.plan[2 + b];

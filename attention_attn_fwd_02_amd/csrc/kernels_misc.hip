@@ -7,6 +7,8 @@ namespace attn {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+// plans of at most this many splits get a longest-first work order
+constexpr int kPlanSortMax = 4096;
 
 __device__ __forceinline__ int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
@@ -17,12 +19,20 @@ __device__ __forceinline__ int cdiv(long a, long b) { return (int)((a + b - 1) /
 //   bps    = max(min_blocks, ceil(sum nblk_b * upb / (num_cu * waves)))
 //   ns_b   = min(max_splits, max(1, ceil(nblk_b / bps)))
 //   pps_b  = ceil(nblk_b / ns_b), ns_b = ceil(nblk_b / pps_b)
-// One workgroup; each thread owns a contiguous run of sequences.
+// One workgroup; each thread owns a contiguous run of sequences. The work
+// order after the triples lists the splits longest first (ties in split
+// order): the decode workgroups take splits in that order, the
+// longest-processing-time rule of list scheduling. The keys ((2^31 - 1 -
+// length) << 32 | index) are unique, so the result does not depend on how
+// they are sorted: by rank (one split per thread) up to kPlanThreads
+// splits, by a bitonic network in LDS up to kPlanSortMax.
 __global__ void __launch_bounds__(kPlanThreads)
 k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_cu, int waves,
        int max_splits, int min_blocks, int32_t* __restrict__ plan) {
   __shared__ long red[kPlanThreads];
   __shared__ int scan[kPlanThreads];
+  __shared__ __attribute__((aligned(16))) unsigned long long skey[kPlanSortMax];
+
   const int tid = threadIdx.x;
   const int per = (batch + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
@@ -55,6 +65,8 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
     __syncthreads();
   }
   int ptr = scan[tid] - mine;
+  const int total = scan[kPlanThreads - 1];
+  const bool sort = total <= kPlanSortMax;
   int32_t* split_ptr = plan + 2;
   int32_t* tri = plan + 3 + batch;
   for (int b = b0; b < b1; ++b) {
@@ -66,9 +78,13 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
       const int pps = cdiv(nb, ns);
       ns = cdiv(nb, pps);
       for (int s = 0; s < ns; ++s) {
+        const int kv0 = s * pps * page, kv1 = min((s + 1) * pps * page, len);
         tri[3 * (ptr + s)] = b;
-        tri[3 * (ptr + s) + 1] = s * pps * page;
-        tri[3 * (ptr + s) + 2] = min((s + 1) * pps * page, len);
+        tri[3 * (ptr + s) + 1] = kv0;
+        tri[3 * (ptr + s) + 2] = kv1;
+        if (sort)
+          skey[ptr + s] = ((unsigned long long)(0x7FFFFFFF - (kv1 - kv0)) << 32) |
+                          (unsigned)(ptr + s);
       }
       ptr += ns;
     }
@@ -77,6 +93,54 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
     split_ptr[batch] = scan[tid];
     plan[0] = scan[tid];
     plan[1] = bps;
+  }
+  int32_t* order = plan + 3 + batch + 3 * batch * max_splits;
+  if (sort && total <= kPlanThreads) {
+    // one split per thread: its rank is the number of smaller keys (fewer
+    // barriers than the bitonic network for the usual few hundred splits).
+    // Keys are read 16 at a time (16-byte reads; the pad above total is
+    // larger than any key) into independent counts, so that the reads of
+    // one iteration overlap.
+    const int n16 = (total + 15) & ~15;
+    if (tid >= total && tid < n16) skey[tid] = ~0ull;
+    __syncthreads();
+    if (tid < total) {
+      typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+      const unsigned long long mine = skey[tid];
+      const u64x2* kv = reinterpret_cast<const u64x2*>(skey);
+      int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int i = 0; i < n16 / 2; i += 8) {
+        u64x2 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = kv[i + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] += (x[u][0] < mine) + (x[u][1] < mine);
+      }
+      order[((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]))] = tid;
+    }
+  } else if (sort) {
+    int n2 = 1;
+    while (n2 < total) n2 <<= 1;
+    for (int i = total + tid; i < n2; i += kPlanThreads) skey[i] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kPlanThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long x = skey[i], y = skey[l];
+            if ((x > y) == ((i & k) == 0)) {
+              skey[i] = y;
+              skey[l] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < total; i += kPlanThreads) order[i] = (int32_t)(unsigned)skey[i];
+  } else {
+    for (int i = tid; i < total; i += kPlanThreads) order[i] = i;
   }
 }
 

@@ -262,7 +262,12 @@ int32_t attn_fwd_varlen_kvcache_fp8(const void* q, const void* k, const void* v,
  *  (device int32, batch) and writes `plan` (device int32, attn_plan_words):
  *    plan[0] = total splits, plan[1] = pages per split target (bps),
  *    plan[2 .. 2+batch] = split_ptr (exclusive prefix sum, batch+1 words),
- *    then one (batch, kv_start, kv_end) triple per split, batch-major.
+ *    then one (batch, kv_start, kv_end) triple per split, batch-major
+ *    (batch * max_splits triples reserved), then the work order: batch *
+ *    max_splits words of which the first plan[0] are the split indices in
+ *    the order the decode workgroups take them, longest split
+ *    (kv_end - kv_start) first and ties in split order, or in split order
+ *    when there are more than 4096 splits.
  *  Rule: nblk = ceil(len / page_size) (0 if len <= 0);
  *        bps  = max(min_blocks, ceil(sum nblk * units_per_block / (num_cu * waves)));
  *        ns   = min(max_splits, max(1, ceil(nblk / bps))), pps = ceil(nblk / ns),

@@ -52,3 +52,16 @@ def compare(name, o_gpu, lse_gpu, o_ref, lse_ref, tol_o, tol_lse=TOL_LSE, mask=N
     assert err_o <= tol_o, f"{name}: output error {err_o} > {tol_o}"
     assert err_l <= tol_lse, f"{name}: LSE error {err_l} > {tol_lse}"
     return err_o, err_l
+
+
+def assert_plan_equal(got, ref, batch, max_splits):
+    """The GPU plan equals the oracle's bit for bit where it is defined: the
+    header, split_ptr, the total_splits triples and the work order."""
+    got = np.asarray(got)
+    n = 3 + batch + 3 * int(ref[0])
+    assert np.array_equal(got[:n], ref[:n]), \
+        f"plan mismatch at {np.nonzero(got[:n] != ref[:n])[0][:8]}"
+    o = 3 + batch + 3 * batch * max_splits
+    t = int(ref[0])
+    assert np.array_equal(got[o:o + t], ref[o:o + t]), \
+        f"work order mismatch at {np.nonzero(got[o:o + t] != ref[o:o + t])[0][:8]}"

@@ -129,7 +129,7 @@ def test_varlen_kvcache_host_checks(lib):
 
 
 def test_plan_host_checks(lib):
-    assert lib.attn_plan_words(4, 16) == 3 + 4 + 3 * 4 * 16
+    assert lib.attn_plan_words(4, 16) == 3 + 4 + 4 * 4 * 16
     assert lib.attn_plan_words(0, 16) == 0
     assert lib.attn_plan_splits(P, 0, 64, 1, 256, 4, 16, 4, P, None) == B.ATTN_EEMPTY
     assert lib.attn_plan_splits(P, 4, 64, 1, 256, 4, 17, 4, P, None) == B.ATTN_EINVAL

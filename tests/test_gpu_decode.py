@@ -7,7 +7,7 @@ import torch
 from attention_attn_fwd_02_amd import binding as B
 from attention_attn_fwd_02_amd import inputs
 from oracle import attention as orc
-from tests.gpu_util import TOL_O_BF16, compare, dev, host, log
+from tests.gpu_util import assert_plan_equal, TOL_O_BF16, compare, dev, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -32,9 +32,7 @@ def test_plan_bit_exact(case):
     log("case plan", name, len(lens))
     plan = B.attn_plan_splits(dev(lens), page, upb, ncu, waves, ms, mb)
     ref = orc.plan_splits(lens, page, upb, ncu, waves, ms, mb)
-    got = host(plan)
-    n = 3 + len(lens) + 3 * int(ref[0])
-    assert np.array_equal(got[:n], ref[:n]), f"plan mismatch at {np.nonzero(got[:n] != ref[:n])[0][:8]}"
+    assert_plan_equal(host(plan), ref, len(lens), ms)
 
 
 # ---------------------------------------------------------------------- GQA
@@ -93,8 +91,7 @@ def test_decode_gqa(case):
     compare(name, o, lse, ro, rl, TOL_O_BF16)
     ref_plan = orc.plan_splits(w.cache_seqlens, page, hkv * ((sq * hq // hkv + 15) // 16),
                                B.attn_device_info(0), waves, ms, mb)
-    n = 3 + len(lens) + 3 * int(ref_plan[0])
-    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+    assert_plan_equal(host(plan), ref_plan, len(lens), ms)
 
 
 DECODE_MASK_CASES = [
@@ -176,8 +173,7 @@ def test_decode_gqa_full():
     compare("decode_gqa_full", o, lse, ro, rl, TOL_O_BF16)
     ms, waves, mb = B.GQA_DECODE_PLAN
     ref_plan = orc.plan_splits(w.cache_seqlens, 64, 8, B.attn_device_info(0), waves, ms, mb)
-    n = 3 + len(w.cache_seqlens) + 3 * int(ref_plan[0])
-    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+    assert_plan_equal(host(plan), ref_plan, len(w.cache_seqlens), ms)
 
 
 # ----------------------------------------------------------------------- MLA
@@ -241,8 +237,7 @@ def test_mla_decode_full():
     compare("mla_decode_full", o, lse, ro, rl, TOL_O_BF16)
     ms, waves, mb = B.MLA_DECODE_PLAN
     ref_plan = orc.plan_splits(w.cache_seqlens, 64, 2, B.attn_device_info(0), waves, ms, mb)
-    n = 3 + len(w.cache_seqlens) + 3 * int(ref_plan[0])
-    assert np.array_equal(host(plan)[:n], ref_plan[:n])
+    assert_plan_equal(host(plan), ref_plan, len(w.cache_seqlens), ms)
 
 
 def test_mla_mate_example():
