@@ -47,6 +47,11 @@ VARLEN_CASES = [
     ("window_both", [260], None, 4, 4, 64, False, (31, 9), False),
     ("sinks_causal", [150, 3], None, 8, 2, 128, True, (-1, -1), True),
     ("empty_sequence", [30, 0, 70], None, 4, 2, 128, True, (-1, -1), False),
+    # long key ranges: leading, steady and trailing steps of the pipelined loop
+    ("long_window_left", [1200, 700], None, 8, 2, 128, True, (200, -1), False),
+    ("long_noncausal_q_lt_k", [900, 33], [1500, 800], 4, 1, 128, False, (-1, -1), False),
+    ("long_window_both_sinks", [600], [900], 4, 2, 128, False, (100, 50), True),
+    ("long_causal_odd_tiles", [1057, 801, 95], None, 8, 4, 128, True, (-1, -1), False),
 ]
 
 
