@@ -632,9 +632,9 @@ def attn_debug_gather_sparse(kv, sparse_indices, sparse_mode=3, block_table=None
 # on MI355X for each decode shape; the composed calls below default to them,
 # and the benchmark and the full-size parity tests use the same tuples.
 GQA_DECODE_PLAN = (16, 8, 2)       # bf16 K and V tiles: 8 workgroups per CU
-FP8_DECODE_PLAN = (16, 16, 2)      # half-size FP8 tiles: twice as many
-ONLY_QV_DECODE_PLAN = (16, 16, 2)  # V-only tiles: half the bytes, as FP8
-MLA_DECODE_PLAN = (8, 3, 8)        # 128-row MLA tiles: 3 per CU, >= 8 pages per split
+FP8_DECODE_PLAN = (16, 8, 4)       # FP8 tiles: as bf16 (twice the keys per workgroup)
+ONLY_QV_DECODE_PLAN = (16, 16, 2)  # V-only tiles: half the bytes, twice the workgroups
+MLA_DECODE_PLAN = (4, 3, 8)        # 128-row MLA tiles: at most 4 splits, >= 8 pages each
 GQA_ROWS_PER_WG = 16
 MLA_ROWS_PER_WG = 128
 
@@ -685,14 +685,15 @@ def paged_decode_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, scale=N
                     q_descale=None, k_descale=None, v_descale=None, causal=False, only_qv=False,
                     max_splits=16, waves=None, min_blocks=2, num_cu=None):
     """plan -> attn_decode_paged_qv -> attn_combine (bfloat16 out). The plan
-    defaults follow the bytes per tile: those of paged_decode for bf16 K and
-    V tiles, twice the workgroups per CU (as paged_decode_fp8) for the
-    half-size tiles of FP8 or only_qv (measured on MI355X)."""
+    defaults are the measured ones of each tile kind: paged_decode's for bf16
+    K and V tiles, paged_decode_fp8's for FP8 tiles, and twice the workgroups
+    per CU for the V-only tiles of only_qv (measured on MI355X)."""
     b, sq, hq, _ = qv.shape
     hkv = v_cache.shape[2]
     rows = sq * (hq // max(1, hkv))
     upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
-    waves = waves or (GQA_DECODE_PLAN[1] if fmt is None and not only_qv else FP8_DECODE_PLAN[1])
+    waves = waves or (ONLY_QV_DECODE_PLAN[1] if only_qv else
+                      GQA_DECODE_PLAN[1] if fmt is None else FP8_DECODE_PLAN[1])
     plan = attn_plan_splits(cache_seqlens, v_cache.shape[1], upb, num_cu or _num_cu(qv.device),
                             waves, max_splits, min_blocks)
     op, lp = attn_decode_paged_qv(q, qv, k_cache, v_cache, block_table, cache_seqlens, plan,
