@@ -632,8 +632,11 @@ def attn_debug_gather_sparse(kv, sparse_indices, sparse_mode=3, block_table=None
 # on MI355X for each decode shape; the composed calls below default to them,
 # and the benchmark and the full-size parity tests use the same tuples.
 GQA_DECODE_PLAN = (16, 8, 2)       # bf16 K and V tiles: 8 workgroups per CU
-FP8_DECODE_PLAN = (16, 8, 4)       # FP8 tiles: as bf16 (twice the keys per workgroup)
+FP8_DECODE_PLAN = (16, 16, 2)      # FP8: two KV heads per workgroup, twice the splits
 ONLY_QV_DECODE_PLAN = (16, 16, 2)  # V-only tiles: half the bytes, twice the workgroups
+# bf16 at D = 64 with an even number of KV heads runs two KV heads per
+# workgroup (128-byte head rows), so its plan doubles the splits as FP8's
+GQA_D64_DECODE_PLAN = (16, 16, 2)
 MLA_DECODE_PLAN = (4, 3, 8)        # 128-row MLA tiles: at most 4 splits, >= 8 pages each
 GQA_ROWS_PER_WG = 16
 MLA_ROWS_PER_WG = 128
@@ -644,13 +647,17 @@ def _num_cu(device):
 
 
 def paged_decode(q, k_cache, v_cache, block_table, cache_seqlens, scale=None, causal=False,
-                 sinks=None, max_splits=GQA_DECODE_PLAN[0], waves=GQA_DECODE_PLAN[1],
+                 sinks=None, max_splits=GQA_DECODE_PLAN[0], waves=None,
                  min_blocks=GQA_DECODE_PLAN[2], num_cu=None, out_dtype=torch.bfloat16,
                  mask=None):
     """plan -> attn_decode_paged (or attn_decode_paged_mask) -> attn_combine.
-    Returns (out (B,Sq,Hq,Dv), lse (B,Hq,Sq), plan)."""
-    b, sq, hq, _ = q.shape
+    Returns (out (B,Sq,Hq,Dv), lse (B,Hq,Sq), plan). waves defaults to the
+    measured plan of the head dimension (GQA_DECODE_PLAN, or
+    GQA_D64_DECODE_PLAN for D = 64 with an even number of KV heads)."""
+    b, sq, hq, d = q.shape
     hkv = k_cache.shape[2]
+    if waves is None:
+        waves = (GQA_D64_DECODE_PLAN[1] if d == 64 and hkv % 2 == 0 else GQA_DECODE_PLAN[1])
     rows = sq * (hq // max(1, hkv))
     upb = hkv * ((rows + GQA_ROWS_PER_WG - 1) // GQA_ROWS_PER_WG)
     plan = attn_plan_splits(cache_seqlens, k_cache.shape[1], upb, num_cu or _num_cu(q.device),

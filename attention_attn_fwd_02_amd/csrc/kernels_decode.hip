@@ -36,28 +36,41 @@ inline int round_grid(long total, int grp) {
 // DUMP: the gather-test instance; the same work items and tile issue, but each
 // staged tile is copied out (rows of the split's keys, un-swizzled) instead of
 // being computed on.
-template <class C, bool DUMP = false>
-__global__ void __launch_bounds__(C::THREADS)
+// HP = 2 (one-wave tiles only): each workgroup takes two adjacent KV heads of
+// a split, one per wave, each wave running the engine on its own part of the
+// LDS ring with its own rows. A cache row holds the KV heads side by side, so
+// when one head's slice of a token row is only 128 bytes (FP8 codes at
+// D = 128, bfloat16 at D = 64) the two waves' DMA after each shared barrier
+// asks for the token's two adjacent slices together: 256 contiguous bytes,
+// as the bfloat16 D = 128 tile reads. Reading 128-byte slices one head per
+// workgroup measured 14 % below 256-byte ones on the same bytes.
+template <class C, bool DUMP = false, int HP = 1>
+__global__ void __launch_bounds__(C::THREADS * HP)
 k_decode(DecodeArgs a) {
   using T = StreamTile<C>;
   using M = Mfma<16>;
-  __shared__ __attribute__((aligned(1024))) char ring[C::STAGES * C::STAGE_BYTES];
+  static_assert(HP == 1 || (HP == 2 && C::NW == 1), "head pairs: one wave per head");
+  __shared__ __attribute__((aligned(1024))) char ring_all[HP * C::STAGES * C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) char xchg[C::XCHG_BYTES > 0 ? C::XCHG_BYTES : 16];
+  // the head of the pair this wave takes, and its part of the ring
+  const int hsub = HP > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  char* ring = ring_all + hsub * (C::STAGES * C::STAGE_BYTES);
   const int grp = a.hq / a.hkv;
   const int nrows = a.sq * grp;
   const int mtiles = (nrows + C::ROWS - 1) / C::ROWS;
+  const int hunits = a.hkv / HP;  // KV heads, or head pairs
   // Work items follow the plan's work order (splits longest first, total =
-  // plan[0]): item = (split, kv head, row tile). Real items come first, so
-  // they spread over all XCDs; the row tiles of one (split, kv head) read
-  // the same keys and are placed on one XCD.
+  // plan[0]): item = (split, kv head or head pair, row tile). Real items
+  // come first, so they spread over all XCDs; the row tiles of one (split,
+  // kv head) read the same keys and are placed on one XCD.
   const int logical = xcd_group(blockIdx.x, mtiles);
   const int total = a.plan[0];
-  if (logical >= total * a.hkv * mtiles) return;
+  if (logical >= total * hunits * mtiles) return;
   const int mt = logical % mtiles;
-  const int kvh = (logical / mtiles) % a.hkv;
+  const int kvh = ((logical / mtiles) % hunits) * HP + hsub;
   // the plan's work order: longest splits first
   const int split =
-      a.plan[3 + a.batch + 3 * a.batch * a.max_splits + logical / (mtiles * a.hkv)];
+      a.plan[3 + a.batch + 3 * a.batch * a.max_splits + logical / (mtiles * hunits)];
   const int* tri = a.plan + 3 + a.batch + 3 * split;
   const int b = tri[0], kv0 = tri[1], kv1 = tri[2];
   const int s = split - a.plan[2 + b];
@@ -65,7 +78,8 @@ k_decode(DecodeArgs a) {
   const int delta = lk - a.sq;
 
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // the engine's wave index (the waves of a head pair each run a one-wave engine)
+  const int wave = HP > 1 ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = mt * C::ROWS + (wave / C::DSPLIT) * C::R + (lane & 15);
   const bool row_ok = r < nrows;
   const int tq = row_ok ? r / grp : 0;
@@ -188,11 +202,13 @@ k_decode(DecodeArgs a) {
       const int j0 = kv0 + ti * C::BN, n = min(C::BN, kv1 - j0);
       dump_rows<UNITS>(
           st, n, [](int r, int u) { return T::lds_unit(false, r, u); },
-          [&](int r) { return dst(a.dump_k, j0 + r); }, threadIdx.x, C::THREADS);
+          [&](int r) { return dst(a.dump_k, j0 + r); }, threadIdx.x - hsub * C::THREADS,
+          C::THREADS);
       if constexpr (!C::VSHARED)
         dump_rows<UNITS>(
             st, n, [](int r, int u) { return T::lds_unit(true, r, u); },
-            [&](int r) { return dst(a.dump_v, j0 + r); }, threadIdx.x, C::THREADS);
+            [&](int r) { return dst(a.dump_v, j0 + r); }, threadIdx.x - hsub * C::THREADS,
+            C::THREADS);
     });
     return;
   }
@@ -464,9 +480,14 @@ k_sparse(SparseArgs a) {
 
 template <int QV = 0, int D = 128, bool MASK = false>
 using CfgDecodeGqa = StreamCfg<D, D, 1, 3, false, 1, 0, QV, 32, MASK>;
-// FP8 tiles of 64 keys: the bytes of a 32-key bf16 tile
+// FP8 tiles of 64 keys: the bytes of a 32-key bf16 tile (one KV head per
+// workgroup, for an odd number of KV heads)
 template <int FMT, int QV = 0>
 using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 64>;
+// FP8 head pairs: 32-key tiles per head, so a pair's 3-stage ring is the
+// 48 KB of one 64-key tile's (3 workgroups, 6 waves per CU)
+template <int FMT, int QV = 0>
+using CfgDecodeGqa8P = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 32>;
 using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
 // a 2-stage ring: one tile of gathered rows in flight per workgroup measured
 // 6-10 % faster than two (sparse and block-sparse workloads)
@@ -474,51 +495,53 @@ using CfgSparseMla = StreamCfg<576, 512, 8, 2, true, 2>;
 
 }  // namespace
 
-hipError_t launch_decode_gqa(const DecodeArgs& a, int d, hipStream_t s) {
-  using C = CfgDecodeGqa<>;
+namespace {
+// k_decode over (split, KV head or head pair, row tile) work items
+template <class C, bool DUMP = false, int HP = 1>
+hipError_t launch_k_decode(const DecodeArgs& a, hipStream_t s) {
   const int nrows = a.sq * (a.hq / a.hkv);
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
-  const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-  static_assert(CfgDecodeGqa<0, 64>::ROWS == C::ROWS, "one grid for both head dims");
-  if (a.mask) {
-    if (d == 64)
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 64, true>>), dim3(grid), dim3(C::THREADS), 0, s,
-                         a);
-    else
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 128, true>>), dim3(grid), dim3(C::THREADS), 0,
-                         s, a);
-  } else if (d == 64)
-    hipLaunchKernelGGL((k_decode<CfgDecodeGqa<0, 64>>), dim3(grid), dim3(C::THREADS), 0, s, a);
-  else if (a.qv && a.only_qv)
-    hipLaunchKernelGGL(k_decode<CfgDecodeGqa<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
-  else if (a.qv)
-    hipLaunchKernelGGL(k_decode<CfgDecodeGqa<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_decode<C>, dim3(grid), dim3(C::THREADS), 0, s, a);
+  const int grid = round_grid((long)a.batch * a.max_splits * (a.hkv / HP) * mt, mt);
+  hipLaunchKernelGGL((k_decode<C, DUMP, HP>), dim3(grid), dim3(C::THREADS * HP), 0, s, a);
   return hipGetLastError();
 }
+}  // namespace
+
+hipError_t launch_decode_gqa(const DecodeArgs& a, int d, hipStream_t s) {
+  // D = 64 rows of a KV head are 128 bytes: head pairs when the count is even
+  const bool pairs = a.hkv % 2 == 0;
+  if (a.mask) {
+    if (d == 64)
+      return pairs ? launch_k_decode<CfgDecodeGqa<0, 64, true>, false, 2>(a, s)
+                   : launch_k_decode<CfgDecodeGqa<0, 64, true>>(a, s);
+    return launch_k_decode<CfgDecodeGqa<0, 128, true>>(a, s);
+  }
+  if (d == 64)
+    return pairs ? launch_k_decode<CfgDecodeGqa<0, 64>, false, 2>(a, s)
+                 : launch_k_decode<CfgDecodeGqa<0, 64>>(a, s);
+  if (a.qv && a.only_qv) return launch_k_decode<CfgDecodeGqa<2>>(a, s);
+  if (a.qv) return launch_k_decode<CfgDecodeGqa<1>>(a, s);
+  return launch_k_decode<CfgDecodeGqa<>>(a, s);
+}
+
+namespace {
+template <int FMT>
+hipError_t launch_decode_fp8_fmt(const DecodeArgs& a, hipStream_t s) {
+  // FP8 rows of a KV head are 128 bytes: head pairs when the count is even
+  const int qv = a.qv ? (a.only_qv ? 2 : 1) : 0;
+  if (a.hkv % 2 == 0) {
+    if (qv == 2) return launch_k_decode<CfgDecodeGqa8P<FMT, 2>, false, 2>(a, s);
+    if (qv == 1) return launch_k_decode<CfgDecodeGqa8P<FMT, 1>, false, 2>(a, s);
+    return launch_k_decode<CfgDecodeGqa8P<FMT>, false, 2>(a, s);
+  }
+  if (qv == 2) return launch_k_decode<CfgDecodeGqa8<FMT, 2>>(a, s);
+  if (qv == 1) return launch_k_decode<CfgDecodeGqa8<FMT, 1>>(a, s);
+  return launch_k_decode<CfgDecodeGqa8<FMT>>(a, s);
+}
+}  // namespace
 
 hipError_t launch_decode_gqa_fp8(const DecodeArgs& a, int fmt, hipStream_t s) {
-  using C = CfgDecodeGqa8<1>;
-  const int nrows = a.sq * (a.hq / a.hkv);
-  const int mt = (nrows + C::ROWS - 1) / C::ROWS;
-  const int grid = round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-  if (a.qv && a.only_qv) {
-    if (fmt == 1)
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<1, 2>>), dim3(grid), dim3(C::THREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<2, 2>>), dim3(grid), dim3(C::THREADS), 0, s, a);
-  } else if (a.qv) {
-    if (fmt == 1)
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<1, 1>>), dim3(grid), dim3(C::THREADS), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_decode<CfgDecodeGqa8<2, 1>>), dim3(grid), dim3(C::THREADS), 0, s, a);
-  } else if (fmt == 1) {
-    hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<1>>, dim3(grid), dim3(C::THREADS), 0, s, a);
-  } else {
-    hipLaunchKernelGGL(k_decode<CfgDecodeGqa8<2>>, dim3(grid), dim3(C::THREADS), 0, s, a);
-  }
-  return hipGetLastError();
+  return fmt == 1 ? launch_decode_fp8_fmt<1>(a, s) : launch_decode_fp8_fmt<2>(a, s);
 }
 
 namespace {
@@ -526,11 +549,6 @@ int mla_grid(const DecodeArgs& a) {
   using C = CfgDecodeMla;
   const int nrows = a.sq * (a.hq / a.hkv);
   const int mt = (nrows + C::ROWS - 1) / C::ROWS;
-  return round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
-}
-int gqa_grid(const DecodeArgs& a, int rows) {
-  const int nrows = a.sq * (a.hq / a.hkv);
-  const int mt = (nrows + rows - 1) / rows;
   return round_grid((long)a.batch * a.max_splits * a.hkv * mt, mt);
 }
 }  // namespace
@@ -548,20 +566,17 @@ hipError_t launch_dump_mla(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_dump_decode(const DecodeArgs& a, int d, int fmt, hipStream_t s) {
-  if (fmt == 0 && d == 64) {
-    using C = CfgDecodeGqa<0, 64>;
-    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
-  } else if (fmt == 0) {
-    using C = CfgDecodeGqa<>;
-    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
-  } else if (fmt == 1) {
-    using C = CfgDecodeGqa8<1>;
-    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
-  } else {
-    using C = CfgDecodeGqa8<2>;
-    hipLaunchKernelGGL((k_decode<C, true>), dim3(gqa_grid(a, C::ROWS)), dim3(C::THREADS), 0, s, a);
-  }
-  return hipGetLastError();
+  // the gather test runs the instance (tile size, head pairing) the decode runs
+  const bool pairs = a.hkv % 2 == 0;
+  if (fmt == 0 && d == 64)
+    return pairs ? launch_k_decode<CfgDecodeGqa<0, 64>, true, 2>(a, s)
+                 : launch_k_decode<CfgDecodeGqa<0, 64>, true>(a, s);
+  if (fmt == 0) return launch_k_decode<CfgDecodeGqa<>, true>(a, s);
+  if (fmt == 1)
+    return pairs ? launch_k_decode<CfgDecodeGqa8P<1>, true, 2>(a, s)
+                 : launch_k_decode<CfgDecodeGqa8<1>, true>(a, s);
+  return pairs ? launch_k_decode<CfgDecodeGqa8P<2>, true, 2>(a, s)
+               : launch_k_decode<CfgDecodeGqa8<2>, true>(a, s);
 }
 
 hipError_t launch_sparse_mla(const SparseArgs& a, hipStream_t s) {
