@@ -7,10 +7,36 @@ namespace attn {
 namespace {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 // plans of at most this many splits get a longest-first work order
 constexpr int kPlanSortMax = 4096;
 
-__device__ __forceinline__ int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+// ceil(a / b) for a >= 0, b > 0, with no overflow near the type's maximum
+__device__ __forceinline__ int cdiv(int a, int b) { return a / b + (a % b != 0); }
+__device__ __forceinline__ long cdiv(long a, long b) { return a / b + (a % b != 0); }
+
+// Number of splits of a sequence of nb > 0 blocks; pps = blocks per split.
+__device__ __forceinline__ int plan_splits_of(int nb, int bps, int max_splits, int& pps) {
+  const int ns = min(max_splits, max(1, cdiv(nb, bps)));
+  pps = cdiv(nb, ns);
+  return cdiv(nb, pps);
+}
+
+// Inclusive prefix sum over the lanes of a wave.
+__device__ __forceinline__ long wave_prefix_sum(long v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long u = __shfl_up(v, (unsigned)d, 64);
+    if (lane >= d) v += u;
+  }
+  return v;
+}
+
+// Work-order key of a split: longer first, then lower split index.
+__device__ __forceinline__ unsigned long long order_key(int length, int index) {
+  return ((unsigned long long)(0x7FFFFFFF - length) << 32) | (unsigned)index;
+}
 
 // Split plan [MATE get_scheduler_metadata / get_mla_metadata; CANN
 // flash_attn_metadata: a metadata pass that fixes the work split before the
@@ -19,54 +45,63 @@ __device__ __forceinline__ int cdiv(long a, long b) { return (int)((a + b - 1) /
 //   bps    = max(min_blocks, ceil(sum nblk_b * upb / (num_cu * waves)))
 //   ns_b   = min(max_splits, max(1, ceil(nblk_b / bps)))
 //   pps_b  = ceil(nblk_b / ns_b), ns_b = ceil(nblk_b / pps_b)
-// One workgroup; each thread owns a contiguous run of sequences. The work
+// One workgroup; each thread owns a contiguous run of sequences, and the
+// sums over sequences are wave prefix sums joined through LDS. The work
 // order after the triples lists the splits longest first (ties in split
 // order): the decode workgroups take splits in that order, the
 // longest-processing-time rule of list scheduling. The keys ((2^31 - 1 -
 // length) << 32 | index) are unique, so the result does not depend on how
-// they are sorted: by rank (one split per thread) up to kPlanThreads
-// splits, by a bitonic network in LDS up to kPlanSortMax.
+// they are sorted. All splits of a sequence but its last have one length and
+// consecutive indices, so they form a group that no other key falls inside:
+// a group's place in the order is the total size of the groups whose first
+// key is smaller, and the sort reduces to ranking at most two groups per
+// sequence (one group per thread, up to kPlanThreads groups). Beyond that, a
+// bitonic network in LDS sorts the split keys themselves, up to kPlanSortMax.
 __global__ void __launch_bounds__(kPlanThreads)
 k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_cu, int waves,
        int max_splits, int min_blocks, int32_t* __restrict__ plan) {
-  __shared__ long red[kPlanThreads];
-  __shared__ int scan[kPlanThreads];
+  __shared__ long wsum[2][kPlanWaves];
   __shared__ __attribute__((aligned(16))) unsigned long long skey[kPlanSortMax];
+  __shared__ __attribute__((aligned(16))) int gsize[kPlanThreads];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int per = (batch + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(batch, tid * per), b1 = min(batch, b0 + per);
   long blocks = 0;
   for (int b = b0; b < b1; ++b) blocks += lens[b] > 0 ? cdiv(lens[b], page) : 0;
-  red[tid] = blocks;
+  blocks = wave_prefix_sum(blocks);
+  if ((tid & 63) == 63) wsum[0][wave] = blocks;
   __syncthreads();
-  for (int w = kPlanThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  const long total_units = red[0] * upb;
-  const int bps = max(min_blocks, cdiv(total_units, (long)num_cu * waves));
-  int mine = 0;
+  long total_blocks = 0;
+  for (int w = 0; w < kPlanWaves; ++w) total_blocks += wsum[0][w];
+  const long total_units = total_blocks * upb;
+  const int bps = (int)max((long)min_blocks, cdiv(total_units, (long)num_cu * waves));
+
+  // splits (high word) and groups (low word) of this thread's sequences
+  long mine = 0;
   for (int b = b0; b < b1; ++b) {
     const int nb = lens[b] > 0 ? cdiv(lens[b], page) : 0;
     if (nb) {
-      int ns = min(max_splits, max(1, cdiv(nb, bps)));
-      ns = cdiv(nb, cdiv(nb, ns));
-      mine += ns;
+      int pps;
+      const int ns = plan_splits_of(nb, bps, max_splits, pps);
+      mine += ((long)ns << 32) + (ns > 1 ? 2 : 1);
     }
   }
-  scan[tid] = mine;
+  const long incl = wave_prefix_sum(mine);
+  if ((tid & 63) == 63) wsum[1][wave] = incl;
   __syncthreads();
-  // inclusive Hillis-Steele scan over the per-thread split counts
-  for (int w = 1; w < kPlanThreads; w <<= 1) {
-    const int v = tid >= w ? scan[tid - w] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
+  long before = 0, all = 0;
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const long v = wsum[1][w];
+    before += w < wave ? v : 0;
+    all += v;
   }
-  int ptr = scan[tid] - mine;
-  const int total = scan[kPlanThreads - 1];
+  const long first = before + incl - mine;
+  int ptr = (int)(first >> 32), gptr = (int)(first & 0xFFFFFFFFl);
+  const int total = (int)(all >> 32), ngroups = (int)(all & 0xFFFFFFFFl);
   const bool sort = total <= kPlanSortMax;
+  const bool by_group = sort && ngroups <= kPlanThreads;
+
   int32_t* split_ptr = plan + 2;
   int32_t* tri = plan + 3 + batch;
   for (int b = b0; b < b1; ++b) {
@@ -74,49 +109,65 @@ k_plan(const int32_t* __restrict__ lens, int batch, int page, int upb, int num_c
     const int len = lens[b];
     const int nb = len > 0 ? cdiv(len, page) : 0;
     if (nb) {
-      int ns = min(max_splits, max(1, cdiv(nb, bps)));
-      const int pps = cdiv(nb, ns);
-      ns = cdiv(nb, pps);
+      int pps;
+      const int ns = plan_splits_of(nb, bps, max_splits, pps);
+      const long span = (long)pps * page;
       for (int s = 0; s < ns; ++s) {
-        const int kv0 = s * pps * page, kv1 = min((s + 1) * pps * page, len);
+        const int kv0 = (int)(s * span), kv1 = (int)min((s + 1) * span, (long)len);
         tri[3 * (ptr + s)] = b;
         tri[3 * (ptr + s) + 1] = kv0;
         tri[3 * (ptr + s) + 2] = kv1;
-        if (sort)
-          skey[ptr + s] = ((unsigned long long)(0x7FFFFFFF - (kv1 - kv0)) << 32) |
-                          (unsigned)(ptr + s);
+        if (sort && !by_group) skey[ptr + s] = order_key(kv1 - kv0, ptr + s);
+      }
+      if (by_group) {
+        if (ns > 1) {
+          skey[gptr] = order_key((int)span, ptr);
+          gsize[gptr++] = ns - 1;
+        }
+        skey[gptr] = order_key(len - (int)((ns - 1) * span), ptr + ns - 1);
+        gsize[gptr++] = 1;
       }
       ptr += ns;
     }
   }
   if (tid == kPlanThreads - 1) {
-    split_ptr[batch] = scan[tid];
-    plan[0] = scan[tid];
+    split_ptr[batch] = total;
+    plan[0] = total;
     plan[1] = bps;
   }
   int32_t* order = plan + 3 + batch + 3 * batch * max_splits;
-  if (sort && total <= kPlanThreads) {
-    // one split per thread: its rank is the number of smaller keys (fewer
-    // barriers than the bitonic network for the usual few hundred splits).
-    // Keys are read 16 at a time (16-byte reads; the pad above total is
-    // larger than any key) into independent counts, so that the reads of
-    // one iteration overlap.
-    const int n16 = (total + 15) & ~15;
-    if (tid >= total && tid < n16) skey[tid] = ~0ull;
+  if (by_group) {
+    // Keys and sizes are read 8 at a time (the pad up to a multiple of 8 has
+    // keys above any group's and size 0) into independent sums, so that the
+    // reads of one iteration overlap.
+    const int n8 = (ngroups + 7) & ~7;
+    if (tid >= ngroups && tid < n8) {
+      skey[tid] = ~0ull;
+      gsize[tid] = 0;
+    }
     __syncthreads();
-    if (tid < total) {
+    if (tid < ngroups) {
       typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
-      const unsigned long long mine = skey[tid];
+      typedef int i32x4 __attribute__((ext_vector_type(4)));
+      const unsigned long long key = skey[tid];
       const u64x2* kv = reinterpret_cast<const u64x2*>(skey);
-      int r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      for (int i = 0; i < n16 / 2; i += 8) {
-        u64x2 x[8];
+      const i32x4* sz = reinterpret_cast<const i32x4*>(gsize);
+      int r[4] = {0, 0, 0, 0};
+      for (int i = 0; i < n8; i += 8) {
+        u64x2 k[4];
+        i32x4 z[2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = kv[i + u];
+        for (int u = 0; u < 4; ++u) k[u] = kv[i / 2 + u];
+        z[0] = sz[i / 4];
+        z[1] = sz[i / 4 + 1];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) r[u] += (x[u][0] < mine) + (x[u][1] < mine);
+        for (int u = 0; u < 4; ++u)
+          r[u] += (k[u][0] < key ? z[u / 2][2 * (u % 2)] : 0) +
+                  (k[u][1] < key ? z[u / 2][2 * (u % 2) + 1] : 0);
       }
-      order[((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]))] = tid;
+      const int pos = (r[0] + r[1]) + (r[2] + r[3]);
+      const int idx = (int)(unsigned)key;
+      for (int i = 0; i < gsize[tid]; ++i) order[pos + i] = idx + i;
     }
   } else if (sort) {
     int n2 = 1;

@@ -19,6 +19,14 @@ PLAN_CASES = [
     ("mla_lens", None, 64, 4, 256, 2, 16, 4),
     ("with_zeros", [0, 1, 64, 65, 0, 40000, 12], 64, 1, 4, 1, 3, 2),
     ("many_seqs", list(range(0, 5000 * 97, 97)), 16, 3, 256, 8, 16, 1),
+    # 3560 splits in 475 groups (up to 15 splits of one length per sequence)
+    ("many_splits_few_groups",
+     [int(x) for x in np.random.default_rng(9).integers(1, 200000, 240)], 16, 1, 256, 64, 16, 1),
+    # more than 1024 groups with at most 4096 splits: the bitonic network
+    ("bitonic_one_split_each", [3000 + (i % 7) * 16 for i in range(1500)], 16, 1, 256, 2, 4, 64),
+    ("bitonic_two_splits_each", [1000 + (i % 5) * 40 for i in range(800)], 16, 1, 256, 4, 2, 40),
+    # equal lengths across sequences, lengths that fill their last page exactly
+    ("ties_and_full_pages", [4096] * 100 + [4095, 1, 0, 4097, 64, 128], 64, 2, 256, 16, 16, 1),
 ]
 
 
