@@ -44,7 +44,7 @@ struct DmaSrc {
 // the same 16 query rows, each holds half of every Q row and half of every
 // output row, computes the partial S^T over its half of the head dimension,
 // and the two partials are summed through LDS so that both waves continue
-// with identical scores. Only the even wave of a pair issues DMA. This halves
+// with identical scores. Waves 0 .. NW/2-1 issue the DMA. This halves
 // the registers a wave needs for wide heads (MLA: 576 / 512), so two waves
 // fit on each SIMD and hide each other's LDS latency.
 //
@@ -236,13 +236,15 @@ struct StreamTile {
 
   // This wave's share of the DMA of one tile into `stage`. krow(r) / vrow(r)
   // give the global address of the K / V row of key r of the tile (r in
-  // [0, BN)); vrow is unused when V shares the K row. With DSPLIT = 2 the odd
-  // waves issue nothing.
+  // [0, BN)); vrow is unused when V shares the K row. With DSPLIT = 2 only
+  // waves 0 .. DMA_WAVES-1 issue: one on each SIMD of an 8-wave workgroup
+  // (waves w and w+4 share one), so the other wave of that SIMD keeps its
+  // MFMA pipe busy while the issuing wave waits for the address unit.
   template <class KRow, class VRow>
   __device__ __forceinline__ static void dma_tile(char* stage, KRow krow, VRow vrow, int wave,
                                                   int lane) {
-    if (C::DSPLIT == 2 && (wave & 1)) return;
-    const int dw = C::DMA_WAVES == 1 ? 0 : wave / C::DSPLIT;
+    if (C::DSPLIT == 2 && wave >= C::DMA_WAVES) return;
+    const int dw = C::DMA_WAVES == 1 ? 0 : wave;
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       // dw is 0 for single-DMA-wave workgroups and a uniform (SGPR) value
@@ -310,8 +312,8 @@ struct StreamTile {
   // instruction covering rows sub*8 .. sub*8+7 of block rb.
   template <class KSrc, class VSrc>
   __device__ __forceinline__ static void dma_tile_sv(char* stage, KSrc ksrc, VSrc vsrc, int wave) {
-    if (C::DSPLIT == 2 && (wave & 1)) return;
-    const int dw = C::DMA_WAVES == 1 ? 0 : wave / C::DSPLIT;
+    if (C::DSPLIT == 2 && wave >= C::DMA_WAVES) return;
+    const int dw = C::DMA_WAVES == 1 ? 0 : wave;
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       const int inst = dw * C::DMA_PER_WAVE + n;

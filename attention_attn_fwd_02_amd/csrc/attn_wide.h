@@ -105,7 +105,9 @@ struct WideTile {
   // DMA of one tile. Instruction inst covers the 16-row block inst / (NCH/4)
   // and chunks 4 (inst % (NCH/4)) .. +3; lane -> chunk +(lane >> 4), row
   // (lane & 15) ^ sw(lane >> 4) of the block, landing at 16 * lane of the
-  // instruction's 1 KB. Only the even wave of each pair issues.
+  // instruction's 1 KB. Waves 0 .. DMA_WAVES-1 issue: one on each SIMD
+  // (waves w and w+4 share one), so the other wave of that SIMD keeps its
+  // MFMA pipe busy while the issuing wave waits for the address unit.
   __device__ __forceinline__ static uint32_t dma_lane_row(int lane) {
     return (uint32_t)((lane & 15) ^ sw(lane >> 4));
   }
@@ -116,8 +118,8 @@ struct WideTile {
   // the tile plus the uniform column offset colb, and the lane's offset.
   template <class KSrc>
   __device__ __forceinline__ static void dma_tile_sv(char* stage, KSrc ksrc, int wave) {
-    if (wave & 1) return;
-    const int dw = wave >> 1;
+    if (wave >= C::DMA_WAVES) return;
+    const int dw = wave;
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       constexpr int IPB = C::NCH / 4;
@@ -129,8 +131,8 @@ struct WideTile {
   // per-lane form: krow(r) is the global address of tile row r
   template <class KRow>
   __device__ __forceinline__ static void dma_tile(char* stage, KRow krow, int wave, int lane) {
-    if (wave & 1) return;
-    const int dw = wave >> 1;
+    if (wave >= C::DMA_WAVES) return;
+    const int dw = wave;
 #pragma unroll
     for (int n = 0; n < C::DMA_PER_WAVE; ++n) {
       constexpr int IPB = C::NCH / 4;
