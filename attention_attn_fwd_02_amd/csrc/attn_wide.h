@@ -27,7 +27,7 @@ namespace attn {
 
 // QLDS of each wave's Q fragments are kept in LDS instead of registers (the
 // register file holds 2 waves per SIMD only just: 128 accumulator registers
-// for O and 72 for Q of a 576-wide head).
+// for O and 72 for Q of a 576-wide head); 0 keeps Q wholly in registers.
 template <int D_, int DV_, int STAGES_, int QLDS_ = 2>
 struct WideCfg {
   static constexpr int D = D_, DV = DV_, STAGES = STAGES_, QLDS = QLDS_;

@@ -488,7 +488,9 @@ using CfgDecodeGqa8 = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 64>;
 // 48 KB of one 64-key tile's (3 workgroups, 6 waves per CU)
 template <int FMT, int QV = 0>
 using CfgDecodeGqa8P = StreamCfg<128, 128, 1, 3, false, 1, FMT, QV, 32>;
-using CfgDecodeMla = WideCfg<576, 512, 3, 2>;
+// Q wholly in registers (246 VGPRs, no spill): 1 % faster than two of its
+// fragments in LDS, whose reads added 16 KB per tile to the LDS traffic
+using CfgDecodeMla = WideCfg<576, 512, 3, 0>;
 // a 2-stage ring: one tile of gathered rows in flight per workgroup measured
 // 6-10 % faster than two (sparse and block-sparse workloads)
 using CfgSparseMla = StreamCfg<576, 512, 8, 2, true, 2>;
