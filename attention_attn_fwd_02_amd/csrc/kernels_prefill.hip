@@ -155,6 +155,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   const int row0 = w.qt * C::ROWS;
   if (row0 >= lq) return;
   const int k0 = a.cu_k[w.b];
+  const int tq_all = a.cu_q[a.batch];  // LSE row stride, read with the bounds
   const int lc = KVC ? a.cache_lens[w.b] : 0;  // cached keys come first
   const int lk = lc + a.cu_k[w.b + 1] - k0;
   const int row_last = min(lq, row0 + C::ROWS) - 1;
@@ -353,7 +354,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
       t.finish(a.sinks != nullptr, a.sinks ? a.sinks[w.h] * kLog2e : 0.f, lse) * vscale;
   if (row_ok) {
     t.store(static_cast<bf16_t*>(a.out) + ((size_t)(q0 + trow) * a.hq + w.h) * C::DV, inv, lane);
-    if (a.lse && lane < 32) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
+    if (a.lse && lane < 32) a.lse[(size_t)w.h * tq_all + q0 + trow] = lse;
   }
 }
 
@@ -420,6 +421,9 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
   if (row0 >= lq) return;
   const int k0 = a.cu_k[w.b];
   const int lk = a.cu_k[w.b + 1] - k0;
+  // the LSE row stride, read with the sequence bounds rather than after the
+  // merge, where it would add a memory round trip to this short kernel
+  const int tq_all = a.cu_q[a.batch];
   const int row_last = min(lq, row0 + C::ROWS) - 1;
   const Band bd = make_band(row0, row_last, lq, lk, a.causal, a.wl, a.wr, C::BN);
 
@@ -576,7 +580,7 @@ __global__ void __launch_bounds__(256) k_varlen_f32(VarlenArgs a) {
                                            part * C::DPL);
     orow[0] = f32x4{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
     orow[1] = f32x4{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-    if (a.lse && part == 0) a.lse[(size_t)w.h * a.cu_q[a.batch] + q0 + trow] = lse;
+    if (a.lse && part == 0) a.lse[(size_t)w.h * tq_all + q0 + trow] = lse;
   }
 }
 
