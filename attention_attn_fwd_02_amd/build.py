@@ -3,6 +3,11 @@
 Usage: python -m attention_attn_fwd_02_amd.build   (or build() from Python)
 Each .hip file is compiled to an object in parallel, then linked in-tree next
 to this file, where the binding loads it.
+
+ATTN_BUILD_DEFINES (environment, optional): extra -D flags for a debug build,
+e.g. ATTN_BUILD_DEFINES=-DATTN_LDS_POISON=1 fills every LDS block with NaN
+bits before its DMA, so that a read ahead of a missing wait shows up as NaN in
+the GPU tests. Rebuild without it before measuring.
 """
 from __future__ import annotations
 
@@ -33,9 +38,17 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def _defines():
+    extra = os.environ.get("ATTN_BUILD_DEFINES", "").split()
+    bad = [f for f in extra if not f.startswith("-D")]
+    if bad:
+        raise ValueError(f"ATTN_BUILD_DEFINES takes -D flags only, got {bad}")
+    return extra
+
+
 def _compile(src):
     obj = os.path.join(OBJ, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *_defines(), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

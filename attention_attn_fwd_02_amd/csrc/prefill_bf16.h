@@ -46,6 +46,25 @@ namespace attn {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// ATTN_LDS_POISON (a debug build, off by default): before each DMA
+// instruction the issuing lanes fill their 16 bytes of its LDS destination
+// with all-ones bits (NaN as bfloat16, float32 and both FP8 formats) and wait
+// for those writes, so that a read of a stage before its DMA has landed (a
+// missing vmcnt wait or barrier) turns the results into NaN instead of
+// silently reusing the previous tile's data.
+#ifndef ATTN_LDS_POISON
+#define ATTN_LDS_POISON 0
+#endif
+__device__ __forceinline__ void lds_poison16(void* lds_dst_uniform) {
+  if constexpr (ATTN_LDS_POISON != 0) {
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+    *reinterpret_cast<u32x4_*>(static_cast<char*>(lds_dst_uniform) + lane * 16) =
+        u32x4_{~0u, ~0u, ~0u, ~0u};
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fill lands before the DMA's data
+  }
+}
+
 // 16 bytes per lane from gsrc into LDS at lds_dst_uniform + 16*lane
 // (global_load_lds_dwordx4; the LDS base goes through M0 and must be
 // wave-uniform). The instruction has no register results. It is issued from
@@ -53,6 +72,7 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // reads of the other buffer: callers wait on vmcnt themselves before the
 // barrier that publishes a tile.
 __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst_uniform) {
+  lds_poison16(lds_dst_uniform);
   const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_dst_uniform);
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m0) : "memory");
 }
@@ -62,6 +82,7 @@ __device__ __forceinline__ void lds_dma16(const void* gsrc, void* lds_dst_unifor
 // per-lane part can be computed once and reused for every tile.
 __device__ __forceinline__ void lds_dma16_sv(const void* sbase_uniform, uint32_t voff,
                                              void* lds_dst_uniform) {
+  lds_poison16(lds_dst_uniform);
   const uint32_t m0 = (uint32_t)(uintptr_t)(lds_void_ptr)(lds_dst_uniform);
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase_uniform), "{m0}"(m0)
                : "memory");
