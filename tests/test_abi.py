@@ -438,3 +438,15 @@ def test_noalloc_host_checks(lib):
     # 4096 x 16 splits x 32 rows x 128 floats: far above the fixed scratch
     assert call(batch=4096) == B.ATTN_EINVAL
     assert b"scratch" in lib.attn_last_error()
+
+
+def test_build_debug_defines(monkeypatch):
+    """ATTN_BUILD_DEFINES adds -D flags to every compile and accepts nothing else."""
+    from attention_attn_fwd_02_amd import build
+    monkeypatch.delenv("ATTN_BUILD_DEFINES", raising=False)
+    assert build._defines() == []
+    monkeypatch.setenv("ATTN_BUILD_DEFINES", "-DATTN_LDS_POISON=1")
+    assert build._defines() == ["-DATTN_LDS_POISON=1"]
+    monkeypatch.setenv("ATTN_BUILD_DEFINES", "-DATTN_LDS_POISON=1 -O0")
+    with pytest.raises(ValueError):
+        build._defines()
