@@ -956,6 +956,12 @@ def main():
     rf = dict(head["roofline"])
     if head_key == "prefill":
         rf["algorithmic_bytes_per_launch"] = runs["prefill"].extra["algorithmic_bytes_per_launch"]
+        # the convention of most published causal-attention rates: 2*D*Hq*sum L^2
+        # (half of 4*D*Hq*L^2), which leaves out the diagonal's L extra pairs
+        fa = sum(2.0 * 128 * 32 * int(L) * int(L) for L in runs["prefill"].extra["lens"])
+        rf["fa_style"] = {"flop_per_launch": fa,
+                          "value": fa / (head["ms_per_step"] * 1e-3) / 1e12,
+                          "unit": "TFLOP/s"}
     rec = {
         "metric": METRIC if head_key == "prefill" else head["metric"],
         "value": head["value"],
