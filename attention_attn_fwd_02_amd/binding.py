@@ -44,6 +44,10 @@ _SIGNATURES = {
                                 _P, _F, _I, _I, _I, _P, _I, _P, _P, _P]),
     "attn_fwd_varlen_kvcache": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                      _I, _I, _I, _F, _I, _I, _I, _P, _P, _I, _I, _P, _P, _P]),
+    # q, qv, k, v, cu_q, cu_k, k_cache, v_cache, block_table, max_pages, cache_lens, page,
+    # batch, max_q, hq, hkv, d, dv, scale, causal, wl, wr, sinks, only_qv, out, lse, stream
+    "attn_fwd_varlen_kvcache_qv": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I,
+                                        _I, _I, _I, _I, _F, _I, _I, _I, _P, _I, _P, _P, _P]),
     "attn_fwd_varlen_kvcache_fp8": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I,
                                          _I, _I, _I, _I, _P, _P, _P, _F, _I, _I, _I, _P, _P, _P,
                                          _P]),
@@ -306,6 +310,40 @@ def attn_fwd_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cach
         int(bool(causal)), int(window[0]), int(window[1]), _ptr(sinks), _ptr(mask),
         0 if mask is None else mask.shape[0], 0 if mask is None else mask.shape[2], _ptr(out),
         _ptr(lse), _stream()))
+    return out, lse
+
+
+def attn_fwd_varlen_kvcache_qv(q, qv, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
+                               block_table, cache_seqlens, max_seqlen_q, scale=None,
+                               causal=False, window=(-1, -1), sinks=None, only_qv=False,
+                               out=None, lse=None, return_lse=True):
+    """attn_fwd_varlen_kvcache (bf16, D = Dv = 128) with a second query qv
+    (Tq,Hq,128) scored against the value rows, cached and current. only_qv:
+    q, k and k_cache are not used (may be None). Returns (out (Tq,Hq,128) bf16,
+    lse (Hq,Tq) fp32 or None)."""
+    _dev(q, qv, k, v, k_cache, v_cache, dtype=torch.bfloat16)
+    _dev(cu_seqlens_q, cu_seqlens_k, block_table, cache_seqlens, dtype=torch.int32)
+    _dev(sinks, dtype=torch.float32)
+    if qv is None or v is None or v_cache is None:
+        raise ValueError("qv, v and v_cache are required")
+    tq, hq, dv = qv.shape
+    hkv = v_cache.shape[2]
+    d = dv if only_qv or q is None else q.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if block_table.dim() != 2 or block_table.shape[0] != batch or cache_seqlens.numel() != batch:
+        raise ValueError("block_table must be (batch, max_pages) and cache_seqlens (batch)")
+    if out is None:
+        out = torch.empty((tq, hq, dv), dtype=torch.bfloat16, device=qv.device)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=qv.device)
+    _dev(out, dtype=torch.bfloat16)
+    _dev(lse, dtype=torch.float32)
+    _check(load().attn_fwd_varlen_kvcache_qv(
+        _ptr(q), _ptr(qv), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_table), block_table.shape[1],
+        _ptr(cache_seqlens), v_cache.shape[1], batch, int(max_seqlen_q), hq, hkv, d, dv,
+        _scale(scale, qv if q is None else q), int(bool(causal)), int(window[0]),
+        int(window[1]), _ptr(sinks), int(bool(only_qv)), _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -134,7 +134,8 @@ template <class C, bool KVC, bool MASK, bool QV = false, bool DUMP = false>
 __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
   using T = PrefillTile<C, QV>;
   static_assert(C::FP8 == 0 || !MASK, "FP8 tiles: no mask");
-  static_assert(!QV || (!KVC && !MASK), "qv: current keys, no mask");
+  static_assert(!QV || !MASK, "qv: no mask");
+  static_assert(!QV || !KVC || C::FP8 == 0, "qv over a cache: bfloat16");
   constexpr int MASK_BAND = C::R * C::BN * 2;              // one wave's rows of a tile
   constexpr int VK_OFF = 2 * C::TILE_BYTES;                // V in the K layout (QV)
   constexpr int MASK_OFF = VK_OFF + (QV ? C::TILE_BYTES : 0);
@@ -252,6 +253,7 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
         auto vblk = [&](int rb) { return vcb + slot(rb) * row_bytes; };
         T::template dma_tile_blk<false>(buf, kblk, row_bytes, koff, wave);
         T::template dma_tile_blk<true>(buf + C::TILE_BYTES, vblk, row_bytes, voff, wave);
+        if constexpr (QV) T::template dma_tile_blk<false>(buf + VK_OFF, vblk, row_bytes, koff, wave);
       } else {
         // the tile straddles the end of the cache (or is the last tile):
         // per-lane rows, cached ones through the block slots above
@@ -264,6 +266,9 @@ __device__ __forceinline__ void varlen_body(const VarlenArgs& a) {
         T::template dma_tile<false>(buf, [&](int r) { return row(kcb, kb, r); }, wave, ln);
         T::template dma_tile<true>(buf + C::TILE_BYTES, [&](int r) { return row(vcb, vb, r); },
                                    wave, ln);
+        if constexpr (QV)
+          T::template dma_tile<false>(buf + VK_OFF, [&](int r) { return row(vcb, vb, r); }, wave,
+                                      ln);
       }
     }
   };
@@ -376,6 +381,12 @@ __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_fp8_kvc(Var
 template <class C>
 __global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv(VarlenArgs a) {
   varlen_body<C, false, false, true>(a);
+}
+
+// qv over a paged cache plus the current rows (bfloat16)
+template <class C>
+__global__ void __launch_bounds__(C::THREADS, C::MIN_WAVES) k_varlen_qv_kvc(VarlenArgs a) {
+  varlen_body<C, true, false, true>(a);
 }
 
 // gather test: the cache-plus-current tile issue with the tiles copied out
@@ -687,6 +698,12 @@ hipError_t launch_varlen_qv(const VarlenArgs& a, int fmt, hipStream_t s) {
     hipLaunchKernelGGL(k_varlen_qv<CfgPQv<1>>, dim3(grid), dim3(CfgPQv<1>::THREADS), 0, s, a);
   else
     hipLaunchKernelGGL(k_varlen_qv<CfgPQv<2>>, dim3(grid), dim3(CfgPQv<2>::THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_kvcache_qv_bf16(const VarlenArgs& a, hipStream_t s) {
+  const int grid = prefill_grid(a.batch, a.hq, a.hkv, a.nqt);
+  hipLaunchKernelGGL(k_varlen_qv_kvc<CfgPQv<0>>, dim3(grid), dim3(CfgPQv<0>::THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -120,6 +120,7 @@ int varlen_f32_rows(int d);
 hipError_t launch_varlen_bf16(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_f32(const VarlenArgs& a, int d, hipStream_t s);
 hipError_t launch_varlen_kvcache_bf16(const VarlenArgs& a, int d, hipStream_t s);  // mask: a.mask
+hipError_t launch_varlen_kvcache_qv_bf16(const VarlenArgs& a, hipStream_t s);  // d = dv = 128
 hipError_t launch_varlen_fp8(const VarlenArgs& a, int fmt, hipStream_t s);  // d = 128
 hipError_t launch_varlen_kvcache_fp8(const VarlenArgs& a, int fmt, hipStream_t s);  // d = 128
 // q.k + qv.v scores; fmt 0 bf16, 1 e4m3, 2 e5m2; d = dv = 128

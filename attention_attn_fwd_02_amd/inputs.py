@@ -195,11 +195,12 @@ class DenseKV(Dense):
 def varlen_kvcache(seed: int, lens_q, lens_new, lens_cache, hq: int = 32, hkv: int = 8,
                    d: int = 128, page: int = 64, causal: bool = True, window=(-1, -1),
                    scale: float | None = None, with_sinks: bool = False,
-                   spare_pages: int = 0) -> DenseKV:
+                   spare_pages: int = 0, with_qv: bool = False) -> DenseKV:
     """Chunked prefill: per sequence lens_q queries and lens_new current K/V
     rows (packed as in varlen), after lens_cache earlier rows held in a paged
     bf16 cache. The pool has spare_pages pages that no sequence references.
-    Draw order: Q, K, V, K cache, V cache, page permutation, sinks."""
+    Draw order: Q, K, V, K cache, V cache, page permutation, sinks, then qv
+    (Tq, Hq, D) when with_qv."""
     rng = np.random.default_rng(seed)
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_new = np.asarray(lens_new, dtype=np.int64)
@@ -221,9 +222,12 @@ def varlen_kvcache(seed: int, lens_q, lens_new, lens_cache, hq: int = 32, hkv: i
     sinks = rng.standard_normal(hq, dtype=np.float32) if with_sinks else None
     cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lens_new)]).astype(np.int32)
-    return DenseKV(q, k, v, cu_q, cu_k, "bf16", scale if scale is not None else 1.0 / np.sqrt(d),
-                   causal, tuple(window), sinks, k_cache=k_cache, v_cache=v_cache,
-                   block_table=table, cache_seqlens=lens_cache.astype(np.int32), page_size=page)
+    w = DenseKV(q, k, v, cu_q, cu_k, "bf16", scale if scale is not None else 1.0 / np.sqrt(d),
+                causal, tuple(window), sinks, k_cache=k_cache, v_cache=v_cache,
+                block_table=table, cache_seqlens=lens_cache.astype(np.int32), page_size=page)
+    if with_qv:
+        w.qv = _normal_bf16(rng, (tq, hq, d))
+    return w
 
 
 def chunked_prefill(seed: int = SEED_CHUNKED_PREFILL, nseq: int = 8, chunk: int = 1024,

@@ -221,6 +221,32 @@ int32_t attn_fwd_varlen_kvcache(const void* q, const void* k, const void* v,
                                 void* out, float* lse, void* stream);
 
 /*
+ * attn_fwd_varlen_kvcache_qv - attn_fwd_varlen_kvcache (bfloat16) with a
+ * second query qv scored against the value rows, cached and current.
+ * [MATE "Attention" page, FMHA notes: the optional qv input and only_qv
+ *  flag of the forward functions; Modular flash_attention_split_kv: cache and
+ *  current K/V as separate inputs]
+ *
+ *  qv (Tq, hq, dv) bf16: the score of query row r with key j is
+ *      scale * (q_r . k_j + qv_r . v_j), or scale * qv_r . v_j with
+ *      only_qv != 0 (q, k and k_cache are then not read and may be NULL).
+ *  The other arguments, the key sequence (cached rows first), the masks,
+ *  sinks, outputs and errors are those of attn_fwd_varlen_kvcache without
+ *  an additive mask.
+ *  Supported: d = dv = 128, page_size a multiple of 16.
+ */
+int32_t attn_fwd_varlen_kvcache_qv(const void* q, const void* qv, const void* k, const void* v,
+                                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_table, int32_t max_pages_per_seq,
+                                   const int32_t* cache_seqlens, int32_t page_size,
+                                   int32_t batch, int32_t max_seqlen_q, int32_t hq, int32_t hkv,
+                                   int32_t d, int32_t dv, float scale, int32_t causal,
+                                   int32_t window_left, int32_t window_right,
+                                   const float* sinks, int32_t only_qv, void* out, float* lse,
+                                   void* stream);
+
+/*
  * attn_fwd_varlen_kvcache_fp8 - attn_fwd_varlen_kvcache with FP8 Q, K, V and
  * caches (chunked / append prefill on FP8 inputs).
  * [MATE "Attention" page, FMHA forward dtype notes: the varlen and KV-cache

@@ -273,7 +273,8 @@ def attention_paged(q, k_cache, v_cache, block_table, cache_seqlens, page_size, 
 # --------------------------------------------------------------------------
 def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cache,
                              block_table, cache_seqlens, page_size, scale, causal=False,
-                             window=(-1, -1), sinks=None, seqs=None, mask=None):
+                             window=(-1, -1), sinks=None, seqs=None, mask=None, qv=None,
+                             only_qv=False):
     """Packed queries over a paged cache of earlier tokens plus the current
     K/V rows.                                   [MOJO flash_attention_split_kv]
 
@@ -284,6 +285,9 @@ def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cac
     cache rows 0..Lc-1 followed by the current rows, Lk = Lc + Ln; masks are
     those of attention_varlen over that sequence (bottom-right causal); mask
     columns are key positions of that sequence (cache rows first).
+    qv / only_qv: the second query scored against the value rows (cached and
+    current), as in attention_varlen [MATE FMHA notes: optional qv]; with
+    only_qv, k and k_cache are not read.
     Written as its definition: the concatenated K/V, then attention_varlen.
     Returns O (Tq, Hq, Dv) and LSE (Hq, Tq).
     """
@@ -291,15 +295,21 @@ def attention_varlen_kvcache(q, k, v, cu_seqlens_q, cu_seqlens_k, k_cache, v_cac
     ks, vs, cu = [], [], [0]
     for b in range(bsz):
         lc = int(cache_seqlens[b])
-        kb = np.concatenate([gather_paged(k_cache, block_table, b, lc, page_size),
-                             k[cu_seqlens_k[b]:cu_seqlens_k[b + 1]]])
         vb = np.concatenate([gather_paged(v_cache, block_table, b, lc, page_size),
                              v[cu_seqlens_k[b]:cu_seqlens_k[b + 1]]])
+        if only_qv:
+            ks.append(vb)
+            vs.append(vb)
+            cu.append(cu[-1] + len(vb))
+            continue
+        kb = np.concatenate([gather_paged(k_cache, block_table, b, lc, page_size),
+                             k[cu_seqlens_k[b]:cu_seqlens_k[b + 1]]])
         ks.append(kb)
         vs.append(vb)
         cu.append(cu[-1] + len(kb))
     return attention_varlen(q, np.concatenate(ks), np.concatenate(vs), cu_seqlens_q,
-                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs, mask)
+                            np.asarray(cu, np.int64), scale, causal, window, sinks, seqs, mask,
+                            qv=qv, only_qv=only_qv)
 
 
 # Plans of at most this many splits carry a longest-first work order; larger

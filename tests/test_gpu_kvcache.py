@@ -221,3 +221,43 @@ def test_kvcache_chunked_mask_workload():
         inputs.bits_to_f32(w.k_cache), inputs.bits_to_f32(w.v_cache), w.block_table,
         w.cache_seqlens, w.page_size, w.scale, True, seqs=[0, 4], mask=inputs.bits_to_f32(mbits))
     compare("kvcache_chunked_mask_workload", o, lse, ro, rl, TOL_O_BF16)
+
+
+QV_CASES = [
+    # name, lens_q, lens_new, lens_cache, hq, hkv, page, causal, window, sinks, only_qv
+    ("qv_straddle", [37, 200, 64], [37, 200, 64], [100, 333, 0], 8, 2, 64, True, (-1, -1),
+     False, False),
+    ("qv_page16_window", [70, 33], [70, 33], [190, 64], 4, 4, 16, False, (50, 20), False,
+     False),
+    ("qv_cache_only_keys", [4, 1], [0, 0], [300, 65], 8, 2, 32, False, (-1, -1), False, False),
+    ("qv_sinks_aligned", [64, 5], [64, 5], [512, 1024], 4, 2, 64, True, (-1, -1), True, False),
+    ("only_qv_straddle", [37, 200, 64], [37, 200, 64], [100, 333, 0], 8, 2, 64, True,
+     (-1, -1), False, True),
+    ("only_qv_page16_empty_seq", [30, 0, 70], [30, 0, 70], [20, 50, 0], 4, 2, 16, True,
+     (-1, -1), False, True),
+]
+
+
+@pytest.mark.parametrize("case", QV_CASES, ids=[c[0] for c in QV_CASES])
+def test_varlen_kvcache_qv(case):
+    """attn_fwd_varlen_kvcache_qv: scores q.k + qv.v (or qv.v alone) over the
+    cached and current rows, against the float64 oracle."""
+    name, lq, ln, lc, hq, hkv, page, causal, window, sinks, only_qv = case
+    log("case", name)
+    w = inputs.varlen_kvcache(5200 + len(name), lq, ln, lc, hq=hq, hkv=hkv, d=128, page=page,
+                              causal=causal, window=window, with_sinks=sinks, spare_pages=2,
+                              with_qv=True)
+    o, lse = B.attn_fwd_varlen_kvcache_qv(
+        None if only_qv else dev(w.q), dev(w.qv), None if only_qv else dev(w.k), dev(w.v),
+        dev(w.cu_seqlens_q), dev(w.cu_seqlens_k), None if only_qv else dev(w.k_cache),
+        dev(w.v_cache), dev(w.block_table), dev(w.cache_seqlens),
+        max(1, int(np.diff(w.cu_seqlens_q).max())), w.scale, w.causal, w.window,
+        None if w.sinks is None else dev(w.sinks), only_qv=only_qv)
+    torch.cuda.synchronize()
+    ro, rl = orc.attention_varlen_kvcache(
+        None if only_qv else w.f32("q"), None if only_qv else w.f32("k"), w.f32("v"),
+        w.cu_seqlens_q, w.cu_seqlens_k,
+        None if only_qv else inputs.bits_to_f32(w.k_cache), inputs.bits_to_f32(w.v_cache),
+        w.block_table, w.cache_seqlens, w.page_size, w.scale, w.causal, w.window, w.sinks,
+        qv=w.f32("qv"), only_qv=only_qv)
+    compare(name, o, lse, ro, rl, TOL_O_BF16)

@@ -381,6 +381,44 @@ def test_additive_mask():
     check_additive_mask()
 
 
+def check_kvcache_qv():
+    """qv over a cache plus current rows [MATE FMHA notes: qv; MOJO cache +
+    current K/V]. With K = 0 (cached and current) and qv = q the scores are
+    scale q.v, so the result is the plain cache-plus-current attention with V
+    in the role of K; only_qv with qv equals that attention with qv as the
+    query and V as the keys; with no cached rows it is attention_varlen with
+    the same qv; and qv = 0 leaves the plain result."""
+    q, k, v, cq, ck, kc, vc, table, lc, page = _kvcache_case(61, [4, 3, 2], [3, 4, 0], [5, 2, 6])
+    plain_vk = orc.attention_varlen_kvcache(q, v, v, cq, ck, vc, vc, table, lc, page, 0.6, True)
+    got = orc.attention_varlen_kvcache(q, np.zeros_like(k), v, cq, ck, np.zeros_like(kc), vc,
+                                       table, lc, page, 0.6, True, qv=q)
+    np.testing.assert_allclose(got[0], plain_vk[0], atol=1e-13)
+    np.testing.assert_allclose(got[1], plain_vk[1], atol=1e-13)
+    qv = _rng(62).standard_normal(q.shape)
+    only = orc.attention_varlen_kvcache(None, None, v, cq, ck, None, vc, table, lc, page, 0.6,
+                                        True, qv=qv, only_qv=True)
+    ref = orc.attention_varlen_kvcache(qv, v, v, cq, ck, vc, vc, table, lc, page, 0.6, True)
+    np.testing.assert_allclose(only[0], ref[0], atol=1e-13)
+    np.testing.assert_allclose(only[1], ref[1], atol=1e-13)
+    none = np.zeros(len(lc), np.int64)
+    a = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, none, page, 0.6, True, qv=qv)
+    b = orc.attention_varlen(q, k, v, cq, ck, 0.6, True, qv=qv)
+    np.testing.assert_allclose(a[0], b[0], atol=1e-13, equal_nan=True)
+    np.testing.assert_allclose(a[1], b[1], atol=1e-13, equal_nan=True)
+    z = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True,
+                                     qv=np.zeros_like(q))
+    base = orc.attention_varlen_kvcache(q, k, v, cq, ck, kc, vc, table, lc, page, 0.6, True)
+    np.testing.assert_allclose(z[0], base[0], atol=1e-13)
+    # a planted mistake (the qv term dropped) fails the first identity
+    bad = orc.attention_varlen_kvcache(q, np.zeros_like(k), v, cq, ck, np.zeros_like(kc), vc,
+                                       table, lc, page, 0.6, True)
+    assert not np.allclose(bad[0], plain_vk[0], atol=1e-6)
+
+
+def test_kvcache_qv():
+    check_kvcache_qv()
+
+
 def check_paged_mask():
     """Additive mask on the paged decode [MOJO input_mask_fn]: zeros change
     nothing; a constant c per (sequence, head) leaves O and adds c to LSE; a
